@@ -1,0 +1,195 @@
+/*
+ * muon.h - C ABI of the MI355X (gfx950) Muon-step library.
+ *
+ * The Muon step for a 2-D weight matrix is: momentum M <- mu M + G, an
+ * approximate polar factor O of M by Newton-Schulz iteration, and the weight
+ * update W <- W - lr (O + wd W).  Sources, cited by short name:
+ *
+ *   [GNS]   "优化器 (3)（Gram Newton-Schulz）", blog notes on Gram Newton-Schulz
+ *           (phycat-blog): §1.1 eq.(1) the step, §1.2 eq.(2) standard NS,
+ *           §2.3 Alg.1 naive Gram NS, §3.2 restarts, §3.3 fp16 and eq.(13),
+ *           §3.4 Alg.2 stabilised Gram NS.
+ *   [GRASP] notes on "Achieving low-bit Muon through subspace preservation and
+ *           grid quantization", overall framework: momentum, NS, update; the
+ *           full example adds weight decay.
+ *   [LiMuon] notes on LiMuon, design 3: the quintic (3.4445, -4.7750, 2.0315).
+ *   [MuonBlog] "Muon Optimizer" blog post, §1: Muon is for 2-D matrices.
+ *
+ * Conventions shared by every entry point:
+ *
+ *   Matrices are dense, row-major, contiguous (leading dimension = cols) and
+ *   live in device memory.  A call works on a batch of `batch` matrices of one
+ *   shape rows x cols; matrix arguments are DEVICE arrays of `batch` device
+ *   pointers (one per matrix), so independent tensors can be batched.  The
+ *   caller owns every buffer, including the workspace; the library allocates
+ *   no device memory.  A matrix with rows > cols is iterated transposed
+ *   ([GNS §1.2] works with n = min(rows, cols) <= m = max(rows, cols)); the
+ *   result has the input's shape.
+ *
+ *   Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  Results are valid after the stream is synchronised.  Calls on
+ *   one stream are ordered; calls that share a workspace must not overlap.
+ *
+ *   Errors: every argument is checked before anything is enqueued; on an
+ *   error a status other than MUON_OK is returned and no buffer is touched.
+ *   A failed launch returns MUON_ERR_HIP (buffers may then be partly written).
+ *   Nothing is printed and nothing aborts.  NaN/Inf in the inputs propagate
+ *   to the outputs.  A zero matrix gives O = 0 ([GNS §2.3 Alg.1]: eps keeps
+ *   the normalisation finite).
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+#define MUON_MAX_T 16
+#define MUON_MAX_DIM (1 << 20)
+
+/* Element types.  F32 = IEEE binary32, BF16 = bfloat16, F16 = IEEE binary16. */
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1, MUON_F16 = 2 } muon_dtype;
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1, /* bad shape, count, pointer, or parameter   */
+  MUON_ERR_UNSUPPORTED = 2, /* a dtype combination the library lacks     */
+  MUON_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required   */
+  MUON_ERR_HIP = 4          /* a HIP runtime call or launch failed       */
+} muon_status;
+
+typedef enum {
+  MUON_NS_STANDARD = 0, /* [GNS §1.2 eq.(2)]                              */
+  MUON_NS_GRAM = 1      /* [GNS §2.3 Alg.1] / [GNS §3.4 Alg.2] (restarts) */
+} muon_ns_variant;
+
+/*
+ * Newton-Schulz settings.  Fill with muon_ns_config_init() and change fields.
+ *
+ *   T            iterations, 1..MUON_MAX_T (the pages use 5).
+ *   coeffs       HOST pointer to T*3 floats (a_t, b_t, c_t) for t = 1..T, read
+ *                during the call only; NULL = (3.4445, -4.7750, 2.0315) for
+ *                every t ([LiMuon design 3]).
+ *   eps          X0 = X / (||X||_F + eps), default 1e-7 ([GNS §2.3 Alg.1]).
+ *   restart_mask Gram only: bit (t-1) set = restart after iteration t ([GNS
+ *                §3.2]); needs t < T.  Default 1u << 1 (after iteration 2, the
+ *                choice of [GNS §3.2] and [GNS §3.4 Alg.2]); 0 = Alg.1.
+ *                Ignored by the standard variant.
+ *   compute      MFMA operand type: MUON_BF16 (standard default), MUON_F16
+ *                (Gram default: [GNS §3.3] casts to float16), or MUON_F32 for
+ *                the slow fp32 check path (fp32 operands, fp64 accumulation).
+ *                Products always accumulate in fp32 or wider.
+ *   shift        1 (default): each iteration splits its a_t I term into a
+ *                diagonal shift a' (the mean of a_t + b_t l + c_t l^2 over the
+ *                eigenvalues l of the Gram matrix, from its trace and
+ *                Frobenius norm) that is applied in fp32, and the rest, which
+ *                is folded into the 16-bit operand.  Exact in real arithmetic;
+ *                it extends [GNS §3.3 eq.(13)] (keep the a_t arithmetic in
+ *                fp32) and cuts 16-bit rounding error.  0 = plain a_t.
+ */
+typedef struct muon_ns_config {
+  int32_t T;
+  const float *coeffs;
+  float eps;
+  uint32_t restart_mask;
+  muon_dtype compute;
+  int32_t shift;
+} muon_ns_config;
+
+/* Defaults for a variant (see above).  `cfg` must not be NULL. */
+void muon_ns_config_init(muon_ns_config *cfg, muon_ns_variant variant);
+
+/*
+ * Bytes of device workspace an orthogonalisation or step on `batch` matrices
+ * of rows x cols needs (the same figure for ns_orthogonalize,
+ * gram_ns_orthogonalize and muon_step with that variant).  Returns 0 when the
+ * arguments are invalid.  cfg NULL = defaults.
+ */
+size_t muon_workspace_size(int batch, int rows, int cols, muon_ns_variant variant,
+                           const muon_ns_config *cfg);
+
+/*
+ * Standard Newton-Schulz orthogonalisation [GNS §1.2 eq.(2)]:
+ *   X0 = X / (||X||_F + eps); for t = 1..T: A = X X^T, B = b_t A + c_t A^2,
+ *   X <- a_t X + B X; O = X_T.  Each matrix is normalised on its own.
+ *
+ *   M        device array of `batch` device pointers to rows x cols inputs of
+ *            type m_dtype (F32, BF16 or F16).  Not modified.
+ *   O        device array of `batch` device pointers to rows x cols outputs of
+ *            type o_dtype (F32 or BF16); must not alias M.
+ *   cfg      NULL = defaults of the standard variant.
+ *   workspace, ws_bytes  device buffer of at least muon_workspace_size() bytes,
+ *            256-byte aligned; contents on entry are ignored.
+ */
+muon_status ns_orthogonalize(int batch, int rows, int cols,
+                             const void *const *M, muon_dtype m_dtype,
+                             void *const *O, muon_dtype o_dtype,
+                             const muon_ns_config *cfg,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Gram Newton-Schulz orthogonalisation [GNS §2.3 Alg.1, §3.4 Alg.2]:
+ *   R = X0 X0^T, Q = I; for t = 1..T: Z = b_t R + c_t R^2, Q <- Q Z + a_t Q,
+ *   then a restart (X <- Q X, R = X X^T, Q = I) after the iterations in
+ *   restart_mask, otherwise RZ = R Z + a_t R, R <- Z RZ + a_t RZ (not done at
+ *   t = T); O = Q X.  Same arguments as ns_orthogonalize; cfg NULL = Gram
+ *   defaults (fp16 operands, restart after iteration 2).
+ */
+muon_status gram_ns_orthogonalize(int batch, int rows, int cols,
+                                  const void *const *M, muon_dtype m_dtype,
+                                  void *const *O, muon_dtype o_dtype,
+                                  const muon_ns_config *cfg,
+                                  void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One Muon step on a batch of same-shape weights ([GRASP framework], [GNS
+ * §1.1 eq.(1)], [MuonBlog §1]):
+ *   M <- mu M + G          (computed exactly in fp64, rounded to nearest even
+ *                           into state_dtype; M is updated in place)
+ *   O  = NS(M)             (variant and cfg as above, on the stored M)
+ *   W <- W - lr (O + weight_decay W)   (fp32 arithmetic, W updated in place)
+ *
+ *   W       device array of device pointers, rows x cols, w_dtype F32 or BF16.
+ *   M       device array of device pointers, momentum, state_dtype F32 or
+ *           BF16.  The first step of a run passes zeros (M_0 = 0).
+ *   G       device array of device pointers, gradients, state_dtype.
+ *   O_out   NULL, or a device array of device pointers that receive O in
+ *           o_dtype (F32 or BF16), e.g. for checking.
+ *   cfg     NULL = defaults of `variant`.
+ * W, M, G and O_out must not alias one another.
+ */
+muon_status muon_step(int batch, int rows, int cols,
+                      void *const *W, muon_dtype w_dtype,
+                      void *const *M, const void *const *G, muon_dtype state_dtype,
+                      float mu, float lr, float weight_decay,
+                      muon_ns_variant variant, const muon_ns_config *cfg,
+                      void *const *O_out, muon_dtype o_dtype,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Floating-point operations of one orthogonalisation of a rows x cols matrix
+ * ([GNS §1.2], §2.4, §3.4).  symmetric_aware = 1 counts half for products
+ * whose result is symmetric (only one triangle is computed): standard NS
+ * T(3 alpha + 1) n^3, Gram NS (17 + 3 alpha) n^3 with no restart and
+ * (14 + 6 alpha) n^3 with one restart at T = 5.  symmetric_aware = 0 gives the
+ * dense-equivalent count ((20 alpha + 10) n^3 for standard NS at T = 5).
+ * Returns 0 for invalid arguments.
+ */
+double muon_ns_flops(int rows, int cols, muon_ns_variant variant,
+                     const muon_ns_config *cfg, int symmetric_aware);
+
+/* Static description of a status code (never NULL). */
+const char *muon_status_string(muon_status status);
+
+/* MUON_ABI_VERSION of the loaded library. */
+int muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

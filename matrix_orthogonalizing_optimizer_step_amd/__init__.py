@@ -1,0 +1,8 @@
+"""MI355X-native Muon optimizer step: momentum, standard or Gram Newton-Schulz
+orthogonalisation and the weight update, in hand-written HIP kernels for
+gfx950 behind the C ABI of include/muon.h.  This package is the thin ctypes
+binding (``binding``) and the build script (``_build``)."""
+from .binding import (  # noqa: F401
+    BF16, F16, F32, GRAM, STANDARD, MuonError, NSConfig, abi_version, gram_ns_orthogonalize,
+    load_library, muon_step, ns_flops, ns_orthogonalize, pointer_array, workspace, workspace_size,
+)

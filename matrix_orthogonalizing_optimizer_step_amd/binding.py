@@ -1,0 +1,244 @@
+"""ctypes binding of ``libmuon.so`` (the C ABI in include/muon.h).
+
+Argument marshalling only: PyTorch supplies device memory and the stream;
+every step of the computation runs in the library's HIP kernels.  The
+functions keep the C names: ``ns_orthogonalize``, ``gram_ns_orthogonalize``
+and ``muon_step`` take lists of same-shape device tensors (one per matrix of
+the batch).  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon.so")
+
+F32, BF16, F16 = 0, 1, 2
+STANDARD, GRAM = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_DT_NAMES = {"f32": F32, "bf16": BF16, "f16": F16}
+_VARIANTS = {"standard": STANDARD, "gram": GRAM}
+
+
+class MuonError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"muon status {status}: {msg}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("coeffs", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("restart_mask", ctypes.c_uint32), ("compute", ctypes.c_int), ("shift", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libmuon.so once; raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m matrix_orthogonalizing_optimizer_step_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    cfgp = ctypes.POINTER(_Config)
+    lib.muon_ns_config_init.argtypes = [cfgp, i32]
+    lib.muon_ns_config_init.restype = None
+    lib.muon_workspace_size.argtypes = [i32, i32, i32, i32, cfgp]
+    lib.muon_workspace_size.restype = sz
+    sig = [i32, i32, i32, vp, i32, vp, i32, cfgp, vp, sz, vp]
+    for name in ("ns_orthogonalize", "gram_ns_orthogonalize"):
+        f = getattr(lib, name)
+        f.argtypes = sig
+        f.restype = i32
+    lib.muon_step.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, ctypes.c_float,
+                              ctypes.c_float, i32, cfgp, vp, i32, vp, sz, vp]
+    lib.muon_step.restype = i32
+    lib.muon_ns_flops.argtypes = [i32, i32, i32, cfgp, i32]
+    lib.muon_ns_flops.restype = ctypes.c_double
+    lib.muon_status_string.argtypes = [i32]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_abi_version.argtypes = []
+    lib.muon_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+@dataclass
+class NSConfig:
+    """Python view of muon_ns_config; None fields take the variant default."""
+    T: int = 5
+    coeffs: Optional[Sequence[Sequence[float]]] = None
+    eps: float = 1e-7
+    restart_mask: Optional[int] = None
+    compute: Optional[str] = None  # "bf16", "f16" or "f32"
+    shift: bool = True
+
+    def to_c(self, variant: int):
+        lib = load_library()
+        c = _Config()
+        lib.muon_ns_config_init(ctypes.byref(c), variant)
+        c.T = int(self.T)
+        c.eps = float(self.eps)
+        if self.restart_mask is not None:
+            c.restart_mask = int(self.restart_mask)
+        if self.compute is not None:
+            c.compute = _DT_NAMES[self.compute]
+        c.shift = 1 if self.shift else 0
+        keep = None
+        if self.coeffs is not None:
+            flat = [float(x) for row in self.coeffs for x in row]
+            keep = (ctypes.c_float * len(flat))(*flat)
+            c.coeffs = ctypes.cast(keep, ctypes.c_void_p)
+        return c, keep
+
+
+def _variant(v) -> int:
+    return _VARIANTS[v] if isinstance(v, str) else int(v)
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise MuonError(status, lib.muon_status_string(status).decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_ptr_cache: dict = {}
+
+
+def pointer_array(tensors: Sequence[torch.Tensor]) -> torch.Tensor:
+    """A device array holding the data pointers of ``tensors`` (cached)."""
+    ptrs = tuple(int(t.data_ptr()) for t in tensors)
+    dev = tensors[0].device
+    key = (str(dev), ptrs)
+    arr = _ptr_cache.get(key)
+    if arr is None:
+        if len(_ptr_cache) > 256:
+            _ptr_cache.clear()
+        arr = torch.tensor(ptrs, dtype=torch.int64).to(dev)
+        _ptr_cache[key] = arr
+    return arr
+
+
+def _batch(tensors: Sequence[torch.Tensor], name: str):
+    if len(tensors) == 0:
+        raise ValueError(f"{name}: empty batch")
+    t0 = tensors[0]
+    if t0.dim() != 2:
+        raise ValueError(f"{name}: matrices must be 2-D")
+    for t in tensors:
+        if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device:
+            raise ValueError(f"{name}: all matrices must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: matrices must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: matrices must be device tensors")
+    return t0.shape[0], t0.shape[1], _DT[t0.dtype]
+
+
+_ws_cache: dict = {}
+
+
+def workspace_size(batch: int, rows: int, cols: int, variant="standard", cfg: Optional[NSConfig] = None) -> int:
+    lib = load_library()
+    v = _variant(variant)
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    n = lib.muon_workspace_size(batch, rows, cols, v, ctypes.byref(c))
+    if n == 0:
+        raise MuonError(1, "invalid arguments for the workspace size")
+    return int(n)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A cached device byte buffer of at least ``nbytes`` (256-byte aligned)."""
+    key = str(torch.device(device))
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _orthogonalize(fname, variant, M, O, cfg, ws, stream):
+    lib = load_library()
+    rows, cols, mdt = _batch(M, "M")
+    _, _, odt = _batch(O, "O")
+    if tuple(O[0].shape) != (rows, cols) or len(O) != len(M):
+        raise ValueError("O must match M")
+    c, _keep = (cfg or NSConfig()).to_c(variant)
+    need = lib.muon_workspace_size(len(M), rows, cols, variant, ctypes.byref(c))
+    if ws is None:
+        ws = workspace(need, M[0].device)
+    pm, po = pointer_array(M), pointer_array(O)
+    st = getattr(lib, fname)(len(M), rows, cols, pm.data_ptr(), mdt, po.data_ptr(), odt, ctypes.byref(c),
+                             ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st)
+    return O
+
+
+def ns_orthogonalize(M, O, cfg: Optional[NSConfig] = None, workspace=None, stream=None):
+    """Standard Newton-Schulz of every matrix in ``M`` into ``O`` (lists of tensors)."""
+    return _orthogonalize("ns_orthogonalize", STANDARD, M, O, cfg, workspace, stream)
+
+
+def gram_ns_orthogonalize(M, O, cfg: Optional[NSConfig] = None, workspace=None, stream=None):
+    """Gram Newton-Schulz of every matrix in ``M`` into ``O`` (lists of tensors)."""
+    return _orthogonalize("gram_ns_orthogonalize", GRAM, M, O, cfg, workspace, stream)
+
+
+def muon_step(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant="standard",
+              cfg: Optional[NSConfig] = None, O_out=None, workspace=None, stream=None):
+    """One Muon step on lists of same-shape tensors; W and M are updated in place."""
+    lib = load_library()
+    v = _variant(variant)
+    rows, cols, wdt = _batch(W, "W")
+    r2, c2, sdt = _batch(M, "M")
+    r3, c3, gdt = _batch(G, "G")
+    if (r2, c2) != (rows, cols) or (r3, c3) != (rows, cols) or gdt != sdt:
+        raise ValueError("W, M and G must share the shape; M and G the dtype")
+    if not (len(W) == len(M) == len(G)):
+        raise ValueError("W, M and G must have one tensor per matrix")
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    need = lib.muon_workspace_size(len(W), rows, cols, v, ctypes.byref(c))
+    if workspace is None:
+        workspace = globals()["workspace"](need, W[0].device)
+    po, odt = None, F32
+    if O_out is not None:
+        _, _, odt = _batch(O_out, "O_out")
+        po = pointer_array(O_out)
+    pw, pm, pg = pointer_array(W), pointer_array(M), pointer_array(G)
+    st = lib.muon_step(len(W), rows, cols, pw.data_ptr(), wdt, pm.data_ptr(), pg.data_ptr(), sdt,
+                       float(mu), float(lr), float(weight_decay), v, ctypes.byref(c),
+                       po.data_ptr() if po is not None else None, odt,
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+
+
+def ns_flops(rows: int, cols: int, variant="standard", cfg: Optional[NSConfig] = None,
+             symmetric_aware: bool = True) -> float:
+    """FLOPs of one orthogonalisation (see muon_ns_flops in include/muon.h)."""
+    lib = load_library()
+    v = _variant(variant)
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    return float(lib.muon_ns_flops(rows, cols, v, ctypes.byref(c), 1 if symmetric_aware else 0))
+
+
+def abi_version() -> int:
+    return int(load_library().muon_abi_version())

@@ -1,0 +1,512 @@
+// Host side of the C ABI in include/muon.h: argument checks, workspace
+// layout and the launch schedule of the standard and Gram Newton-Schulz
+// iterations.  All work is enqueued on the caller's stream; nothing blocks.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};  // [LiMuon design 3]
+
+struct Config {
+  int T;
+  float c[MUON_MAX_T][3];
+  double eps;
+  uint32_t restart_mask;
+  int op;
+  int shift;
+};
+
+struct Plan {
+  int batch, rows, cols;
+  int n, m, n_pad, m_pad, transposed;
+  int op, esz, tile;
+  muon_ns_variant variant;
+  size_t XN, XT[2];
+  size_t A16, B16;                                        // standard
+  size_t R32, Q32, RZ32, R16, Z16, RZ16, Q16[2];          // Gram
+  size_t normpart, tilepart, shift;
+  size_t total;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(muon_dtype d) { return d == MUON_F32 || d == MUON_BF16 || d == MUON_F16; }
+
+muon_status make_config(const muon_ns_config* user, muon_ns_variant v, Config* out) {
+  muon_ns_config cfg;
+  if (user != nullptr) {
+    cfg = *user;
+  } else {
+    muon_ns_config_init(&cfg, v);
+  }
+  if (cfg.T < 1 || cfg.T > MUON_MAX_T) return MUON_ERR_INVALID_ARG;
+  if (!(cfg.eps >= 0.0f) || !isfinite(cfg.eps)) return MUON_ERR_INVALID_ARG;
+  if (cfg.shift != 0 && cfg.shift != 1) return MUON_ERR_INVALID_ARG;
+  if (!valid_dtype(cfg.compute)) return MUON_ERR_INVALID_ARG;
+  if (v == MUON_NS_GRAM && (cfg.restart_mask >> (cfg.T - 1)) != 0u) return MUON_ERR_INVALID_ARG;
+  out->T = cfg.T;
+  for (int t = 0; t < cfg.T; ++t) {
+    for (int k = 0; k < 3; ++k) {
+      const float x = cfg.coeffs != nullptr ? cfg.coeffs[3 * t + k] : kQuintic[k];
+      if (!isfinite(x)) return MUON_ERR_INVALID_ARG;
+      out->c[t][k] = x;
+    }
+  }
+  out->eps = cfg.eps;
+  out->restart_mask = v == MUON_NS_GRAM ? cfg.restart_mask : 0u;
+  out->op = cfg.compute == MUON_F32 ? kOpF32 : (cfg.compute == MUON_BF16 ? kOpBF16 : kOpF16);
+  out->shift = cfg.shift;
+  return MUON_OK;
+}
+
+// Workspace layout; returns false on invalid shapes or size overflow.
+bool make_plan(int batch, int rows, int cols, muon_ns_variant v, const Config& c, Plan* p) {
+  if (batch < 1 || rows < 1 || cols < 1 || rows > MUON_MAX_DIM || cols > MUON_MAX_DIM) return false;
+  if (v != MUON_NS_STANDARD && v != MUON_NS_GRAM) return false;
+  memset(p, 0, sizeof(*p));
+  p->batch = batch;
+  p->rows = rows;
+  p->cols = cols;
+  p->transposed = rows > cols;
+  p->n = p->transposed ? cols : rows;
+  p->m = p->transposed ? rows : cols;
+  p->n_pad = static_cast<int>(round_up(p->n, kPad));
+  p->m_pad = static_cast<int>(round_up(p->m, kPad));
+  p->op = c.op;
+  p->esz = c.op == kOpF32 ? 4 : 2;
+  p->tile = gemm_tile(c.op);
+  p->variant = v;
+  const double bytes_x = static_cast<double>(batch) * p->n_pad * p->m_pad * p->esz;
+  const double bytes_nn = static_cast<double>(batch) * p->n_pad * p->n_pad;
+  if (bytes_x * 3 + bytes_nn * 24 > 4.0e14) return false;  // far beyond any device
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = round_up(cur + bytes, 256);
+    return at;
+  };
+  const size_t nx = static_cast<size_t>(batch) * p->n_pad * p->m_pad;
+  const size_t nn = static_cast<size_t>(batch) * p->n_pad * p->n_pad;
+  p->XN = take(nx * p->esz);
+  p->XT[0] = take(nx * p->esz);
+  p->XT[1] = take(nx * p->esz);
+  if (v == MUON_NS_STANDARD) {
+    p->A16 = take(nn * p->esz);
+    p->B16 = take(nn * p->esz);
+  } else {
+    p->R32 = take(nn * 4);
+    p->Q32 = take(nn * 4);
+    p->RZ32 = take(nn * 4);
+    p->R16 = take(nn * p->esz);
+    p->Z16 = take(nn * p->esz);
+    p->RZ16 = take(nn * p->esz);
+    p->Q16[0] = take(nn * p->esz);
+    p->Q16[1] = take(nn * p->esz);
+  }
+  const int nt = p->n_pad / p->tile;
+  p->normpart = take(static_cast<size_t>(batch) * kNormBlocks * sizeof(double));
+  p->tilepart = take(static_cast<size_t>(batch) * nt * (nt + 1) / 2 * 2 * sizeof(double));
+  p->shift = take(static_cast<size_t>(batch) * sizeof(float));
+  p->total = cur;
+  return true;
+}
+
+GemmArgs base_args(const Plan& p) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.n_real = p.n;
+  g.m_real = p.m;
+  g.alpha_c = 1.0f;
+  return g;
+}
+
+// C = P P^T-style symmetric product of two n_pad x n_pad (or n_pad x K) operands.
+void set_sym(GemmArgs& g, const Plan& p, const void* P, const void* Q, int K, int64_t sPQ, int ld) {
+  g.Mdim = g.Ndim = p.n_pad;
+  g.K = K;
+  g.sym = 1;
+  g.P = P;
+  g.Q = Q;
+  g.sP = g.sQ = sPQ;
+  g.ldp = g.ldq = ld;
+  const int nt = p.n_pad / p.tile;
+  g.ntiles = nt * (nt + 1) / 2;
+  g.sO = static_cast<int64_t>(p.n_pad) * p.n_pad;
+  g.ldo = p.n_pad;
+  g.sE = g.sO;
+  g.lde = p.n_pad;
+}
+
+// C = P X with P an n_pad x n_pad operand and X given as X^T (m_pad x n_pad).
+void set_px(GemmArgs& g, const Plan& p, const void* P, const void* XT) {
+  g.Mdim = p.n_pad;
+  g.Ndim = p.m_pad;
+  g.K = p.n_pad;
+  g.sym = 0;
+  g.P = P;
+  g.sP = static_cast<int64_t>(p.n_pad) * p.n_pad;
+  g.ldp = p.n_pad;
+  g.Q = XT;
+  g.sQ = static_cast<int64_t>(p.m_pad) * p.n_pad;
+  g.ldq = p.n_pad;
+  g.ntiles = (p.n_pad / p.tile) * (p.m_pad / p.tile);
+  g.sO = static_cast<int64_t>(p.n_pad) * p.m_pad;
+  g.ldo = p.m_pad;
+  g.sE = g.sO;
+  g.lde = p.m_pad;
+  g.sOT = static_cast<int64_t>(p.m_pad) * p.n_pad;
+  g.ldot = p.n_pad;
+}
+
+struct Final {
+  void* const* W;
+  int w_dtype;
+  void* const* O;
+  int o_dtype;
+  float lr, wd;
+};
+
+void set_final(GemmArgs& g, const Plan& p, const Final& f) {
+  g.final_mode = 1;
+  g.W = f.W;
+  g.w_dtype = f.w_dtype;
+  g.Oout = f.O;
+  g.o_dtype = f.o_dtype;
+  g.transposed = p.transposed;
+  g.user_ld = p.cols;
+  g.lr = f.lr;
+  g.wd = f.wd;
+}
+
+#define MUON_LAUNCH(expr)                        \
+  do {                                           \
+    if ((expr) != hipSuccess) return MUON_ERR_HIP; \
+  } while (0)
+
+// Norm (and momentum), then X0 in both layouts.
+muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* const* M, int m_dtype,
+                         const void* const* G, void* const* Mw, double mu, hipStream_t s) {
+  NormArgs na;
+  na.M = M;
+  na.m_dtype = m_dtype;
+  na.G = G;
+  na.Mw = Mw;
+  na.mu = mu;
+  na.count = static_cast<int64_t>(p.rows) * p.cols;
+  na.partials = reinterpret_cast<double*>(ws + p.normpart);
+  MUON_LAUNCH(launch_norm(na, p.batch, s));
+  PrepArgs pa;
+  pa.M = Mw != nullptr ? reinterpret_cast<const void* const*>(Mw) : M;
+  pa.m_dtype = m_dtype;
+  pa.rows = p.rows;
+  pa.cols = p.cols;
+  pa.transposed = p.transposed;
+  pa.n = p.n;
+  pa.m = p.m;
+  pa.n_pad = p.n_pad;
+  pa.m_pad = p.m_pad;
+  pa.partials = na.partials;
+  pa.eps = c.eps;
+  pa.XN = ws + p.XN;
+  pa.sXN = static_cast<int64_t>(p.n_pad) * p.m_pad;
+  pa.XT = ws + p.XT[0];
+  pa.sXT = pa.sXN;
+  MUON_LAUNCH(launch_prep(pa, p.batch, p.op, s));
+  return MUON_OK;
+}
+
+// Standard Newton-Schulz ([GNS §1.2 eq.(2)]): per iteration A = X X^T,
+// B' = c A^2 + b A + (a - a') I, X <- a' X + B' X (a' = a without the shift).
+muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& f, hipStream_t s) {
+  const int64_t sx = static_cast<int64_t>(p.n_pad) * p.m_pad;
+  const int64_t snn = static_cast<int64_t>(p.n_pad) * p.n_pad;
+  double* tp = reinterpret_cast<double*>(ws + p.tilepart);
+  float* shift = reinterpret_cast<float*>(ws + p.shift);
+  const int nt = p.n_pad / p.tile;
+  const int ntri = nt * (nt + 1) / 2;
+  int xc = 0;
+  for (int t = 0; t < c.T; ++t) {
+    const float a = c.c[t][0], b = c.c[t][1], cc = c.c[t][2];
+    // A = X X^T
+    GemmArgs g = base_args(p);
+    set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
+    g.out16 = ws + p.A16;
+    g.part_out = c.shift ? tp : nullptr;
+    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    // B' = c A A + b A + (a - a') I
+    g = base_args(p);
+    set_sym(g, p, ws + p.A16, ws + p.A16, p.n_pad, snn, p.n_pad);
+    g.alpha_c = cc;
+    g.E16 = ws + p.A16;
+    g.beta_c = b;
+    g.gamma_c = a;
+    g.gamma_a = -1.0f;
+    g.coef_a = a;
+    g.coef_b = b;
+    g.coef_c = cc;
+    if (c.shift) {
+      g.part_in = tp;
+      g.npart_in = ntri;
+      g.shift_out = shift;
+    }
+    g.out16 = ws + p.B16;
+    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    // X <- a' X + B' X
+    g = base_args(p);
+    set_px(g, p, ws + p.B16, ws + p.XT[xc]);
+    g.E16 = ws + p.XN;
+    g.beta_a = 1.0f;
+    g.coef_a = a;
+    g.shift_in = c.shift ? shift : nullptr;
+    if (t + 1 < c.T) {
+      g.out16 = ws + p.XN;
+      g.outT16 = ws + p.XT[xc ^ 1];
+      xc ^= 1;
+    } else {
+      set_final(g, p, f);
+    }
+    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+  }
+  return MUON_OK;
+}
+
+// Gram Newton-Schulz ([GNS §2.3 Alg.1], [GNS §3.4 Alg.2]) with restarts.
+muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, hipStream_t s) {
+  const int64_t sx = static_cast<int64_t>(p.n_pad) * p.m_pad;
+  double* tp = reinterpret_cast<double*>(ws + p.tilepart);
+  float* shift = reinterpret_cast<float*>(ws + p.shift);
+  float* R32 = reinterpret_cast<float*>(ws + p.R32);
+  float* Q32 = reinterpret_cast<float*>(ws + p.Q32);
+  float* RZ32 = reinterpret_cast<float*>(ws + p.RZ32);
+  char* R16 = ws + p.R16;
+  char* Z16 = ws + p.Z16;
+  char* RZ16 = ws + p.RZ16;
+  const int64_t snn = static_cast<int64_t>(p.n_pad) * p.n_pad;
+  const int nt = p.n_pad / p.tile;
+  const int ntri = nt * (nt + 1) / 2;
+  int xc = 0, qc = 0;
+
+  auto gram_of_x = [&]() {  // R = X X^T (fp32 and operand copies) + partials
+    GemmArgs g = base_args(p);
+    set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
+    g.out32 = R32;
+    g.out16 = R16;
+    g.part_out = c.shift ? tp : nullptr;
+    return launch_gemm(g, p.batch, p.op, s);
+  };
+  MUON_LAUNCH(gram_of_x());
+  bool fresh = true;
+  for (int t = 1; t <= c.T; ++t) {
+    const float a = c.c[t - 1][0], b = c.c[t - 1][1], cc = c.c[t - 1][2];
+    // Z' = c R R + b R + (a - a') I; a fresh Q becomes Z' + a' I
+    GemmArgs g = base_args(p);
+    set_sym(g, p, R16, R16, p.n_pad, snn, p.n_pad);
+    g.alpha_c = cc;
+    g.E16 = R16;
+    g.beta_c = b;
+    g.gamma_c = a;
+    g.gamma_a = -1.0f;
+    g.coef_a = a;
+    g.coef_b = b;
+    g.coef_c = cc;
+    if (c.shift) {
+      g.part_in = tp;
+      g.npart_in = ntri;
+      g.shift_out = shift;
+    }
+    g.out16 = Z16;
+    if (fresh) {
+      g.q32 = Q32;
+      g.q16 = ws + p.Q16[qc];
+    }
+    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    const float* sh = c.shift ? shift : nullptr;
+    if (!fresh) {  // Q <- Q Z' + a' Q
+      g = base_args(p);
+      set_sym(g, p, ws + p.Q16[qc], Z16, p.n_pad, snn, p.n_pad);
+      g.E32 = Q32;
+      g.beta_a = 1.0f;
+      g.coef_a = a;
+      g.shift_in = sh;
+      g.out32 = Q32;
+      g.out16 = ws + p.Q16[qc ^ 1];
+      qc ^= 1;
+      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    }
+    fresh = false;
+    if (t < c.T && ((c.restart_mask >> (t - 1)) & 1u)) {
+      // restart: X <- Q X, R = X X^T, Q = I
+      g = base_args(p);
+      set_px(g, p, ws + p.Q16[qc], ws + p.XT[xc]);
+      g.out16 = ws + p.XN;
+      g.outT16 = ws + p.XT[xc ^ 1];
+      xc ^= 1;
+      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      MUON_LAUNCH(gram_of_x());
+      fresh = true;
+    } else if (t < c.T) {
+      // RZ = R Z' + a' R
+      g = base_args(p);
+      set_sym(g, p, R16, Z16, p.n_pad, snn, p.n_pad);
+      g.E32 = R32;
+      g.beta_a = 1.0f;
+      g.coef_a = a;
+      g.shift_in = sh;
+      g.out32 = RZ32;
+      g.out16 = RZ16;
+      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      // R <- Z' RZ + a' RZ
+      g = base_args(p);
+      set_sym(g, p, Z16, RZ16, p.n_pad, snn, p.n_pad);
+      g.E32 = RZ32;
+      g.beta_a = 1.0f;
+      g.coef_a = a;
+      g.shift_in = sh;
+      g.out32 = R32;
+      g.out16 = R16;
+      g.part_out = c.shift ? tp : nullptr;
+      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    }
+  }
+  // O = Q X
+  GemmArgs g = base_args(p);
+  set_px(g, p, ws + p.Q16[qc], ws + p.XT[xc]);
+  set_final(g, p, f);
+  MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+  return MUON_OK;
+}
+
+muon_status orthogonalize(muon_ns_variant v, int batch, int rows, int cols, const void* const* M,
+                          muon_dtype m_dtype, void* const* O, muon_dtype o_dtype,
+                          const muon_ns_config* cfg, void* workspace, size_t ws_bytes, void* stream) {
+  Config c;
+  muon_status st = make_config(cfg, v, &c);
+  if (st != MUON_OK) return st;
+  Plan p;
+  if (!make_plan(batch, rows, cols, v, c, &p)) return MUON_ERR_INVALID_ARG;
+  if (M == nullptr || O == nullptr) return MUON_ERR_INVALID_ARG;
+  if (reinterpret_cast<const void*>(M) == reinterpret_cast<const void*>(O)) return MUON_ERR_INVALID_ARG;
+  if (!valid_dtype(m_dtype)) return MUON_ERR_INVALID_ARG;
+  if (o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
+  if (workspace == nullptr || ws_bytes < p.total) return MUON_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = run_prologue(p, c, ws, M, m_dtype, nullptr, nullptr, 0.0, s);
+  if (st != MUON_OK) return st;
+  Final f{nullptr, 0, O, o_dtype, 0.0f, 0.0f};
+  return v == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_ns_config_init(muon_ns_config* cfg, muon_ns_variant variant) {
+  if (cfg == nullptr) return;
+  cfg->T = 5;
+  cfg->coeffs = nullptr;
+  cfg->eps = 1e-7f;
+  cfg->restart_mask = variant == MUON_NS_GRAM ? (1u << 1) : 0u;
+  cfg->compute = variant == MUON_NS_GRAM ? MUON_F16 : MUON_BF16;
+  cfg->shift = 1;
+}
+
+size_t muon_workspace_size(int batch, int rows, int cols, muon_ns_variant variant,
+                           const muon_ns_config* cfg) {
+  Config c;
+  if (make_config(cfg, variant, &c) != MUON_OK) return 0;
+  Plan p;
+  if (!make_plan(batch, rows, cols, variant, c, &p)) return 0;
+  return p.total;
+}
+
+muon_status ns_orthogonalize(int batch, int rows, int cols, const void* const* M, muon_dtype m_dtype,
+                             void* const* O, muon_dtype o_dtype, const muon_ns_config* cfg,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return orthogonalize(MUON_NS_STANDARD, batch, rows, cols, M, m_dtype, O, o_dtype, cfg, workspace,
+                       ws_bytes, stream);
+}
+
+muon_status gram_ns_orthogonalize(int batch, int rows, int cols, const void* const* M,
+                                  muon_dtype m_dtype, void* const* O, muon_dtype o_dtype,
+                                  const muon_ns_config* cfg, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  return orthogonalize(MUON_NS_GRAM, batch, rows, cols, M, m_dtype, O, o_dtype, cfg, workspace,
+                       ws_bytes, stream);
+}
+
+muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype w_dtype, void* const* M,
+                      const void* const* G, muon_dtype state_dtype, float mu, float lr,
+                      float weight_decay, muon_ns_variant variant, const muon_ns_config* cfg,
+                      void* const* O_out, muon_dtype o_dtype, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
+  Config c;
+  muon_status st = make_config(cfg, variant, &c);
+  if (st != MUON_OK) return st;
+  Plan p;
+  if (!make_plan(batch, rows, cols, variant, c, &p)) return MUON_ERR_INVALID_ARG;
+  if (W == nullptr || M == nullptr || G == nullptr) return MUON_ERR_INVALID_ARG;
+  const void* arrays[4] = {W, M, G, O_out};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (arrays[i] != nullptr && arrays[i] == arrays[j]) return MUON_ERR_INVALID_ARG;
+  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay)) return MUON_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_dtype(state_dtype)) return MUON_ERR_INVALID_ARG;
+  if (w_dtype == MUON_F16 || state_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
+  if (O_out != nullptr && o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
+  if (workspace == nullptr || ws_bytes < p.total) return MUON_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(M), state_dtype, G, M,
+                    static_cast<double>(mu), s);
+  if (st != MUON_OK) return st;
+  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay};
+  return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+}
+
+double muon_ns_flops(int rows, int cols, muon_ns_variant variant, const muon_ns_config* cfg,
+                     int symmetric_aware) {
+  Config c;
+  if (make_config(cfg, variant, &c) != MUON_OK) return 0.0;
+  if (rows < 1 || cols < 1) return 0.0;
+  const double n = rows < cols ? rows : cols;
+  const double m = rows < cols ? cols : rows;
+  const double n3 = n * n * n, mn2 = m * n * n;
+  const double T = c.T;
+  const double k = symmetric_aware ? 1.0 : 2.0;  // cost of a symmetric product relative to n^3 / m n^2
+  if (variant == MUON_NS_STANDARD) {
+    // per iteration: X X^T (m n^2, symmetric), A A (n^3, symmetric), B X (2 m n^2)
+    return T * (k * mn2 + k * n3 + 2.0 * mn2);
+  }
+  int r = 0;
+  for (int t = 1; t < c.T; ++t) r += (c.restart_mask >> (t - 1)) & 1u;
+  // R R every iteration; Q Z except when Q is fresh (t = 1 and after each
+  // restart); R Z and Z (RZ) for t < T without a restart; X X^T and Q X once
+  // plus once per restart.
+  const double rr = T, qz = T - 1 - r, upd = 2.0 * (T - 1 - r), sy = 1 + r, qx = 1 + r;
+  return k * (rr + qz + upd) * n3 + (k * sy + 2.0 * qx) * mn2;
+}
+
+const char* muon_status_string(muon_status status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported dtype combination";
+    case MUON_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MUON_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Element conversions with explicit rounding (round to nearest, ties to even).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 x;
+  __builtin_memcpy(&x, &h, 2);
+  return static_cast<float>(x);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 x = static_cast<_Float16>(f);  // v_cvt_f16_f32: round to nearest even
+  uint16_t h;
+  __builtin_memcpy(&h, &x, 2);
+  return h;
+}
+
+// float64 -> bfloat16 with a single rounding: round the binary64 significand
+// to 8 bits first (the result is then exact in binary32 and in bfloat16).
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  uint64_t au = u & 0x7fffffffffffffffull;
+  if (au > 0x7ff0000000000000ull) return static_cast<uint16_t>(((u >> 48) & 0x8000u) | 0x7fc0u);
+  int e = static_cast<int>(au >> 52) - 1023;
+  float f;
+  if (au == 0x7ff0000000000000ull) {
+    f = static_cast<float>(x);
+  } else if (e >= -126) {
+    const uint64_t half = 1ull << 44;
+    uint64_t low = u & ((1ull << 45) - 1);
+    uint64_t keep = u >> 45;
+    if (low > half || (low == half && (keep & 1ull))) keep += 1;
+    f = static_cast<float>(__longlong_as_double(static_cast<long long>(keep << 45)));
+  } else {
+    // bfloat16 subnormals: a fixed quantum of 2^-133
+    double q = rint(x * 0x1p133);
+    f = static_cast<float>(q * 0x1p-133);
+  }
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+// Storage dtype helpers for user buffers (0 = f32, 1 = bf16, 2 = f16).
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t idx, int dtype) {
+  if (dtype == 0) return static_cast<const float*>(p)[idx];
+  uint16_t h = static_cast<const uint16_t*>(p)[idx];
+  return dtype == 1 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+__device__ __forceinline__ void store_from_f32(void* p, int64_t idx, int dtype, float v) {
+  if (dtype == 0) {
+    static_cast<float*>(p)[idx] = v;
+  } else {
+    static_cast<uint16_t*>(p)[idx] = dtype == 1 ? f32_to_bf16(v) : f32_to_f16(v);
+  }
+}
+
+// Operand types: OP = 0 f32, 1 bf16, 2 f16.
+template <int OP> struct OpT;
+template <> struct OpT<0> {
+  using T = float;
+  static __device__ __forceinline__ float to_f(T x) { return x; }
+  static __device__ __forceinline__ T from_f(float x) { return x; }
+};
+template <> struct OpT<1> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float to_f(T x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ T from_f(float x) { return f32_to_bf16(x); }
+};
+template <> struct OpT<2> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float to_f(T x) { return f16_to_f32(x); }
+  static __device__ __forceinline__ T from_f(float x) { return f32_to_f16(x); }
+};
+
+}  // namespace muon

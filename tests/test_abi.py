@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/muon.h declares, validates arguments before touching the
+device, and its FLOP helper agrees with the oracle's counted products."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_orthogonalizing_optimizer_step_amd as mu
+from matrix_orthogonalizing_optimizer_step_amd import binding as bd
+from oracle import muon_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "muon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_library_exports_every_declared_function():
+    lib = mu.load_library()
+    names = header_functions()
+    assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert mu.abi_version() == 1
+
+
+def test_status_strings():
+    lib = mu.load_library()
+    for s in range(5):
+        assert lib.muon_status_string(s)
+    assert lib.muon_status_string(99) == b"unknown status"
+
+
+def test_default_config():
+    c, _ = bd.NSConfig().to_c(bd.STANDARD)
+    assert (c.T, c.restart_mask, c.compute, c.shift) == (5, 0, bd.BF16, 1)
+    assert abs(c.eps - 1e-7) < 1e-12
+    c, _ = bd.NSConfig().to_c(bd.GRAM)
+    assert (c.restart_mask, c.compute) == (2, bd.F16)
+
+
+@pytest.mark.parametrize("rows,cols", [(8, 8), (8, 32), (32, 8), (6, 18), (4, 32), (5, 7)])
+@pytest.mark.parametrize("variant,restarts", [("standard", ()), ("gram", ()), ("gram", (2,)),
+                                              ("gram", (1, 2, 3, 4)), ("gram", (1, 3))])
+def test_flop_helper_matches_oracle_count(rows, cols, variant, restarts):
+    mask = sum(1 << (t - 1) for t in restarts)
+    cfg = bd.NSConfig(restart_mask=mask)
+    d, s, _ = orc.counted_flops(rows, cols, variant, restarts=restarts)
+    assert mu.ns_flops(rows, cols, variant, cfg, symmetric_aware=True) == s
+    assert mu.ns_flops(rows, cols, variant, cfg, symmetric_aware=False) == d
+
+
+def test_workspace_size_validation():
+    assert mu.workspace_size(1, 256, 512) > 0
+    assert mu.workspace_size(3, 512, 256, "gram") == mu.workspace_size(3, 256, 512, "gram")
+    for args in [(0, 4, 4), (1, 0, 4), (1, 4, 0), (-1, 4, 4), (1, (1 << 20) + 1, 4)]:
+        with pytest.raises(bd.MuonError):
+            mu.workspace_size(*args)
+    for cfg in [bd.NSConfig(T=0), bd.NSConfig(T=17), bd.NSConfig(eps=-1.0), bd.NSConfig(eps=float("nan")),
+                bd.NSConfig(coeffs=[(1.0, float("inf"), 0.0)] * 5)]:
+        with pytest.raises(bd.MuonError):
+            mu.workspace_size(1, 4, 4, "standard", cfg)
+    # a restart needs a later iteration: bit (t-1) with t >= T is rejected
+    with pytest.raises(bd.MuonError):
+        mu.workspace_size(1, 4, 4, "gram", bd.NSConfig(T=2, restart_mask=1 << 1))
+    assert mu.workspace_size(1, 4, 4, "gram", bd.NSConfig(T=3, restart_mask=1 << 1)) > 0
+
+
+def _call_orth(lib, batch=1, rows=4, cols=4, M=1, mdt=0, O=2, odt=0, cfg=None, ws=256, wsb=1 << 30):
+    return lib.ns_orthogonalize(batch, rows, cols, M, mdt, O, odt, cfg, ws, wsb, None)
+
+
+def test_invalid_calls_fail_before_any_device_work():
+    """Each case is rejected by the host-side checks; no pointer is
+    dereferenced, so bogus addresses are safe here."""
+    lib = mu.load_library()
+    ok_ws = mu.workspace_size(1, 4, 4)
+    cases = [
+        (dict(batch=0), 1), (dict(rows=0), 1), (dict(cols=-3), 1),
+        (dict(M=None), 1), (dict(O=None), 1), (dict(O=1), 1),          # O aliases M
+        (dict(mdt=7), 1), (dict(odt=2), 2),                           # f16 output unsupported
+        (dict(ws=None), 3), (dict(wsb=ok_ws - 1), 3), (dict(ws=256 + 64), 3),
+    ]
+    for kw, code in cases:
+        assert _call_orth(lib, **kw) == code, kw
+    bad = bd._Config()
+    lib.muon_ns_config_init(ctypes.byref(bad), 0)
+    bad.T = 0
+    assert _call_orth(lib, cfg=ctypes.byref(bad)) == 1
+    bad.T = 5
+    bad.compute = 9
+    assert _call_orth(lib, cfg=ctypes.byref(bad)) == 1
+    bad.compute = 1
+    bad.shift = 3
+    assert _call_orth(lib, cfg=ctypes.byref(bad)) == 1
+
+
+def test_invalid_muon_step_calls():
+    lib = mu.load_library()
+    ws = mu.workspace_size(1, 4, 4)
+
+    def call(W=1, wdt=0, M=2, G=3, sdt=1, mu_=0.9, lr=0.1, wd=0.0, v=0, O=None, odt=0, wsb=ws):
+        return lib.muon_step(1, 4, 4, W, wdt, M, G, sdt, mu_, lr, wd, v, None, O, odt, 256, wsb, None)
+
+    assert call(W=None) == 1
+    assert call(M=1) == 1                 # aliasing
+    assert call(O=3) == 1                 # O_out aliases G
+    assert call(mu_=float("nan")) == 1
+    assert call(lr=float("inf")) == 1
+    assert call(sdt=2) == 2               # f16 state unsupported
+    assert call(wdt=2) == 2
+    assert call(O=4, odt=2) == 2
+    assert call(v=5) == 1
+    assert call(wsb=ws - 1) == 3
+
+
+def test_binding_rejects_bad_batches():
+    import torch
+    with pytest.raises(ValueError):
+        bd._batch([], "M")
+    with pytest.raises(ValueError):
+        bd._batch([torch.zeros(3)], "M")
+    with pytest.raises(ValueError):
+        bd._batch([torch.zeros(3, 3), torch.zeros(3, 4)], "M")
+    with pytest.raises(ValueError):
+        bd._batch([torch.zeros(3, 3)], "M")  # not a device tensor
