@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Muon-step benchmark on one MI355X.
+
+A step is one full Muon step (momentum, Newton-Schulz orthogonalisation,
+weight update) over every matrix of the workload, one library call per
+same-shape group.  The default workload is the Qwen2.5-7B-shaped layer set
+(q, o 3584x3584; k, v 3584x512; gate, up, down 3584x18944) with Gram
+Newton-Schulz (one restart after iteration 2, T = 5); the standard variant
+is timed beside it.  Inputs are seeded and synthetic (synth/inputs.py) and
+already resident in HBM when the timed region starts.
+
+Prints one JSON line.  ``value`` is the algorithmic (symmetric-aware)
+Newton-Schulz TFLOP/s of the whole step; the roofline block reports the
+dominant kernel from HIP events recorded around each launch on the launch
+stream; the cpu_baseline block times the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_16BIT_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_F32_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+METRIC = "NS orthogonalization TFLOP/s (% bf16 MFMA peak) + Muon steps/s per layer batch"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen2.5-7b")
+    ap.add_argument("--variant", default="gram", choices=["gram", "standard"])
+    ap.add_argument("--compute", default=None, help="operand type override: bf16, f16 or f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the step shards by "
+              "matrix ownership across GPUs, which this build does not run)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import matrix_orthogonalizing_optimizer_step_amd as mu
+    from synth import inputs as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = syn.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.key}: {wl.matrices} matrices, {wl.elements / 1e6:.1f}M elements")
+
+    # ---------------------------------------------------------------- inputs
+    groups = []
+    for gi, g in enumerate(wl.groups):
+        Ws, Ms, Gs = syn.group_inputs(wl, gi)
+        groups.append(dict(g=g, W=[w.to(dev) for w in Ws], M=[m.to(dev) for m in Ms], G=[x.to(dev) for x in Gs]))
+        log(f"[bench] group {g.name}: {g.count} x {g.rows}x{g.cols} uploaded")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def cfg_for(variant):
+        return mu.NSConfig(compute=args.compute)
+
+    def flops_for(variant, symmetric_aware=True):
+        return sum(x["g"].count * mu.ns_flops(x["g"].rows, x["g"].cols, variant, cfg_for(variant), symmetric_aware)
+                   for x in groups)
+
+    ws_bytes = max(mu.workspace_size(x["g"].count, x["g"].rows, x["g"].cols, v, cfg_for(v))
+                   for x in groups for v in ("gram", "standard"))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    log(f"[bench] workspace {ws_bytes / 2**30:.2f} GiB")
+
+    def step(variant):
+        for x in groups:
+            mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant), workspace=ws,
+                         stream=stream)
+
+    def timed(variant, steps, warmup):
+        for _ in range(warmup):
+            step(variant)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(variant)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def summary(variant, sec):
+        alg = flops_for(variant, True)
+        dense = flops_for(variant, False)
+        return {
+            "ms_per_step": sec * 1e3,
+            "tflops_algorithmic": alg / sec / 1e12,
+            "pct_of_16bit_peak": 100.0 * alg / sec / 1e12 / PEAK_16BIT_TFLOPS,
+            "tflops_dense_equivalent": dense / sec / 1e12,
+            "steps_per_s": 1.0 / sec,
+            "matrices_per_s": wl.matrices / sec,
+            "algorithmic_flops_per_step": alg,
+        }
+
+    results = {}
+    variants = [args.variant] + ([] if args.no_other_variant else [v for v in ("gram", "standard") if v != args.variant])
+    for v in variants:
+        sec = timed(v, args.steps, args.warmup)
+        results[v] = summary(v, sec)
+        log(f"[bench] {v}: {sec * 1e3:.3f} ms/step, {results[v]['tflops_algorithmic']:.1f} TFLOP/s")
+
+    # ------------------------------------------------ per-kernel durations (HIP events)
+    mu.trace_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(args.variant)
+    torch.cuda.synchronize()
+    traced_sec = (time.perf_counter() - t0) / args.steps
+    recs = mu.trace_collect()
+    mu.trace_enable(False)
+    kern = {}
+    for r in recs:
+        k = kern.setdefault(r["kernel"], dict(ms=0.0, flops=0.0, bytes=0.0, launches=0))
+        k["ms"] += r["ms"]
+        k["flops"] += r["flops"]
+        k["bytes"] += r["bytes"]
+        k["launches"] += 1
+    roles = {}
+    for r in recs:
+        key = f'{r["kernel"]}:{r["role"]}'
+        k = roles.setdefault(key, dict(ms=0.0, flops=0.0, launches=0))
+        k["ms"] += r["ms"] / args.steps
+        k["flops"] += r["flops"] / args.steps
+        k["launches"] += 1
+    dom_name, dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
+    avg_ms = dom["ms"] / dom["launches"]
+    is_mfma = dom["flops"] > 0
+    if is_mfma:
+        achieved = dom["flops"] / (dom["ms"] / 1e3) / 1e12
+        peak = PEAK_F32_TFLOPS if dom_name.endswith("f64acc") else PEAK_16BIT_TFLOPS
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                    "traffic": None, "kernel": dom_name, "launches_per_step": dom["launches"] // args.steps,
+                    "avg_launch_ms": avg_ms, "flops_per_launch": dom["flops"] / dom["launches"]}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom_name, "avg_launch_ms": avg_ms}
+    kernels = {k: {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] // args.steps,
+                   "avg_launch_ms": v["ms"] / v["launches"],
+                   "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None,
+                   "gbs": v["bytes"] / (v["ms"] / 1e3) / 1e9} for k, v in kern.items()}
+    role_tab = {k: {"ms_per_step": v["ms"], "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None}
+                for k, v in sorted(roles.items(), key=lambda kv: -kv[1]["ms"])}
+
+    # ------------------------------------------------ CPU baseline: the fp64 oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.variant, mu, syn)
+
+    primary = results[args.variant]
+    compute = args.compute or ("f16" if args.variant == "gram" else "bf16")
+    out = {
+        "metric": METRIC,
+        "value": primary["tflops_algorithmic"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": primary["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": compute,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.key} layer set: " + "; ".join(f"{g.count} x {g.rows}x{g.cols}" for g in wl.groups),
+            "variant": args.variant, "T": 5,
+            "restart_after_iteration": 2 if args.variant == "gram" else None,
+            "matrices": wl.matrices, "w_dtype": wl.w_dtype, "state_dtype": wl.state_dtype,
+            "value_counts": "symmetric-aware Newton-Schulz FLOPs of the whole step / step time",
+        },
+        "pct_of_16bit_peak": primary["pct_of_16bit_peak"],
+        "steps_per_s": primary["steps_per_s"],
+        "matrices_per_s": primary["matrices_per_s"],
+        "variants": results,
+        "roofline": roofline,
+        "kernels": kernels,
+        "roles": role_tab,
+        "traced_ms_per_step": traced_sec * 1e3,
+        "cpu_baseline": cpu,
+        "pages_context": {
+            "gram_ns_optimizer_time_saving": "up to 50% (Kimi K2, hardware not stated)",
+            "ns_runtime_reduction": "40-50% (Kimi K2, hardware not stated)",
+            "optimizer_share_of_step": "about 1-3% (distributed Muon, BF16, hardware not stated)",
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, variant, mu, syn):
+    """Time the fp64 oracle on one matrix per group (the first matrix of each)."""
+    import numpy as np
+
+    from oracle import muon_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    flops = 0.0
+    t0 = time.perf_counter()
+    names = []
+    for gi, g in enumerate(wl.groups):
+        Ws, Ms, Gs = syn.group_inputs(wl, gi, count=1)
+        W, M, G = (syn.to_f64(x[0]) for x in (Ws, Ms, Gs))
+        orc.muon_step(W, M, G, float(np.float32(0.95)), float(np.float32(0.02)), 0.0, variant,
+                      state_dtype=wl.state_dtype, w_dtype=wl.w_dtype)
+        flops += mu.ns_flops(g.rows, g.cols, variant, mu.NSConfig(), True)
+        names.append(f"{g.rows}x{g.cols}")
+    sec = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: {sec:.1f} s for {len(names)} matrices")
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"one Muon step ({variant} NS, fp64 numpy) on one matrix of each group: " + ", ".join(names),
+            "seconds": sec, "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

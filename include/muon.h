@@ -182,6 +182,32 @@ muon_status muon_step(int batch, int rows, int cols,
 double muon_ns_flops(int rows, int cols, muon_ns_variant variant,
                      const muon_ns_config *cfg, int symmetric_aware);
 
+/*
+ * Opt-in launch trace, for profiling.  While enabled, every kernel the
+ * library launches is bracketed by two hipEvents recorded on the call's
+ * stream, and tagged with its kernel, its role in the iteration and its
+ * algorithmic work: FLOPs (symmetric products count one triangle) and bytes
+ * (each operand read once, each output written once).  The library keeps this
+ * one piece of process-wide state; enabling or disabling clears it.
+ */
+typedef struct muon_trace_record {
+  char kernel[40]; /* kernel symbol family, e.g. "gemm_nt_mfma_f16"      */
+  char role[24];   /* e.g. "XXt", "A2", "BX", "ZRZ", "momentum_norm"     */
+  double flops;    /* algorithmic floating-point operations              */
+  double bytes;    /* algorithmic HBM bytes                              */
+  float ms;        /* measured duration between the two events           */
+} muon_trace_record;
+
+/* Turn the trace on (1) or off (0); returns the previous setting. */
+int muon_trace_enable(int enable);
+
+/*
+ * Wait for the recorded events, copy up to `max` records (oldest first) into
+ * `out` (may be NULL with max = 0) and return how many were recorded.  The
+ * records are then cleared.  Returns -1 if a HIP event call failed.
+ */
+int muon_trace_collect(muon_trace_record *out, int max);
+
 /* Static description of a status code (never NULL). */
 const char *muon_status_string(muon_status status);
 

@@ -34,6 +34,11 @@ class MuonError(RuntimeError):
         self.status = status
 
 
+class TraceRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 40), ("role", ctypes.c_char * 24), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("ms", ctypes.c_float)]
+
+
 class _Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("coeffs", ctypes.c_void_p), ("eps", ctypes.c_float),
                 ("restart_mask", ctypes.c_uint32), ("compute", ctypes.c_int), ("shift", ctypes.c_int32)]
@@ -69,6 +74,10 @@ def load_library():
     lib.muon_ns_flops.restype = ctypes.c_double
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_trace_enable.argtypes = [i32]
+    lib.muon_trace_enable.restype = i32
+    lib.muon_trace_collect.argtypes = [ctypes.POINTER(TraceRecord), i32]
+    lib.muon_trace_collect.restype = i32
     lib.muon_abi_version.argtypes = []
     lib.muon_abi_version.restype = i32
     _lib = lib
@@ -242,3 +251,24 @@ def ns_flops(rows: int, cols: int, variant="standard", cfg: Optional[NSConfig] =
 
 def abi_version() -> int:
     return int(load_library().muon_abi_version())
+
+
+def trace_enable(on: bool = True) -> bool:
+    """Turn the library's launch trace on or off (clears it); returns the old setting."""
+    return bool(load_library().muon_trace_enable(1 if on else 0))
+
+
+def trace_collect():
+    """Wait for the traced launches and return them as dicts (oldest first)."""
+    lib = load_library()
+    cap = 4096
+    while True:
+        buf = (TraceRecord * cap)()
+        n = lib.muon_trace_collect(buf, cap)
+        if n < 0:
+            raise MuonError(4, "trace event query failed")
+        recs = [dict(kernel=buf[i].kernel.decode(), role=buf[i].role.decode(), flops=buf[i].flops,
+                     bytes=buf[i].bytes, ms=float(buf[i].ms)) for i in range(min(n, cap))]
+        if n > cap:
+            raise MuonError(1, f"trace held {n} records, more than {cap}")
+        return recs

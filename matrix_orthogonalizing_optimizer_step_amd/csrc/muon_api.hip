@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/muon.h"
 #include "muon_internal.h"
 
@@ -35,6 +38,65 @@ struct Plan {
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// opt-in launch trace (muon_trace_enable / muon_trace_collect)
+// ---------------------------------------------------------------------------
+struct TraceRec {
+  muon_trace_record rec;
+  hipEvent_t e0, e1;
+};
+
+struct Trace {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TraceRec> recs;
+  std::vector<hipEvent_t> pool;
+} g_trace;
+
+hipEvent_t trace_event() {  // caller holds g_trace.mu
+  if (!g_trace.pool.empty()) {
+    hipEvent_t e = g_trace.pool.back();
+    g_trace.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void copy_name(char* dst, size_t n, const char* src) {
+  strncpy(dst, src, n - 1);
+  dst[n - 1] = '\0';
+}
+
+template <class F>
+hipError_t traced(hipStream_t s, const char* kernel, const char* role, double flops, double bytes,
+                  F&& launch) {
+  if (!g_trace.on) return launch();
+  std::lock_guard<std::mutex> lock(g_trace.mu);
+  TraceRec r;
+  memset(&r.rec, 0, sizeof(r.rec));
+  copy_name(r.rec.kernel, sizeof(r.rec.kernel), kernel);
+  copy_name(r.rec.role, sizeof(r.rec.role), role);
+  r.rec.flops = flops;
+  r.rec.bytes = bytes;
+  r.e0 = trace_event();
+  r.e1 = trace_event();
+  if (r.e0 == nullptr || r.e1 == nullptr) return hipErrorOutOfMemory;
+  hipError_t err = hipEventRecord(r.e0, s);
+  if (err != hipSuccess) return err;
+  err = launch();
+  if (err != hipSuccess) return err;
+  err = hipEventRecord(r.e1, s);
+  if (err != hipSuccess) return err;
+  g_trace.recs.push_back(r);
+  return hipSuccess;
+}
+
+const char* gemm_kernel_name(int op) {
+  return op == kOpBF16 ? "gemm_nt_mfma_bf16" : (op == kOpF16 ? "gemm_nt_mfma_f16" : "gemm_nt_f64acc");
+}
 
 bool valid_dtype(muon_dtype d) { return d == MUON_F32 || d == MUON_BF16 || d == MUON_F16; }
 
@@ -189,6 +251,39 @@ void set_final(GemmArgs& g, const Plan& p, const Final& f) {
     if ((expr) != hipSuccess) return MUON_ERR_HIP; \
   } while (0)
 
+// One GEMM launch with its algorithmic work for the trace: a symmetric
+// product counts one triangle (n^2 K FLOPs), a general one 2 n m K; bytes are
+// each operand read once plus each output written once (real sizes).
+hipError_t gemm(const Plan& p, const GemmArgs& g, const char* role, hipStream_t s) {
+  const double n = p.n, m = p.m, esz = p.esz;
+  double flops, bytes;
+  if (g.sym) {
+    const double K = g.K == p.m_pad ? m : n;
+    flops = n * n * K;
+    bytes = (g.P == g.Q ? 1.0 : 2.0) * n * K * esz;
+    if (g.E32 != nullptr) bytes += n * n * 4;
+    if (g.E16 != nullptr && g.E16 != g.P) bytes += n * n * esz;
+    if (g.out32 != nullptr) bytes += n * n * 4;
+    if (g.out16 != nullptr) bytes += n * n * esz;
+    if (g.q32 != nullptr) bytes += n * n * 4;
+    if (g.q16 != nullptr) bytes += n * n * esz;
+  } else {
+    flops = 2.0 * n * n * m;
+    bytes = n * n * esz + n * m * esz;
+    if (g.E16 != nullptr) bytes += n * m * esz;
+    if (g.out16 != nullptr) bytes += n * m * esz;
+    if (g.outT16 != nullptr) bytes += n * m * esz;
+    if (g.final_mode) {
+      const double wsz = g.w_dtype == kF32 ? 4 : 2;
+      if (g.W != nullptr) bytes += 2 * n * m * wsz;
+      if (g.Oout != nullptr) bytes += n * m * (g.o_dtype == kF32 ? 4 : 2);
+    }
+  }
+  if (g.final_mode) role = strcmp(role, "BX") == 0 ? "BX_final" : "QX_final";
+  return traced(s, gemm_kernel_name(p.op), role, flops * p.batch, bytes * p.batch,
+                [&] { return launch_gemm(g, p.batch, p.op, s); });
+}
+
 // Norm (and momentum), then X0 in both layouts.
 muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* const* M, int m_dtype,
                          const void* const* G, void* const* Mw, double mu, hipStream_t s) {
@@ -200,7 +295,13 @@ muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* c
   na.mu = mu;
   na.count = static_cast<int64_t>(p.rows) * p.cols;
   na.partials = reinterpret_cast<double*>(ws + p.normpart);
-  MUON_LAUNCH(launch_norm(na, p.batch, s));
+  {
+    const double cnt = static_cast<double>(na.count) * p.batch;
+    const double esz_m = m_dtype == kF32 ? 4 : 2;
+    const double bytes = cnt * esz_m * (G != nullptr ? 3.0 : 1.0);
+    MUON_LAUNCH(traced(s, "norm_kernel", G != nullptr ? "momentum_norm" : "norm", 0.0, bytes,
+                       [&] { return launch_norm(na, p.batch, s); }));
+  }
   PrepArgs pa;
   pa.M = Mw != nullptr ? reinterpret_cast<const void* const*>(Mw) : M;
   pa.m_dtype = m_dtype;
@@ -217,7 +318,11 @@ muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* c
   pa.sXN = static_cast<int64_t>(p.n_pad) * p.m_pad;
   pa.XT = ws + p.XT[0];
   pa.sXT = pa.sXN;
-  MUON_LAUNCH(launch_prep(pa, p.batch, p.op, s));
+  {
+    const double cnt = static_cast<double>(p.n) * p.m * p.batch;
+    const double bytes = cnt * ((m_dtype == kF32 ? 4 : 2) + 2.0 * p.esz);
+    MUON_LAUNCH(traced(s, "prep_kernel", "prep", 0.0, bytes, [&] { return launch_prep(pa, p.batch, p.op, s); }));
+  }
   return MUON_OK;
 }
 
@@ -238,7 +343,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
     g.out16 = ws + p.A16;
     g.part_out = c.shift ? tp : nullptr;
-    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    MUON_LAUNCH(gemm(p, g, "XXt", s));
     // B' = c A A + b A + (a - a') I
     g = base_args(p);
     set_sym(g, p, ws + p.A16, ws + p.A16, p.n_pad, snn, p.n_pad);
@@ -256,7 +361,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
       g.shift_out = shift;
     }
     g.out16 = ws + p.B16;
-    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    MUON_LAUNCH(gemm(p, g, "A2", s));
     // X <- a' X + B' X
     g = base_args(p);
     set_px(g, p, ws + p.B16, ws + p.XT[xc]);
@@ -271,7 +376,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     } else {
       set_final(g, p, f);
     }
-    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    MUON_LAUNCH(gemm(p, g, "BX", s));
   }
   return MUON_OK;
 }
@@ -298,7 +403,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
     g.out32 = R32;
     g.out16 = R16;
     g.part_out = c.shift ? tp : nullptr;
-    return launch_gemm(g, p.batch, p.op, s);
+    return gemm(p, g, "XXt", s);
   };
   MUON_LAUNCH(gram_of_x());
   bool fresh = true;
@@ -325,7 +430,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.q32 = Q32;
       g.q16 = ws + p.Q16[qc];
     }
-    MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+    MUON_LAUNCH(gemm(p, g, "Z", s));
     const float* sh = c.shift ? shift : nullptr;
     if (!fresh) {  // Q <- Q Z' + a' Q
       g = base_args(p);
@@ -337,7 +442,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.out32 = Q32;
       g.out16 = ws + p.Q16[qc ^ 1];
       qc ^= 1;
-      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      MUON_LAUNCH(gemm(p, g, "QZ", s));
     }
     fresh = false;
     if (t < c.T && ((c.restart_mask >> (t - 1)) & 1u)) {
@@ -347,7 +452,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.out16 = ws + p.XN;
       g.outT16 = ws + p.XT[xc ^ 1];
       xc ^= 1;
-      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      MUON_LAUNCH(gemm(p, g, "QX", s));
       MUON_LAUNCH(gram_of_x());
       fresh = true;
     } else if (t < c.T) {
@@ -360,7 +465,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.shift_in = sh;
       g.out32 = RZ32;
       g.out16 = RZ16;
-      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      MUON_LAUNCH(gemm(p, g, "RZ", s));
       // R <- Z' RZ + a' RZ
       g = base_args(p);
       set_sym(g, p, Z16, RZ16, p.n_pad, snn, p.n_pad);
@@ -371,14 +476,14 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.out32 = R32;
       g.out16 = R16;
       g.part_out = c.shift ? tp : nullptr;
-      MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+      MUON_LAUNCH(gemm(p, g, "ZRZ", s));
     }
   }
   // O = Q X
   GemmArgs g = base_args(p);
   set_px(g, p, ws + p.Q16[qc], ws + p.XT[xc]);
   set_final(g, p, f);
-  MUON_LAUNCH(launch_gemm(g, p.batch, p.op, s));
+  MUON_LAUNCH(gemm(p, g, "QX", s));
   return MUON_OK;
 }
 
@@ -508,5 +613,34 @@ const char* muon_status_string(muon_status status) {
 }
 
 int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+int muon_trace_enable(int enable) {
+  std::lock_guard<std::mutex> lock(g_trace.mu);
+  const int prev = g_trace.on ? 1 : 0;
+  for (TraceRec& r : g_trace.recs) {
+    g_trace.pool.push_back(r.e0);
+    g_trace.pool.push_back(r.e1);
+  }
+  g_trace.recs.clear();
+  g_trace.on = enable != 0;
+  return prev;
+}
+
+int muon_trace_collect(muon_trace_record* out, int max) {
+  std::lock_guard<std::mutex> lock(g_trace.mu);
+  int failed = 0;
+  const int count = static_cast<int>(g_trace.recs.size());
+  for (int i = 0; i < count; ++i) {
+    TraceRec& r = g_trace.recs[i];
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) failed = 1;
+    r.rec.ms = ms;
+    if (out != nullptr && i < max) out[i] = r.rec;
+    g_trace.pool.push_back(r.e0);
+    g_trace.pool.push_back(r.e1);
+  }
+  g_trace.recs.clear();
+  return failed ? -1 : count;
+}
 
 }  // extern "C"
