@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--compute", default=None, help="operand type override: bf16, f16 or f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="issue every group on one stream (default: one stream per group)")
     return ap.parse_args()
 
 
@@ -72,7 +74,6 @@ def main():
         groups.append(dict(g=g, W=[w.to(dev) for w in Ws], M=[m.to(dev) for m in Ms], G=[x.to(dev) for x in Gs]))
         log(f"[bench] group {g.name}: {g.count} x {g.rows}x{g.cols} uploaded")
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
 
     def cfg_for(variant):
         return mu.NSConfig(compute=args.compute)
@@ -81,15 +82,36 @@ def main():
         return sum(x["g"].count * mu.ns_flops(x["g"].rows, x["g"].cols, variant, cfg_for(variant), symmetric_aware)
                    for x in groups)
 
-    ws_bytes = max(mu.workspace_size(x["g"].count, x["g"].rows, x["g"].cols, v, cfg_for(v))
-                   for x in groups for v in ("gram", "standard"))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    log(f"[bench] workspace {ws_bytes / 2**30:.2f} GiB")
-
-    def step(variant):
+    # The groups are independent: each gets its own stream (default priority)
+    # and workspace so their launches overlap; the step ends when all are done.
+    main = torch.cuda.current_stream()
+    total_ws = 0
+    for x in groups:
+        nb = max(mu.workspace_size(x["g"].count, x["g"].rows, x["g"].cols, v, cfg_for(v)) for v in ("gram", "standard"))
+        x["ws"] = torch.empty(nb, dtype=torch.uint8, device=dev)
+        x["stream"] = main if args.one_stream else torch.cuda.Stream(device=dev)
+        total_ws += nb
+    if args.one_stream:
+        shared = max(groups, key=lambda x: x["ws"].numel())["ws"]
         for x in groups:
-            mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant), workspace=ws,
-                         stream=stream)
+            x["ws"] = shared
+    log(f"[bench] workspace {total_ws / 2**30:.2f} GiB, {'one stream' if args.one_stream else 'one stream per group'}")
+
+    def step(variant, serial=False):
+        serial = serial or args.one_stream
+        if not serial:
+            ev = torch.cuda.Event()
+            ev.record(main)
+        for x in groups:
+            if not serial:
+                x["stream"].wait_event(ev)
+            mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant), workspace=x["ws"],
+                         stream=main if serial else x["stream"])
+        if not serial:
+            for x in groups:
+                done = torch.cuda.Event()
+                done.record(x["stream"])
+                main.wait_event(done)
 
     def timed(variant, steps, warmup):
         for _ in range(warmup):
@@ -122,10 +144,12 @@ def main():
         log(f"[bench] {v}: {sec * 1e3:.3f} ms/step, {results[v]['tflops_algorithmic']:.1f} TFLOP/s")
 
     # ------------------------------------------------ per-kernel durations (HIP events)
+    # The traced steps run the groups back to back on one stream so that each
+    # launch's event pair measures that kernel alone on the GPU.
     mu.trace_enable(True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(args.variant)
+        step(args.variant, serial=True)
     torch.cuda.synchronize()
     traced_sec = (time.perf_counter() - t0) / args.steps
     recs = mu.trace_collect()
@@ -190,6 +214,7 @@ def main():
             "restart_after_iteration": 2 if args.variant == "gram" else None,
             "matrices": wl.matrices, "w_dtype": wl.w_dtype, "state_dtype": wl.state_dtype,
             "value_counts": "symmetric-aware Newton-Schulz FLOPs of the whole step / step time",
+            "streams": 1 if args.one_stream else len(groups),
         },
         "pct_of_16bit_peak": primary["pct_of_16bit_peak"],
         "steps_per_s": primary["steps_per_s"],
@@ -199,6 +224,7 @@ def main():
         "kernels": kernels,
         "roles": role_tab,
         "traced_ms_per_step": traced_sec * 1e3,
+        "traced_note": "traced steps run the groups serially on one stream (per-kernel event timing)",
         "cpu_baseline": cpu,
         "pages_context": {
             "gram_ns_optimizer_time_saving": "up to 50% (Kimi K2, hardware not stated)",

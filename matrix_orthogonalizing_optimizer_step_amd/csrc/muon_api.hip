@@ -147,6 +147,8 @@ bool make_plan(int batch, int rows, int cols, muon_ns_variant v, const Config& c
   const double bytes_x = static_cast<double>(batch) * p->n_pad * p->m_pad * p->esz;
   const double bytes_nn = static_cast<double>(batch) * p->n_pad * p->n_pad;
   if (bytes_x * 3 + bytes_nn * 24 > 4.0e14) return false;  // far beyond any device
+  // the GEMM addresses one operand matrix with 32-bit byte offsets
+  if (static_cast<double>(p->n_pad) * p->m_pad * p->esz >= 2147483648.0) return false;
   size_t cur = 0;
   auto take = [&](size_t bytes) {
     const size_t at = cur;

@@ -87,4 +87,19 @@ template <> struct OpT<2> {
   static __device__ __forceinline__ T from_f(float x) { return f32_to_f16(x); }
 };
 
+// Element index of (r, k) in an operand buffer with row length K.  16-bit
+// operands: packed fragment layout, blocks of 32 rows x 64 k (4 KB) ordered by
+// (row block, k block); inside, four 1 KB MFMA fragments (k-steps of 16), each
+// holding lane l = 32 * ((k % 16) / 8) + r % 32 with 8 consecutive k.  fp32
+// (check path): row-major.
+template <int OP>
+__device__ __forceinline__ int64_t op_index(int r, int k, int K) {
+  if constexpr (OP == 0) {
+    return static_cast<int64_t>(r) * K + k;
+  } else {
+    return ((static_cast<int64_t>(r >> 5) * (K >> 6) + (k >> 6)) << 11) + (((k >> 4) & 3) << 9) +
+           (((((k >> 3) & 1) << 5) | (r & 31)) << 3) + (k & 7);
+  }
+}
+
 }  // namespace muon

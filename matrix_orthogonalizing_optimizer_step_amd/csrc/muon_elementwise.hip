@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void norm_kernel(NormArgs a) {
 }
 
 // X0 = M / (||M||_F + eps) rounded to the operand type, written as X (n_pad x
-// m_pad) and X^T (m_pad x n_pad) with zero padding.  X = M, or M^T when the
+// m_pad) and X^T (m_pad x n_pad) in the operand layout (op_index) with zero
+// padding.  X = M, or M^T when the
 // user matrix has more rows than columns.  One 64 x 64 tile per block, staged
 // through LDS so both layouts are written with coalesced stores.
 template <int D, int OP>
@@ -147,10 +148,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     const int r = e >> 6, c = e & 63;
     // X[i0 + r][j0 + c]
     const float xn = a.transposed ? tile[c][r] : tile[r][c];
-    XN[static_cast<int64_t>(i0 + r) * a.m_pad + j0 + c] = O::from_f(xn);
+    XN[op_index<OP>(i0 + r, j0 + c, a.m_pad)] = O::from_f(xn);
     // X^T[j0 + r][i0 + c] = X[i0 + c][j0 + r]
     const float xt = a.transposed ? tile[r][c] : tile[c][r];
-    XT[static_cast<int64_t>(j0 + r) * a.n_pad + i0 + c] = O::from_f(xt);
+    XT[op_index<OP>(j0 + r, i0 + c, a.n_pad)] = O::from_f(xt);
   }
 }
 

@@ -2,8 +2,7 @@
 //
 // Every product of the standard and Gram Newton-Schulz iterations ([GNS §1.2]
 // and [GNS §2.3-3.4] of the Gram Newton-Schulz notes) is written in the
-// "NT" form C[i][j] = sum_k P[i][k] Q[j][k] with both operands contiguous
-// along k:
+// "NT" form C[i][j] = sum_k P[i][k] Q[j][k] over k:
 //   X X^T            P = Q = X (n x m)                      symmetric
 //   A A, R R, Q Z,   P, Q symmetric n x n (Q^T = Q)         symmetric
 //   R Z, Z (RZ)
@@ -13,8 +12,12 @@
 // on or below the diagonal and store each value at (i, j) and (j, i), the
 // triangle-only scheme the notes describe for their symmetric GEMM [GNS §4].
 //
-// 16-bit operands run on CDNA4 MFMA (v_mfma_f32_32x32x16_{bf16,f16}) with
-// fp32 accumulation; the fp32 check path accumulates fp32 operands in fp64.
+// 16-bit operands are stored in a packed fragment layout (op_index below):
+// each 32-row x 16-k block is 1 KB in the lane order of the MFMA operand, so
+// a wave fetches a fragment with one contiguous 16-byte-per-lane access,
+// from global memory or from LDS.  They run on CDNA4 MFMA
+// (v_mfma_f32_32x32x16_{bf16,f16}) with fp32 accumulation.  The fp32 check
+// path keeps row-major fp32 operands and accumulates in fp64.
 #include "muon_convert.h"
 #include "muon_internal.h"
 
@@ -113,97 +116,19 @@ __device__ void block_partials(const GemmArgs& a, int b, int tile, double* red, 
   }
 }
 
-// Epilogue, first half, for element (i, j) of matrix b (for symmetric
-// products only i >= j is passed): v = alpha acc + beta E + gamma [i == j];
-// stores v (and a fresh Q) at (i, j), accumulates the partial sums, and in
-// the last product updates W (unless W is stored transposed, see epi_mirror).
-template <int OP>
-__device__ __forceinline__ float epi_value(const GemmArgs& a, int b, int i, int j, float acc, EpiState& st) {
-  using O = OpT<OP>;
-  using T = typename O::T;
-  float e = 0.0f;
-  const int64_t ie = static_cast<int64_t>(b) * a.sE + static_cast<int64_t>(i) * a.lde + j;
-  if (a.E32 != nullptr) {
-    e = a.E32[ie];
-  } else if (a.E16 != nullptr) {
-    e = O::to_f(static_cast<const T*>(a.E16)[ie]);
-  }
-  const bool diag = (i == j) && (i < a.n_real);
-  float v = st.alpha * acc + st.beta * e;
-  if (diag) v += st.gamma;
-  if (a.final_mode) {
-    if (!a.transposed && i < a.n_real && j < a.m_real) {
-      const int64_t idx = static_cast<int64_t>(i) * a.user_ld + j;
-      if (a.W != nullptr) {
-        void* w = a.W[b];
-        const float wv = load_as_f32(w, idx, a.w_dtype);
-        store_from_f32(w, idx, a.w_dtype, wv - a.lr * (v + a.wd * wv));
-      }
-      if (a.Oout != nullptr) store_from_f32(a.Oout[b], idx, a.o_dtype, v);
-    }
-    return v;
-  }
-  const int64_t o = static_cast<int64_t>(b) * a.sO + static_cast<int64_t>(i) * a.ldo + j;
-  if (a.out32 != nullptr) a.out32[o] = v;
-  if (a.out16 != nullptr) static_cast<T*>(a.out16)[o] = O::from_f(v);
-  if (a.q32 != nullptr || a.q16 != nullptr) {
-    const float q = diag ? v + st.ap : v;
-    if (a.q32 != nullptr) a.q32[o] = q;
-    if (a.q16 != nullptr) static_cast<T*>(a.q16)[o] = O::from_f(q);
-  }
-  if (a.part_out != nullptr && i < a.n_real && j < a.n_real) {
-    if (diag) st.tr += v;
-    st.ss += static_cast<double>(v) * v * ((a.sym && i != j) ? 2.0 : 1.0);
-  }
-  return v;
-}
-
-// Whether the transposed pass has work: mirrored symmetric stores, the X^T
-// copy, or the update of a weight stored transposed.
+// ---------------------------------------------------------------------------
+// Epilogue helpers.  The staged epilogue computes, per element of C,
+//   v = alpha * C + beta * E[i][j] + gamma * [i == j < n_real]
+// (alpha, beta, gamma affine in the diagonal shift a'), stores v in fp32
+// and/or the 16-bit operand layout, a fresh Q = v + a' I, the per-tile trace
+// and sum of squares, the transposed copy X^T, and in the last product the
+// update of W.  For symmetric products a block owns the elements with i >= j
+// and mirrors them to (j, i).
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ bool epi_has_mirror(const GemmArgs& a) {
   return a.final_mode ? a.transposed != 0 : (a.sym != 0 || a.outT16 != nullptr);
 }
 
-// Epilogue, second half: the stores at (j, i).
-template <int OP>
-__device__ __forceinline__ void epi_mirror(const GemmArgs& a, int b, int i, int j, float v, const EpiState& st) {
-  using O = OpT<OP>;
-  using T = typename O::T;
-  if (a.final_mode) {
-    if (i < a.n_real && j < a.m_real) {
-      const int64_t idx = static_cast<int64_t>(j) * a.user_ld + i;
-      if (a.W != nullptr) {
-        void* w = a.W[b];
-        const float wv = load_as_f32(w, idx, a.w_dtype);
-        store_from_f32(w, idx, a.w_dtype, wv - a.lr * (v + a.wd * wv));
-      }
-      if (a.Oout != nullptr) store_from_f32(a.Oout[b], idx, a.o_dtype, v);
-    }
-    return;
-  }
-  if (a.sym) {
-    if (i == j) return;
-    const bool diag = false;
-    const int64_t oT = static_cast<int64_t>(b) * a.sO + static_cast<int64_t>(j) * a.ldo + i;
-    if (a.out32 != nullptr) a.out32[oT] = v;
-    if (a.out16 != nullptr) static_cast<T*>(a.out16)[oT] = O::from_f(v);
-    if (a.q32 != nullptr) a.q32[oT] = diag ? v + st.ap : v;
-    if (a.q16 != nullptr) static_cast<T*>(a.q16)[oT] = O::from_f(v);
-    return;
-  }
-  if (a.outT16 != nullptr) {
-    static_cast<T*>(a.outT16)[static_cast<int64_t>(b) * a.sOT + static_cast<int64_t>(j) * a.ldot + i] =
-        O::from_f(v);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Vectorised epilogue over a 32 x TN block of one wave's sub-tile, staged in
-// LDS (row-major, leading dimension LDE floats).  Pass 1 gives each lane four
-// consecutive columns of a row, batches the loads of several rows before any
-// arithmetic, and stores at (i, j); pass 2 gives each lane four consecutive
-// rows of a column for the stores at (j, i).
-// ---------------------------------------------------------------------------
 template <int OP>
 __device__ __forceinline__ float4 load4_op(const void* base, int64_t idx) {
   if constexpr (OP == kOpF32) {
@@ -225,6 +150,15 @@ __device__ __forceinline__ void store4_op(void* base, int64_t idx, float4 v) {
     h.x = static_cast<uint32_t>(O::from_f(v.x)) | (static_cast<uint32_t>(O::from_f(v.y)) << 16);
     h.y = static_cast<uint32_t>(O::from_f(v.z)) | (static_cast<uint32_t>(O::from_f(v.w)) << 16);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = h;
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ void store1_op(void* base, int64_t idx, float v) {
+  if constexpr (OP == kOpF32) {
+    static_cast<float*>(base)[idx] = v;
+  } else {
+    static_cast<uint16_t*>(base)[idx] = OpT<OP>::from_f(v);
   }
 }
 
@@ -282,10 +216,15 @@ __device__ __forceinline__ void final_update4(const GemmArgs& a, int b, int64_t 
   if (a.Oout != nullptr) user_store4(a.Oout[b], idx, a.o_dtype, valid, o);
 }
 
+// Epilogue over a 32 x TN block of C staged in LDS (row-major, leading
+// dimension LDE floats), rows i0.., columns j0..  Pass 1 gives each lane four
+// consecutive columns of a row (loads of several rows are issued before any
+// arithmetic) and stores at (i, j); pass 2 gives each lane four consecutive
+// rows of a column for the stores at (j, i).  All threads of the block call
+// it (it contains a barrier).
 template <int OP, int TN, int LDE>
 __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiState& st, float* ep, int i0, int j0,
                                                int lane, bool mirror) {
-  using T = typename OpT<OP>::T;
   constexpr int LPR = TN / 4;        // lanes per row in pass 1
   constexpr int RPIT = 64 / LPR;     // rows per pass-1 iteration
   constexpr int NIT = 32 / RPIT;
@@ -294,6 +233,8 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
   const int rl = lane / LPR;
   const bool has_e = a.E32 != nullptr || a.E16 != nullptr;
   const bool wrow = a.final_mode && !a.transposed && a.W != nullptr;
+  const int64_t bE = static_cast<int64_t>(b) * a.sE;
+  const int64_t bO = static_cast<int64_t>(b) * a.sO;
   for (int it0 = 0; it0 < NIT; it0 += UNR) {
     float4 ev[UNR], wv[UNR];
 #pragma unroll
@@ -301,8 +242,8 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       const int i = i0 + (it0 + u) * RPIT + rl, j = j0 + cl;
       ev[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       wv[u] = ev[u];
-      const int64_t ie = static_cast<int64_t>(b) * a.sE + static_cast<int64_t>(i) * a.lde + j;
-      if (has_e) ev[u] = a.E32 != nullptr ? load4_op<kOpF32>(a.E32, ie) : load4_op<OP>(a.E16, ie);
+      if (a.E32 != nullptr) ev[u] = load4_op<kOpF32>(a.E32, bE + static_cast<int64_t>(i) * a.lde + j);
+      else if (has_e) ev[u] = load4_op<OP>(a.E16, bE + op_index<OP>(i, j, a.lde));
       if (wrow && i < a.n_real) {
         const int valid = a.m_real - j;
         if (valid > 0) wv[u] = user_load4(a.W[b], static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
@@ -330,20 +271,21 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       // symmetric products own i >= j only
       const int own = a.sym ? (dk >= 3 ? 4 : (dk < 0 ? 0 : dk + 1)) : 4;
       if (own == 0) continue;
-      const int64_t o = static_cast<int64_t>(b) * a.sO + static_cast<int64_t>(i) * a.ldo + j;
       float4 q = v;
       if (dg) f4set(q, dk, f4get(q, dk) + st.ap);
+      const int64_t o32 = bO + static_cast<int64_t>(i) * a.ldo + j;
+      const int64_t o16 = bO + op_index<OP>(i, j, a.ldo);
       if (own == 4) {
-        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o, v);
-        if (a.out16 != nullptr) store4_op<OP>(a.out16, o, v);
-        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o, q);
-        if (a.q16 != nullptr) store4_op<OP>(a.q16, o, q);
+        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o32, v);
+        if (a.out16 != nullptr) store4_op<OP>(a.out16, o16, v);
+        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o32, q);
+        if (a.q16 != nullptr) store4_op<OP>(a.q16, o16, q);
       } else {
         for (int k = 0; k < own; ++k) {
-          if (a.out32 != nullptr) a.out32[o + k] = f4get(v, k);
-          if (a.out16 != nullptr) static_cast<T*>(a.out16)[o + k] = OpT<OP>::from_f(f4get(v, k));
-          if (a.q32 != nullptr) a.q32[o + k] = f4get(q, k);
-          if (a.q16 != nullptr) static_cast<T*>(a.q16)[o + k] = OpT<OP>::from_f(f4get(q, k));
+          if (a.out32 != nullptr) a.out32[o32 + k] = f4get(v, k);
+          if (a.out16 != nullptr) store1_op<OP>(a.out16, o16 + k, f4get(v, k));
+          if (a.q32 != nullptr) a.q32[o32 + k] = f4get(q, k);
+          if (a.q16 != nullptr) store1_op<OP>(a.q16, o16 + k, f4get(q, k));
         }
       }
       if (a.part_out != nullptr && i < a.n_real) {
@@ -380,92 +322,26 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       // elements i + k > j are mirrored to (j, i + k)
       const int first = j - i + 1;  // first k with i + k > j
       if (first >= 4) continue;
-      const int64_t o = static_cast<int64_t>(b) * a.sO + static_cast<int64_t>(j) * a.ldo + i;
+      const int64_t o32 = bO + static_cast<int64_t>(j) * a.ldo + i;
+      const int64_t o16 = bO + op_index<OP>(j, i, a.ldo);
       if (first <= 0) {
-        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o, v);
-        if (a.out16 != nullptr) store4_op<OP>(a.out16, o, v);
-        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o, v);
-        if (a.q16 != nullptr) store4_op<OP>(a.q16, o, v);
+        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o32, v);
+        if (a.out16 != nullptr) store4_op<OP>(a.out16, o16, v);
+        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o32, v);
+        if (a.q16 != nullptr) store4_op<OP>(a.q16, o16, v);
       } else {
         for (int k = first; k < 4; ++k) {
           const float x = f4get(v, k);
-          if (a.out32 != nullptr) a.out32[o + k] = x;
-          if (a.out16 != nullptr) static_cast<T*>(a.out16)[o + k] = OpT<OP>::from_f(x);
-          if (a.q32 != nullptr) a.q32[o + k] = x;
-          if (a.q16 != nullptr) static_cast<T*>(a.q16)[o + k] = OpT<OP>::from_f(x);
+          if (a.out32 != nullptr) a.out32[o32 + k] = x;
+          if (a.out16 != nullptr) store1_op<OP>(a.out16, o16 + k, x);
+          if (a.q32 != nullptr) a.q32[o32 + k] = x;
+          if (a.q16 != nullptr) store1_op<OP>(a.q16, o16 + k, x);
         }
       }
     } else if (a.outT16 != nullptr) {
-      store4_op<OP>(a.outT16, static_cast<int64_t>(b) * a.sOT + static_cast<int64_t>(j) * a.ldot + i, v);
+      store4_op<OP>(a.outT16, static_cast<int64_t>(b) * a.sOT + op_index<OP>(j, i, a.ldot), v);
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// 16-bit MFMA kernel.  Block tile BM x BN, k-slab BK = 64, WGM x WGN waves,
-// each wave owning a (BM/WGM) x (BN/WGN) sub-tile of 32x32x16 MFMA blocks.
-// Operands are fetched with buffer loads (one descriptor per operand, the
-// k offset in a scalar register) into registers one slab ahead, then stored
-// to one of two LDS stages; 16-byte chunks are XOR-swizzled across rows so
-// the fragment reads of 32 consecutive rows spread over all banks.
-// ---------------------------------------------------------------------------
-template <int OP>
-__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
-  if constexpr (OP == kOpBF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-}
-
-#ifndef MUON_BM
-#define MUON_BM 256
-#endif
-#ifndef MUON_BN
-#define MUON_BN 256
-#endif
-#ifndef MUON_WGM
-#define MUON_WGM 2
-#endif
-#ifndef MUON_WGN
-#define MUON_WGN 4
-#endif
-#ifndef MUON_BK
-#define MUON_BK 32
-#endif
-#ifndef MUON_STAGES
-#define MUON_STAGES 4
-#endif
-
-constexpr int kBM = MUON_BM, kBN = MUON_BN, kWGM = MUON_WGM, kWGN = MUON_WGN;
-constexpr int kBK = MUON_BK, kCH = kBK / 8;  // k-slab and 16-byte chunks per slab row
-constexpr int kStages = MUON_STAGES;
-constexpr int kNT = 64 * kWGM * kWGN;
-static_assert(kBK == 32 || kBK == 64, "k-slab of 32 or 64 elements");
-
-// 16-byte chunk c of slab row r lives at chunk c ^ f(r) so that the
-// fragment reads (32 consecutive rows, one chunk each) hit distinct banks
-// for both 8- and 16-lane LDS service groups.
-__device__ __forceinline__ int swz_f(int r) {
-  return kCH == 8 ? ((r >> 1) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
-}
-__device__ __forceinline__ int swz(int r, int c) { return r * kCH + (c ^ swz_f(r)); }
-
-// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
-// (7 = no wait), lgkmcnt [11:8] (15 = no wait).
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
 // Map the linear block id to (matrix, tile): consecutive ids go to different
@@ -496,39 +372,140 @@ __device__ __forceinline__ void block_coords(const GemmArgs& a, int BM, int BN, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit MFMA kernel on packed operands.
+//
+// Block tile 256 (i) x 256 (j), 4 waves; wave w owns rows i0 + 64 w .. + 64
+// against all 256 columns (2 x 8 MFMA 32x32x16 blocks, 256 accumulator
+// registers).  k runs in slabs of 64 (4 MFMA k-steps):
+//  * the P rows of a wave are private to it, so its P fragments go straight
+//    from global memory (L2) into registers with one contiguous 1 KB load per
+//    fragment, two slabs ahead (three register slab buffers);
+//  * the Q tile is shared by all waves: it is streamed into a 4-stage LDS
+//    ring with buffer_load ... lds (1 KB per instruction, lane l landing at
+//    byte 16 l), three slabs ahead, and each fragment is read back with one
+//    contiguous, conflict-free 16-byte-per-lane LDS read.
+// One barrier per slab, after the third k-step: by then every wave has read
+// the whole slab into registers, so its stage can take the slab four ahead,
+// and the MFMAs already issued keep the matrix pipe busy through the wait.
+// ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Copy one k-slab of ROWS rows from global memory straight into LDS.  One
-// buffer_load ... lds instruction moves 1 KB: lane l lands at byte 16 l of the
-// destination (rows r0 + l / kCH, physical chunk l % kCH), so the lane fetches
-// the logical chunk the swizzle maps there.  PER_WAVE instructions per wave.
-template <int ROWS>
-__device__ __forceinline__ void slab_to_lds(__amdgpu_buffer_rsrc_t rsrc, const int* voff, int soff,
-                                            uint4* stage_rows, int wave) {
-  constexpr int RPI = 64 / kCH;                         // rows per instruction
-  constexpr int PER_WAVE = ROWS / (kNT / 64) / RPI;
-#pragma unroll
-  for (int e = 0; e < PER_WAVE; ++e) {
-    const int r0 = (wave * PER_WAVE + e) * RPI;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(stage_rows + r0 * kCH), 16, voff[e], soff, 0, 0);
+template <int OP>
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  if constexpr (OP == kOpBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
+}
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kNW = 4, kNT = 64 * kNW;
+constexpr int kFM = kBM / kNW / 32;   // MFMA row blocks per wave (2)
+constexpr int kFN = kBN / 32;         // MFMA column blocks per wave (8)
+constexpr int kKS = kBK / 16;         // k-steps per slab (4)
+constexpr int kStages = 4;            // LDS ring depth for Q
+constexpr int kStageBytes = kBN * kBK * 2;   // 32 KB
+constexpr int kTN = kBN;              // epilogue: columns per wave
+constexpr int kLDE = kTN + 4;         // staged row length (floats)
+// each LDS stage array also holds one wave's 32-row epilogue staging block
+constexpr int kStageAlloc = kStageBytes > 32 * kLDE * 4 ? kStageBytes : 32 * kLDE * 4;
+// per-wave loads per slab: P: kFM row blocks x kKS fragments; Q: 8 row blocks / kNW waves x kKS
+constexpr int kLoadsA = kFM * kKS;
+constexpr int kLoadsB = (kBN / 32) / kNW * kKS;
+static_assert(kLoadsA == kLoadsB, "the vmcnt bookkeeping assumes equal A and B load groups");
+
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
+// (7 = no wait), lgkmcnt [11:8] (15 = no wait).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// The P fragments of slab kt for this wave: kFM row blocks x kKS k-steps.
+__device__ __forceinline__ void load_a_slab(uint4 (&buf)[kFM][kKS], __amdgpu_buffer_rsrc_t r, int voff,
+                                            int sbase, int rb_stride, int kt) {
+#pragma unroll
+  for (int f = 0; f < kFM; ++f)
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      buf[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                r, voff, sbase + f * rb_stride + kt * 4096 + s * 1024, 0));
+}
+
+// The Q slab kt into LDS stage `stage`: this wave's 2 row blocks x 4 fragments.
+__device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t r, int voff, int sbase,
+                                            int rb_stride, int kt, int wave) {
+#pragma unroll
+  for (int f = 0; f < (kBN / 32) / kNW; ++f) {
+    const int rb = wave * ((kBN / 32) / kNW) + f;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + (rb * kKS + s) * 64), 16, voff,
+                                               sbase + rb * rb_stride + kt * 4096 + s * 1024, 0, 0);
+  }
+}
+
+// MFMAs of one k-step with the Q fragments of the next k-step read in between.
+template <int OP>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], int s,
+                                      const uint4 (&bcur)[kFN], uint4 (&bnext)[kFN], const uint4* next_frags,
+                                      bool read_next, int lane) {
+  if (read_next) {
+#pragma unroll
+    for (int y = 0; y < kFN; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
+  }
+#pragma unroll
+  for (int y = 0; y < kFN; ++y)
+#pragma unroll
+    for (int x = 0; x < kFM; ++x) acc[x][y] = mfma32<OP>(a[x][s], bcur[y], acc[x][y]);
+  if (read_next) {
+#pragma unroll
+    for (int g = 0; g < kFN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    }
+  }
+}
+
+// One slab: k-steps 0..3 of slab kt from registers `a` and LDS stage `cur`,
+// reading ahead into bf; the barrier and the ring refill (slab kt + 4 into
+// `cur`) sit after k-step 2.  Loads are issued unconditionally, also past
+// the last slab: buffer loads are range-checked against the descriptor and
+// the data is never used, and straight-line code lets the compiler count
+// outstanding loads exactly.
+template <int OP>
+__device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], uint4 (&bf)[2][kFN],
+                                     uint4* cur, const uint4* nxt, __amdgpu_buffer_rsrc_t rQ, int voff, int sQ,
+                                     int qstride, int kt, int wave, int lane) {
+  kstep<OP>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
+  kstep<OP>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
+  kstep<OP>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
+  // This wave's reads of slab kt have landed and its part of slab kt + 1 is
+  // in LDS (the 5 load groups issued after it may still be in flight); after
+  // the barrier the whole slab kt + 1 is visible and nobody reads `cur`.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 0));
+  block_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_b_slab(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
+  kstep<OP>(acc, a, 3, bf[1], bf[0], nxt, true, lane);
+}
+
 template <int OP>
 __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
-  constexpr int TM = kBM / kWGM, TN = kBN / kWGN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int NW = kNT / 64;
-  constexpr int RPI = 64 / kCH;
-  constexpr int LP = kBM / NW / RPI, LQ = kBN / NW / RPI;  // direct-load instructions per wave per slab
-  constexpr int STAGE = (kBM + kBN) * kCH;                 // uint4 per LDS stage
-  constexpr int KS = kBK / 16;                             // MFMA k-steps per slab
-  static_assert(FM <= 8, "the epilogue handles up to 8 MFMA rows per wave");
-  static_assert(KS >= 2, "the barrier sits after the first k-step of a slab");
-  __shared__ uint4 smem[kStages * STAGE];
-  __shared__ double red[2 * kNT / 64];
+  // The Q ring is four separate arrays, each named statically at every access,
+  // so the compiler's wait for an LDS read covers only the DMA into that stage.
+  __shared__ uint4 stg0[kStageAlloc / 16], stg1[kStageAlloc / 16], stg2[kStageAlloc / 16], stg3[kStageAlloc / 16];
+  __shared__ double red[2 * kNW];
   int b, tile, I, J;
   block_coords(a, kBM, kBN, b, tile, I, J);
   EpiState st;
@@ -537,158 +514,106 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t pbytes = (static_cast<int64_t>(a.Mdim - I * kBM) * a.ldp) * 2;
-  const int64_t qbytes = (static_cast<int64_t>(a.Ndim - J * kBN) * a.ldq) * 2;
-  const uint16_t* Pb = static_cast<const uint16_t*>(a.P) + static_cast<int64_t>(b) * a.sP +
-                       static_cast<int64_t>(I) * kBM * a.ldp;
-  const uint16_t* Qb = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(b) * a.sQ +
-                       static_cast<int64_t>(J) * kBN * a.ldq;
-  const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pb, pbytes);
-  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qb, qbytes);
-  int voffP[LP], voffQ[LQ];
-#pragma unroll
-  for (int e = 0; e < LP; ++e) {
-    const int r = (wave * LP + e) * RPI + lane / kCH;
-    voffP[e] = (r * a.ldp + ((lane % kCH) ^ swz_f(r)) * 8) * 2;
-  }
-#pragma unroll
-  for (int e = 0; e < LQ; ++e) {
-    const int r = (wave * LQ + e) * RPI + lane / kCH;
-    voffQ[e] = (r * a.ldq + ((lane % kCH) ^ swz_f(r)) * 8) * 2;
-  }
+  const uint16_t* Pm = static_cast<const uint16_t*>(a.P) + static_cast<int64_t>(b) * a.sP;
+  const uint16_t* Qm = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(b) * a.sQ;
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pm, static_cast<int64_t>(a.Mdim) * a.ldp * 2);
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qm, static_cast<int64_t>(a.Ndim) * a.ldq * 2);
+  const int voff = lane * 16;
+  // byte offset of a row block = (row / 32) * (K / 64) * 4 KB
+  const int pstride = (a.ldp >> 6) * 4096, qstride = (a.ldq >> 6) * 4096;
+  const int sP = (I * (kBM / 32) + wave * kFM) * pstride;
+  const int sQ = J * (kBN / 32) * qstride;
 
-  const int wm = wave / kWGN, wn = wave % kWGN;
-  const int lr = lane & 31, lk = lane >> 5;
-  int aoff[FM], boff[FN];
+  f32x16_t acc[kFM][kFN];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) aoff[f] = wm * TM + f * 32 + lr;
+  for (int x = 0; x < kFM; ++x)
 #pragma unroll
-  for (int f = 0; f < FN; ++f) boff[f] = kBM + wn * TN + f * 32 + lr;
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int x = 0; x < FM; ++x)
-#pragma unroll
-    for (int y = 0; y < FN; ++y)
+    for (int y = 0; y < kFN; ++y)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
 
-  const int nk = a.K / kBK;
-  // prologue: slabs 0 .. kStages-1 in flight, one per stage
-#pragma unroll
-  for (int s0 = 0; s0 < kStages; ++s0) {
-    if (s0 < nk) {
-      slab_to_lds<kBM>(rP, voffP, s0 * kBK * 2, smem + s0 * STAGE, wave);
-      slab_to_lds<kBN>(rQ, voffQ, s0 * kBK * 2, smem + s0 * STAGE + kBM * kCH, wave);
-    }
-  }
-  // slab 0 landed for every wave
-  if (nk >= kStages) __builtin_amdgcn_s_waitcnt(waitcnt_imm((kStages - 1) * (LP + LQ), 15));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  const int nk = a.K / kBK;  // a multiple of 4: every operand dimension is a multiple of 256
+  uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS];
+  uint4 bf[2][kFN];
+  // prologue: Q slabs 0..3 into the ring, P slabs 0 and 1 into registers
+  load_b_slab(stg0, rQ, voff, sQ, qstride, 0, wave);
+  load_b_slab(stg1, rQ, voff, sQ, qstride, 1, wave);
+  load_b_slab(stg2, rQ, voff, sQ, qstride, 2, wave);
+  load_b_slab(stg3, rQ, voff, sQ, qstride, 3, wave);
+  load_a_slab(abuf0, rP, voff, sP, pstride, 0);
+  load_a_slab(abuf1, rP, voff, sP, pstride, 1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 15));  // Q slab 0 landed
   block_barrier();
+#pragma unroll
+  for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
 
-  uint4 af[2][FM], bf[2][FN];
-#pragma unroll
-  for (int f = 0; f < FM; ++f) af[0][f] = smem[swz(aoff[f], lk)];
-#pragma unroll
-  for (int f = 0; f < FN; ++f) bf[0][f] = smem[swz(boff[f], lk)];
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = (kt % kStages) * STAGE;
-    const int nxt = ((kt + 1) % kStages) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int rb = ks & 1, wb = rb ^ 1;
-      if (ks + 1 < KS) {
-        const int c = (ks + 1) * 2 + lk;
-#pragma unroll
-        for (int f = 0; f < FM; ++f) af[wb][f] = smem[cur + swz(aoff[f], c)];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) bf[wb][f] = smem[cur + swz(boff[f], c)];
-      } else if (kt + 1 < nk) {
-#pragma unroll
-        for (int f = 0; f < FM; ++f) af[wb][f] = smem[nxt + swz(aoff[f], lk)];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) bf[wb][f] = smem[nxt + swz(boff[f], lk)];
-      }
-#pragma unroll
-      for (int x = 0; x < FM; ++x)
-#pragma unroll
-        for (int y = 0; y < FN; ++y) acc[x][y] = mfma32<OP>(af[rb][x], bf[rb][y], acc[x][y]);
-#pragma unroll
-      for (int g = 0; g < FM + FN; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      }
-      if (ks == KS - 2) {
-        // Every wave has read slab kt into registers and its own part of slab
-        // kt + 1 has landed: after the barrier, slab kt + 1 is complete and
-        // the stage of slab kt can take slab kt + kStages.  The MFMAs issued
-        // above keep the matrix pipe busy while the wave waits here.
-        if (kt + kStages - 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_imm((kStages - 2) * (LP + LQ), 0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-        block_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + kStages < nk) {
-          const int soff = (kt + kStages) * kBK * 2;
-          slab_to_lds<kBM>(rP, voffP, soff, smem + cur, wave);
-          slab_to_lds<kBN>(rQ, voffQ, soff, smem + cur + kBM * kCH, wave);
-        }
-      }
+  // 12 slabs per trip (lcm of the 4 LDS stages and the 3 P register buffers);
+  // nk is a multiple of 4, so a remainder of 4 or 8 slabs follows.
+#define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
+  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 2);                                             \
+  slab<OP>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
+  int kt = 0;
+  for (; kt + 12 <= nk; kt += 12) {
+    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
+    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
+    MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
+    MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
+    MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
+    MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
+    MUON_SLAB(8, abuf2, abuf1, stg0, stg1)
+    MUON_SLAB(9, abuf0, abuf2, stg1, stg2)
+    MUON_SLAB(10, abuf1, abuf0, stg2, stg3)
+    MUON_SLAB(11, abuf2, abuf1, stg3, stg0)
+  }
+  if (kt + 4 <= nk) {
+    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
+    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
+    if (kt + 8 <= nk) {
+      MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
+      MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
+      MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
+      MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
     }
   }
+#undef MUON_SLAB
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   block_barrier();
 
-  // Epilogue: one 32-row block of every wave's sub-tile at a time is staged
-  // through LDS (the MFMA 32x32 result layout: lane l, register v hold row
-  // 8*(v/4) + 4*(l/32) + v%4, column l%32), then written out by
-  // epilogue_block.
-  constexpr int LDE = TN + 4;
-  static_assert(kWGM * kWGN * 32 * LDE * 4 <= sizeof(smem), "epilogue staging must fit in LDS");
-  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LDE;
+  // Epilogue: one 32-row block of every wave's 64 x 256 sub-tile at a time is
+  // staged through LDS (the MFMA 32x32 result layout: lane l, register v hold
+  // row 8*(v/4) + 4*(l/32) + v%4, column l%32), then written by epilogue_block.
+  float* ep = reinterpret_cast<float*>(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
   const bool mirror = epi_has_mirror(a);
-  // The x loop stays rolled (its body is large); the accumulator row is
-  // picked with constant indices so acc never needs dynamic indexing.
-  for (int x = 0; x < FM; ++x) {
-    switch (x) {
-#define MUON_SCATTER_ROW(X)                                                                      \
-  case X:                                                                                        \
-    if constexpr (X < FM) {                                                                      \
-      _Pragma("unroll") for (int y = 0; y < FN; ++y)                                             \
-          _Pragma("unroll") for (int v = 0; v < 16; ++v)                                         \
-              ep[(8 * (v >> 2) + 4 * lk + (v & 3)) * LDE + y * 32 + lr] = acc[X][y][v];           \
-    }                                                                                            \
-    break;
-      MUON_SCATTER_ROW(0)
-      MUON_SCATTER_ROW(1)
-      MUON_SCATTER_ROW(2)
-      MUON_SCATTER_ROW(3)
-      MUON_SCATTER_ROW(4)
-      MUON_SCATTER_ROW(5)
-      MUON_SCATTER_ROW(6)
-      MUON_SCATTER_ROW(7)
-#undef MUON_SCATTER_ROW
-      default:
-        break;
-    }
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int x = 0; x < kFM; ++x) {
+#pragma unroll
+    for (int y = 0; y < kFN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ep[(8 * (v >> 2) + 4 * lk + (v & 3)) * kLDE + y * 32 + lr] = acc[x][y][v];
     __syncthreads();
-    epilogue_block<OP, TN, LDE>(a, b, st, ep, I * kBM + wm * TM + x * 32, J * kBN + wn * TN, lane, mirror);
+    epilogue_block<OP, kTN, kLDE>(a, b, st, ep, I * kBM + wave * (kBM / kNW) + x * 32, J * kBN, lane, mirror);
     __syncthreads();
   }
   block_partials<kNT>(a, b, tile, red, st);
 }
 
 // ---------------------------------------------------------------------------
-// fp32 check path: fp32 operands, exact products and fp64 accumulation.
-// 64 x 64 block tile, 16 x 16 threads with 4 x 4 outputs each.  Slow.
+// fp32 check path: fp32 row-major operands, exact products and fp64
+// accumulation.  64 x 64 block tile, 16 x 16 threads with 4 x 4 outputs each;
+// the tile is staged in LDS and written by the same epilogue.  Slow.
 // ---------------------------------------------------------------------------
 constexpr int kCB = 64;
 
 __global__ __launch_bounds__(256) void gemm_nt_f64acc(GemmArgs a) {
   __shared__ float sP[16][kCB + 1];
   __shared__ float sQ[16][kCB + 1];
-  __shared__ double red[16];
+  __shared__ float stage[4][32 * (32 + 4)];
+  __shared__ double red[8];
   int b, tile, I, J;
   block_coords(a, kCB, kCB, b, tile, I, J);
   EpiState st;
@@ -724,16 +649,20 @@ __global__ __launch_bounds__(256) void gemm_nt_f64acc(GemmArgs a) {
     }
     __syncthreads();
   }
+  // 64 x 64 tile = 2 x 2 blocks of 32 x 32, one per wave
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* ep = stage[wave];
+  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int i = I * kCB + ty + 16 * u;
-      const int j = J * kCB + tx + 16 * w;
-      if (a.sym && i < j) continue;
-      const float v = epi_value<kOpF32>(a, b, i, j, static_cast<float>(acc[u][w]), st);
-      if (epi_has_mirror(a) && !(a.sym && i == j)) epi_mirror<kOpF32>(a, b, i, j, v, st);
+      const int r = ty + 16 * u, c = tx + 16 * w;  // position in the 64 x 64 tile
+      stage[(r >> 5) * 2 + (c >> 5)][(r & 31) * 36 + (c & 31)] = static_cast<float>(acc[u][w]);
     }
+  __syncthreads();
+  epilogue_block<kOpF32, 32, 36>(a, b, st, ep, I * kCB + wr, J * kCB + wc, lane, epi_has_mirror(a));
+  __syncthreads();
   block_partials<256>(a, b, tile, red, st);
 }
 
