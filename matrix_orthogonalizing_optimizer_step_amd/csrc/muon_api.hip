@@ -367,7 +367,12 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     // X <- a' X + B' X
     g = base_args(p);
     set_px(g, p, ws + p.B16, ws + p.XT[xc]);
-    g.E16 = ws + p.XN;
+    if (p.op == kOpF32) {
+      g.E16 = ws + p.XN;
+    } else {  // the MFMA epilogue reads the a' X term from X^T
+      g.E16 = ws + p.XT[xc];
+      g.lde = p.n_pad;
+    }
     g.beta_a = 1.0f;
     g.coef_a = a;
     g.shift_in = c.shift ? shift : nullptr;

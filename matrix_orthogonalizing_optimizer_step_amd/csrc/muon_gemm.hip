@@ -39,6 +39,8 @@ __device__ __forceinline__ void tri_tile(int t, int& I, int& J) {
 struct EpiState {
   float alpha, beta, gamma, ap;
   double tr, ss;
+  void* w;  // this matrix's W and O in the final product (read once, before any store)
+  void* o;
 };
 
 // The diagonal shift a' of matrix b: mean of a + b l + c l^2 over the
@@ -46,7 +48,7 @@ struct EpiState {
 // reduced from per-tile partials in a fixed order, so every block of a
 // launch gets the same value).  All threads of the block must call this.
 template <int NT>
-__device__ float block_shift(const GemmArgs& a, int b, double* red) {
+__device__ __forceinline__ float block_shift(const GemmArgs& a, int b, double* red) {
   if (a.part_in != nullptr) {
     double tr = 0.0, ss = 0.0;
     const double* p = a.part_in + static_cast<int64_t>(b) * a.npart_in * 2;
@@ -78,7 +80,7 @@ __device__ float block_shift(const GemmArgs& a, int b, double* red) {
 }
 
 template <int NT>
-__device__ void block_init(const GemmArgs& a, int b, int tile, double* red, EpiState& st) {
+__device__ __forceinline__ void block_init(const GemmArgs& a, int b, int tile, double* red, EpiState& st) {
   st.ap = block_shift<NT>(a, b, red);
   if (a.shift_out != nullptr && tile == 0 && threadIdx.x == 0) a.shift_out[b] = st.ap;
   st.alpha = a.alpha_c + a.alpha_a * st.ap;
@@ -86,11 +88,13 @@ __device__ void block_init(const GemmArgs& a, int b, int tile, double* red, EpiS
   st.gamma = a.gamma_c + a.gamma_a * st.ap;
   st.tr = 0.0;
   st.ss = 0.0;
+  st.w = a.final_mode && a.W != nullptr ? a.W[b] : nullptr;
+  st.o = a.final_mode && a.Oout != nullptr ? a.Oout[b] : nullptr;
 }
 
 // Write the (trace, sum of squares) partial of this tile.
 template <int NT>
-__device__ void block_partials(const GemmArgs& a, int b, int tile, double* red, EpiState& st) {
+__device__ __forceinline__ void block_partials(const GemmArgs& a, int b, int tile, double* red, EpiState& st) {
   if (a.part_out == nullptr) return;
   double tr = st.tr, ss = st.ss;
   for (int off = 32; off > 0; off >>= 1) {
@@ -203,17 +207,18 @@ __device__ __forceinline__ void user_store4(void* p, int64_t idx, int dtype, int
 
 // W <- W - lr (O + wd W) and the optional O store for four consecutive
 // elements of the user's matrix at idx (valid of them in range).
-__device__ __forceinline__ void final_update4(const GemmArgs& a, int b, int64_t idx, int valid, float4 o, float4 w) {
+__device__ __forceinline__ void final_update4(const GemmArgs& a, const EpiState& st, int64_t idx, int valid, float4 o,
+                                              float4 w) {
   if (valid <= 0) return;
-  if (a.W != nullptr) {
+  if (st.w != nullptr) {
     float4 nw;
     nw.x = w.x - a.lr * (o.x + a.wd * w.x);
     nw.y = w.y - a.lr * (o.y + a.wd * w.y);
     nw.z = w.z - a.lr * (o.z + a.wd * w.z);
     nw.w = w.w - a.lr * (o.w + a.wd * w.w);
-    user_store4(a.W[b], idx, a.w_dtype, valid, nw);
+    user_store4(st.w, idx, a.w_dtype, valid, nw);
   }
-  if (a.Oout != nullptr) user_store4(a.Oout[b], idx, a.o_dtype, valid, o);
+  if (st.o != nullptr) user_store4(st.o, idx, a.o_dtype, valid, o);
 }
 
 // Epilogue over a 32 x TN block of C staged in LDS (row-major, leading
@@ -246,7 +251,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       else if (has_e) ev[u] = load4_op<OP>(a.E16, bE + op_index<OP>(i, j, a.lde));
       if (wrow && i < a.n_real) {
         const int valid = a.m_real - j;
-        if (valid > 0) wv[u] = user_load4(a.W[b], static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
+        if (valid > 0) wv[u] = user_load4(st.w, static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
       }
     }
 #pragma unroll
@@ -265,7 +270,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       if (dg) f4set(v, dk, f4get(v, dk) + st.gamma);
       *slot = v;
       if (a.final_mode) {
-        if (!a.transposed && i < a.n_real) final_update4(a, b, static_cast<int64_t>(i) * a.user_ld + j, a.m_real - j, v, wv[u]);
+        if (!a.transposed && i < a.n_real) final_update4(a, st, static_cast<int64_t>(i) * a.user_ld + j, a.m_real - j, v, wv[u]);
         continue;
       }
       // symmetric products own i >= j only
@@ -313,8 +318,8 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       if (j < a.m_real && i < a.n_real) {
         const int64_t idx = static_cast<int64_t>(j) * a.user_ld + i;
         const int valid = a.n_real - i;
-        const float4 w = a.W != nullptr ? user_load4(a.W[b], idx, a.w_dtype, valid) : v;
-        final_update4(a, b, idx, valid, v, w);
+        const float4 w = st.w != nullptr ? user_load4(st.w, idx, a.w_dtype, valid) : v;
+        final_update4(a, st, idx, valid, v, w);
       }
       continue;
     }
@@ -500,6 +505,348 @@ __device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)
   kstep<OP>(acc, a, 3, bf[1], bf[0], nxt, true, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Register epilogue of the MFMA kernel.
+//
+// For the 32 x 32 MFMA block at rows ib.., columns jb.. a lane holds 16
+// values in the accumulator arrangement "A": lane l, register r is element
+//   (ib + 8 (r / 4) + 4 (l / 32) + r % 4,  jb + l % 32).
+// Exchanging registers 4..7 of the lower half-wave with registers 0..3 of the
+// upper half-wave (and 12..15 with 8..11) by v_permlane32_swap gives "N":
+// lane l, register 8 h + e is (ib + 16 h + 8 (l / 32) + e, jb + l % 32), so a
+// lane holds 8 consecutive rows of one column: in the packed operand layout
+// that is this lane's 16 bytes of a fragment of C^T (row j, k = i).  Using
+// such a fragment as the MFMA A operand against an identity B fragment gives
+// the block transposed, exactly (products with 1 and sums with 0), in
+// arrangement "T": lane l, register 8 h + e is (ib + l % 32, jb + 16 h +
+// 8 (l / 32) + e), a fragment of C itself (row i, k = j).  Both C and C^T are
+// thus written as whole 1 KB fragments from registers, and the 16-bit
+// epilogue input is read as fragments of E^T (E is symmetric, or E = X read
+// from X^T).
+//
+// fp32 side matrices (R, Q, RZ of the Gram iteration) are only ever read by
+// this epilogue at the same block positions, so they are kept in arrangement
+// A, one 4 KB record per 32 x 32 block (lower-triangle blocks only): record
+// (ib / 32, jb / 32) of an ld x ld matrix, register r of lane l at offset
+// 256 (r / 4) + 4 l + r % 4.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t acc_rec(int ib, int jb, int ld) {
+  return (static_cast<int64_t>(ib >> 5) * (ld >> 5) + (jb >> 5)) << 10;
+}
+
+// Exchange the upper half-wave of x with the lower half-wave of y.
+__device__ __forceinline__ void xchg_halves(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return OP == kOpBF16 ? f32x2_to_bf16x2(lo, hi) : f32x2_to_f16x2(lo, hi);
+}
+
+// 16 values in arrangement A -> two 16-bit fragments in arrangement N.
+template <int OP>
+__device__ __forceinline__ void a_to_n16(const float (&v)[16], uint4 (&f)[2]) {
+  uint32_t d[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k] = pack2<OP>(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    xchg_halves(d[4 * h], d[4 * h + 2]);
+    xchg_halves(d[4 * h + 1], d[4 * h + 3]);
+  }
+  f[0] = make_uint4(d[0], d[1], d[2], d[3]);
+  f[1] = make_uint4(d[4], d[5], d[6], d[7]);
+}
+
+// Two 16-bit fragments in arrangement N -> 16 fp32 values in arrangement A.
+template <int OP>
+__device__ __forceinline__ void n16_to_a(const uint4& f0, const uint4& f1, float (&v)[16]) {
+  uint32_t d[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    xchg_halves(d[4 * h], d[4 * h + 2]);
+    xchg_halves(d[4 * h + 1], d[4 * h + 3]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    v[2 * k] = OpT<OP>::to_f(static_cast<uint16_t>(d[k] & 0xffffu));
+    v[2 * k + 1] = OpT<OP>::to_f(static_cast<uint16_t>(d[k] >> 16));
+  }
+}
+
+// B fragment h of the 32 x 32 identity: lane l holds B[k][n] for n = l % 32,
+// k = 8 (l / 32) + e, equal to 1 where n == 16 h + k.
+template <int OP>
+__device__ __forceinline__ uint4 ident_frag(int h, int lane) {
+  const uint32_t one = OP == kOpBF16 ? 0x3F80u : 0x3C00u;
+  const int e = (lane & 31) - 16 * h - 8 * (lane >> 5);
+  uint32_t d[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) d[k] = (e >= 0 && (e >> 1) == k) ? one << (16 * (e & 1)) : 0u;
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// Fragments in arrangement N -> the transposed block in arrangement T.
+template <int OP>
+__device__ __forceinline__ void transpose16(const uint4 (&n)[2], const uint4 (&id)[2], uint4 (&t)[2]) {
+  f32x16_t d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) d[r] = 0.0f;
+  d = mfma32<OP>(n[0], id[0], d);
+  d = mfma32<OP>(n[1], id[1], d);
+  float dv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dv[r] = d[r];
+  a_to_n16<OP>(dv, t);
+}
+
+// Diagonal block of a symmetric product: N and T fragments address the same
+// elements (p, q) = (l % 32, 16 h + 8 (l / 32) + e); keep the owned value
+// C[max][min], which is T where p >= q and N elsewhere.
+__device__ __forceinline__ uint4 sym_select(const uint4& t, const uint4& n, int h, int lane) {
+  const int p = lane & 31, q0 = 16 * h + 8 * (lane >> 5);
+  const uint32_t tv[4] = {t.x, t.y, t.z, t.w}, nv[4] = {n.x, n.y, n.z, n.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = (p >= q0 + 2 * k ? 0x0000ffffu : 0u) | (p >= q0 + 2 * k + 1 ? 0xffff0000u : 0u);
+    r[k] = (tv[k] & m) | (nv[k] & ~m);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+template <int OP>
+__device__ __forceinline__ void store_frag(void* base, int64_t off, int lane, const uint4& f) {
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off + 8 * lane) = f;
+}
+
+// The 16-bit stores of one block: both triangles of a symmetric product, or
+// X (from T) and X^T (from N) of a general one.
+template <int OP>
+__device__ __forceinline__ void store16(const GemmArgs& a, void* out, int64_t bO, const float (&v)[16], int ib, int jb,
+                                        int lane, const uint4 (&id)[2]) {
+  uint4 n16[2], t16[2];
+  a_to_n16<OP>(v, n16);
+  transpose16<OP>(n16, id, t16);
+  uint16_t* o = static_cast<uint16_t*>(out) + bO;
+  if (ib == jb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) store_frag<OP>(o, op_index<OP>(ib, jb + 16 * h, a.ldo), lane, sym_select(t16[h], n16[h], h, lane));
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      store_frag<OP>(o, op_index<OP>(ib, jb + 16 * h, a.ldo), lane, t16[h]);
+      store_frag<OP>(o, op_index<OP>(jb, ib + 16 * h, a.ldo), lane, n16[h]);
+    }
+  }
+}
+
+// Epilogue of one 32 x 32 block (see the comment above): v = alpha C +
+// beta E + gamma [i == j < n_real] in arrangement A, then its stores and
+// partial sums.  `ein` holds the block's epilogue input as loaded (16-bit
+// fragments of E^T in ein[0..1], or the fp32 record in ein[0..3]).  FINAL:
+// v goes to the wave's LDS staging area `ep` (row-major, kLDE floats per row,
+// this block at column ycol) for the update of W.
+template <int OP, bool FINAL>
+__device__ __forceinline__ void epi_block(const GemmArgs& a, int b, EpiState& st, const f32x16_t& c,
+                                          const uint4 (&ein)[4], int ib, int jb, int lane, const uint4 (&id)[2],
+                                          float* ep, int ycol) {
+  const bool dblk = ib == jb;
+  const int jr = lane & 31, ir0 = 4 * (lane >> 5);
+  float e[16];
+  if (a.E16 != nullptr) {
+    n16_to_a<OP>(ein[0], ein[1], e);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint4& w = ein[r >> 2];
+      const uint32_t u = (r & 3) == 0 ? w.x : ((r & 3) == 1 ? w.y : ((r & 3) == 2 ? w.z : w.w));
+      e[r] = a.E32 != nullptr ? __uint_as_float(u) : 0.0f;
+    }
+  }
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = st.alpha * c[r] + st.beta * e[r];
+  if (dblk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+      if (ir == jr && ib + ir < a.n_real) v[r] += st.gamma;
+    }
+  }
+  if constexpr (FINAL) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + ir0 + (r & 3)) * kLDE + ycol + jr] = v[r];
+    return;
+  }
+  const int64_t bO = static_cast<int64_t>(b) * a.sO;
+  if (a.part_out != nullptr) {  // symmetric products: an off-diagonal value stands for two
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+      const double x = v[r];
+      if (!dblk || ir > jr) {
+        st.ss += 2.0 * x * x;
+      } else if (ir == jr) {
+        st.ss += x * x;
+        st.tr += x;
+      }
+    }
+  }
+  if (a.out32 != nullptr) {
+    float* o = a.out32 + bO + acc_rec(ib, jb, a.ldo) + 4 * lane;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *reinterpret_cast<float4*>(o + 256 * g) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+  }
+  if (a.sym) {
+    if (a.out16 != nullptr) store16<OP>(a, a.out16, bO, v, ib, jb, lane, id);
+  } else {
+    uint4 n16[2];
+    a_to_n16<OP>(v, n16);
+    if (a.outT16 != nullptr) {
+      uint16_t* o = static_cast<uint16_t*>(a.outT16) + static_cast<int64_t>(b) * a.sOT;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) store_frag<OP>(o, op_index<OP>(jb, ib + 16 * h, a.ldot), lane, n16[h]);
+    }
+    if (a.out16 != nullptr) {
+      uint4 t16[2];
+      transpose16<OP>(n16, id, t16);
+      uint16_t* o = static_cast<uint16_t*>(a.out16) + bO;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) store_frag<OP>(o, op_index<OP>(ib, jb + 16 * h, a.ldo), lane, t16[h]);
+    }
+  }
+  if (a.q32 != nullptr || a.q16 != nullptr) {  // a fresh Q = v + a' I (symmetric products)
+    float q[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+      q[r] = (dblk && ir == jr && ib + ir < a.n_real) ? v[r] + st.ap : v[r];
+    }
+    if (a.q32 != nullptr) {
+      float* o = a.q32 + bO + acc_rec(ib, jb, a.ldo) + 4 * lane;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *reinterpret_cast<float4*>(o + 256 * g) = make_float4(q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]);
+    }
+    if (a.q16 != nullptr) store16<OP>(a, a.q16, bO, q, ib, jb, lane, id);
+  }
+}
+
+// Final product: W <- W - lr (O + wd W) and the optional store of O, for
+// rows i0 .. i0 + 31 and columns j0 .. j0 + 255 of O staged in LDS
+// (row-major, LDE floats per row).  The loads of W for 16 rows (or columns)
+// are issued together before any of them is used.
+template <int LDE>
+__device__ __forceinline__ void final_rows(const GemmArgs& a, const EpiState& st, const float* ep, int i0, int j0,
+                                           int lane) {
+  constexpr int R = 16;
+  if (!a.transposed) {  // W is n x m: lane -> columns j .. j + 3 of every row
+    const int j = j0 + 4 * lane;
+    const int valid = a.m_real - j;
+    for (int r0 = 0; r0 < 32; r0 += R) {
+      float4 w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = i0 + r0 + r;
+        w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (st.w != nullptr && i < a.n_real && valid > 0)
+          w[r] = user_load4(st.w, static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = i0 + r0 + r;
+        if (i < a.n_real)
+          final_update4(a, st, static_cast<int64_t>(i) * a.user_ld + j, valid,
+                        *reinterpret_cast<const float4*>(ep + (r0 + r) * LDE + 4 * lane), w[r]);
+      }
+    }
+  } else {  // W is m x n: lane -> W[j][i .. i + 3] for 32 columns j of O
+    const int r4 = (lane & 7) * 4;
+    const int i = i0 + r4;
+    const int valid = a.n_real - i;
+    for (int c0 = 0; c0 < 256; c0 += 8 * R) {
+      float4 w[R];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int j = j0 + c0 + 8 * t + (lane >> 3);
+        w[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (st.w != nullptr && j < a.m_real && valid > 0)
+          w[t] = user_load4(st.w, static_cast<int64_t>(j) * a.user_ld + i, a.w_dtype, valid);
+      }
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int c = c0 + 8 * t + (lane >> 3);
+        if (j0 + c < a.m_real) {
+          const float4 o = make_float4(ep[(r4 + 0) * LDE + c], ep[(r4 + 1) * LDE + c], ep[(r4 + 2) * LDE + c],
+                                       ep[(r4 + 3) * LDE + c]);
+          final_update4(a, st, static_cast<int64_t>(j0 + c) * a.user_ld + i, valid, o, w[t]);
+        }
+      }
+    }
+  }
+}
+
+// Four MFMA blocks (row block X, column blocks Y0 .. Y0 + 3) of the register
+// epilogue: their epilogue inputs are loaded together first.  The blocks are
+// spelled out (not a loop) so the accumulators are always named statically.
+template <int OP, bool FINAL, int X, int Y0>
+__device__ __forceinline__ void epi_group(const GemmArgs& a, int b, EpiState& st, const f32x16_t (&acc)[kFM][kFN],
+                                          int I, int J, int wave, int lane, const uint4 (&id)[2], float* ep) {
+  constexpr int kEG = 4;
+  const int64_t bE = static_cast<int64_t>(b) * a.sE;
+  const int ib = I * kBM + wave * (kBM / kNW) + 32 * X;
+  const int jb0 = J * kBN + 32 * Y0;
+  uint4 ein[kEG][4];
+#pragma unroll
+  for (int u = 0; u < kEG; ++u) {
+    const int jb = jb0 + 32 * u;
+    if (a.sym && ib < jb) continue;  // the mirror of an owned block
+    if (a.E16 != nullptr) {
+      const uint16_t* E16 = static_cast<const uint16_t*>(a.E16) + bE;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ein[u][h] = *reinterpret_cast<const uint4*>(E16 + op_index<OP>(jb, ib + 16 * h, a.lde) + 8 * lane);
+    } else if (a.E32 != nullptr) {
+      const float* E32 = a.E32 + bE + acc_rec(ib, jb, a.lde) + 4 * lane;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ein[u][g] = *reinterpret_cast<const uint4*>(E32 + 256 * g);
+    }
+  }
+  if (!(a.sym && ib < jb0 + 0)) epi_block<OP, FINAL>(a, b, st, acc[X][Y0 + 0], ein[0], ib, jb0 + 0, lane, id, ep, 32 * (Y0 + 0));
+  if (!(a.sym && ib < jb0 + 32)) epi_block<OP, FINAL>(a, b, st, acc[X][Y0 + 1], ein[1], ib, jb0 + 32, lane, id, ep, 32 * (Y0 + 1));
+  if (!(a.sym && ib < jb0 + 64)) epi_block<OP, FINAL>(a, b, st, acc[X][Y0 + 2], ein[2], ib, jb0 + 64, lane, id, ep, 32 * (Y0 + 2));
+  if (!(a.sym && ib < jb0 + 96)) epi_block<OP, FINAL>(a, b, st, acc[X][Y0 + 3], ein[3], ib, jb0 + 96, lane, id, ep, 32 * (Y0 + 3));
+}
+
+// The register epilogue over a wave's 64 x 256 sub-tile.
+template <int OP>
+__device__ __forceinline__ void epilogue_regs(const GemmArgs& a, int b, EpiState& st, const f32x16_t (&acc)[kFM][kFN],
+                                              int I, int J, int wave, int lane) {
+  static_assert(kFM == 2 && kFN == 8, "the epilogue groups are spelled out for 2 x 8 MFMA blocks");
+  const uint4 id[2] = {ident_frag<OP>(0, lane), ident_frag<OP>(1, lane)};
+  epi_group<OP, false, 0, 0>(a, b, st, acc, I, J, wave, lane, id, nullptr);
+  epi_group<OP, false, 0, 4>(a, b, st, acc, I, J, wave, lane, id, nullptr);
+  epi_group<OP, false, 1, 0>(a, b, st, acc, I, J, wave, lane, id, nullptr);
+  epi_group<OP, false, 1, 4>(a, b, st, acc, I, J, wave, lane, id, nullptr);
+}
+
+// Final product, row block X of the wave: O = v goes through the wave's LDS
+// staging area (row-major, kLDE floats per row) into the update of W, so the
+// user's row-major W is read and written along its rows.
+template <int OP, int X>
+__device__ __forceinline__ void final_stage(const GemmArgs& a, int b, EpiState& st, const f32x16_t (&acc)[kFM][kFN],
+                                            float* ep, int I, int J, int wave, int lane) {
+  const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // unused in the final product
+  epi_group<OP, true, X, 0>(a, b, st, acc, I, J, wave, lane, id, ep);
+  epi_group<OP, true, X, 4>(a, b, st, acc, I, J, wave, lane, id, ep);
+  __syncthreads();
+  final_rows<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + X * 32, J * kBN, lane);
+  __syncthreads();
+}
+
 template <int OP>
 __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   // The Q ring is four separate arrays, each named statically at every access,
@@ -583,21 +930,13 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   block_barrier();
 
-  // Epilogue: one 32-row block of every wave's 64 x 256 sub-tile at a time is
-  // staged through LDS (the MFMA 32x32 result layout: lane l, register v hold
-  // row 8*(v/4) + 4*(l/32) + v%4, column l%32), then written by epilogue_block.
-  float* ep = reinterpret_cast<float*>(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
-  const bool mirror = epi_has_mirror(a);
-  const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-  for (int x = 0; x < kFM; ++x) {
-#pragma unroll
-    for (int y = 0; y < kFN; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ep[(8 * (v >> 2) + 4 * lk + (v & 3)) * kLDE + y * 32 + lr] = acc[x][y][v];
-    __syncthreads();
-    epilogue_block<OP, kTN, kLDE>(a, b, st, ep, I * kBM + wave * (kBM / kNW) + x * 32, J * kBN, lane, mirror);
-    __syncthreads();
+  // Epilogue from registers; the final product goes through LDS.
+  if (a.final_mode) {
+    float* ep = reinterpret_cast<float*>(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
+    final_stage<OP, 0>(a, b, st, acc, ep, I, J, wave, lane);
+    final_stage<OP, 1>(a, b, st, acc, ep, I, J, wave, lane);
+  } else {
+    epilogue_regs<OP>(a, b, st, acc, I, J, wave, lane);
   }
   block_partials<kNT>(a, b, tile, red, st);
 }
