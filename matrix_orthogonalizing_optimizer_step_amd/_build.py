@@ -10,15 +10,17 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
-SOURCES = ["muon_gemm.hip", "muon_elementwise.hip", "muon_api.hip"]
+SOURCES = ["muon_gemm_bf16.hip", "muon_gemm_f16.hip", "muon_gemm_f32.hip", "muon_gemm.hip",
+           "muon_elementwise.hip", "muon_api.hip"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    "-O3", "-std=c++17", "-fPIC", "-Wall",
     f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,20 +34,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; writes libmuon.so atomically and returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd: list[str], verbose: bool) -> subprocess.Popen:
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(proc: subprocess.Popen, what: str, verbose: bool) -> None:
+    out, _ = proc.communicate()
     noise = "is not a recognized feature for this target"
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    msgs = "\n".join(l for l in out.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one process per source, in parallel); writes
+    libmuon.so atomically and returns its path."""
+    objdir = tempfile.mkdtemp(prefix="muon_build_")
+    try:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            objs.append(obj)
+            procs.append((src, _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)))
+        for src, proc in procs:
+            _finish(proc, src, verbose)
+        tmp = LIB + ".tmp"
+        _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose), "link", verbose)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 

@@ -1,0 +1,691 @@
+// The 16-bit MFMA GEMM kernel (main loop and register epilogue), included by
+// one translation unit per operand type.
+#pragma once
+
+#include "muon_gemm_common.h"
+
+namespace muon {
+
+// ---------------------------------------------------------------------------
+// 16-bit MFMA kernel on packed operands.
+//
+// Block tile 256 (i) x 256 (j), 4 waves; wave w owns rows i0 + 64 w .. + 64
+// against all 256 columns (2 x 8 MFMA 32x32x16 blocks, 256 accumulator
+// registers).  k runs in slabs of 64 (4 MFMA k-steps):
+//  * the P rows of a wave are private to it, so its P fragments go straight
+//    from global memory (L2) into registers with one contiguous 1 KB load per
+//    fragment, two slabs ahead (three register slab buffers);
+//  * the Q tile is shared by all waves: it is streamed into a 4-stage LDS
+//    ring with buffer_load ... lds (1 KB per instruction, lane l landing at
+//    byte 16 l), three slabs ahead, and each fragment is read back with one
+//    contiguous, conflict-free 16-byte-per-lane LDS read.
+// One barrier per slab, after the third k-step: by then every wave has read
+// the whole slab into registers, so its stage can take the slab four ahead,
+// and the MFMAs already issued keep the matrix pipe busy through the wait.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int OP>
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  if constexpr (OP == kOpBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+constexpr int kBM = kMfmaTile, kBN = kMfmaTile, kBK = 64;
+constexpr int kNW = 4, kNT = 64 * kNW;
+constexpr int kFM = kBM / kNW / 32;   // MFMA row blocks per wave (2)
+constexpr int kFN = kBN / 32;         // MFMA column blocks per wave (8)
+constexpr int kKS = kBK / 16;         // k-steps per slab (4)
+constexpr int kStages = 4;            // LDS ring depth for Q
+constexpr int kStageBytes = kBN * kBK * 2;   // 32 KB
+constexpr int kTN = kBN;              // epilogue: columns per wave
+constexpr int kLDE = kTN + 4;         // staged row length (floats)
+// each LDS stage array also holds one wave's 32-row epilogue staging block
+constexpr int kStageAlloc = kStageBytes > 32 * kLDE * 4 ? kStageBytes : 32 * kLDE * 4;
+// per-wave loads per slab: P: kFM row blocks x kKS fragments; Q: 8 row blocks / kNW waves x kKS
+constexpr int kLoadsA = kFM * kKS;
+constexpr int kLoadsB = (kBN / 32) / kNW * kKS;
+static_assert(kLoadsA == kLoadsB, "the vmcnt bookkeeping assumes equal A and B load groups");
+
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
+// (7 = no wait), lgkmcnt [11:8] (15 = no wait).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The P fragments of slab kt for this wave: kFM row blocks x kKS k-steps.
+__device__ __forceinline__ void load_a_slab(uint4 (&buf)[kFM][kKS], __amdgpu_buffer_rsrc_t r, int voff,
+                                            int sbase, int rb_stride, int kt) {
+#pragma unroll
+  for (int f = 0; f < kFM; ++f)
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      buf[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                r, voff, sbase + f * rb_stride + kt * 4096 + s * 1024, 0));
+}
+
+// The Q slab kt into LDS stage `stage`: this wave's 2 row blocks x 4 fragments.
+__device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t r, int voff, int sbase,
+                                            int rb_stride, int kt, int wave) {
+#pragma unroll
+  for (int f = 0; f < (kBN / 32) / kNW; ++f) {
+    const int rb = wave * ((kBN / 32) / kNW) + f;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + (rb * kKS + s) * 64), 16, voff,
+                                               sbase + rb * rb_stride + kt * 4096 + s * 1024, 0, 0);
+  }
+}
+
+// MFMAs of one k-step with the Q fragments of the next k-step read in between.
+template <int OP>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], int s,
+                                      const uint4 (&bcur)[kFN], uint4 (&bnext)[kFN], const uint4* next_frags,
+                                      bool read_next, int lane) {
+  if (read_next) {
+#pragma unroll
+    for (int y = 0; y < kFN; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
+  }
+#pragma unroll
+  for (int y = 0; y < kFN; ++y)
+#pragma unroll
+    for (int x = 0; x < kFM; ++x) acc[x][y] = mfma32<OP>(a[x][s], bcur[y], acc[x][y]);
+  if (read_next) {
+#pragma unroll
+    for (int g = 0; g < kFN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    }
+  }
+}
+
+// One slab: k-steps 0..3 of slab kt from registers `a` and LDS stage `cur`,
+// reading ahead into bf; the barrier and the ring refill (slab kt + 4 into
+// `cur`) sit after k-step 2.  Loads are issued unconditionally, also past
+// the last slab: buffer loads are range-checked against the descriptor and
+// the data is never used, and straight-line code lets the compiler count
+// outstanding loads exactly.
+template <int OP>
+__device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], uint4 (&bf)[2][kFN],
+                                     uint4* cur, const uint4* nxt, __amdgpu_buffer_rsrc_t rQ, int voff, int sQ,
+                                     int qstride, int kt, int wave, int lane) {
+  kstep<OP>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
+  kstep<OP>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
+  kstep<OP>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
+  // This wave's reads of slab kt have landed and its part of slab kt + 1 is
+  // in LDS (the 5 load groups issued after it may still be in flight); after
+  // the barrier the whole slab kt + 1 is visible and nobody reads `cur`.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 0));
+  block_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_b_slab(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
+  kstep<OP>(acc, a, 3, bf[1], bf[0], nxt, true, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Register epilogue of the MFMA kernel.
+//
+// For the 32 x 32 MFMA block at rows ib.., columns jb.. a lane holds 16
+// values in the accumulator arrangement "A": lane l, register r is element
+//   (ib + 8 (r / 4) + 4 (l / 32) + r % 4,  jb + l % 32).
+// Exchanging registers 4..7 of the lower half-wave with registers 0..3 of the
+// upper half-wave (and 12..15 with 8..11) by v_permlane32_swap gives "N":
+// lane l, register 8 h + e is (ib + 16 h + 8 (l / 32) + e, jb + l % 32), so a
+// lane holds 8 consecutive rows of one column: in the packed operand layout
+// that is this lane's 16 bytes of a fragment of C^T (row j, k = i).  Using
+// such a fragment as the MFMA A operand against an identity B fragment gives
+// the block transposed, exactly (products with 1 and sums with 0), in
+// arrangement "T": lane l, register 8 h + e is (ib + l % 32, jb + 16 h +
+// 8 (l / 32) + e), a fragment of C itself (row i, k = j).  Both C and C^T are
+// thus written as whole 1 KB fragments from registers, and the 16-bit
+// epilogue input is read as fragments of E^T (E is symmetric, or E = X read
+// from X^T).
+//
+// fp32 side matrices (R, Q, RZ of the Gram iteration) are only ever read by
+// this epilogue at the same block positions, so they are kept in arrangement
+// A, one 4 KB record per 32 x 32 block (lower-triangle blocks only): record
+// (ib / 32, jb / 32) of an ld x ld matrix, register r of lane l at offset
+// 256 (r / 4) + 4 l + r % 4.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t acc_rec(int ib, int jb, int ld) {
+  return (static_cast<int64_t>(ib >> 5) * (ld >> 5) + (jb >> 5)) << 10;
+}
+
+// Exchange the upper half-wave of x with the lower half-wave of y.
+__device__ __forceinline__ void xchg_halves(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return OP == kOpBF16 ? f32x2_to_bf16x2(lo, hi) : f32x2_to_f16x2(lo, hi);
+}
+
+// 16 values in arrangement A -> two 16-bit fragments in arrangement N.
+template <int OP>
+__device__ __forceinline__ void a_to_n16(const float (&v)[16], uint4 (&f)[2]) {
+  uint32_t d[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k] = pack2<OP>(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    xchg_halves(d[4 * h], d[4 * h + 2]);
+    xchg_halves(d[4 * h + 1], d[4 * h + 3]);
+  }
+  f[0] = make_uint4(d[0], d[1], d[2], d[3]);
+  f[1] = make_uint4(d[4], d[5], d[6], d[7]);
+}
+
+// Two 16-bit fragments in arrangement N -> 16 fp32 values in arrangement A.
+template <int OP>
+__device__ __forceinline__ void n16_to_a(const uint4& f0, const uint4& f1, float (&v)[16]) {
+  uint32_t d[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    xchg_halves(d[4 * h], d[4 * h + 2]);
+    xchg_halves(d[4 * h + 1], d[4 * h + 3]);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    v[2 * k] = OpT<OP>::to_f(static_cast<uint16_t>(d[k] & 0xffffu));
+    v[2 * k + 1] = OpT<OP>::to_f(static_cast<uint16_t>(d[k] >> 16));
+  }
+}
+
+// B fragment h of the 32 x 32 identity: lane l holds B[k][n] for n = l % 32,
+// k = 8 (l / 32) + e, equal to 1 where n == 16 h + k.
+template <int OP>
+__device__ __forceinline__ uint4 ident_frag(int h, int lane) {
+  const uint32_t one = OP == kOpBF16 ? 0x3F80u : 0x3C00u;
+  const int e = (lane & 31) - 16 * h - 8 * (lane >> 5);
+  uint32_t d[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) d[k] = (e >= 0 && (e >> 1) == k) ? one << (16 * (e & 1)) : 0u;
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// Fragments in arrangement N -> the transposed block in arrangement T.
+template <int OP>
+__device__ __forceinline__ void transpose16(const uint4 (&n)[2], const uint4 (&id)[2], uint4 (&t)[2]) {
+  f32x16_t d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) d[r] = 0.0f;
+  d = mfma32<OP>(n[0], id[0], d);
+  d = mfma32<OP>(n[1], id[1], d);
+  float dv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dv[r] = d[r];
+  a_to_n16<OP>(dv, t);
+}
+
+// Diagonal block of a symmetric product: N and T fragments address the same
+// elements (p, q) = (l % 32, 16 h + 8 (l / 32) + e); keep the owned value
+// C[max][min], which is T where p >= q and N elsewhere.
+__device__ __forceinline__ uint4 sym_select(const uint4& t, const uint4& n, int h, int lane) {
+  const int p = lane & 31, q0 = 16 * h + 8 * (lane >> 5);
+  const uint32_t tv[4] = {t.x, t.y, t.z, t.w}, nv[4] = {n.x, n.y, n.z, n.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = (p >= q0 + 2 * k ? 0x0000ffffu : 0u) | (p >= q0 + 2 * k + 1 ? 0xffff0000u : 0u);
+    r[k] = (tv[k] & m) | (nv[k] & ~m);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+template <int OP>
+__device__ __forceinline__ void store_frag(void* base, int64_t off, int lane, const uint4& f) {
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off + 8 * lane) = f;
+}
+
+// Final product: W <- W - lr (O + wd W) and the optional store of O, for
+// rows i0 .. i0 + 31 and columns j0 .. j0 + 255 of O staged in LDS
+// (row-major, LDE floats per row).  The loads of W for 16 rows (or columns)
+// are issued together before any of them is used.
+template <int LDE>
+__device__ __forceinline__ void final_rows(const GemmArgs& a, const EpiState& st, const float* ep, int i0, int j0,
+                                           int lane) {
+  constexpr int R = 16;
+  if (!a.transposed) {  // W is n x m: lane -> columns j .. j + 3 of every row
+    const int j = j0 + 4 * lane;
+    const int valid = a.m_real - j;
+    for (int r0 = 0; r0 < 32; r0 += R) {
+      float4 w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = i0 + r0 + r;
+        w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (st.w != nullptr && i < a.n_real && valid > 0)
+          w[r] = user_load4(st.w, static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = i0 + r0 + r;
+        if (i < a.n_real)
+          final_update4(a, st, static_cast<int64_t>(i) * a.user_ld + j, valid,
+                        *reinterpret_cast<const float4*>(ep + (r0 + r) * LDE + 4 * lane), w[r]);
+      }
+    }
+  } else {  // W is m x n: lane -> W[j][i .. i + 3] for 32 columns j of O
+    const int r4 = (lane & 7) * 4;
+    const int i = i0 + r4;
+    const int valid = a.n_real - i;
+    for (int c0 = 0; c0 < 256; c0 += 8 * R) {
+      float4 w[R];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int j = j0 + c0 + 8 * t + (lane >> 3);
+        w[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (st.w != nullptr && j < a.m_real && valid > 0)
+          w[t] = user_load4(st.w, static_cast<int64_t>(j) * a.user_ld + i, a.w_dtype, valid);
+      }
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int c = c0 + 8 * t + (lane >> 3);
+        if (j0 + c < a.m_real) {
+          const float4 o = make_float4(ep[(r4 + 0) * LDE + c], ep[(r4 + 1) * LDE + c], ep[(r4 + 2) * LDE + c],
+                                       ep[(r4 + 3) * LDE + c]);
+          final_update4(a, st, static_cast<int64_t>(j0 + c) * a.user_ld + i, valid, o, w[t]);
+        }
+      }
+    }
+  }
+}
+
+struct EpiSpec {
+  bool sym, fin, out32, q;
+  int e;  // epilogue input: 0 none, 1 16-bit fragments of E^T, 2 fp32 records
+};
+
+constexpr EpiSpec epi_spec(int k) {
+  return k == kEpiSym       ? EpiSpec{true, false, false, false, 0}
+         : k == kEpiSym32   ? EpiSpec{true, false, true, false, 0}
+         : k == kEpiSymE16  ? EpiSpec{true, false, false, false, 1}
+         : k == kEpiSymE16Q ? EpiSpec{true, false, false, true, 1}
+         : k == kEpiSymE32  ? EpiSpec{true, false, true, false, 2}
+         : k == kEpiGen     ? EpiSpec{false, false, false, false, 0}
+         : k == kEpiGenE16  ? EpiSpec{false, false, false, false, 1}
+         : k == kEpiFin     ? EpiSpec{false, true, false, false, 0}
+                            : EpiSpec{false, true, false, false, 1};
+}
+
+// This wave's output and input addresses, in elements, at MFMA block (0, 0)
+// of its 64 x 256 sub-tile (rows ib0 = 256 I + 64 w, columns jb0 = 256 J).
+// In the packed layout the fragments of block (x, y), half h, sit at
+//   T (rows i, k = j):  t16 + x rs_t + 2048 (y / 2) + 512 (2 (y % 2) + h)
+//   N (rows j, k = i):  n16 + y rs_n + 512 (2 x + h)
+// and the fp32 record of block (x, y) at r32 + x rx32 + 1024 y.
+struct EpiPtrs {
+  uint16_t *t16, *n16, *tq, *nq;
+  float *r32, *q32;
+  const uint16_t* e16;
+  const float* e32;
+  int64_t rs_t, rs_n, rs_e16, rx32, rxe32;
+};
+
+template <int KIND>
+__device__ __forceinline__ EpiPtrs epi_ptrs(const GemmArgs& a, int b, int I, int J, int wave) {
+  constexpr EpiSpec S = epi_spec(KIND);
+  EpiPtrs p{};
+  const int64_t ib5 = (I * kBM + wave * (kBM / kNW)) >> 5, ib6 = ib5 >> 1;
+  const int64_t jb5 = (J * kBN) >> 5, jb6 = jb5 >> 1;
+  const int64_t bO = static_cast<int64_t>(b) * a.sO;
+  if constexpr (!S.fin) {
+    uint16_t* o16 = static_cast<uint16_t*>(a.out16) + bO;
+    p.rs_t = static_cast<int64_t>(a.ldo >> 6) * 2048;
+    p.t16 = o16 + (ib5 * (a.ldo >> 6) + jb6) * 2048;
+    if constexpr (S.sym) {
+      p.rs_n = p.rs_t;
+      p.n16 = o16 + (jb5 * (a.ldo >> 6) + ib6) * 2048;
+    } else {
+      uint16_t* oT = static_cast<uint16_t*>(a.outT16) + static_cast<int64_t>(b) * a.sOT;
+      p.rs_n = static_cast<int64_t>(a.ldot >> 6) * 2048;
+      p.n16 = oT + (jb5 * (a.ldot >> 6) + ib6) * 2048;
+    }
+    p.rx32 = static_cast<int64_t>(a.ldo >> 5) * 1024;
+    if constexpr (S.out32) p.r32 = a.out32 + bO + (ib5 * (a.ldo >> 5) + jb5) * 1024;
+    if constexpr (S.q) {
+      uint16_t* q16 = static_cast<uint16_t*>(a.q16) + bO;
+      p.tq = q16 + (ib5 * (a.ldo >> 6) + jb6) * 2048;
+      p.nq = q16 + (jb5 * (a.ldo >> 6) + ib6) * 2048;
+      p.q32 = a.q32 + bO + (ib5 * (a.ldo >> 5) + jb5) * 1024;
+    }
+  }
+  const int64_t bE = static_cast<int64_t>(b) * a.sE;
+  if constexpr (S.e == 1) {
+    p.rs_e16 = static_cast<int64_t>(a.lde >> 6) * 2048;
+    p.e16 = static_cast<const uint16_t*>(a.E16) + bE + (jb5 * (a.lde >> 6) + ib6) * 2048;
+  }
+  if constexpr (S.e == 2) {
+    p.rxe32 = static_cast<int64_t>(a.lde >> 5) * 1024;
+    p.e32 = a.E32 + bE + (ib5 * (a.lde >> 5) + jb5) * 1024;
+  }
+  return p;
+}
+
+// The epilogue input of block (x, y): two 16-bit fragments of E^T, or the
+// four float4 of an fp32 record.
+template <int KIND>
+__device__ __forceinline__ void load_ein(const EpiPtrs& p, int x, int y, int lane, uint4 (&ein)[4]) {
+  constexpr EpiSpec S = epi_spec(KIND);
+  if constexpr (S.e == 1) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ein[h] = *reinterpret_cast<const uint4*>(p.e16 + y * p.rs_e16 + 512 * (2 * x + h) + 8 * lane);
+  } else if constexpr (S.e == 2) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      ein[g] = *reinterpret_cast<const uint4*>(p.e32 + x * p.rxe32 + 1024 * y + 256 * g + 4 * lane);
+  }
+}
+
+__device__ __forceinline__ void store_rec(float* r, int lane, const float (&v)[16]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<float4*>(r + 256 * g + 4 * lane) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+}
+
+// Both 16-bit copies of one block: T at (i, j) and N at (j, i) (symmetric),
+// or X and X^T (general).  On a diagonal block the two address the same
+// elements and both get the owned values.
+template <int OP, bool SYMDIAG>
+__device__ __forceinline__ void store_tn(uint16_t* t, uint16_t* n, const float (&v)[16], int lane, const uint4 (&id)[2],
+                                         bool dblk) {
+  uint4 n16[2], t16[2];
+  a_to_n16<OP>(v, n16);
+  transpose16<OP>(n16, id, t16);
+  if constexpr (SYMDIAG) {
+    if (dblk) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        t16[h] = sym_select(t16[h], n16[h], h, lane);
+        n16[h] = t16[h];
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    *reinterpret_cast<uint4*>(t + 512 * h + 8 * lane) = t16[h];
+    *reinterpret_cast<uint4*>(n + 512 * h + 8 * lane) = n16[h];
+  }
+}
+
+// Epilogue of MFMA block (x, y) of the wave (rows ib.., columns jb..):
+// v = alpha C + beta E + gamma [i == j < n_real] in arrangement A, then its
+// stores and partial sums.  MAYDIAG: the tile is on the diagonal of a
+// symmetric product and dblk says whether this block is (ib == jb).  Final
+// kinds write v to the wave's LDS staging area ep (row-major, kLDE floats per
+// row) for the update of W.
+template <int OP, int KIND, bool MAYDIAG>
+__device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const EpiPtrs& p, const f32x16_t& c,
+                                          const uint4 (&ein)[4], int x, int y, int ib, bool dblk, int lane,
+                                          const uint4 (&id)[2], float* ep) {
+  constexpr EpiSpec S = epi_spec(KIND);
+  const int jr = lane & 31, ir0 = 4 * (lane >> 5);
+  float v[16];
+  if constexpr (S.e == 1) {
+    float e[16];
+    n16_to_a<OP>(ein[0], ein[1], e);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = st.alpha * c[r] + st.beta * e[r];
+  } else if constexpr (S.e == 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint4& w = ein[r >> 2];
+      const uint32_t u = (r & 3) == 0 ? w.x : ((r & 3) == 1 ? w.y : ((r & 3) == 2 ? w.z : w.w));
+      v[r] = st.alpha * c[r] + st.beta * __uint_as_float(u);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = st.alpha * c[r];
+  }
+  if constexpr (MAYDIAG) {
+    if (dblk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+        if (ir == jr && ib + ir < a.n_real) v[r] += st.gamma;
+      }
+    }
+  }
+  if constexpr (S.fin) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + ir0 + (r & 3)) * kLDE + 32 * y + jr] = v[r];
+    return;
+  }
+  if constexpr (S.sym) {
+    if (a.part_out != nullptr) {  // an off-diagonal value stands for two
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+        const double xv = v[r];
+        if (!MAYDIAG || !dblk || ir > jr) {
+          st.ss += 2.0 * xv * xv;
+        } else if (ir == jr) {
+          st.ss += xv * xv;
+          st.tr += xv;
+        }
+      }
+    }
+  }
+  if constexpr (S.out32) store_rec(p.r32 + x * p.rx32 + 1024 * y, lane, v);
+  uint16_t* t = p.t16 + x * p.rs_t + 2048 * (y >> 1) + 512 * (2 * (y & 1));
+  uint16_t* n = p.n16 + y * p.rs_n + 512 * (2 * x);
+  store_tn<OP, S.sym && MAYDIAG>(t, n, v, lane, id, dblk);
+  if constexpr (S.q) {  // a fresh Q = v + a' I; it differs from v on diagonal blocks only
+    uint16_t* tq = p.tq + x * p.rs_t + 2048 * (y >> 1) + 512 * (2 * (y & 1));
+    uint16_t* nq = p.nq + y * p.rs_t + 512 * (2 * x);
+    if (MAYDIAG && dblk) {
+      float q[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r >> 2) + ir0 + (r & 3);
+        q[r] = (ir == jr && ib + ir < a.n_real) ? v[r] + st.ap : v[r];
+      }
+      store_rec(p.q32 + x * p.rx32 + 1024 * y, lane, q);
+      store_tn<OP, true>(tq, nq, q, lane, id, true);
+    } else {
+      store_rec(p.q32 + x * p.rx32 + 1024 * y, lane, v);
+      store_tn<OP, false>(tq, nq, v, lane, id, false);
+    }
+  }
+}
+
+// Block BLK + U of a group (see epi_run); recursion keeps every block index a
+// compile-time constant.
+template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int U>
+__device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
+                                         const f32x16_t (&acc)[kFM][kFN], const uint4 (&cur)[G][4], int I, int wave,
+                                         int lane, const uint4 (&id)[2], float* ep) {
+  constexpr int x = (BLK + U) / kFN, y = (BLK + U) % kFN;
+  const int rel = y - (2 * wave + x);  // diagonal tiles: > 0 is the mirror of an owned block
+  if (!MAYDIAG || rel <= 0)
+    epi_block<OP, KIND, MAYDIAG>(a, st, p, acc[x][y], cur[U], x, y, I * kBM + wave * (kBM / kNW) + 32 * x,
+                                 MAYDIAG && rel == 0, lane, id, ep);
+  if constexpr (U + 1 < G) epi_unit<OP, KIND, MAYDIAG, G, BLK, U + 1>(a, st, p, acc, cur, I, wave, lane, id, ep);
+}
+
+// Blocks BLK .. BLK + G - 1 (block index 8 x + y) of the wave's register
+// epilogue with their inputs in `cur`; the inputs of the next group are
+// loaded first, so their latency overlaps this group's work.  All blocks are
+// named by template arguments: the accumulators stay in registers.
+template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int END>
+__device__ __forceinline__ void epi_run(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
+                                        const f32x16_t (&acc)[kFM][kFN], uint4 (&cur)[G][4], int I, int wave,
+                                        int lane, const uint4 (&id)[2], float* ep) {
+  uint4 nxt[G][4];
+  if constexpr (BLK + G < END) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int x = (BLK + G + u) / kFN, y = (BLK + G + u) % kFN;
+      if (!MAYDIAG || y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, nxt[u]);
+    }
+  }
+  epi_unit<OP, KIND, MAYDIAG, G, BLK, 0>(a, st, p, acc, cur, I, wave, lane, id, ep);
+  if constexpr (BLK + G < END) epi_run<OP, KIND, MAYDIAG, G, BLK + G, END>(a, st, p, acc, nxt, I, wave, lane, id, ep);
+}
+
+template <int OP, int KIND, bool MAYDIAG, int BEGIN, int END>
+__device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
+                                          const f32x16_t (&acc)[kFM][kFN], int I, int wave, int lane,
+                                          const uint4 (&id)[2], float* ep) {
+  constexpr int G = epi_spec(KIND).e == 2 ? 2 : 4;  // fp32 inputs take 16 registers a block
+  uint4 cur[G][4];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int x = (BEGIN + u) / kFN, y = (BEGIN + u) % kFN;
+    if (!MAYDIAG || y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, cur[u]);
+  }
+  epi_run<OP, KIND, MAYDIAG, G, BEGIN, END>(a, st, p, acc, cur, I, wave, lane, id, ep);
+}
+
+// The register epilogue of the wave's 64 x 256 sub-tile; the last product
+// stages O through LDS one 32-row block at a time so that the user's
+// row-major W is read and written along its rows.
+template <int OP, int KIND>
+__device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st, const f32x16_t (&acc)[kFM][kFN], int b,
+                                              int I, int J, int wave, int lane, float* ep) {
+  static_assert(kFM == 2 && kFN == 8, "the epilogue walks 2 x 8 MFMA blocks");
+  constexpr EpiSpec S = epi_spec(KIND);
+  const EpiPtrs p = epi_ptrs<KIND>(a, b, I, J, wave);
+  if constexpr (S.fin) {
+    const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // no transposes here
+    epi_range<OP, KIND, false, 0, 8>(a, st, p, acc, I, wave, lane, id, ep);
+    __syncthreads();
+    final_rows<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * kBN, lane);
+    __syncthreads();
+    epi_range<OP, KIND, false, 8, 16>(a, st, p, acc, I, wave, lane, id, ep);
+    __syncthreads();
+    final_rows<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * kBN, lane);
+  } else {
+    const uint4 id[2] = {ident_frag<OP>(0, lane), ident_frag<OP>(1, lane)};
+    if (S.sym && I == J)
+      epi_range<OP, KIND, S.sym, 0, 16>(a, st, p, acc, I, wave, lane, id, ep);
+    else
+      epi_range<OP, KIND, false, 0, 16>(a, st, p, acc, I, wave, lane, id, ep);
+  }
+}
+
+template <int OP, int KIND>
+__global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
+  // The Q ring is four separate arrays, each named statically at every access,
+  // so the compiler's wait for an LDS read covers only the DMA into that stage.
+  __shared__ uint4 stg0[kStageAlloc / 16], stg1[kStageAlloc / 16], stg2[kStageAlloc / 16], stg3[kStageAlloc / 16];
+  __shared__ double red[2 * kNW];
+  int b, tile, I, J;
+  block_coords(a, kBM, kBN, b, tile, I, J);
+  EpiState st;
+  block_init<kNT>(a, b, tile, red, st);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint16_t* Pm = static_cast<const uint16_t*>(a.P) + static_cast<int64_t>(b) * a.sP;
+  const uint16_t* Qm = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(b) * a.sQ;
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pm, static_cast<int64_t>(a.Mdim) * a.ldp * 2);
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qm, static_cast<int64_t>(a.Ndim) * a.ldq * 2);
+  const int voff = lane * 16;
+  // byte offset of a row block = (row / 32) * (K / 64) * 4 KB
+  const int pstride = (a.ldp >> 6) * 4096, qstride = (a.ldq >> 6) * 4096;
+  const int sP = (I * (kBM / 32) + wave * kFM) * pstride;
+  const int sQ = J * (kBN / 32) * qstride;
+
+  f32x16_t acc[kFM][kFN];
+#pragma unroll
+  for (int x = 0; x < kFM; ++x)
+#pragma unroll
+    for (int y = 0; y < kFN; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
+
+  const int nk = a.K / kBK;  // a multiple of 4: every operand dimension is a multiple of 256
+  uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS];
+  uint4 bf[2][kFN];
+  // prologue: Q slabs 0..3 into the ring, P slabs 0 and 1 into registers
+  load_b_slab(stg0, rQ, voff, sQ, qstride, 0, wave);
+  load_b_slab(stg1, rQ, voff, sQ, qstride, 1, wave);
+  load_b_slab(stg2, rQ, voff, sQ, qstride, 2, wave);
+  load_b_slab(stg3, rQ, voff, sQ, qstride, 3, wave);
+  load_a_slab(abuf0, rP, voff, sP, pstride, 0);
+  load_a_slab(abuf1, rP, voff, sP, pstride, 1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 15));  // Q slab 0 landed
+  block_barrier();
+#pragma unroll
+  for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
+
+  // 12 slabs per trip (lcm of the 4 LDS stages and the 3 P register buffers);
+  // nk is a multiple of 4, so a remainder of 4 or 8 slabs follows.
+#define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
+  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 2);                                             \
+  slab<OP>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
+  int kt = 0;
+  for (; kt + 12 <= nk; kt += 12) {
+    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
+    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
+    MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
+    MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
+    MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
+    MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
+    MUON_SLAB(8, abuf2, abuf1, stg0, stg1)
+    MUON_SLAB(9, abuf0, abuf2, stg1, stg2)
+    MUON_SLAB(10, abuf1, abuf0, stg2, stg3)
+    MUON_SLAB(11, abuf2, abuf1, stg3, stg0)
+  }
+  if (kt + 4 <= nk) {
+    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
+    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
+    if (kt + 8 <= nk) {
+      MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
+      MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
+      MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
+      MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
+    }
+  }
+#undef MUON_SLAB
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  block_barrier();
+
+  // The epilogue runs from registers; the last product stages O through this
+  // wave's LDS stage.
+  float* ep = reinterpret_cast<float*>(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
+  epilogue_mfma<OP, KIND>(a, st, acc, b, I, J, wave, lane, ep);
+  block_partials<kNT>(a, b, tile, red, st);
+}
+
+template <int OP>
+hipError_t launch_gemm_mfma(const GemmArgs& a, int batch, int kind, hipStream_t s) {
+  const dim3 grid(a.ntiles, batch), block(kNT);
+  switch (kind) {
+    case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym>), grid, block, 0, s, a); break;
+    case kEpiSym32: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym32>), grid, block, 0, s, a); break;
+    case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16>), grid, block, 0, s, a); break;
+    case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q>), grid, block, 0, s, a); break;
+    case kEpiSymE32: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE32>), grid, block, 0, s, a); break;
+    case kEpiGen: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGen>), grid, block, 0, s, a); break;
+    case kEpiGenE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGenE16>), grid, block, 0, s, a); break;
+    case kEpiFin: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFin>), grid, block, 0, s, a); break;
+    case kEpiFinE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFinE16>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -55,8 +55,34 @@ struct GemmArgs {
   float lr, wd;
 };
 
+// Block tile edges of the MFMA kernels (16-bit operands) and of the fp32
+// check path.
+constexpr int kMfmaTile = 256;
+constexpr int kCheckTile = 64;
+
+// Epilogue kinds of the MFMA kernel, one kernel instantiation each, so that
+// every epilogue is straight-line code.
+enum EpiKind : int {
+  kEpiSym = 0,  // symmetric: C -> 16-bit (X X^T of the standard iteration)
+  kEpiSym32,    // symmetric: C -> fp32 record + 16-bit (R = X X^T of the Gram iteration)
+  kEpiSymE16,   // symmetric: v = alpha C + beta E + gamma I, E 16-bit -> 16-bit (B', Z')
+  kEpiSymE16Q,  // as kEpiSymE16, plus a fresh Q = v + a' I (fp32 record + 16-bit)
+  kEpiSymE32,   // symmetric: v = alpha C + beta E, E an fp32 record -> fp32 record + 16-bit
+  kEpiGen,      // general: C -> X and X^T (Q X at a restart)
+  kEpiGenE16,   // general: v = alpha C + beta X -> X and X^T (B X)
+  kEpiFin,      // last product: O = C -> update of W
+  kEpiFinE16,   // last product: O = alpha C + beta X -> update of W
+  kNumEpiKinds
+};
+
+// The epilogue kind a launch's arguments ask for, or -1 if none matches.
+int epi_kind(const GemmArgs& a);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_gemm(const GemmArgs& a, int batch, int op, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, int batch, int kind, hipStream_t s);
+hipError_t launch_gemm_f16(const GemmArgs& a, int batch, int kind, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, int batch, hipStream_t s);
 int gemm_tile(int op);  // block tile edge of the GEMM kernel used for an operand type
 
 struct NormArgs {
