@@ -32,7 +32,7 @@ struct Plan {
   muon_ns_variant variant;
   size_t XN, XT[2];
   size_t A16, B16;                                        // standard
-  size_t R32, Q32, RZ32, R16, Z16, RZ16, Q16[2];          // Gram
+  size_t R16, Z16, RZ16, Q16[2];                         // Gram
   size_t normpart, tilepart, shift;
   size_t total;
 };
@@ -164,9 +164,6 @@ bool make_plan(int batch, int rows, int cols, muon_ns_variant v, const Config& c
     p->A16 = take(nn * p->esz);
     p->B16 = take(nn * p->esz);
   } else {
-    p->R32 = take(nn * 4);
-    p->Q32 = take(nn * 4);
-    p->RZ32 = take(nn * 4);
     p->R16 = take(nn * p->esz);
     p->Z16 = take(nn * p->esz);
     p->RZ16 = take(nn * p->esz);
@@ -263,11 +260,8 @@ hipError_t gemm(const Plan& p, const GemmArgs& g, const char* role, hipStream_t 
     const double K = g.K == p.m_pad ? m : n;
     flops = n * n * K;
     bytes = (g.P == g.Q ? 1.0 : 2.0) * n * K * esz;
-    if (g.E32 != nullptr) bytes += n * n * 4;
-    if (g.E16 != nullptr && g.E16 != g.P) bytes += n * n * esz;
-    if (g.out32 != nullptr) bytes += n * n * 4;
+    if (g.E16 != nullptr && g.E16 != g.P && g.E16 != g.Q) bytes += n * n * esz;
     if (g.out16 != nullptr) bytes += n * n * esz;
-    if (g.q32 != nullptr) bytes += n * n * 4;
     if (g.q16 != nullptr) bytes += n * n * esz;
   } else {
     flops = 2.0 * n * n * m;
@@ -393,9 +387,6 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
   const int64_t sx = static_cast<int64_t>(p.n_pad) * p.m_pad;
   double* tp = reinterpret_cast<double*>(ws + p.tilepart);
   float* shift = reinterpret_cast<float*>(ws + p.shift);
-  float* R32 = reinterpret_cast<float*>(ws + p.R32);
-  float* Q32 = reinterpret_cast<float*>(ws + p.Q32);
-  float* RZ32 = reinterpret_cast<float*>(ws + p.RZ32);
   char* R16 = ws + p.R16;
   char* Z16 = ws + p.Z16;
   char* RZ16 = ws + p.RZ16;
@@ -404,10 +395,9 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
   const int ntri = nt * (nt + 1) / 2;
   int xc = 0, qc = 0;
 
-  auto gram_of_x = [&]() {  // R = X X^T (fp32 and operand copies) + partials
+  auto gram_of_x = [&]() {  // R = X X^T + partials
     GemmArgs g = base_args(p);
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
-    g.out32 = R32;
     g.out16 = R16;
     g.part_out = c.shift ? tp : nullptr;
     return gemm(p, g, "XXt", s);
@@ -433,20 +423,16 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.shift_out = shift;
     }
     g.out16 = Z16;
-    if (fresh) {
-      g.q32 = Q32;
-      g.q16 = ws + p.Q16[qc];
-    }
+    if (fresh) g.q16 = ws + p.Q16[qc];
     MUON_LAUNCH(gemm(p, g, "Z", s));
     const float* sh = c.shift ? shift : nullptr;
     if (!fresh) {  // Q <- Q Z' + a' Q
       g = base_args(p);
       set_sym(g, p, ws + p.Q16[qc], Z16, p.n_pad, snn, p.n_pad);
-      g.E32 = Q32;
+      g.E16 = ws + p.Q16[qc];
       g.beta_a = 1.0f;
       g.coef_a = a;
       g.shift_in = sh;
-      g.out32 = Q32;
       g.out16 = ws + p.Q16[qc ^ 1];
       qc ^= 1;
       MUON_LAUNCH(gemm(p, g, "QZ", s));
@@ -466,21 +452,19 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       // RZ = R Z' + a' R
       g = base_args(p);
       set_sym(g, p, R16, Z16, p.n_pad, snn, p.n_pad);
-      g.E32 = R32;
+      g.E16 = R16;
       g.beta_a = 1.0f;
       g.coef_a = a;
       g.shift_in = sh;
-      g.out32 = RZ32;
       g.out16 = RZ16;
       MUON_LAUNCH(gemm(p, g, "RZ", s));
       // R <- Z' RZ + a' RZ
       g = base_args(p);
       set_sym(g, p, Z16, RZ16, p.n_pad, snn, p.n_pad);
-      g.E32 = RZ32;
+      g.E16 = RZ16;
       g.beta_a = 1.0f;
       g.coef_a = a;
       g.shift_in = sh;
-      g.out32 = R32;
       g.out16 = R16;
       g.part_out = c.shift ? tp : nullptr;
       MUON_LAUNCH(gemm(p, g, "ZRZ", s));

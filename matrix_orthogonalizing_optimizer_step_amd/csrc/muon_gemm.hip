@@ -6,25 +6,19 @@ namespace muon {
 int gemm_tile(int op) { return op == kOpF32 ? kCheckTile : kMfmaTile; }
 
 int epi_kind(const GemmArgs& g) {
-  const bool e16 = g.E16 != nullptr, e32 = g.E32 != nullptr, q = g.q16 != nullptr || g.q32 != nullptr;
-  if (e16 && e32) return -1;
+  const bool e16 = g.E16 != nullptr, q = g.q16 != nullptr;
   if (g.final_mode) {
-    if (g.sym || e32 || q || g.out16 != nullptr || g.outT16 != nullptr || g.out32 != nullptr || g.part_out != nullptr)
-      return -1;
+    if (g.sym || q || g.out16 != nullptr || g.outT16 != nullptr || g.part_out != nullptr) return -1;
     return e16 ? kEpiFinE16 : kEpiFin;
   }
   if (g.out16 == nullptr) return -1;
   if (g.sym) {
     if (g.outT16 != nullptr) return -1;
-    if (q) {  // a fresh Q comes with Z' only
-      return e16 && g.q16 != nullptr && g.q32 != nullptr && g.out32 == nullptr ? kEpiSymE16Q : -1;
-    }
-    if (e32) return g.out32 != nullptr ? kEpiSymE32 : -1;
-    if (e16) return g.out32 == nullptr ? kEpiSymE16 : -1;
-    return g.out32 != nullptr ? kEpiSym32 : kEpiSym;
+    if (q) return e16 ? kEpiSymE16Q : -1;  // a fresh Q comes with Z' only
+    return e16 ? kEpiSymE16 : kEpiSym;
   }
   // general products write X and X^T and have no diagonal term
-  if (g.outT16 == nullptr || g.out32 != nullptr || e32 || q || g.part_out != nullptr) return -1;
+  if (g.outT16 == nullptr || q || g.part_out != nullptr) return -1;
   if (g.gamma_c != 0.0f || g.gamma_a != 0.0f) return -1;
   return e16 ? kEpiGenE16 : kEpiGen;
 }

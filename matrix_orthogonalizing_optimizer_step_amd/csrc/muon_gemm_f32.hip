@@ -19,7 +19,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
   constexpr int UNR = NIT < 4 ? NIT : 4;
   const int cl = (lane % LPR) * 4;
   const int rl = lane / LPR;
-  const bool has_e = a.E32 != nullptr || a.E16 != nullptr;
+  const bool has_e = a.E16 != nullptr;
   const bool wrow = a.final_mode && !a.transposed && a.W != nullptr;
   const int64_t bE = static_cast<int64_t>(b) * a.sE;
   const int64_t bO = static_cast<int64_t>(b) * a.sO;
@@ -30,8 +30,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       const int i = i0 + (it0 + u) * RPIT + rl, j = j0 + cl;
       ev[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       wv[u] = ev[u];
-      if (a.E32 != nullptr) ev[u] = load4_op<kOpF32>(a.E32, bE + static_cast<int64_t>(i) * a.lde + j);
-      else if (has_e) ev[u] = load4_op<OP>(a.E16, bE + op_index<OP>(i, j, a.lde));
+      if (has_e) ev[u] = load4_op<OP>(a.E16, bE + op_index<OP>(i, j, a.lde));
       if (wrow && i < a.n_real) {
         const int valid = a.m_real - j;
         if (valid > 0) wv[u] = user_load4(st.w, static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
@@ -61,18 +60,13 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       if (own == 0) continue;
       float4 q = v;
       if (dg) f4set(q, dk, f4get(q, dk) + st.ap);
-      const int64_t o32 = bO + static_cast<int64_t>(i) * a.ldo + j;
       const int64_t o16 = bO + op_index<OP>(i, j, a.ldo);
       if (own == 4) {
-        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o32, v);
         if (a.out16 != nullptr) store4_op<OP>(a.out16, o16, v);
-        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o32, q);
         if (a.q16 != nullptr) store4_op<OP>(a.q16, o16, q);
       } else {
         for (int k = 0; k < own; ++k) {
-          if (a.out32 != nullptr) a.out32[o32 + k] = f4get(v, k);
           if (a.out16 != nullptr) store1_op<OP>(a.out16, o16 + k, f4get(v, k));
-          if (a.q32 != nullptr) a.q32[o32 + k] = f4get(q, k);
           if (a.q16 != nullptr) store1_op<OP>(a.q16, o16 + k, f4get(q, k));
         }
       }
@@ -110,19 +104,14 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& a, int b, EpiStat
       // elements i + k > j are mirrored to (j, i + k)
       const int first = j - i + 1;  // first k with i + k > j
       if (first >= 4) continue;
-      const int64_t o32 = bO + static_cast<int64_t>(j) * a.ldo + i;
       const int64_t o16 = bO + op_index<OP>(j, i, a.ldo);
       if (first <= 0) {
-        if (a.out32 != nullptr) store4_op<kOpF32>(a.out32, o32, v);
         if (a.out16 != nullptr) store4_op<OP>(a.out16, o16, v);
-        if (a.q32 != nullptr) store4_op<kOpF32>(a.q32, o32, v);
         if (a.q16 != nullptr) store4_op<OP>(a.q16, o16, v);
       } else {
         for (int k = first; k < 4; ++k) {
           const float x = f4get(v, k);
-          if (a.out32 != nullptr) a.out32[o32 + k] = x;
           if (a.out16 != nullptr) store1_op<OP>(a.out16, o16 + k, x);
-          if (a.q32 != nullptr) a.q32[o32 + k] = x;
           if (a.q16 != nullptr) store1_op<OP>(a.q16, o16 + k, x);
         }
       }

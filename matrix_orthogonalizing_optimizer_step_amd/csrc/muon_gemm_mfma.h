@@ -153,16 +153,6 @@ __device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)
 // epilogue input is read as fragments of E^T (E is symmetric, or E = X read
 // from X^T).
 //
-// fp32 side matrices (R, Q, RZ of the Gram iteration) are only ever read by
-// this epilogue at the same block positions, so they are kept in arrangement
-// A, one 4 KB record per 32 x 32 block (lower-triangle blocks only): record
-// (ib / 32, jb / 32) of an ld x ld matrix, register r of lane l at offset
-// 256 (r / 4) + 4 l + r % 4.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t acc_rec(int ib, int jb, int ld) {
-  return (static_cast<int64_t>(ib >> 5) * (ld >> 5) + (jb >> 5)) << 10;
-}
-
 // Exchange the upper half-wave of x with the lower half-wave of y.
 __device__ __forceinline__ void xchg_halves(uint32_t& x, uint32_t& y) {
   const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
@@ -307,20 +297,18 @@ __device__ __forceinline__ void final_rows(const GemmArgs& a, const EpiState& st
 }
 
 struct EpiSpec {
-  bool sym, fin, out32, q;
-  int e;  // epilogue input: 0 none, 1 16-bit fragments of E^T, 2 fp32 records
+  bool sym, fin, q;
+  bool e;  // an epilogue input E, read as 16-bit fragments of E^T
 };
 
 constexpr EpiSpec epi_spec(int k) {
-  return k == kEpiSym       ? EpiSpec{true, false, false, false, 0}
-         : k == kEpiSym32   ? EpiSpec{true, false, true, false, 0}
-         : k == kEpiSymE16  ? EpiSpec{true, false, false, false, 1}
-         : k == kEpiSymE16Q ? EpiSpec{true, false, false, true, 1}
-         : k == kEpiSymE32  ? EpiSpec{true, false, true, false, 2}
-         : k == kEpiGen     ? EpiSpec{false, false, false, false, 0}
-         : k == kEpiGenE16  ? EpiSpec{false, false, false, false, 1}
-         : k == kEpiFin     ? EpiSpec{false, true, false, false, 0}
-                            : EpiSpec{false, true, false, false, 1};
+  return k == kEpiSym       ? EpiSpec{true, false, false, false}
+         : k == kEpiSymE16  ? EpiSpec{true, false, false, true}
+         : k == kEpiSymE16Q ? EpiSpec{true, false, true, true}
+         : k == kEpiGen     ? EpiSpec{false, false, false, false}
+         : k == kEpiGenE16  ? EpiSpec{false, false, false, true}
+         : k == kEpiFin     ? EpiSpec{false, true, false, false}
+                            : EpiSpec{false, true, false, true};
 }
 
 // This wave's output and input addresses, in elements, at MFMA block (0, 0)
@@ -328,13 +316,11 @@ constexpr EpiSpec epi_spec(int k) {
 // In the packed layout the fragments of block (x, y), half h, sit at
 //   T (rows i, k = j):  t16 + x rs_t + 2048 (y / 2) + 512 (2 (y % 2) + h)
 //   N (rows j, k = i):  n16 + y rs_n + 512 (2 x + h)
-// and the fp32 record of block (x, y) at r32 + x rx32 + 1024 y.
+// and the fragments of E^T for block (x, y) at e16 + y rs_e16 + 512 (2 x + h).
 struct EpiPtrs {
   uint16_t *t16, *n16, *tq, *nq;
-  float *r32, *q32;
   const uint16_t* e16;
-  const float* e32;
-  int64_t rs_t, rs_n, rs_e16, rx32, rxe32;
+  int64_t rs_t, rs_n, rs_e16;
 };
 
 template <int KIND>
@@ -356,47 +342,27 @@ __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmArgs& a, int b, int I, int
       p.rs_n = static_cast<int64_t>(a.ldot >> 6) * 2048;
       p.n16 = oT + (jb5 * (a.ldot >> 6) + ib6) * 2048;
     }
-    p.rx32 = static_cast<int64_t>(a.ldo >> 5) * 1024;
-    if constexpr (S.out32) p.r32 = a.out32 + bO + (ib5 * (a.ldo >> 5) + jb5) * 1024;
     if constexpr (S.q) {
       uint16_t* q16 = static_cast<uint16_t*>(a.q16) + bO;
       p.tq = q16 + (ib5 * (a.ldo >> 6) + jb6) * 2048;
       p.nq = q16 + (jb5 * (a.ldo >> 6) + ib6) * 2048;
-      p.q32 = a.q32 + bO + (ib5 * (a.ldo >> 5) + jb5) * 1024;
     }
   }
-  const int64_t bE = static_cast<int64_t>(b) * a.sE;
-  if constexpr (S.e == 1) {
+  if constexpr (S.e) {
     p.rs_e16 = static_cast<int64_t>(a.lde >> 6) * 2048;
-    p.e16 = static_cast<const uint16_t*>(a.E16) + bE + (jb5 * (a.lde >> 6) + ib6) * 2048;
-  }
-  if constexpr (S.e == 2) {
-    p.rxe32 = static_cast<int64_t>(a.lde >> 5) * 1024;
-    p.e32 = a.E32 + bE + (ib5 * (a.lde >> 5) + jb5) * 1024;
+    p.e16 = static_cast<const uint16_t*>(a.E16) + static_cast<int64_t>(b) * a.sE + (jb5 * (a.lde >> 6) + ib6) * 2048;
   }
   return p;
 }
 
-// The epilogue input of block (x, y): two 16-bit fragments of E^T, or the
-// four float4 of an fp32 record.
+// The epilogue input of block (x, y): its two 16-bit fragments of E^T.
 template <int KIND>
-__device__ __forceinline__ void load_ein(const EpiPtrs& p, int x, int y, int lane, uint4 (&ein)[4]) {
-  constexpr EpiSpec S = epi_spec(KIND);
-  if constexpr (S.e == 1) {
+__device__ __forceinline__ void load_ein(const EpiPtrs& p, int x, int y, int lane, uint4 (&ein)[2]) {
+  if constexpr (epi_spec(KIND).e) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       ein[h] = *reinterpret_cast<const uint4*>(p.e16 + y * p.rs_e16 + 512 * (2 * x + h) + 8 * lane);
-  } else if constexpr (S.e == 2) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      ein[g] = *reinterpret_cast<const uint4*>(p.e32 + x * p.rxe32 + 1024 * y + 256 * g + 4 * lane);
   }
-}
-
-__device__ __forceinline__ void store_rec(float* r, int lane, const float (&v)[16]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-    *reinterpret_cast<float4*>(r + 256 * g + 4 * lane) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
 }
 
 // Both 16-bit copies of one block: T at (i, j) and N at (j, i) (symmetric),
@@ -432,23 +398,16 @@ __device__ __forceinline__ void store_tn(uint16_t* t, uint16_t* n, const float (
 // row) for the update of W.
 template <int OP, int KIND, bool MAYDIAG>
 __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const EpiPtrs& p, const f32x16_t& c,
-                                          const uint4 (&ein)[4], int x, int y, int ib, bool dblk, int lane,
+                                          const uint4 (&ein)[2], int x, int y, int ib, bool dblk, int lane,
                                           const uint4 (&id)[2], float* ep) {
   constexpr EpiSpec S = epi_spec(KIND);
   const int jr = lane & 31, ir0 = 4 * (lane >> 5);
   float v[16];
-  if constexpr (S.e == 1) {
+  if constexpr (S.e) {
     float e[16];
     n16_to_a<OP>(ein[0], ein[1], e);
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = st.alpha * c[r] + st.beta * e[r];
-  } else if constexpr (S.e == 2) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint4& w = ein[r >> 2];
-      const uint32_t u = (r & 3) == 0 ? w.x : ((r & 3) == 1 ? w.y : ((r & 3) == 2 ? w.z : w.w));
-      v[r] = st.alpha * c[r] + st.beta * __uint_as_float(u);
-    }
   } else {
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = st.alpha * c[r];
@@ -482,7 +441,6 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
       }
     }
   }
-  if constexpr (S.out32) store_rec(p.r32 + x * p.rx32 + 1024 * y, lane, v);
   uint16_t* t = p.t16 + x * p.rs_t + 2048 * (y >> 1) + 512 * (2 * (y & 1));
   uint16_t* n = p.n16 + y * p.rs_n + 512 * (2 * x);
   store_tn<OP, S.sym && MAYDIAG>(t, n, v, lane, id, dblk);
@@ -496,10 +454,8 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
         const int ir = 8 * (r >> 2) + ir0 + (r & 3);
         q[r] = (ir == jr && ib + ir < a.n_real) ? v[r] + st.ap : v[r];
       }
-      store_rec(p.q32 + x * p.rx32 + 1024 * y, lane, q);
       store_tn<OP, true>(tq, nq, q, lane, id, true);
     } else {
-      store_rec(p.q32 + x * p.rx32 + 1024 * y, lane, v);
       store_tn<OP, false>(tq, nq, v, lane, id, false);
     }
   }
@@ -509,7 +465,7 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
 // compile-time constant.
 template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int U>
 __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
-                                         const f32x16_t (&acc)[kFM][kFN], const uint4 (&cur)[G][4], int I, int wave,
+                                         const f32x16_t (&acc)[kFM][kFN], const uint4 (&cur)[G][2], int I, int wave,
                                          int lane, const uint4 (&id)[2], float* ep) {
   constexpr int x = (BLK + U) / kFN, y = (BLK + U) % kFN;
   const int rel = y - (2 * wave + x);  // diagonal tiles: > 0 is the mirror of an owned block
@@ -525,9 +481,9 @@ __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const 
 // named by template arguments: the accumulators stay in registers.
 template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int END>
 __device__ __forceinline__ void epi_run(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
-                                        const f32x16_t (&acc)[kFM][kFN], uint4 (&cur)[G][4], int I, int wave,
+                                        const f32x16_t (&acc)[kFM][kFN], uint4 (&cur)[G][2], int I, int wave,
                                         int lane, const uint4 (&id)[2], float* ep) {
-  uint4 nxt[G][4];
+  uint4 nxt[G][2];
   if constexpr (BLK + G < END) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
@@ -543,8 +499,8 @@ template <int OP, int KIND, bool MAYDIAG, int BEGIN, int END>
 __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
                                           const f32x16_t (&acc)[kFM][kFN], int I, int wave, int lane,
                                           const uint4 (&id)[2], float* ep) {
-  constexpr int G = epi_spec(KIND).e == 2 ? 2 : 4;  // fp32 inputs take 16 registers a block
-  uint4 cur[G][4];
+  constexpr int G = 4;
+  uint4 cur[G][2];
 #pragma unroll
   for (int u = 0; u < G; ++u) {
     const int x = (BEGIN + u) / kFN, y = (BEGIN + u) % kFN;
@@ -675,10 +631,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int batch, int kind, hipStream_t 
   const dim3 grid(a.ntiles, batch), block(kNT);
   switch (kind) {
     case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym>), grid, block, 0, s, a); break;
-    case kEpiSym32: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym32>), grid, block, 0, s, a); break;
     case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16>), grid, block, 0, s, a); break;
     case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q>), grid, block, 0, s, a); break;
-    case kEpiSymE32: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE32>), grid, block, 0, s, a); break;
     case kEpiGen: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGen>), grid, block, 0, s, a); break;
     case kEpiGenE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGenE16>), grid, block, 0, s, a); break;
     case kEpiFin: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFin>), grid, block, 0, s, a); break;

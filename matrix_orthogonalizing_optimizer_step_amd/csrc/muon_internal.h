@@ -39,11 +39,11 @@ struct GemmArgs {
   const float* shift_in;               // per-matrix a' from an earlier launch
   float* shift_out;                    // per-matrix a' written by tile 0
 
-  const float* E32; const void* E16; int64_t sE; int lde;  // epilogue input (one or none)
+  const void* E16; int64_t sE; int lde;   // epilogue input E (operand type) or null
 
-  float* out32; void* out16; int64_t sO; int ldo;          // outputs, layout of C
+  void* out16; int64_t sO; int ldo;       // output (operand type and layout)
   void* outT16; int64_t sOT; int ldot;                     // transposed copy (non-symmetric only)
-  float* q32; void* q16;                                   // v + a' I (fresh Q), layout of out
+  void* q16;                              // v + a' I (a fresh Q), layout of out16
   double* part_out;                                        // (trace, sumsq) of v per tile
 
   int final_mode;                   // 1: v is O; update W and optionally store O
@@ -63,11 +63,9 @@ constexpr int kCheckTile = 64;
 // Epilogue kinds of the MFMA kernel, one kernel instantiation each, so that
 // every epilogue is straight-line code.
 enum EpiKind : int {
-  kEpiSym = 0,  // symmetric: C -> 16-bit (X X^T of the standard iteration)
-  kEpiSym32,    // symmetric: C -> fp32 record + 16-bit (R = X X^T of the Gram iteration)
-  kEpiSymE16,   // symmetric: v = alpha C + beta E + gamma I, E 16-bit -> 16-bit (B', Z')
-  kEpiSymE16Q,  // as kEpiSymE16, plus a fresh Q = v + a' I (fp32 record + 16-bit)
-  kEpiSymE32,   // symmetric: v = alpha C + beta E, E an fp32 record -> fp32 record + 16-bit
+  kEpiSym = 0,  // symmetric: C -> 16-bit (A or R = X X^T)
+  kEpiSymE16,   // symmetric: v = alpha C + beta E + gamma I (B', Z', Q Z', R Z', Z' RZ)
+  kEpiSymE16Q,  // as kEpiSymE16, plus a fresh Q = v + a' I
   kEpiGen,      // general: C -> X and X^T (Q X at a restart)
   kEpiGenE16,   // general: v = alpha C + beta X -> X and X^T (B X)
   kEpiFin,      // last product: O = C -> update of W
