@@ -178,34 +178,64 @@ __device__ __forceinline__ void f4set(float4& v, int k, float x) {
 
 // Four consecutive elements idx..idx+3 of a user buffer (dtype f32 or bf16):
 // vector access when aligned and all four are in range, else element-wise.
+// The user's W and O are device memory: accessing them through
+// global-address-space pointers gives global_* instead of flat_* instructions.
+typedef float gf32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu32x2_t __attribute__((ext_vector_type(2)));
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr(void* p, int64_t idx) {
+  return (__attribute__((address_space(1))) T*)p + idx;
+}
+__device__ __forceinline__ float4 gload_f32x4(void* p, int64_t byte_off) {
+  const gf32x4_t v = *(__attribute__((address_space(1))) gf32x4_t*)gptr<char>(p, byte_off);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 gload_bf16x4(void* p, int64_t byte_off) {
+  const gu32x2_t h = *(__attribute__((address_space(1))) gu32x2_t*)gptr<char>(p, byte_off);
+  return make_float4(bf16_to_f32(static_cast<uint16_t>(h.x & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(h.x >> 16)),
+                     bf16_to_f32(static_cast<uint16_t>(h.y & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(h.y >> 16)));
+}
+__device__ __forceinline__ void gstore_f32x4(void* p, int64_t byte_off, const float4& v) {
+  *(__attribute__((address_space(1))) gf32x4_t*)gptr<char>(p, byte_off) = gf32x4_t{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void gstore_bf16x4(void* p, int64_t byte_off, const float4& v) {
+  *(__attribute__((address_space(1))) gu32x2_t*)gptr<char>(p, byte_off) =
+      gu32x2_t{f32x2_to_bf16x2(v.x, v.y), f32x2_to_bf16x2(v.z, v.w)};
+}
+
 __device__ __forceinline__ bool user4_vec(const void* p, int64_t idx, int dtype, int valid) {
   const int esz = dtype == kF32 ? 4 : 2;
   return valid >= 4 && ((reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(idx) * esz) & (4 * esz - 1)) == 0;
 }
-__device__ __forceinline__ float4 user_load4(const void* p, int64_t idx, int dtype, int valid) {
-  if (user4_vec(p, idx, dtype, valid)) {
-    if (dtype == kF32) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
-    const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + idx);
-    return make_float4(bf16_to_f32(static_cast<uint16_t>(h.x & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(h.x >> 16)),
-                       bf16_to_f32(static_cast<uint16_t>(h.y & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(h.y >> 16)));
+__device__ __forceinline__ float user_load1(void* p, int64_t idx, int dtype) {
+  return dtype == kF32 ? *gptr<float>(p, idx) : bf16_to_f32(*gptr<uint16_t>(p, idx));
+}
+__device__ __forceinline__ void user_store1(void* p, int64_t idx, int dtype, float v) {
+  if (dtype == kF32) {
+    *gptr<float>(p, idx) = v;
+  } else {
+    *gptr<uint16_t>(p, idx) = f32_to_bf16(v);
   }
+}
+// Four consecutive elements idx .. idx + 3 of a user buffer (dtype f32 or
+// bf16): vector access when aligned and all four are in range, else
+// element-wise.
+__device__ __forceinline__ float4 user_load4(void* p, int64_t idx, int dtype, int valid) {
+  if (user4_vec(p, idx, dtype, valid)) return dtype == kF32 ? gload_f32x4(p, idx * 4) : gload_bf16x4(p, idx * 2);
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < 4 && k < valid; ++k) f4set(r, k, load_as_f32(p, idx + k, dtype));
+  for (int k = 0; k < 4 && k < valid; ++k) f4set(r, k, user_load1(p, idx + k, dtype));
   return r;
 }
 __device__ __forceinline__ void user_store4(void* p, int64_t idx, int dtype, int valid, float4 v) {
   if (user4_vec(p, idx, dtype, valid)) {
     if (dtype == kF32) {
-      *reinterpret_cast<float4*>(static_cast<float*>(p) + idx) = v;
+      gstore_f32x4(p, idx * 4, v);
     } else {
-      uint2 h;
-      h.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-      h.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + idx) = h;
+      gstore_bf16x4(p, idx * 2, v);
     }
     return;
   }
-  for (int k = 0; k < 4 && k < valid; ++k) store_from_f32(p, idx + k, dtype, f4get(v, k));
+  for (int k = 0; k < 4 && k < valid; ++k) user_store1(p, idx + k, dtype, f4get(v, k));
 }
 
 // W <- W - lr (O + wd W) and the optional O store for four consecutive

@@ -24,6 +24,13 @@ namespace muon {
 // and the MFMAs already issued keep the matrix pipe busy through the wait.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// The per-wave epilogue staging area, typed as LDS so its accesses are
+// ds_read / ds_write rather than flat instructions.
+typedef __attribute__((address_space(3))) float lds_f32;
+__device__ __forceinline__ float4 lds_load4(const lds_f32* p) {
+  const gf32x4_t v = *(const __attribute__((address_space(3))) gf32x4_t*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 template <int OP>
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
@@ -58,9 +65,16 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
+// A buffer resource for `bytes` bytes at `base` (a block-uniform address;
+// readfirstlane states that to the compiler, so the descriptor stays in
+// scalar registers).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+  const uint64_t u = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u & 0xffffffffu)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -242,13 +256,122 @@ __device__ __forceinline__ void store_frag(void* base, int64_t off, int lane, co
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off + 8 * lane) = f;
 }
 
-// Final product: W <- W - lr (O + wd W) and the optional store of O, for
-// rows i0 .. i0 + 31 and columns j0 .. j0 + 255 of O staged in LDS
-// (row-major, LDE floats per row).  The loads of W for 16 rows (or columns)
-// are issued together before any of them is used.
+// Four consecutive user elements of dtype D (kF32 or kBF16) at byte offset
+// off of p, aligned to four elements.
+template <int D>
+__device__ __forceinline__ float4 ld4(void* p, int64_t off) {
+  return D == kF32 ? gload_f32x4(p, off) : gload_bf16x4(p, off);
+}
+template <int D>
+__device__ __forceinline__ void st4(void* p, int64_t off, const float4& v) {
+  if constexpr (D == kF32) {
+    gstore_f32x4(p, off, v);
+  } else {
+    gstore_bf16x4(p, off, v);
+  }
+}
+
+// The final update for a staged 32 x 256 block of O that lies wholly inside
+// the user's matrix, whose rows are aligned to four elements: W of dtype WD
+// and O of dtype OD (-1: absent).  Loads of W for 16 rows (or columns) are
+// issued together; there are no per-element range checks.
+template <int WD, int OD, int LDE>
+__device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
+                                                int lane) {
+  constexpr int R = 16;
+  constexpr int wsz = WD == kF32 ? 4 : 2, osz = OD == kF32 ? 4 : 2;
+  void* w = st.w;
+  void* o = st.o;
+  const int64_t ld = a.user_ld;
+  const float lr = a.lr, wd = a.wd;
+  auto update = [&](float4& nw, const float4& ov) {
+    nw.x -= lr * (ov.x + wd * nw.x);
+    nw.y -= lr * (ov.y + wd * nw.y);
+    nw.z -= lr * (ov.z + wd * nw.z);
+    nw.w -= lr * (ov.w + wd * nw.w);
+  };
+  if (!a.transposed) {  // W[i][j .. j + 3], lane -> columns j0 + 4 lane
+    const int64_t base = static_cast<int64_t>(i0) * ld + j0 + 4 * lane;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += R) {
+      float4 wv[R];
+      if constexpr (WD >= 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) wv[r] = ld4<WD>(w, (base + (r0 + r) * ld) * wsz);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4 ov = lds_load4(ep + (r0 + r) * LDE + 4 * lane);
+        if constexpr (OD >= 0) st4<OD>(o, (base + (r0 + r) * ld) * osz, ov);
+        if constexpr (WD >= 0) {
+          update(wv[r], ov);
+          st4<WD>(w, (base + (r0 + r) * ld) * wsz, wv[r]);
+        }
+      }
+    }
+  } else {  // W[j][i .. i + 3], lane -> rows i0 + r4 .. + 3 of columns j0 + c
+    const int r4 = (lane & 7) * 4;
+    const int64_t base = static_cast<int64_t>(j0 + (lane >> 3)) * ld + i0 + r4;
+#pragma unroll
+    for (int c0 = 0; c0 < 256; c0 += 8 * R) {
+      float4 wv[R];
+      if constexpr (WD >= 0) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) wv[t] = ld4<WD>(w, (base + (c0 + 8 * t) * ld) * wsz);
+      }
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const int c = c0 + 8 * t + (lane >> 3);
+        const float4 ov = make_float4(ep[(r4 + 0) * LDE + c], ep[(r4 + 1) * LDE + c], ep[(r4 + 2) * LDE + c],
+                                      ep[(r4 + 3) * LDE + c]);
+        if constexpr (OD >= 0) st4<OD>(o, (base + (c0 + 8 * t) * ld) * osz, ov);
+        if constexpr (WD >= 0) {
+          update(wv[t], ov);
+          st4<WD>(w, (base + (c0 + 8 * t) * ld) * wsz, wv[t]);
+        }
+      }
+    }
+  }
+}
+
+// Whether final_rows_fast may take this block: inside the matrix and with
+// rows of W and O aligned to four elements.
+__device__ __forceinline__ bool final_fast_ok(const GemmArgs& a, const EpiState& st, int i0, int j0) {
+  if (i0 + 32 > a.n_real || j0 + kBN > a.m_real || (a.user_ld & 3) != 0) return false;
+  const uintptr_t wal = a.w_dtype == kF32 ? 15 : 7, oal = a.o_dtype == kF32 ? 15 : 7;
+  return (reinterpret_cast<uintptr_t>(st.w) & wal) == 0 && (reinterpret_cast<uintptr_t>(st.o) & oal) == 0;
+}
+
 template <int LDE>
-__device__ __forceinline__ void final_rows(const GemmArgs& a, const EpiState& st, const float* ep, int i0, int j0,
-                                           int lane) {
+__device__ __forceinline__ void final_rows_any(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
+                                               int lane);
+
+// The update of one staged block: the fast form for the dtype pair, or the
+// general one (ragged edges, unaligned rows).
+template <int LDE>
+__device__ __forceinline__ void final_block(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
+                                            int lane) {
+  if (final_fast_ok(a, st, i0, j0)) {
+    const int wdt = st.w != nullptr ? a.w_dtype : -1, odt = st.o != nullptr ? a.o_dtype : -1;
+#define MUON_FAST(WD, OD)                                               \
+  if (wdt == WD && odt == OD) {                                         \
+    final_rows_fast<WD, OD, LDE>(a, st, ep, i0, j0, lane);              \
+    return;                                                             \
+  }
+    MUON_FAST(kF32, -1) MUON_FAST(kBF16, -1) MUON_FAST(-1, kF32) MUON_FAST(-1, kBF16)
+    MUON_FAST(kF32, kF32) MUON_FAST(kF32, kBF16) MUON_FAST(kBF16, kF32) MUON_FAST(kBF16, kBF16)
+#undef MUON_FAST
+  }
+  final_rows_any<LDE>(a, st, ep, i0, j0, lane);
+}
+
+// Final product, general form (ragged edges, unaligned rows): W <- W -
+// lr (O + wd W) and the optional store of O, for rows i0 .. i0 + 31 and
+// columns j0 .. j0 + 255 of O staged in LDS (row-major, LDE floats per row),
+// with per-element range checks.
+template <int LDE>
+__device__ __forceinline__ void final_rows_any(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
+                                               int lane) {
   constexpr int R = 16;
   if (!a.transposed) {  // W is n x m: lane -> columns j .. j + 3 of every row
     const int j = j0 + 4 * lane;
@@ -267,7 +390,7 @@ __device__ __forceinline__ void final_rows(const GemmArgs& a, const EpiState& st
         const int i = i0 + r0 + r;
         if (i < a.n_real)
           final_update4(a, st, static_cast<int64_t>(i) * a.user_ld + j, valid,
-                        *reinterpret_cast<const float4*>(ep + (r0 + r) * LDE + 4 * lane), w[r]);
+                        lds_load4(ep + (r0 + r) * LDE + 4 * lane), w[r]);
       }
     }
   } else {  // W is m x n: lane -> W[j][i .. i + 3] for 32 columns j of O
@@ -399,7 +522,7 @@ __device__ __forceinline__ void store_tn(uint16_t* t, uint16_t* n, const float (
 template <int OP, int KIND, bool MAYDIAG>
 __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const EpiPtrs& p, const f32x16_t& c,
                                           const uint4 (&ein)[2], int x, int y, int ib, bool dblk, int lane,
-                                          const uint4 (&id)[2], float* ep) {
+                                          const uint4 (&id)[2], lds_f32* ep) {
   constexpr EpiSpec S = epi_spec(KIND);
   const int jr = lane & 31, ir0 = 4 * (lane >> 5);
   float v[16];
@@ -466,7 +589,7 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
 template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int U>
 __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
                                          const f32x16_t (&acc)[kFM][kFN], const uint4 (&cur)[G][2], int I, int wave,
-                                         int lane, const uint4 (&id)[2], float* ep) {
+                                         int lane, const uint4 (&id)[2], lds_f32* ep) {
   constexpr int x = (BLK + U) / kFN, y = (BLK + U) % kFN;
   const int rel = y - (2 * wave + x);  // diagonal tiles: > 0 is the mirror of an owned block
   if (!MAYDIAG || rel <= 0)
@@ -482,7 +605,7 @@ __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const 
 template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int END>
 __device__ __forceinline__ void epi_run(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
                                         const f32x16_t (&acc)[kFM][kFN], uint4 (&cur)[G][2], int I, int wave,
-                                        int lane, const uint4 (&id)[2], float* ep) {
+                                        int lane, const uint4 (&id)[2], lds_f32* ep) {
   uint4 nxt[G][2];
   if constexpr (BLK + G < END) {
 #pragma unroll
@@ -498,7 +621,7 @@ __device__ __forceinline__ void epi_run(const GemmArgs& a, EpiState& st, const E
 template <int OP, int KIND, bool MAYDIAG, int BEGIN, int END>
 __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
                                           const f32x16_t (&acc)[kFM][kFN], int I, int wave, int lane,
-                                          const uint4 (&id)[2], float* ep) {
+                                          const uint4 (&id)[2], lds_f32* ep) {
   constexpr int G = 4;
   uint4 cur[G][2];
 #pragma unroll
@@ -514,7 +637,7 @@ __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const
 // row-major W is read and written along its rows.
 template <int OP, int KIND>
 __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st, const f32x16_t (&acc)[kFM][kFN], int b,
-                                              int I, int J, int wave, int lane, float* ep) {
+                                              int I, int J, int wave, int lane, lds_f32* ep) {
   static_assert(kFM == 2 && kFN == 8, "the epilogue walks 2 x 8 MFMA blocks");
   constexpr EpiSpec S = epi_spec(KIND);
   const EpiPtrs p = epi_ptrs<KIND>(a, b, I, J, wave);
@@ -522,11 +645,11 @@ __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st, c
     const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // no transposes here
     epi_range<OP, KIND, false, 0, 8>(a, st, p, acc, I, wave, lane, id, ep);
     __syncthreads();
-    final_rows<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * kBN, lane);
+    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * kBN, lane);
     __syncthreads();
     epi_range<OP, KIND, false, 8, 16>(a, st, p, acc, I, wave, lane, id, ep);
     __syncthreads();
-    final_rows<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * kBN, lane);
+    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * kBN, lane);
   } else {
     const uint4 id[2] = {ident_frag<OP>(0, lane), ident_frag<OP>(1, lane)};
     if (S.sym && I == J)
@@ -534,6 +657,22 @@ __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st, c
     else
       epi_range<OP, KIND, false, 0, 16>(a, st, p, acc, I, wave, lane, id, ep);
   }
+}
+
+// The kernel's argument block, loaded again from the kernel argument segment
+// through a pointer the compiler cannot follow (so it cannot reuse values
+// loaded before the main loop).
+__device__ __forceinline__ GemmArgs reload_args() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef const __attribute__((address_space(4))) GemmArgs* kargs_ptr;
+  kargs_ptr p = (kargs_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  GemmArgs r;
+  __builtin_memcpy(&r, (const __attribute__((address_space(4))) void*)p, sizeof(GemmArgs));
+  return r;
+#else
+  return GemmArgs{};  // device code only
+#endif
 }
 
 template <int OP, int KIND>
@@ -557,8 +696,8 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   const int voff = lane * 16;
   // byte offset of a row block = (row / 32) * (K / 64) * 4 KB
   const int pstride = (a.ldp >> 6) * 4096, qstride = (a.ldq >> 6) * 4096;
-  const int sP = (I * (kBM / 32) + wave * kFM) * pstride;
-  const int sQ = J * (kBN / 32) * qstride;
+  const int sP = __builtin_amdgcn_readfirstlane((I * (kBM / 32) + wave * kFM) * pstride);
+  const int sQ = __builtin_amdgcn_readfirstlane(J * (kBN / 32) * qstride);
 
   f32x16_t acc[kFM][kFN];
 #pragma unroll
@@ -620,10 +759,12 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   block_barrier();
 
   // The epilogue runs from registers; the last product stages O through this
-  // wave's LDS stage.
-  float* ep = reinterpret_cast<float*>(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
-  epilogue_mfma<OP, KIND>(a, st, acc, b, I, J, wave, lane, ep);
-  block_partials<kNT>(a, b, tile, red, st);
+  // wave's LDS stage.  It reads the launch arguments afresh, so they are not
+  // held in scalar registers through the main loop.
+  const GemmArgs ea = reload_args();
+  lds_f32* ep = (lds_f32*)(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
+  epilogue_mfma<OP, KIND>(ea, st, acc, b, I, J, wave, lane, ep);
+  block_partials<kNT>(ea, b, tile, red, st);
 }
 
 template <int OP>
