@@ -47,11 +47,127 @@ def parse():
     ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue every group on one stream (default: one stream per group)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help=f"finish with {COPY_PROBE_REPS} plain device copies of {COPY_PROBE_BYTES >> 20} MiB "
+                         "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profile summary of the dominant kernel from three rocprofv3 output "
+                         "directories (--stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE) and exit")
+    ap.add_argument("--kernel", default=None, help="kernel name for --summarize-counters")
+    ap.add_argument("--out", default=None, help="output file for --summarize-counters")
+    ap.add_argument("--command", default="", help="the profiled command, recorded by --summarize-counters")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30
+COPY_PROBE_REPS = 3
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_step_amd", "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources: a traffic figure holds only for the code it was taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    safe = "".join(c if c.isalnum() else "_" for c in kernel).strip("_")
+    return os.path.join(PROFILES, f"{safe}_{workload}_traffic.txt")
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from its committed counter summary, or
+    None when there is none or the sources changed since it was taken."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest() or fields.get("kernel") != kernel:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_counters(args):
+    """Write the profile summary of args.kernel: its rocprofv3 --stats line,
+    and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same counters
+    read for the plain copies of --copy-probe."""
+    stats = [r for r in _csv_rows(args.summarize_counters[0], "kernel_stats.csv") if args.kernel in r["Name"]]
+    if len(stats) != 1:
+        raise SystemExit(f"expected one kernel_stats line for {args.kernel}, found {len(stats)}")
+    st = stats[0]
+
+    def per_dispatch(d, counter):
+        vals, copies = [], []
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if args.kernel in r["Kernel_Name"]:
+                vals.append(v)
+            elif "copy" in r["Kernel_Name"].lower() and int(r["Grid_Size"]) > 0:
+                copies.append(v)
+        if not vals or not copies:
+            raise SystemExit(f"{counter}: no dispatches of {args.kernel} or of the copy probe in {d}")
+        copy_kib = sorted(copies)[-COPY_PROBE_REPS:]
+        return sum(vals) / len(vals), sum(copy_kib) / len(copy_kib)
+
+    fetch, copy_fetch = per_dispatch(args.summarize_counters[1], "FETCH_SIZE")
+    write, copy_write = per_dispatch(args.summarize_counters[2], "WRITE_SIZE")
+    f_fetch = COPY_PROBE_BYTES / 1024.0 / copy_fetch
+    f_write = COPY_PROBE_BYTES / 1024.0 / copy_write
+    traffic = (fetch * f_fetch + write * f_write) * 1024.0
+    avg_ns = float(st["AverageNs"])
+    lines = [
+        f"kernel: {args.kernel}",
+        f"workload: {args.workload}",
+        f"command: {args.command}",
+        f"source_sha256: {source_digest()}",
+        f"rocprof_calls: {st['Calls']}",
+        f"rocprof_average_us: {avg_ns / 1e3:.2f}",
+        f"rocprof_min_us: {float(st['MinNs']) / 1e3:.2f}",
+        f"rocprof_max_us: {float(st['MaxNs']) / 1e3:.2f}",
+        f"rocprof_total_pct: {float(st['Percentage']):.2f}",
+        f"fetch_kib_per_launch_raw: {fetch:.1f}",
+        f"write_kib_per_launch_raw: {write:.1f}",
+        f"copy_probe_bytes: {COPY_PROBE_BYTES}",
+        f"copy_probe_fetch_kib_raw: {copy_fetch:.1f}",
+        f"copy_probe_write_kib_raw: {copy_write:.1f}",
+        f"scale_fetch: {f_fetch:.4f}",
+        f"scale_write: {f_write:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+    ]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the step shards by "
               "matrix ownership across GPUs, which this build does not run)", file=sys.stderr)
@@ -175,18 +291,31 @@ def main():
         achieved = dom["flops"] / (dom["ms"] / 1e3) / 1e12
         peak = PEAK_F32_TFLOPS if dom_name.endswith("f64acc") else PEAK_16BIT_TFLOPS
         roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                    "traffic": None, "kernel": dom_name, "launches_per_step": dom["launches"] // args.steps,
-                    "avg_launch_ms": avg_ms, "flops_per_launch": dom["flops"] / dom["launches"]}
+                    "traffic": read_traffic(dom_name, wl.key), "kernel": dom_name,
+                    "launches_per_step": dom["launches"] // args.steps,
+                    "avg_launch_ms": avg_ms, "flops_per_launch": dom["flops"] / dom["launches"],
+                    "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"]}
     else:
         achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom_name, "avg_launch_ms": avg_ms}
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(dom_name, wl.key), "kernel": dom_name,
+                    "avg_launch_ms": avg_ms}
     kernels = {k: {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] // args.steps,
                    "avg_launch_ms": v["ms"] / v["launches"],
                    "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None,
                    "gbs": v["bytes"] / (v["ms"] / 1e3) / 1e9} for k, v in kern.items()}
     role_tab = {k: {"ms_per_step": v["ms"], "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None}
                 for k, v in sorted(roles.items(), key=lambda kv: -kv[1]["ms"])}
+
+    if args.copy_probe:  # reference dispatches for the HBM byte counters
+        # uint8 -> int8 keeps every byte but makes torch run its copy kernel
+        # (a same-dtype copy would go to the DMA engine, which has no counters)
+        src = torch.zeros(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty(COPY_PROBE_BYTES, dtype=torch.int8, device=dev)
+        for _ in range(COPY_PROBE_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------ CPU baseline: the fp64 oracle
     cpu = None

@@ -2,6 +2,7 @@
 // layout and the launch schedule of the standard and Gram Newton-Schulz
 // iterations.  All work is enqueued on the caller's stream; nothing blocks.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
@@ -94,8 +95,14 @@ hipError_t traced(hipStream_t s, const char* kernel, const char* role, double fl
   return hipSuccess;
 }
 
-const char* gemm_kernel_name(int op) {
-  return op == kOpBF16 ? "gemm_nt_mfma_bf16" : (op == kOpF16 ? "gemm_nt_mfma_f16" : "gemm_nt_f64acc");
+// The kernel a GEMM launch runs, spelled as the profiler prints it, so the
+// launch trace and a rocprofv3 summary name the same kernels.
+void gemm_kernel_name(const GemmArgs& g, int op, char* out, size_t n) {
+  if (op == kOpF32) {
+    snprintf(out, n, "gemm_nt_f64acc");
+  } else {
+    snprintf(out, n, "gemm_nt_mfma<%d, %d>", op, epi_kind(g));
+  }
 }
 
 bool valid_dtype(muon_dtype d) { return d == MUON_F32 || d == MUON_BF16 || d == MUON_F16; }
@@ -276,7 +283,9 @@ hipError_t gemm(const Plan& p, const GemmArgs& g, const char* role, hipStream_t 
     }
   }
   if (g.final_mode) role = strcmp(role, "BX") == 0 ? "BX_final" : "QX_final";
-  return traced(s, gemm_kernel_name(p.op), role, flops * p.batch, bytes * p.batch,
+  char kname[40];
+  gemm_kernel_name(g, p.op, kname, sizeof(kname));
+  return traced(s, kname, role, flops * p.batch, bytes * p.batch,
                 [&] { return launch_gemm(g, p.batch, p.op, s); });
 }
 
@@ -295,7 +304,9 @@ muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* c
     const double cnt = static_cast<double>(na.count) * p.batch;
     const double esz_m = m_dtype == kF32 ? 4 : 2;
     const double bytes = cnt * esz_m * (G != nullptr ? 3.0 : 1.0);
-    MUON_LAUNCH(traced(s, "norm_kernel", G != nullptr ? "momentum_norm" : "norm", 0.0, bytes,
+    char kname[40];
+    snprintf(kname, sizeof(kname), "norm_kernel<%d>", m_dtype);
+    MUON_LAUNCH(traced(s, kname, G != nullptr ? "momentum_norm" : "norm", 0.0, bytes,
                        [&] { return launch_norm(na, p.batch, s); }));
   }
   PrepArgs pa;
@@ -317,7 +328,13 @@ muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* c
   {
     const double cnt = static_cast<double>(p.n) * p.m * p.batch;
     const double bytes = cnt * ((m_dtype == kF32 ? 4 : 2) + 2.0 * p.esz);
-    MUON_LAUNCH(traced(s, "prep_kernel", "prep", 0.0, bytes, [&] { return launch_prep(pa, p.batch, p.op, s); }));
+    char kname[40];
+    if (p.op == kOpF32) {
+      snprintf(kname, sizeof(kname), "prep_f32_kernel<%d>", m_dtype);
+    } else {
+      snprintf(kname, sizeof(kname), "prep_packed_kernel<%d, %d>", m_dtype, p.op);
+    }
+    MUON_LAUNCH(traced(s, kname, "prep", 0.0, bytes, [&] { return launch_prep(pa, p.batch, p.op, s); }));
   }
   return MUON_OK;
 }
