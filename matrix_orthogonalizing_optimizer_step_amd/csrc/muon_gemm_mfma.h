@@ -14,7 +14,7 @@ namespace muon {
 // registers).  k runs in slabs of 64 (4 MFMA k-steps):
 //  * the P rows of a wave are private to it, so its P fragments go straight
 //    from global memory (L2) into registers with one contiguous 1 KB load per
-//    fragment, two slabs ahead (three register slab buffers);
+//    fragment, three slabs ahead (four register slab buffers);
 //  * the Q tile is shared by all waves: it is streamed into a 4-stage LDS
 //    ring with buffer_load ... lds (1 KB per instruction, lane l landing at
 //    byte 16 l), three slabs ahead, and each fragment is read back with one
@@ -708,51 +708,31 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
 
   const int nk = a.K / kBK;  // a multiple of 4: every operand dimension is a multiple of 256
-  uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS];
+  uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS], abuf3[kFM][kKS];
   uint4 bf[2][kFN];
-  // prologue: Q slabs 0..3 into the ring, P slabs 0 and 1 into registers
+  // prologue: Q slabs 0..3 into the ring, P slabs 0..2 into registers
   load_b_slab(stg0, rQ, voff, sQ, qstride, 0, wave);
   load_b_slab(stg1, rQ, voff, sQ, qstride, 1, wave);
   load_b_slab(stg2, rQ, voff, sQ, qstride, 2, wave);
   load_b_slab(stg3, rQ, voff, sQ, qstride, 3, wave);
   load_a_slab(abuf0, rP, voff, sP, pstride, 0);
   load_a_slab(abuf1, rP, voff, sP, pstride, 1);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 15));  // Q slab 0 landed
+  load_a_slab(abuf2, rP, voff, sP, pstride, 2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(6 * kLoadsB, 15));  // Q slab 0 landed
   block_barrier();
 #pragma unroll
   for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
 
-  // 12 slabs per trip (lcm of the 4 LDS stages and the 3 P register buffers);
-  // nk is a multiple of 4, so a remainder of 4 or 8 slabs follows.
+  // 4 slabs per trip (the 4 LDS stages and the 4 P register buffers, which
+  // are loaded three slabs ahead); nk is a multiple of 4.
 #define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
-  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 2);                                             \
+  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 3);                                             \
   slab<OP>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
-  int kt = 0;
-  for (; kt + 12 <= nk; kt += 12) {
-    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
+  for (int kt = 0; kt < nk; kt += 4) {
+    MUON_SLAB(0, abuf0, abuf3, stg0, stg1)
     MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
     MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
-    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
-    MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
-    MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
-    MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
-    MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
-    MUON_SLAB(8, abuf2, abuf1, stg0, stg1)
-    MUON_SLAB(9, abuf0, abuf2, stg1, stg2)
-    MUON_SLAB(10, abuf1, abuf0, stg2, stg3)
-    MUON_SLAB(11, abuf2, abuf1, stg3, stg0)
-  }
-  if (kt + 4 <= nk) {
-    MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
-    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
-    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
-    MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
-    if (kt + 8 <= nk) {
-      MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
-      MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
-      MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
-      MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
-    }
+    MUON_SLAB(3, abuf3, abuf2, stg3, stg0)
   }
 #undef MUON_SLAB
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
