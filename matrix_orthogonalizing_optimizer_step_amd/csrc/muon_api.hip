@@ -35,10 +35,41 @@ struct Plan {
   size_t A16, B16;                                        // standard
   size_t R16, Z16, RZ16, Q16[2];                         // Gram
   size_t normpart, tilepart, shift;
+  size_t part32, counters;                               // tail split of the MFMA GEMMs
+  int cu;                                                // compute units the split is planned for
+  int max_tail, max_pieces;                              // largest tail over the launches of a call
   size_t total;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Tail split of a GEMM launch of `tiles` tiles with k in `units` units of
+// 256 on `cu` compute units: whole tiles fill the complete rounds, and the
+// tiles of the last, partial round are cut into as many k pieces as the idle
+// compute units allow (at most kMaxPieces).  Only long products are split
+// (k of at least 8192, pieces of at least 1024): handing a partial tile over
+// costs a device-scope fence (an L2 write-back) and an fp32 round trip, which
+// shorter tiles do not amortise (measured: a net loss at k = 3584).
+void tail_split(int64_t tiles, int units, int cu, int* full, int* pieces) {
+  const int64_t rounds = tiles / cu, tail = tiles - rounds * cu;
+  int s = tail > 0 && units >= 32 ? static_cast<int>(cu / tail) : 1;
+  s = s < kMaxPieces ? s : kMaxPieces;
+  s = s < units / 4 ? s : units / 4;
+  if (s < 2) {
+    *full = static_cast<int>(tiles);
+    *pieces = 1;
+  } else {
+    *full = static_cast<int>(rounds * cu);
+    *pieces = s;
+  }
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return 256;
+  return n;
+}
 
 // ---------------------------------------------------------------------------
 // opt-in launch trace (muon_trace_enable / muon_trace_collect)
@@ -181,16 +212,41 @@ bool make_plan(int batch, int rows, int cols, muon_ns_variant v, const Config& c
   p->normpart = take(static_cast<size_t>(batch) * kNormBlocks * sizeof(double));
   p->tilepart = take(static_cast<size_t>(batch) * nt * (nt + 1) / 2 * 2 * sizeof(double));
   p->shift = take(static_cast<size_t>(batch) * sizeof(float));
+  // the tail split's partial tiles and counters, sized for the largest tail
+  // of this call's launches (symmetric K = m or n, general K = n)
+  p->cu = p->op == kOpF32 ? 0 : device_cus();
+  p->max_tail = 0;
+  p->max_pieces = 0;
+  if (p->cu > 0) {
+    const int64_t tri = static_cast<int64_t>(batch) * nt * (nt + 1) / 2;
+    const int64_t gen = static_cast<int64_t>(batch) * nt * (p->m_pad / p->tile);
+    const struct { int64_t tiles; int units; } launches[3] = {
+        {tri, p->m_pad / 256}, {tri, p->n_pad / 256}, {gen, p->n_pad / 256}};
+    for (const auto& l : launches) {
+      int full = 0, pieces = 1;
+      tail_split(l.tiles, l.units, p->cu, &full, &pieces);
+      if (pieces > 1) {
+        const int tail = static_cast<int>(l.tiles - full);
+        p->max_tail = tail > p->max_tail ? tail : p->max_tail;
+        p->max_pieces = tail * pieces > p->max_pieces ? tail * pieces : p->max_pieces;
+      }
+    }
+  }
+  p->part32 = take(static_cast<size_t>(p->max_pieces) * kPartFloats * sizeof(float));
+  p->counters = take(static_cast<size_t>(p->max_tail) * sizeof(int));
   p->total = cur;
   return true;
 }
 
-GemmArgs base_args(const Plan& p) {
+GemmArgs base_args(const Plan& p, char* ws) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.n_real = p.n;
   g.m_real = p.m;
   g.alpha_c = 1.0f;
+  g.kpieces = 1;
+  g.part32 = reinterpret_cast<float*>(ws + p.part32);
+  g.counters = reinterpret_cast<int*>(ws + p.counters);
   return g;
 }
 
@@ -260,7 +316,18 @@ void set_final(GemmArgs& g, const Plan& p, const Final& f) {
 // One GEMM launch with its algorithmic work for the trace: a symmetric
 // product counts one triangle (n^2 K FLOPs), a general one 2 n m K; bytes are
 // each operand read once plus each output written once (real sizes).
-hipError_t gemm(const Plan& p, const GemmArgs& g, const char* role, hipStream_t s) {
+hipError_t gemm(const Plan& p, GemmArgs g, const char* role, hipStream_t s) {
+  const int64_t tiles = static_cast<int64_t>(g.ntiles) * p.batch;
+  g.full_blocks = static_cast<int>(tiles);
+  g.kpieces = 1;
+  if (p.cu > 0) {
+    int full = 0, pieces = 1;
+    tail_split(tiles, g.K / 256, p.cu, &full, &pieces);
+    if (pieces > 1 && (tiles - full) <= p.max_tail && (tiles - full) * pieces <= p.max_pieces) {
+      g.full_blocks = full;
+      g.kpieces = pieces;
+    }
+  }
   const double n = p.n, m = p.m, esz = p.esz;
   double flops, bytes;
   if (g.sym) {
@@ -300,6 +367,8 @@ muon_status run_prologue(const Plan& p, const Config& c, char* ws, const void* c
   na.mu = mu;
   na.count = static_cast<int64_t>(p.rows) * p.cols;
   na.partials = reinterpret_cast<double*>(ws + p.normpart);
+  na.zero = reinterpret_cast<int*>(ws + p.counters);
+  na.nzero = p.max_tail;
   {
     const double cnt = static_cast<double>(na.count) * p.batch;
     const double esz_m = m_dtype == kF32 ? 4 : 2;
@@ -352,13 +421,13 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
   for (int t = 0; t < c.T; ++t) {
     const float a = c.c[t][0], b = c.c[t][1], cc = c.c[t][2];
     // A = X X^T
-    GemmArgs g = base_args(p);
+    GemmArgs g = base_args(p, ws);
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
     g.out16 = ws + p.A16;
     g.part_out = c.shift ? tp : nullptr;
     MUON_LAUNCH(gemm(p, g, "XXt", s));
     // B' = c A A + b A + (a - a') I
-    g = base_args(p);
+    g = base_args(p, ws);
     set_sym(g, p, ws + p.A16, ws + p.A16, p.n_pad, snn, p.n_pad);
     g.alpha_c = cc;
     g.E16 = ws + p.A16;
@@ -376,7 +445,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     g.out16 = ws + p.B16;
     MUON_LAUNCH(gemm(p, g, "A2", s));
     // X <- a' X + B' X
-    g = base_args(p);
+    g = base_args(p, ws);
     set_px(g, p, ws + p.B16, ws + p.XT[xc]);
     if (p.op == kOpF32) {
       g.E16 = ws + p.XN;
@@ -413,7 +482,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
   int xc = 0, qc = 0;
 
   auto gram_of_x = [&]() {  // R = X X^T + partials
-    GemmArgs g = base_args(p);
+    GemmArgs g = base_args(p, ws);
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
     g.out16 = R16;
     g.part_out = c.shift ? tp : nullptr;
@@ -424,7 +493,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
   for (int t = 1; t <= c.T; ++t) {
     const float a = c.c[t - 1][0], b = c.c[t - 1][1], cc = c.c[t - 1][2];
     // Z' = c R R + b R + (a - a') I; a fresh Q becomes Z' + a' I
-    GemmArgs g = base_args(p);
+    GemmArgs g = base_args(p, ws);
     set_sym(g, p, R16, R16, p.n_pad, snn, p.n_pad);
     g.alpha_c = cc;
     g.E16 = R16;
@@ -444,7 +513,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
     MUON_LAUNCH(gemm(p, g, "Z", s));
     const float* sh = c.shift ? shift : nullptr;
     if (!fresh) {  // Q <- Q Z' + a' Q
-      g = base_args(p);
+      g = base_args(p, ws);
       set_sym(g, p, ws + p.Q16[qc], Z16, p.n_pad, snn, p.n_pad);
       g.E16 = ws + p.Q16[qc];
       g.beta_a = 1.0f;
@@ -457,7 +526,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
     fresh = false;
     if (t < c.T && ((c.restart_mask >> (t - 1)) & 1u)) {
       // restart: X <- Q X, R = X X^T, Q = I
-      g = base_args(p);
+      g = base_args(p, ws);
       set_px(g, p, ws + p.Q16[qc], ws + p.XT[xc]);
       g.out16 = ws + p.XN;
       g.outT16 = ws + p.XT[xc ^ 1];
@@ -467,7 +536,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       fresh = true;
     } else if (t < c.T) {
       // RZ = R Z' + a' R
-      g = base_args(p);
+      g = base_args(p, ws);
       set_sym(g, p, R16, Z16, p.n_pad, snn, p.n_pad);
       g.E16 = R16;
       g.beta_a = 1.0f;
@@ -476,7 +545,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.out16 = RZ16;
       MUON_LAUNCH(gemm(p, g, "RZ", s));
       // R <- Z' RZ + a' RZ
-      g = base_args(p);
+      g = base_args(p, ws);
       set_sym(g, p, Z16, RZ16, p.n_pad, snn, p.n_pad);
       g.E16 = RZ16;
       g.beta_a = 1.0f;
@@ -488,7 +557,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
     }
   }
   // O = Q X
-  GemmArgs g = base_args(p);
+  GemmArgs g = base_args(p, ws);
   set_px(g, p, ws + p.Q16[qc], ws + p.XT[xc]);
   set_final(g, p, f);
   MUON_LAUNCH(gemm(p, g, "QX", s));

@@ -98,6 +98,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void norm_kernel(NormArgs a) {
   __shared__ double red[kThreads / 64];
   const int b = blockIdx.y;
+  if (blockIdx.x == 0 && b == 0)
+    for (int i = threadIdx.x; i < a.nzero; i += kThreads) a.zero[i] = 0;
   const void* Mp = a.M[b];
   const void* Gp = a.G != nullptr ? a.G[b] : nullptr;
   void* Wp = a.Mw != nullptr ? a.Mw[b] : nullptr;

@@ -87,7 +87,7 @@ __device__ __forceinline__ void load_a_slab(uint4 (&buf)[kFM][kKS], __amdgpu_buf
 #pragma unroll
     for (int s = 0; s < kKS; ++s)
       buf[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                r, voff, sbase + f * rb_stride + kt * 4096 + s * 1024, 0));
+          r, voff, __builtin_amdgcn_readfirstlane(sbase + f * rb_stride + kt * 4096 + s * 1024), 0));
 }
 
 // The Q slab kt into LDS stage `stage`: this wave's 2 row blocks x 4 fragments.
@@ -98,8 +98,9 @@ __device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t
     const int rb = wave * ((kBN / 32) / kNW) + f;
 #pragma unroll
     for (int s = 0; s < kKS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + (rb * kKS + s) * 64), 16, voff,
-                                               sbase + rb * rb_stride + kt * 4096 + s * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr_t)(stage + (rb * kKS + s) * 64), 16, voff,
+          __builtin_amdgcn_readfirstlane(sbase + rb * rb_stride + kt * 4096 + s * 1024), 0, 0);
   }
 }
 
@@ -675,14 +676,129 @@ __device__ __forceinline__ GemmArgs reload_args() {
 #endif
 }
 
+// This block's work: matrix b, tile (I, J) and slabs [k0, k1), and for a
+// piece of a split tail tile its tail index and piece number (piece = -1 for
+// a whole tile).  Consecutive block ids go to different XCDs (round-robin),
+// so within the whole-tile range and within the tail range the ids are
+// renumbered such that each XCD works through a contiguous range; tiles of a
+// general product are ordered in groups of 8 tile-rows for L2 reuse.
+struct WorkItem {
+  int b, tile, I, J, k0, k1, tail, piece;
+};
+
+__device__ __forceinline__ int xcd_contiguous(int id, int n) {
+  const int q = n >> 3, rem = n & 7, x = id & 7, slot = id >> 3;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + slot;
+}
+
+__device__ __forceinline__ WorkItem work_item(const GemmArgs& a) {
+  WorkItem w;
+  const int hw = blockIdx.x, nfull = a.full_blocks;
+  const int nk = a.K / kBK;
+  int t;
+  if (hw < nfull) {
+    t = xcd_contiguous(hw, nfull);
+    w.k0 = 0;
+    w.k1 = nk;
+    w.tail = -1;
+    w.piece = -1;
+  } else {
+    const int p = xcd_contiguous(hw - nfull, static_cast<int>(gridDim.x) - nfull);
+    w.tail = p / a.kpieces;
+    w.piece = p - w.tail * a.kpieces;
+    t = nfull + w.tail;
+    const int units = nk >> 2;  // k in units of 4 slabs, shared out as evenly as possible
+    w.k0 = 4 * ((units * w.piece) / a.kpieces);
+    w.k1 = 4 * ((units * (w.piece + 1)) / a.kpieces);
+  }
+  w.b = t / a.ntiles;
+  const int tile = t - w.b * a.ntiles;
+  w.tile = tile;
+  if (a.sym) {
+    tri_tile(tile, w.I, w.J);
+  } else {
+    const int ntm = a.Mdim / kBM, ntn = a.Ndim / kBN;
+    constexpr int G = 8;
+    const int grp = tile / (G * ntn);
+    const int first = grp * G;
+    const int rows = ntm - first < G ? ntm - first : G;
+    const int in = tile - grp * G * ntn;
+    w.I = first + in % rows;
+    w.J = in / rows;
+  }
+  return w;
+}
+
+// A piece of a split tail tile: store this block's fp32 partial tile, and
+// return true for the last piece to finish, which then holds the sum of all
+// pieces, added in piece order (so the result does not depend on which piece
+// finishes last), in acc.  Partials are kept per wave as [x][y][g][lane]
+// float4 records (1 KB per store).  All threads of the block call this.
+__device__ __forceinline__ bool tail_reduce(const GemmArgs& a, const WorkItem& w, f32x16_t (&acc)[kFM][kFN], int wave,
+                                            int lane, int* flag) {
+  constexpr int64_t kWaveFloats = kFM * kFN * 16 * 64;
+  auto part = [&](int piece) {
+    return a.part32 + (static_cast<int64_t>(w.tail) * a.kpieces + piece) * kPartFloats + wave * kWaveFloats +
+           4 * lane;
+  };
+  float* mine = part(w.piece);
+#pragma unroll
+  for (int x = 0; x < kFM; ++x)
+#pragma unroll
+    for (int y = 0; y < kFN; ++y)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(mine + ((x * kFN + y) * 4 + g) * 256) =
+            make_float4(acc[x][y][4 * g], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]);
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomicAdd(a.counters + w.tail, 1);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(*flag) != a.kpieces - 1) return false;  // uniform over the block
+  __threadfence();
+  if (threadIdx.x == 0) a.counters[w.tail] = 0;  // ready for the next launch
+#pragma unroll
+  for (int x = 0; x < kFM; ++x)
+#pragma unroll
+    for (int y = 0; y < kFN; ++y) {
+      const f32x16_t own = acc[x][y];
+      f32x16_t sum;
+      for (int p = 0; p < a.kpieces; ++p) {
+        f32x16_t v;
+        if (p == w.piece) {
+          v = own;
+        } else {
+          const float* src = part(p) + (x * kFN + y) * 4 * 256;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 q = *reinterpret_cast<const float4*>(src + g * 256);
+            v[4 * g] = q.x;
+            v[4 * g + 1] = q.y;
+            v[4 * g + 2] = q.z;
+            v[4 * g + 3] = q.w;
+          }
+        }
+        if (p == 0) {
+          sum = v;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum[r] += v[r];
+        }
+      }
+      acc[x][y] = sum;
+    }
+  return true;
+}
+
 template <int OP, int KIND>
 __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   // The Q ring is four separate arrays, each named statically at every access,
   // so the compiler's wait for an LDS read covers only the DMA into that stage.
   __shared__ uint4 stg0[kStageAlloc / 16], stg1[kStageAlloc / 16], stg2[kStageAlloc / 16], stg3[kStageAlloc / 16];
   __shared__ double red[2 * kNW];
-  int b, tile, I, J;
-  block_coords(a, kBM, kBN, b, tile, I, J);
+  __shared__ int tail_flag;
+  const WorkItem w = work_item(a);
+  const int b = w.b, tile = w.tile, I = w.I, J = w.J;
   EpiState st;
   block_init<kNT>(a, b, tile, red, st);
 
@@ -707,28 +823,30 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
 
-  const int nk = a.K / kBK;  // a multiple of 4: every operand dimension is a multiple of 256
+  // slabs k0 .. k1 - 1 (a multiple of 4 of them: every operand dimension is a
+  // multiple of 256 and tail pieces are cut at multiples of 4 slabs)
+  const int k0 = w.k0, k1 = w.k1;
   uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS], abuf3[kFM][kKS];
   uint4 bf[2][kFN];
-  // prologue: Q slabs 0..3 into the ring, P slabs 0..2 into registers
-  load_b_slab(stg0, rQ, voff, sQ, qstride, 0, wave);
-  load_b_slab(stg1, rQ, voff, sQ, qstride, 1, wave);
-  load_b_slab(stg2, rQ, voff, sQ, qstride, 2, wave);
-  load_b_slab(stg3, rQ, voff, sQ, qstride, 3, wave);
-  load_a_slab(abuf0, rP, voff, sP, pstride, 0);
-  load_a_slab(abuf1, rP, voff, sP, pstride, 1);
-  load_a_slab(abuf2, rP, voff, sP, pstride, 2);
+  // prologue: Q slabs k0 .. k0 + 3 into the ring, P slabs k0 .. k0 + 2 into registers
+  load_b_slab(stg0, rQ, voff, sQ, qstride, k0, wave);
+  load_b_slab(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
+  load_b_slab(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
+  load_b_slab(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
+  load_a_slab(abuf0, rP, voff, sP, pstride, k0);
+  load_a_slab(abuf1, rP, voff, sP, pstride, k0 + 1);
+  load_a_slab(abuf2, rP, voff, sP, pstride, k0 + 2);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(6 * kLoadsB, 15));  // Q slab 0 landed
   block_barrier();
 #pragma unroll
   for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
 
   // 4 slabs per trip (the 4 LDS stages and the 4 P register buffers, which
-  // are loaded three slabs ahead); nk is a multiple of 4.
+  // are loaded three slabs ahead).
 #define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
   load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 3);                                             \
   slab<OP>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
-  for (int kt = 0; kt < nk; kt += 4) {
+  for (int kt = k0; kt < k1; kt += 4) {
     MUON_SLAB(0, abuf0, abuf3, stg0, stg1)
     MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
     MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
@@ -737,6 +855,7 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
 #undef MUON_SLAB
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   block_barrier();
+  if (w.piece >= 0 && !tail_reduce(a, w, acc, wave, lane, &tail_flag)) return;
 
   // The epilogue runs from registers; the last product stages O through this
   // wave's LDS stage.  It reads the launch arguments afresh, so they are not
@@ -749,7 +868,8 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
 
 template <int OP>
 hipError_t launch_gemm_mfma(const GemmArgs& a, int batch, int kind, hipStream_t s) {
-  const dim3 grid(a.ntiles, batch), block(kNT);
+  const int64_t tiles = static_cast<int64_t>(a.ntiles) * batch;
+  const dim3 grid(static_cast<unsigned>(a.full_blocks + (tiles - a.full_blocks) * a.kpieces)), block(kNT);
   switch (kind) {
     case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym>), grid, block, 0, s, a); break;
     case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16>), grid, block, 0, s, a); break;

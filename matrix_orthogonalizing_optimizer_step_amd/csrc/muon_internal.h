@@ -20,6 +20,11 @@ enum DType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 // second stage sums a bounded, fixed-order list of partials).
 constexpr int kNormBlocks = 512;
 
+// Block tile edges of the MFMA kernels (16-bit operands) and of the fp32
+// check path.
+constexpr int kMfmaTile = 256;
+constexpr int kCheckTile = 64;
+
 // One GEMM launch over a batch: C[i][j] = sum_k P[i][k] * Q[j][k] (both
 // operands K-contiguous), followed by the fused epilogue
 //   v = alpha * C + beta * E[i][j] + gamma * (i == j < n_real)
@@ -53,12 +58,22 @@ struct GemmArgs {
   int m_real;                       // real m (columns of X)
   int user_ld;                      // leading dimension of the user's W / O
   float lr, wd;
+
+  // Tail split (MFMA kernels): the first full_blocks blocks each take a whole
+  // tile; each of the remaining tiles (tiles beyond full_blocks, over the whole
+  // batch) is cut along k into kpieces pieces, one block each.  The last piece
+  // of a tile to finish adds the fp32 partials of all pieces in piece order
+  // and runs the epilogue.  kpieces = 1: no split (full_blocks = all tiles).
+  int full_blocks;
+  int kpieces;
+  float* part32;     // tail tiles x kpieces partial tiles (kMfmaTile^2 floats each)
+  int* counters;     // one per tail tile, zero between launches
 };
 
-// Block tile edges of the MFMA kernels (16-bit operands) and of the fp32
-// check path.
-constexpr int kMfmaTile = 256;
-constexpr int kCheckTile = 64;
+// Partial-tile storage of the tail split, per tile piece (floats).
+constexpr int64_t kPartFloats = static_cast<int64_t>(kMfmaTile) * kMfmaTile;
+// At most this many k pieces per tail tile.
+constexpr int kMaxPieces = 8;
 
 // Epilogue kinds of the MFMA kernel, one kernel instantiation each, so that
 // every epilogue is straight-line code.
@@ -91,6 +106,8 @@ struct NormArgs {
   double mu;
   int64_t count;          // rows * cols
   double* partials;       // batch * kNormBlocks
+  int* zero;              // zero[0 .. nzero) is cleared by the kernel (GEMM tail counters)
+  int nzero;
 };
 hipError_t launch_norm(const NormArgs& a, int batch, hipStream_t s);
 
