@@ -1,0 +1,88 @@
+"""GPU parity at the benchmark's full sizes and launch configuration.
+
+The Qwen2.5-7B-shaped layer set (q, o 3584x3584; k, v 3584x512; gate, up,
+down 3584x18944), one muon_step call per same-shape group with the default
+configuration (Gram Newton-Schulz, fp16 operands, T = 5, restart after
+iteration 2), fp32 weights and bf16 momentum, as bench.py runs it.  Two
+steps are taken so the momentum update rounds (the first starts from zero).
+
+Checks per group, on every matrix: the stored momentum bit for bit against
+the fp64 rounding of mu M + G, and the weight update against W - lr O in
+fp32.  The orthogonalised momentum O is compared with the fp64 oracle in
+full for the first q/o and k/v matrices (relative Frobenius 2e-2).  For the
+3584x18944 matrices, whose full oracle run is too slow for a test, O is
+checked through properties that hold at any size: its singular values lie in
+the band the quintic coefficients imply, and Gram and standard
+Newton-Schulz on the GPU agree (they are equal in exact arithmetic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import matrix_orthogonalizing_optimizer_step_amd as mu
+from oracle import muon_oracle as orc
+from synth import inputs as syn
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+WL = syn.WORKLOADS["qwen2.5-7b"]
+MU, LR = 0.95, 0.02
+# p_5 of the quintic coefficients maps [0.0015, 1] into this band (exact
+# arithmetic; pinned by the oracle tests); 16-bit arithmetic may move the
+# singular values by about its relative error.
+BAND = (0.681831, 1.202369)
+BAND_SLACK = 0.02
+
+
+def two_steps(gi):
+    Ws, Ms, G0 = syn.group_inputs(WL, gi)
+    _, _, G1 = syn.group_inputs(WL, gi, step=1)
+    W = [w.to(DEV) for w in Ws]
+    M = [m.to(DEV) for m in Ms]
+    mu.muon_step(W, M, [g.to(DEV) for g in G0], MU, LR, 0.0, "gram")
+    W_prev = [w.clone() for w in W]
+    M_prev = [m.cpu() for m in M]
+    O = [torch.empty(w.shape, dtype=torch.float32, device=DEV) for w in W]
+    mu.muon_step(W, M, [g.to(DEV) for g in G1], MU, LR, 0.0, "gram", O_out=O)
+    torch.cuda.synchronize()
+    return W, M, O, W_prev, M_prev, G1
+
+
+def check_momentum_and_weights(W, M, O, W_prev, M_prev, G1):
+    mu32, lr32 = float(np.float32(MU)), float(np.float32(LR))
+    for i in range(len(W)):
+        expect = orc.round_bf16(mu32 * syn.to_f64(M_prev[i]) + syn.to_f64(G1[i]))
+        assert np.array_equal(syn.to_f64(M[i]), expect), i
+        ref = W_prev[i] - torch.tensor(lr32, dtype=torch.float32) * O[i]
+        torch.testing.assert_close(W[i], ref, rtol=2e-7, atol=2e-7)
+
+
+@pytest.mark.parametrize("gi", [0, 1], ids=["qo-3584x3584", "kv-3584x512"])
+def test_fullsize_group_against_oracle(gi):
+    W, M, O, W_prev, M_prev, G1 = two_steps(gi)
+    check_momentum_and_weights(W, M, O, W_prev, M_prev, G1)
+    ref = orc.gram_newton_schulz(syn.to_f64(M[0]))
+    assert orc.relative_frobenius(syn.to_f64(O[0]), ref) < 2e-2
+
+
+def test_fullsize_mlp_group_properties():
+    W, M, O, W_prev, M_prev, G1 = two_steps(2)
+    check_momentum_and_weights(W, M, O, W_prev, M_prev, G1)
+    # singular values of O (rows <= cols: the eigenvalues of O O^T)
+    O0 = O[0]
+    gram = (O0 @ O0.T).double().cpu().numpy()
+    sv = np.sqrt(np.clip(np.linalg.eigvalsh(gram), 0.0, None))
+    assert sv.min() >= BAND[0] - BAND_SLACK, sv.min()
+    assert sv.max() <= BAND[1] + BAND_SLACK, sv.max()
+    # Gram and standard Newton-Schulz agree on the same stored momentum
+    Os = torch.empty_like(O0)
+    mu.ns_orthogonalize([M[0]], [Os])
+    Og = torch.empty_like(O0)
+    mu.gram_ns_orthogonalize([M[0]], [Og])
+    torch.cuda.synchronize()
+    # the step's O is the Gram orthogonalisation of the stored momentum (a batch
+    # of one splits the long X X^T product differently, so not bit for bit)
+    rel = lambda a, b: (torch.linalg.matrix_norm((a - b).double()) / torch.linalg.matrix_norm(b.double())).item()
+    assert rel(Og, O0) < 1e-3
+    assert rel(Os, Og) < 3e-2

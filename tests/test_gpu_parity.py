@@ -101,6 +101,19 @@ def test_deterministic():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("shape", [(256, 8192), (300, 9000), (9000, 300)])
+def test_tail_split_long_k(shape):
+    """X X^T with k >= 8192 on fewer tiles than compute units is cut along k;
+    the pieces' fp32 partials are added in a fixed order: oracle parity and
+    bitwise repeatability."""
+    M = syn.random_matrix(22, *shape, dtype="bf16")
+    for variant, compute in (("standard", "bf16"), ("gram", "f16")):
+        a = gpu_orth(variant, [M], compute)[0]
+        b = gpu_orth(variant, [M], compute)[0]
+        assert np.array_equal(a, b)
+        assert relF(a, oracle_orth(variant, M)) < TOL[compute]
+
+
 def test_zero_matrix_gives_zero():
     M = torch.zeros(64, 96, dtype=torch.bfloat16)
     for variant in ("standard", "gram"):
