@@ -828,14 +828,18 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   const int k0 = w.k0, k1 = w.k1;
   uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS], abuf3[kFM][kKS];
   uint4 bf[2][kFN];
-  // prologue: Q slabs k0 .. k0 + 3 into the ring, P slabs k0 .. k0 + 2 into registers
+  // prologue: Q slabs k0 .. k0 + 3 into the ring, P slabs k0 .. k0 + 2 into
+  // registers, issued in the order the loop itself issues them (P slab j + 3
+  // at the start of slab j, Q slab j + 4 in its middle), so the outstanding
+  // loads at the loop head look the same on entry and on every trip and the
+  // compiler's waits for the P registers stay exact.
   load_b_slab(stg0, rQ, voff, sQ, qstride, k0, wave);
-  load_b_slab(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
-  load_b_slab(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
-  load_b_slab(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
   load_a_slab(abuf0, rP, voff, sP, pstride, k0);
+  load_b_slab(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
   load_a_slab(abuf1, rP, voff, sP, pstride, k0 + 1);
+  load_b_slab(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
   load_a_slab(abuf2, rP, voff, sP, pstride, k0 + 2);
+  load_b_slab(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(6 * kLoadsB, 15));  // Q slab 0 landed
   block_barrier();
 #pragma unroll
