@@ -13,7 +13,9 @@
  *           grid quantization", overall framework: momentum, NS, update; the
  *           full example adds weight decay.
  *   [LiMuon] notes on LiMuon, design 3: the quintic (3.4445, -4.7750, 2.0315).
- *   [MuonBlog] "Muon Optimizer" blog post, §1: Muon is for 2-D matrices.
+ *   [MuonBlog] "Muon Optimizer" blog post, §1: Muon is for 2-D matrices;
+ *           §5 (Muon is no drop-in AdamW replacement) item 4: weight decay and
+ *           a per-parameter update scale.
  *
  * Conventions shared by every entry point:
  *
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 #define MUON_MAX_T 16
 #define MUON_MAX_DIM (1 << 20)
 
@@ -151,7 +153,15 @@ muon_status gram_ns_orthogonalize(int batch, int rows, int cols,
  *   M <- mu M + G          (computed exactly in fp64, rounded to nearest even
  *                           into state_dtype; M is updated in place)
  *   O  = NS(M)             (variant and cfg as above, on the stored M)
- *   W <- W - lr (O + weight_decay W)   (fp32 arithmetic, W updated in place)
+ *   W <- W - lr (update_scale O + weight_decay W)
+ *                          (fp32 arithmetic, W updated in place)
+ *
+ *   update_scale  the per-parameter update scale that [MuonBlog §5 item 4]
+ *           names, with weight decay, as needed for large-scale training; the
+ *           pages give no formula, so it is a plain factor chosen by the
+ *           caller per call (per same-shape parameter group).  1 = the plain
+ *           step of the other pages; it multiplies O in the update only
+ *           (O_out receives O unscaled).  Must be finite.
  *
  *   W       device array of device pointers, rows x cols, w_dtype F32 or BF16.
  *   M       device array of device pointers, momentum, state_dtype F32 or
@@ -165,10 +175,39 @@ muon_status gram_ns_orthogonalize(int batch, int rows, int cols,
 muon_status muon_step(int batch, int rows, int cols,
                       void *const *W, muon_dtype w_dtype,
                       void *const *M, const void *const *G, muon_dtype state_dtype,
-                      float mu, float lr, float weight_decay,
+                      float mu, float lr, float weight_decay, float update_scale,
                       muon_ns_variant variant, const muon_ns_config *cfg,
                       void *const *O_out, muon_dtype o_dtype,
                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Per-iteration coefficient schedule in the manner of the Polar Express
+ * quintics that [GNS §3.2] iterates with (its printed table is garbled, so
+ * the schedule is derived from the method's principle rather than copied):
+ * p_t(x) = a_t x + b_t x^3 + c_t x^5 is the odd quintic nearest to 1 in the
+ * maximum norm on [l_t, u_t], the interval that holds the singular values of
+ * X_{t-1} when those of X0 lie in [ell, 1]; [l_{t+1}, u_{t+1}] is the image of
+ * [l_t, u_t] under the applied polynomial.  The [GNS §3.3] safety factor f
+ * applies each polynomial as p_t(x / f), i.e. (a_t / f, b_t / f^3, c_t / f^5),
+ * so singular values somewhat above the design range still converge.  Once
+ * (u_t - l_t) / u_t <= 1e-2 the minimax polynomials are replaced by their
+ * limit (15/8, -10/8, 3/8) (p(1) = 1, p'(1) = p''(1) = 0; its error there is
+ * below 3e-6, under any 16-bit rounding).  The coefficients
+ * are rounded to fp32, and the intervals follow the rounded polynomials.
+ *
+ *   T       iterations, 1..MUON_MAX_T.
+ *   ell     lower end of the singular values of X0, 0 < ell < 1 (e.g. 1e-3).
+ *   safety  f, 1 <= f <= 2 (1 = none; [GNS §3.3] uses 1.05).
+ *   coeffs  HOST array of 3 T floats receiving (a_t, b_t, c_t), t = 1..T, in
+ *           the layout muon_ns_config.coeffs reads.
+ *   bounds  NULL, or a HOST array of 2 T + 2 doubles receiving l_1, u_1 (=
+ *           ell, 1), l_2, u_2, ..., l_{T+1}, u_{T+1}.
+ * Host-only arithmetic (no device, no stream).  Returns MUON_ERR_INVALID_ARG
+ * for arguments out of range, MUON_ERR_UNSUPPORTED if the minimax exchange
+ * does not settle (not observed for 1e-7 <= ell < 1); outputs are then
+ * partly written.
+ */
+muon_status muon_quintic_schedule(int T, double ell, double safety, float *coeffs, double *bounds);
 
 /*
  * Floating-point operations of one orthogonalisation of a rows x cols matrix

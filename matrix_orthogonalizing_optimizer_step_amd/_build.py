@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
 SOURCES = ["muon_gemm_bf16.hip", "muon_gemm_f16.hip", "muon_gemm_f32.hip", "muon_gemm.hip",
-           "muon_elementwise.hip", "muon_api.hip"]
+           "muon_elementwise.hip", "muon_api.hip", "muon_schedule.cpp"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -57,7 +57,7 @@ def build(verbose: bool = False) -> str:
     try:
         objs, procs = [], []
         for src in SOURCES:
-            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
             procs.append((src, _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)))
         for src, proc in procs:

@@ -68,7 +68,7 @@ def load_library():
         f.argtypes = sig
         f.restype = i32
     lib.muon_step.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, ctypes.c_float,
-                              ctypes.c_float, i32, cfgp, vp, i32, vp, sz, vp]
+                              ctypes.c_float, ctypes.c_float, i32, cfgp, vp, i32, vp, sz, vp]
     lib.muon_step.restype = i32
     lib.muon_ns_flops.argtypes = [i32, i32, i32, cfgp, i32]
     lib.muon_ns_flops.restype = ctypes.c_double
@@ -80,6 +80,9 @@ def load_library():
     lib.muon_trace_collect.restype = i32
     lib.muon_abi_version.argtypes = []
     lib.muon_abi_version.restype = i32
+    lib.muon_quintic_schedule.argtypes = [i32, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_double)]
+    lib.muon_quintic_schedule.restype = i32
     _lib = lib
     return lib
 
@@ -213,8 +216,10 @@ def gram_ns_orthogonalize(M, O, cfg: Optional[NSConfig] = None, workspace=None, 
 
 
 def muon_step(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant="standard",
-              cfg: Optional[NSConfig] = None, O_out=None, workspace=None, stream=None):
-    """One Muon step on lists of same-shape tensors; W and M are updated in place."""
+              cfg: Optional[NSConfig] = None, O_out=None, workspace=None, stream=None,
+              update_scale: float = 1.0):
+    """One Muon step on lists of same-shape tensors; W and M are updated in place:
+    W <- W - lr (update_scale O + weight_decay W)."""
     lib = load_library()
     v = _variant(variant)
     rows, cols, wdt = _batch(W, "W")
@@ -234,7 +239,7 @@ def muon_step(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant=
         po = pointer_array(O_out)
     pw, pm, pg = pointer_array(W), pointer_array(M), pointer_array(G)
     st = lib.muon_step(len(W), rows, cols, pw.data_ptr(), wdt, pm.data_ptr(), pg.data_ptr(), sdt,
-                       float(mu), float(lr), float(weight_decay), v, ctypes.byref(c),
+                       float(mu), float(lr), float(weight_decay), float(update_scale), v, ctypes.byref(c),
                        po.data_ptr() if po is not None else None, odt,
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
@@ -247,6 +252,19 @@ def ns_flops(rows: int, cols: int, variant="standard", cfg: Optional[NSConfig] =
     v = _variant(variant)
     c, _keep = (cfg or NSConfig()).to_c(v)
     return float(lib.muon_ns_flops(rows, cols, v, ctypes.byref(c), 1 if symmetric_aware else 0))
+
+
+def quintic_schedule(T: int = 5, ell: float = 1e-3, safety: float = 1.0):
+    """Per-iteration minimax quintics (see muon_quintic_schedule in
+    include/muon.h).  Returns (coeffs, bounds): T (a, b, c) tuples of fp32
+    values, usable as NSConfig.coeffs, and the T + 1 intervals (l_t, u_t)."""
+    lib = load_library()
+    c = (ctypes.c_float * (3 * T))()
+    b = (ctypes.c_double * (2 * T + 2))()
+    _check(lib.muon_quintic_schedule(int(T), float(ell), float(safety), c, b))
+    coeffs = [(c[3 * t], c[3 * t + 1], c[3 * t + 2]) for t in range(T)]
+    bounds = [(b[2 * t], b[2 * t + 1]) for t in range(T + 1)]
+    return coeffs, bounds
 
 
 def abi_version() -> int:

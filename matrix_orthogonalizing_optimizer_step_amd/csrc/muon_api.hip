@@ -50,9 +50,14 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // (k of at least 8192, pieces of at least 1024): handing a partial tile over
 // costs a device-scope fence (an L2 write-back) and an fp32 round trip, which
 // shorter tiles do not amortise (measured: a net loss at k = 3584).
+#ifndef MUON_TAIL_MIN_UNITS
+#define MUON_TAIL_MIN_UNITS 32
+#endif
+constexpr int kTailMinUnits = MUON_TAIL_MIN_UNITS;
+
 void tail_split(int64_t tiles, int units, int cu, int* full, int* pieces) {
   const int64_t rounds = tiles / cu, tail = tiles - rounds * cu;
-  int s = tail > 0 && units >= 32 ? static_cast<int>(cu / tail) : 1;
+  int s = tail > 0 && units >= kTailMinUnits ? static_cast<int>(cu / tail) : 1;
   s = s < kMaxPieces ? s : kMaxPieces;
   s = s < units / 4 ? s : units / 4;
   if (s < 2) {
@@ -293,7 +298,7 @@ struct Final {
   int w_dtype;
   void* const* O;
   int o_dtype;
-  float lr, wd;
+  float lr, wd, oscale;
 };
 
 void set_final(GemmArgs& g, const Plan& p, const Final& f) {
@@ -306,6 +311,7 @@ void set_final(GemmArgs& g, const Plan& p, const Final& f) {
   g.user_ld = p.cols;
   g.lr = f.lr;
   g.wd = f.wd;
+  g.oscale = f.oscale;
 }
 
 #define MUON_LAUNCH(expr)                        \
@@ -582,7 +588,7 @@ muon_status orthogonalize(muon_ns_variant v, int batch, int rows, int cols, cons
   char* ws = static_cast<char*>(workspace);
   st = run_prologue(p, c, ws, M, m_dtype, nullptr, nullptr, 0.0, s);
   if (st != MUON_OK) return st;
-  Final f{nullptr, 0, O, o_dtype, 0.0f, 0.0f};
+  Final f{nullptr, 0, O, o_dtype, 0.0f, 0.0f, 1.0f};
   return v == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
 }
 
@@ -626,7 +632,7 @@ muon_status gram_ns_orthogonalize(int batch, int rows, int cols, const void* con
 
 muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype w_dtype, void* const* M,
                       const void* const* G, muon_dtype state_dtype, float mu, float lr,
-                      float weight_decay, muon_ns_variant variant, const muon_ns_config* cfg,
+                      float weight_decay, float update_scale, muon_ns_variant variant, const muon_ns_config* cfg,
                       void* const* O_out, muon_dtype o_dtype, void* workspace, size_t ws_bytes,
                       void* stream) {
   if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
@@ -640,7 +646,7 @@ muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype 
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (arrays[i] != nullptr && arrays[i] == arrays[j]) return MUON_ERR_INVALID_ARG;
-  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay)) return MUON_ERR_INVALID_ARG;
+  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay) || !isfinite(update_scale)) return MUON_ERR_INVALID_ARG;
   if (!valid_dtype(w_dtype) || !valid_dtype(state_dtype)) return MUON_ERR_INVALID_ARG;
   if (w_dtype == MUON_F16 || state_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
   if (O_out != nullptr && o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
@@ -651,7 +657,7 @@ muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype 
   st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(M), state_dtype, G, M,
                     static_cast<double>(mu), s);
   if (st != MUON_OK) return st;
-  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay};
+  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
   return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
 }
 

@@ -238,17 +238,17 @@ __device__ __forceinline__ void user_store4(void* p, int64_t idx, int dtype, int
   for (int k = 0; k < 4 && k < valid; ++k) user_store1(p, idx + k, dtype, f4get(v, k));
 }
 
-// W <- W - lr (O + wd W) and the optional O store for four consecutive
+// W <- W - lr (s O + wd W) and the optional O store (O, unscaled) for four consecutive
 // elements of the user's matrix at idx (valid of them in range).
 __device__ __forceinline__ void final_update4(const GemmArgs& a, const EpiState& st, int64_t idx, int valid, float4 o,
                                               float4 w) {
   if (valid <= 0) return;
   if (st.w != nullptr) {
     float4 nw;
-    nw.x = w.x - a.lr * (o.x + a.wd * w.x);
-    nw.y = w.y - a.lr * (o.y + a.wd * w.y);
-    nw.z = w.z - a.lr * (o.z + a.wd * w.z);
-    nw.w = w.w - a.lr * (o.w + a.wd * w.w);
+    nw.x = w.x - a.lr * (a.oscale * o.x + a.wd * w.x);
+    nw.y = w.y - a.lr * (a.oscale * o.y + a.wd * w.y);
+    nw.z = w.z - a.lr * (a.oscale * o.z + a.wd * w.z);
+    nw.w = w.w - a.lr * (a.oscale * o.w + a.wd * w.w);
     user_store4(st.w, idx, a.w_dtype, valid, nw);
   }
   if (st.o != nullptr) user_store4(st.o, idx, a.o_dtype, valid, o);

@@ -284,12 +284,12 @@ __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiStat
   void* w = st.w;
   void* o = st.o;
   const int64_t ld = a.user_ld;
-  const float lr = a.lr, wd = a.wd;
+  const float lr = a.lr, wd = a.wd, os = a.oscale;
   auto update = [&](float4& nw, const float4& ov) {
-    nw.x -= lr * (ov.x + wd * nw.x);
-    nw.y -= lr * (ov.y + wd * nw.y);
-    nw.z -= lr * (ov.z + wd * nw.z);
-    nw.w -= lr * (ov.w + wd * nw.w);
+    nw.x -= lr * (os * ov.x + wd * nw.x);
+    nw.y -= lr * (os * ov.y + wd * nw.y);
+    nw.z -= lr * (os * ov.z + wd * nw.z);
+    nw.w -= lr * (os * ov.w + wd * nw.w);
   };
   if (!a.transposed) {  // W[i][j .. j + 3], lane -> columns j0 + 4 lane
     const int64_t base = static_cast<int64_t>(i0) * ld + j0 + 4 * lane;
@@ -750,12 +750,15 @@ __device__ __forceinline__ bool tail_reduce(const GemmArgs& a, const WorkItem& w
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(mine + ((x * kFN + y) * 4 + g) * 256) =
             make_float4(acc[x][y][4 * g], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]);
-  __threadfence();
+  // Release: this piece's partial is written back to memory before the
+  // counter moves.  Only the last piece acquires (invalidates its caches), so
+  // the other pieces leave the cached operands of their neighbours alone.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) *flag = atomicAdd(a.counters + w.tail, 1);
   __syncthreads();
   if (__builtin_amdgcn_readfirstlane(*flag) != a.kpieces - 1) return false;  // uniform over the block
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) a.counters[w.tail] = 0;  // ready for the next launch
 #pragma unroll
   for (int x = 0; x < kFM; ++x)

@@ -57,7 +57,7 @@ struct GemmArgs {
   int transposed;                   // user matrix is m x n (rows > cols)
   int m_real;                       // real m (columns of X)
   int user_ld;                      // leading dimension of the user's W / O
-  float lr, wd;
+  float lr, wd, oscale;             // W <- W - lr (oscale O + wd W)
 
   // Tail split (MFMA kernels): the first full_blocks blocks each take a whole
   // tile; each of the remaining tiles (tiles beyond full_blocks, over the whole

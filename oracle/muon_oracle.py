@@ -17,7 +17,8 @@ Sources (cited by short name):
 * [LiMuon]  notes on LiMuon (arXiv 2509.14562), design 3: the quintic
             coefficients (3.4445, -4.7750, 2.0315).
 * [MuonBlog] "Muon Optimizer" blog post, section 1: momentum form; Muon is
-            applied to 2-D matrices only.
+            applied to 2-D matrices only; section 5 item 4: weight decay and a
+            per-parameter update scale (no formula given: a plain factor on O).
 
 Readings where the pages are silent or garbled (each also listed in the
 design notes of the repository):
@@ -213,18 +214,21 @@ def gram_newton_schulz(M, coeffs=None, T=5, eps=EPS, restarts=(2,), counter=None
 
 
 # --------------------------------------------------------------------------
-# the Muon step ([GRASP framework], [GNS §1.1 eq.(1)])
+# the Muon step ([GRASP framework], [GNS §1.1 eq.(1)]; weight decay and the
+# per-parameter update scale: [MuonBlog §5 item 4])
 # --------------------------------------------------------------------------
 def muon_step(W, M_prev, G, mu, lr, weight_decay=0.0, variant="standard",
               coeffs=None, T=5, eps=EPS, restarts=(2,), state_dtype="bf16",
-              w_dtype="f32"):
+              w_dtype="f32", update_scale=1.0):
     """One Muon step for a 2-D weight.  Returns (W_new, M_new, O).
 
     M = mu M_prev + G, rounded to ``state_dtype``; O = NS(M) (standard or
-    Gram); W_new = W - lr (O + weight_decay W), rounded to ``w_dtype``.  All
-    arithmetic is float64 on the exact stored input values.  ``mu``, ``lr``
-    and ``weight_decay`` are used as given (pass the float32 values a caller
-    hands the library to compare bit for bit)."""
+    Gram); W_new = W - lr (update_scale O + weight_decay W), rounded to
+    ``w_dtype``.  The pages name the update scale without a formula, so it is
+    a plain factor on O.  All arithmetic is float64 on the exact stored input
+    values.  ``mu``, ``lr``, ``weight_decay`` and ``update_scale`` are used as
+    given (pass the float32 values a caller hands the library to compare bit
+    for bit)."""
     W = np.asarray(W, dtype=np.float64)
     M_prev = np.asarray(M_prev, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
@@ -237,7 +241,7 @@ def muon_step(W, M_prev, G, mu, lr, weight_decay=0.0, variant="standard",
         O = gram_newton_schulz(M_new, coeffs, T, eps, restarts)
     else:
         raise ValueError(f"unknown variant {variant!r}")
-    W_new = round_to(W - lr * (O + weight_decay * W), w_dtype)
+    W_new = round_to(W - lr * (update_scale * O + weight_decay * W), w_dtype)
     return W_new, M_new, O
 
 

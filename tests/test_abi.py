@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert mu.abi_version() == 1
+    assert mu.abi_version() == 2
 
 
 def test_status_strings():
@@ -104,14 +104,16 @@ def test_invalid_muon_step_calls():
     lib = mu.load_library()
     ws = mu.workspace_size(1, 4, 4)
 
-    def call(W=1, wdt=0, M=2, G=3, sdt=1, mu_=0.9, lr=0.1, wd=0.0, v=0, O=None, odt=0, wsb=ws):
-        return lib.muon_step(1, 4, 4, W, wdt, M, G, sdt, mu_, lr, wd, v, None, O, odt, 256, wsb, None)
+    def call(W=1, wdt=0, M=2, G=3, sdt=1, mu_=0.9, lr=0.1, wd=0.0, s=1.0, v=0, O=None, odt=0, wsb=ws):
+        return lib.muon_step(1, 4, 4, W, wdt, M, G, sdt, mu_, lr, wd, s, v, None, O, odt, 256, wsb, None)
 
     assert call(W=None) == 1
     assert call(M=1) == 1                 # aliasing
     assert call(O=3) == 1                 # O_out aliases G
     assert call(mu_=float("nan")) == 1
     assert call(lr=float("inf")) == 1
+    assert call(s=float("nan")) == 1      # update scale must be finite
+    assert call(wd=float("-inf")) == 1
     assert call(sdt=2) == 2               # f16 state unsupported
     assert call(wdt=2) == 2
     assert call(O=4, odt=2) == 2

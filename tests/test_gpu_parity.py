@@ -84,6 +84,24 @@ def test_gram_ns_parity(compute, restarts, shape):
     assert relF(got, ref) < TOL[compute], relF(got, ref)
 
 
+@pytest.mark.parametrize("f", [1.0, 1.05])
+@pytest.mark.parametrize("variant,compute", [("standard", "f16"), ("standard", "f32"), ("gram", "f16"),
+                                             ("gram", "f32")])
+def test_quintic_schedule_parity(variant, compute, f):
+    """Per-iteration minimax quintics from the library's schedule (ell = 1e-3,
+    with and without the safety factor), restart after iteration 2 for Gram,
+    against the oracle run with the same fp32 coefficients.  The steep first
+    polynomials amplify operand rounding: bf16 operands measure up to 2.6e-2
+    on 700 x 256, over the 16-bit tolerance, so the 16-bit case runs with the
+    fp16 operands that the Gram NS notes recommend (section 3.3)."""
+    coeffs, _ = mu.quintic_schedule(5, 1e-3, f)
+    for shape in ((300, 1100), (700, 256)):
+        M = syn.random_matrix(50, *shape, std=1e-3, dtype="bf16")
+        got = gpu_orth(variant, [M], compute, coeffs=coeffs)[0]
+        ref = oracle_orth(variant, M, coeffs=coeffs)
+        assert relF(got, ref) < TOL[compute], shape
+
+
 def test_batch_matches_single_calls_bitwise():
     Ms = [syn.random_matrix(10 + i, 200, 456, dtype="bf16") for i in range(3)]
     for variant in ("standard", "gram"):
@@ -197,6 +215,43 @@ def test_muon_step_transposed_bf16_weights():
     # bf16 weights: the update is within the O tolerance plus one bf16 rounding
     err = np.abs(syn.to_f64(W1[0]) - Wr)
     assert np.all(err <= 0.05 * np.abs(syn.to_f64(O1[0]) - Or) + np.abs(Wr) * 2.0 ** -8 + 1e-6)
+
+
+@pytest.mark.parametrize("variant,compute", [("standard", "bf16"), ("gram", "f16"), ("standard", "f32")])
+@pytest.mark.parametrize("shape", [(256, 700), (300, 200)])
+def test_muon_step_update_scale_and_weight_decay(variant, compute, shape):
+    """W <- W - lr (s O + wd W): against the GPU's own O elementwise (fp32
+    arithmetic), against the oracle at the O tolerance, and s = 1 is the
+    default call bit for bit."""
+    r, c = shape
+    W = syn.random_matrix(40, r, c)
+    M = syn.random_matrix(41, r, c, std=1e-3, dtype="bf16")
+    G = syn.random_matrix(42, r, c, std=1e-3, dtype="bf16")
+    mu_, lr, wd, s = 0.9, 0.05, 0.1, 0.37
+    cfg = mu.NSConfig(compute=compute)
+
+    def step(scale):
+        Wg, Mg = [W.to(DEV)], [M.to(DEV)]
+        Oo = [torch.empty(r, c, dtype=torch.float32, device=DEV)]
+        kw = {} if scale is None else {"update_scale": scale}
+        mu.muon_step(Wg, Mg, [G.to(DEV)], mu_, lr, wd, variant, cfg, O_out=Oo, **kw)
+        torch.cuda.synchronize()
+        return Wg[0].cpu(), Mg[0].cpu(), Oo[0].cpu()
+
+    W1, M1, O1 = step(s)
+    f32 = np.float32
+    ref32 = torch.from_numpy((W.numpy() - f32(lr) * (f32(s) * O1.numpy() + f32(wd) * W.numpy())).astype(np.float32))
+    torch.testing.assert_close(W1, ref32, rtol=2e-7, atol=2e-7)
+    Wr, Mr, Or = orc.muon_step(syn.to_f64(W), syn.to_f64(M), syn.to_f64(G), float(f32(mu_)), float(f32(lr)),
+                               float(f32(wd)), variant, state_dtype="bf16", w_dtype="f64",
+                               update_scale=float(f32(s)))
+    assert np.array_equal(syn.to_f64(M1), Mr)
+    assert relF(syn.to_f64(O1), Or) < TOL[compute]
+    dW = syn.to_f64(W1) - syn.to_f64(W)
+    assert relF(dW, Wr - syn.to_f64(W)) < TOL[compute] + 1e-4
+    Wa, _, _ = step(1.0)
+    Wb, _, _ = step(None)
+    assert torch.equal(Wa, Wb)
 
 
 def test_checkpoint_resume_is_bitwise():

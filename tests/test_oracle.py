@@ -322,6 +322,25 @@ def test_muon_step_identity_momentum():
     np.testing.assert_allclose(W1, -0.5 * scalar_map(x, [ABC] * 5) * np.eye(n), atol=1e-14)
 
 
+def test_muon_step_update_scale_closed_forms():
+    # [MuonBlog §5 item 4]: W <- W - lr (s O + wd W).  s = 0 leaves pure
+    # decoupled decay W (1 - lr wd) although O != 0; with W = 0 and identity
+    # momentum the update is -lr s p_5(x) I (the scalar map of the quintic).
+    r = rng(19)
+    W = r.standard_normal((8, 24))
+    G = r.standard_normal((8, 24))
+    W1, _, O = orc.muon_step(W, np.zeros_like(W), G, 0.95, 0.02, 0.1, state_dtype="f64", w_dtype="f64",
+                             update_scale=0.0)
+    assert np.abs(O).max() > 0.1
+    np.testing.assert_allclose(W1, W * (1.0 - 0.02 * 0.1), rtol=0, atol=1e-15)
+    n = 16
+    for s in (0.5, 2.5):
+        W1, _, _ = orc.muon_step(np.zeros((n, n)), np.zeros((n, n)), np.eye(n), 0.9, 0.5, state_dtype="f32",
+                                 w_dtype="f64", update_scale=s)
+        x = 1.0 / (np.sqrt(n) + 1e-7)
+        np.testing.assert_allclose(W1, -0.5 * s * scalar_map(x, [ABC] * 5) * np.eye(n), atol=1e-14)
+
+
 def test_muon_step_gram_variant_equals_standard():
     r = rng(18)
     W = r.standard_normal((10, 30))

@@ -1,0 +1,167 @@
+"""Per-iteration quintic schedules: pins for the oracle's derivation, and the
+library's own derivation (host code behind the C ABI) against the oracle.
+
+The oracle solves each minimax problem as a linear programme; the pins check
+it against what fixes the answer independently: the alternation theorem (the
+error of the best approximation equioscillates at four points, which certifies
+optimality), the scale covariance of the problem, the limit polynomial, and a
+brute-force evaluation of the composed polynomials over the start interval.
+The library (a Remez exchange in C++) is then compared with the oracle."""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import muon_oracle as orc
+from oracle import quintic_schedule as qs
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_schedule(T, ell, f):
+    return qs.schedule(T, ell, f)
+
+
+def critical_points(p, l, u):
+    a, b, c = p
+    out = []
+    for y in np.roots([5.0 * c, 3.0 * b, a]):
+        if abs(y.imag) < 1e-12 and y.real > 0 and l < np.sqrt(y.real) < u:
+            out.append(float(np.sqrt(y.real)))
+    return sorted(out)
+
+
+# ------------------------------------------------------------ one minimax problem
+@pytest.mark.parametrize("l,u", [(1e-3, 1.0), (0.1, 1.0), (0.5, 1.5), (0.8, 1.2)])
+def test_minimax_equioscillates(l, u):
+    """Alternation certificate: 1 - p = +E, -E, +E, -E at l, the two interior
+    extrema and u, and |1 - p| <= E everywhere on [l, u]; by the alternation
+    theorem for x, x^3, x^5 no odd quintic does better."""
+    p, E = qs.minimax_quintic(l, u)
+    z = critical_points(p, l, u)
+    assert len(z) == 2
+    pts = [l, z[0], z[1], u]
+    err = 1.0 - qs.quintic(p, np.array(pts))
+    np.testing.assert_allclose(err, [E, -E, E, -E], rtol=1e-6, atol=1e-9)
+    x = np.linspace(l, u, 1_000_001)
+    assert np.abs(1.0 - qs.quintic(p, x)).max() <= E * (1 + 1e-6) + 1e-12
+    # a worse candidate is worse: the plain quintic of the step, rescaled
+    assert np.abs(1.0 - qs.quintic(orc.QUINTIC, x / u)).max() > E
+
+
+def test_minimax_scale_covariance():
+    """Best approximation on [k l, k u] is p(x / k): (a / k, b / k^3, c / k^5)."""
+    p1, E1 = qs.minimax_quintic(0.2, 1.0)
+    k = 1.7
+    p2, E2 = qs.minimax_quintic(0.2 * k, 1.0 * k)
+    assert abs(E1 - E2) < 1e-8
+    np.testing.assert_allclose(p2, (p1[0] / k, p1[1] / k ** 3, p1[2] / k ** 5), rtol=1e-6)
+
+
+def test_limit_polynomial():
+    """(15/8, -10/8, 3/8): p(1) = 1, p'(1) = 0, p''(1) = 0, the pages' h of
+    the cubic Newton-Schulz step written as a quintic in x."""
+    a, b, c = qs.LIMIT
+    assert a + b + c == 1.0
+    assert a + 3 * b + 5 * c == 0.0
+    assert 6 * b + 20 * c == 0.0
+    assert list(qs.LIMIT) == GOLDEN["cubic_ns_h"]["value"]
+    # and the minimax polynomials of shrinking intervals around 1 approach it
+    for d, tol in ((0.2, 0.3), (0.05, 0.03)):
+        p, _ = qs.minimax_quintic(1.0 - d, 1.0 + d)
+        assert max(abs(x - y) for x, y in zip(p, qs.LIMIT)) < tol
+
+
+def test_printed_first_row_is_no_minimax_polynomial():
+    """The extracted table cannot be a minimax schedule: p = 0 already has
+    error 1 on any interval, so a best approximation has E <= 1, but the
+    printed p_1 misses 1 by 1.27 at x = 1.  Hence the schedule is derived."""
+    rows = GOLDEN["polar_express_table_printed"]["value"]
+    p1 = rows[0]
+    assert abs(1.0 - qs.quintic(p1, 1.0)) > 1.0
+    # the derived first polynomial of [1e-3, 1] is a proper one
+    p, E = qs.minimax_quintic(1e-3, 1.0)
+    assert E < 1.0
+
+
+# ------------------------------------------------------------ the schedule
+@pytest.mark.parametrize("ell,f", [(1e-3, 1.0), (1e-3, 1.05), (0.05, 1.0)])
+def test_schedule_bounds_are_the_images(ell, f):
+    """Brute force: every x in [ell, 1] stays inside [l_t, u_t] after t
+    polynomials, and the bounds are attained."""
+    coeffs, bounds = oracle_schedule(5, ell, f)
+    x = np.concatenate([np.geomspace(ell, 1.0, 200_001), np.linspace(ell, 1.0, 200_001)])
+    for t, p in enumerate(coeffs):
+        x = qs.quintic(p, x)
+        lo, hi = bounds[t + 1]
+        assert x.min() >= lo - 1e-12 and x.max() <= hi + 1e-12
+        assert x.min() - lo < 1e-6 * max(1.0, hi) and hi - x.max() < 1e-6 * max(1.0, hi)
+    # the intervals tighten around 1 step by step
+    widths = [hi - lo for lo, hi in bounds[1:]]
+    assert all(w1 < w0 for w0, w1 in zip(widths, widths[1:]))
+    assert widths[-1] < (0.4 if ell < 0.01 else 1e-3)
+
+
+def test_safety_factor_rescales_the_first_polynomial():
+    """[GNS §3.3]: the polynomial is applied as p(x / f)."""
+    c1, _ = oracle_schedule(5, 1e-3, 1.0)
+    c2, _ = oracle_schedule(5, 1e-3, 1.05)
+    f = GOLDEN["safety_factor_reach"]["value"]
+    a, b, c = c1[0]
+    np.testing.assert_allclose(c2[0], (a / f, b / f ** 3, c / f ** 5), rtol=1e-6)
+    # with the factor, singular values up to f still land in the first image
+    lo, hi = qs.image(c2[0], 1e-3, f)
+    assert hi <= 2.0 and lo > 0.0
+
+
+def test_schedule_maps_singular_values_into_the_last_interval():
+    """Newton-Schulz with the schedule (oracle, fp64) on a matrix whose
+    normalised singular values lie in [ell, 1] returns singular values inside
+    [l_{T+1}, u_{T+1}] (Prop.1: the iteration acts on each singular value)."""
+    ell = 1e-3
+    coeffs, bounds = oracle_schedule(5, ell, 1.0)
+    r = np.random.default_rng(7)
+    n, m = 24, 60
+    U, _ = np.linalg.qr(r.standard_normal((n, n)))
+    V, _ = np.linalg.qr(r.standard_normal((m, n)))
+    s = np.geomspace(1.0, 0.02, n)
+    M = (U * s) @ V.T
+    x = s / (np.linalg.norm(M) + orc.EPS)
+    assert x.min() >= ell and x.max() <= 1.0
+    O = orc.newton_schulz(M, coeffs, 5)
+    sv = np.linalg.svd(O, compute_uv=False)
+    lo, hi = bounds[-1]
+    assert sv.min() >= lo - 1e-12 and sv.max() <= hi + 1e-12
+    # and Gram NS with a restart gives the same in exact arithmetic
+    Og = orc.gram_newton_schulz(M, coeffs, 5, restarts=(2,))
+    assert orc.relative_frobenius(Og, O) < 1e-12
+
+
+# ------------------------------------------------------------ the library's derivation
+@pytest.mark.parametrize("ell,f", [(1e-3, 1.0), (1e-3, 1.05), (0.05, 1.0), (0.05, 1.05)])
+def test_library_schedule_matches_oracle(ell, f):
+    import matrix_orthogonalizing_optimizer_step_amd as mu
+    c_lib, b_lib = mu.quintic_schedule(5, ell, f)
+    c_or, b_or = oracle_schedule(5, ell, f)
+    for p, q in zip(c_lib, c_or):
+        np.testing.assert_allclose(p, q, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(np.array(b_lib), np.array(b_or), rtol=0, atol=2e-6)
+
+
+def test_library_schedule_rejects_bad_arguments():
+    import ctypes
+
+    import matrix_orthogonalizing_optimizer_step_amd as mu
+    lib = mu.load_library()
+    buf = (ctypes.c_float * 48)()
+    assert lib.muon_quintic_schedule(0, 1e-3, 1.0, buf, None) == 1
+    assert lib.muon_quintic_schedule(17, 1e-3, 1.0, buf, None) == 1
+    assert lib.muon_quintic_schedule(5, 0.0, 1.0, buf, None) == 1
+    assert lib.muon_quintic_schedule(5, 1.0, 1.0, buf, None) == 1
+    assert lib.muon_quintic_schedule(5, 1e-3, 0.9, buf, None) == 1
+    assert lib.muon_quintic_schedule(5, float("nan"), 1.0, buf, None) == 1
+    assert lib.muon_quintic_schedule(5, 1e-3, 1.0, None, None) == 1
+    assert lib.muon_quintic_schedule(16, 1e-7, 1.05, buf, None) == 0
