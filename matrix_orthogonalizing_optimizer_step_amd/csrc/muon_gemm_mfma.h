@@ -96,11 +96,16 @@ __device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t
 #pragma unroll
   for (int f = 0; f < (kBN / 32) / kNW; ++f) {
     const int rb = wave * ((kBN / 32) / kNW) + f;
-#pragma unroll
-    for (int s = 0; s < kKS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_ptr_t)(stage + (rb * kKS + s) * 64), 16, voff,
-          __builtin_amdgcn_readfirstlane(sbase + rb * rb_stride + kt * 4096 + s * 1024), 0, 0);
+    // the 4 fragments of a row block are 1 KB apart both in memory and in
+    // the stage, so they share the LDS base (M0) and the scalar offset and
+    // differ only in the immediate offset, which applies to both addresses
+    lds_ptr_t dst = (lds_ptr_t)(stage + rb * kKS * 64);
+    const int so = __builtin_amdgcn_readfirstlane(sbase + rb * rb_stride + kt * 4096);
+    static_assert(kKS == 4, "four fragments per row block and slab");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, so, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, so, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, so, 3072, 0);
   }
 }
 
@@ -126,6 +131,25 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][kFN], const uint4 (&a
   }
 }
 
+// Half a k-step: the MFMAs of columns Y0 .. Y0 + 3 with the reads of the
+// next k-step's fragments Y0 .. Y0 + 3 in between.
+template <int OP, int Y0>
+__device__ __forceinline__ void kstep_half(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], int s,
+                                           const uint4 (&bcur)[kFN], uint4 (&bnext)[kFN], const uint4* next_frags,
+                                           int lane) {
+#pragma unroll
+  for (int y = Y0; y < Y0 + kFN / 2; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
+#pragma unroll
+  for (int y = Y0; y < Y0 + kFN / 2; ++y)
+#pragma unroll
+    for (int x = 0; x < kFM; ++x) acc[x][y] = mfma32<OP>(a[x][s], bcur[y], acc[x][y]);
+#pragma unroll
+  for (int g = 0; g < kFN / 2; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+  }
+}
+
 // One slab: k-steps 0..3 of slab kt from registers `a` and LDS stage `cur`,
 // reading ahead into bf; the barrier and the ring refill (slab kt + 4 into
 // `cur`) sit after k-step 2.  Loads are issued unconditionally, also past
@@ -139,14 +163,16 @@ __device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)
   kstep<OP>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
   kstep<OP>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
   kstep<OP>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
-  // This wave's reads of slab kt have landed and its part of slab kt + 1 is
-  // in LDS (the 5 load groups issued after it may still be in flight); after
-  // the barrier the whole slab kt + 1 is visible and nobody reads `cur`.
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, 0));
+  kstep_half<OP, 0>(acc, a, 3, bf[1], bf[0], nxt, lane);
+  // This wave's reads of slab kt (all older than the 4 reads of `nxt` just
+  // issued) have landed and its part of slab kt + 1 is in LDS (the 5 load
+  // groups issued after it may still be in flight); after the barrier the
+  // whole slab kt + 1 is visible and nobody reads `cur`.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, kFN / 2));
   block_barrier();
   __builtin_amdgcn_sched_barrier(0);
   load_b_slab(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
-  kstep<OP>(acc, a, 3, bf[1], bf[0], nxt, true, lane);
+  kstep_half<OP, kFN / 2>(acc, a, 3, bf[1], bf[0], nxt, lane);
 }
 
 // ---------------------------------------------------------------------------
