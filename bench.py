@@ -38,8 +38,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen2.5-7b")
     ap.add_argument("--variant", default="gram", choices=["gram", "standard"])
     ap.add_argument("--compute", default=None, help="operand type override: bf16, f16 or f32")
@@ -213,7 +213,7 @@ def main():
             x["ws"] = shared
     log(f"[bench] workspace {total_ws / 2**30:.2f} GiB, {'one stream' if args.one_stream else 'one stream per group'}")
 
-    def step(variant, serial=False):
+    def step(variant, serial=False, orth_only=False):
         serial = serial or args.one_stream
         if not serial:
             ev = torch.cuda.Event()
@@ -221,23 +221,35 @@ def main():
         for x in groups:
             if not serial:
                 x["stream"].wait_event(ev)
-            mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant), workspace=x["ws"],
-                         stream=main if serial else x["stream"])
+            s = main if serial else x["stream"]
+            if orth_only:  # the orthogonalisation alone, M -> O
+                f = mu.gram_ns_orthogonalize if variant == "gram" else mu.ns_orthogonalize
+                f(x["M"], x["O"], cfg_for(variant), workspace=x["ws"], stream=s)
+            else:
+                mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant), workspace=x["ws"],
+                             stream=s)
         if not serial:
             for x in groups:
                 done = torch.cuda.Event()
                 done.record(x["stream"])
                 main.wait_event(done)
 
-    def timed(variant, steps, warmup):
+    def timed(variant, steps, warmup, orth_only=False):
+        """Mean seconds per step over `steps` (host clock, synchronised on both
+        sides) and the per-step durations from events on the main stream."""
         for _ in range(warmup):
-            step(variant)
+            step(variant, orth_only=orth_only)
         torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        for _ in range(steps):
-            step(variant)
+        evs[0].record(main)
+        for i in range(steps):
+            step(variant, orth_only=orth_only)
+            evs[i + 1].record(main)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        sec = (time.perf_counter() - t0) / steps
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        return sec, per
 
     def summary(variant, sec):
         alg = flops_for(variant, True)
@@ -254,10 +266,19 @@ def main():
 
     results = {}
     variants = [args.variant] + ([] if args.no_other_variant else [v for v in ("gram", "standard") if v != args.variant])
+    for x in groups:  # outputs of the orthogonalisation-alone timing
+        x["O"] = [torch.empty(x["g"].rows, x["g"].cols, dtype=torch.float32, device=dev) for _ in range(x["g"].count)]
     for v in variants:
-        sec = timed(v, args.steps, args.warmup)
+        sec, per = timed(v, args.steps, args.warmup)
         results[v] = summary(v, sec)
-        log(f"[bench] {v}: {sec * 1e3:.3f} ms/step, {results[v]['tflops_algorithmic']:.1f} TFLOP/s")
+        results[v]["ms_per_step_p10_p50_p90"] = [float(np.percentile(per, q)) for q in (10, 50, 90)]
+        osec, _ = timed(v, args.steps, args.warmup, orth_only=True)
+        results[v]["orthogonalization_only"] = {
+            "ms_per_step": osec * 1e3, "tflops_algorithmic": flops_for(v, True) / osec / 1e12,
+            "note": "ns_orthogonalize / gram_ns_orthogonalize of every group's momentum (no momentum update, "
+                    "no weight update)"}
+        log(f"[bench] {v}: {sec * 1e3:.3f} ms/step, {results[v]['tflops_algorithmic']:.1f} TFLOP/s; "
+            f"orthogonalisation alone {osec * 1e3:.3f} ms")
 
     # ------------------------------------------------ per-kernel durations (HIP events)
     # The traced steps run the groups back to back on one stream so that each
