@@ -132,6 +132,24 @@ def test_tail_split_long_k(shape):
         assert relF(a, oracle_orth(variant, M)) < TOL[compute]
 
 
+@pytest.mark.parametrize("shape", [(1, 1 << 20), (1 << 20, 1)], ids=["row-2^20", "column-2^20"])
+def test_maximum_dimension_vector(shape):
+    """The largest dimension the ABI accepts (2^20), on the degenerate n = 1
+    case: X X^T is 1 x 1 with k = 2^20 (cut into k pieces), and O is
+    p_5(x) v / ||v|| with x = ||v|| / (||v|| + eps)."""
+    M = syn.random_matrix(23, *shape, std=1e-3, dtype="bf16")
+    v = syn.to_f64(M).reshape(-1)
+    x = np.linalg.norm(v) / (np.linalg.norm(v) + orc.EPS)
+    for _ in range(5):
+        x = QUINTIC5[0][0] * x + QUINTIC5[0][1] * x ** 3 + QUINTIC5[0][2] * x ** 5
+    closed = (x * v / np.linalg.norm(v)).reshape(shape)
+    for variant, compute in (("standard", "bf16"), ("gram", "f16")):
+        got = gpu_orth(variant, [M], compute)[0]
+        ref = oracle_orth(variant, M)
+        assert relF(ref, closed) < 1e-12
+        assert relF(got, ref) < TOL[compute], (variant, relF(got, ref))
+
+
 def test_zero_matrix_gives_zero():
     M = torch.zeros(64, 96, dtype=torch.bfloat16)
     for variant in ("standard", "gram"):
