@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--compute", default=None, help="operand type override: bf16, f16 or f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue every group on one stream (default: one stream per group)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -213,7 +215,8 @@ def main():
             x["ws"] = shared
     log(f"[bench] workspace {total_ws / 2**30:.2f} GiB, {'one stream' if args.one_stream else 'one stream per group'}")
 
-    def step(variant, serial=False, orth_only=False):
+    def step(variant, serial=False, orth_only=False, base=None):
+        main = base or torch.cuda.current_stream()
         serial = serial or args.one_stream
         if not serial:
             ev = torch.cuda.Event()
@@ -251,6 +254,29 @@ def main():
         per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
         return sec, per
 
+    def timed_graph(variant, steps):
+        """Capture one step (every group's stream joined into the capture) in a
+        HIP graph and time `steps` replays."""
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up off the capture: caches the pointer arrays
+            step(variant, base=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(variant, base=torch.cuda.current_stream())
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        del g
+        return sec
+
     def summary(variant, sec):
         alg = flops_for(variant, True)
         dense = flops_for(variant, False)
@@ -279,6 +305,11 @@ def main():
                     "no weight update)"}
         log(f"[bench] {v}: {sec * 1e3:.3f} ms/step, {results[v]['tflops_algorithmic']:.1f} TFLOP/s; "
             f"orthogonalisation alone {osec * 1e3:.3f} ms")
+        if args.graph:
+            gsec = timed_graph(v, args.steps)
+            results[v]["hip_graph"] = {"ms_per_step": gsec * 1e3, "tflops_algorithmic": flops_for(v, True) / gsec / 1e12,
+                                       "note": "the whole step captured once (all streams) and replayed"}
+            log(f"[bench] {v}: HIP graph replay {gsec * 1e3:.3f} ms/step")
 
     # ------------------------------------------------ per-kernel durations (HIP events)
     # The traced steps run the groups back to back on one stream so that each

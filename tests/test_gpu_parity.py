@@ -286,3 +286,39 @@ def test_checkpoint_resume_is_bitwise():
     mu.muon_step(Wc, Mc, [G1[0].to(DEV)], 0.95, 0.02, 0.0, "gram")
     torch.cuda.synchronize()
     assert torch.equal(Wa[0], Wc[0]) and torch.equal(Ma[0], Mc[0])
+
+
+@pytest.mark.parametrize("variant", ["standard", "gram"])
+def test_muon_step_in_a_hip_graph(variant):
+    """The step launches kernels only (no memsets or copies on the stream), so
+    it can be captured in a HIP graph: each of several replays, with eager work
+    and synchronisations in between, equals the same step run eagerly."""
+    wl = syn.WORKLOADS["llama-130m"]
+    Ws, Ms, Gs = syn.group_inputs(wl, 1, count=3)
+    Wg, Mg, Gg = [w.to(DEV) for w in Ws], [m.to(DEV) for m in Ms], [g.to(DEV) for g in Gs]
+    We, Me = [w.clone() for w in Wg], [m.clone() for m in Mg]
+    ws = torch.empty(mu.workspace_size(3, *Ws[0].shape, variant), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture (caches the pointer arrays)
+        Wt, Mt = [w.clone() for w in Wg], [m.clone() for m in Mg]
+        mu.muon_step(Wt, Mt, Gg, 0.95, 0.02, 0.01, variant, None, workspace=ws)
+        mu.muon_step(Wg, Mg, Gg, 0.95, 0.02, 0.01, variant, None, workspace=ws)  # pointers used in the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mu.muon_step(We, Me, Gg, 0.95, 0.02, 0.01, variant, None)  # eager copy of the same first step
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(Wg, We)) and all(torch.equal(a, b) for a, b in zip(Mg, Me))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mu.muon_step(Wg, Mg, Gg, 0.95, 0.02, 0.01, variant, None, workspace=ws)
+    for rep in range(3):
+        g.replay()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # the program's own eager work between replays
+        mu.muon_step(We, Me, Gg, 0.95, 0.02, 0.01, variant, None)
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for a, b in zip(Wg, We):
+            assert torch.equal(a, b), rep
+        for a, b in zip(Mg, Me):
+            assert torch.equal(a, b), rep
