@@ -19,9 +19,11 @@ namespace muon {
 //    ring with buffer_load ... lds (1 KB per instruction, lane l landing at
 //    byte 16 l), three slabs ahead, and each fragment is read back with one
 //    contiguous, conflict-free 16-byte-per-lane LDS read.
-// One barrier per slab, after the third k-step: by then every wave has read
-// the whole slab into registers, so its stage can take the slab four ahead,
-// and the MFMAs already issued keep the matrix pipe busy through the wait.
+// One barrier per slab, half-way through the fourth k-step: by then every
+// wave has read the whole slab into registers (the reads of the last k-step's
+// fragments were issued a k-step earlier), so its stage can take the slab
+// four ahead, and the MFMAs already issued keep the matrix pipe busy through
+// the wait.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // The per-wave epilogue staging area, typed as LDS so its accesses are
@@ -152,7 +154,7 @@ __device__ __forceinline__ void kstep_half(f32x16_t (&acc)[kFM][kFN], const uint
 
 // One slab: k-steps 0..3 of slab kt from registers `a` and LDS stage `cur`,
 // reading ahead into bf; the barrier and the ring refill (slab kt + 4 into
-// `cur`) sit after k-step 2.  Loads are issued unconditionally, also past
+// `cur`) sit half-way through k-step 3.  Loads are issued unconditionally, also past
 // the last slab: buffer loads are range-checked against the descriptor and
 // the data is never used, and straight-line code lets the compiler count
 // outstanding loads exactly.
