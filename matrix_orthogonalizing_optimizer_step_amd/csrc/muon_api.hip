@@ -137,7 +137,7 @@ void gemm_kernel_name(const GemmArgs& g, int op, char* out, size_t n) {
   if (op == kOpF32) {
     snprintf(out, n, "gemm_nt_f64acc");
   } else {
-    snprintf(out, n, "gemm_nt_mfma<%d, %d>", op, epi_kind(g));
+    snprintf(out, n, "gemm_nt_mfma<%d, %d, %d>", op, epi_kind(g), g.bn);
   }
 }
 
@@ -215,7 +215,8 @@ bool make_plan(int batch, int rows, int cols, muon_ns_variant v, const Config& c
   }
   const int nt = p->n_pad / p->tile;
   p->normpart = take(static_cast<size_t>(batch) * kNormBlocks * sizeof(double));
-  p->tilepart = take(static_cast<size_t>(batch) * nt * (nt + 1) / 2 * 2 * sizeof(double));
+  // (trace, sum of squares) per tile of a symmetric product, in 256 x 128 tiles at most
+  p->tilepart = take(static_cast<size_t>(batch) * nt * (nt + 1) * 2 * sizeof(double));
   p->shift = take(static_cast<size_t>(batch) * sizeof(float));
   // the tail split's partial tiles and counters, sized for the largest tail
   // of this call's launches (symmetric K = m or n, general K = n)
@@ -255,6 +256,23 @@ GemmArgs base_args(const Plan& p, char* ws) {
   return g;
 }
 
+// Symmetric MFMA products with k up to this may use 256 x 128 tiles (two
+// blocks per compute unit); longer ones keep 256 x 256 tiles, whose deeper P
+// look-ahead covers operands streamed from HBM.
+constexpr int kHalfTileMaxK = 4096;
+
+// Whether T whole tiles on `cu` compute units finish sooner as 2 T half
+// tiles.  In units of one whole tile's time on a compute unit: whole tiles
+// take ceil(T / cu) rounds; half tiles run two per compute unit (a pair takes
+// about one unit) and a last round of at most one half tile per compute unit
+// takes about 0.6 (one wave per SIMD again).  So the half tiles gain when the
+// last round of whole tiles is at most half full, and tie otherwise (measured:
+// three 3584^2 products, 315 tiles, +25 %; two, 210 tiles, -1 %).
+bool half_tiles_pay(int64_t T, int cu) {
+  const int64_t r = T % cu;
+  return r > 0 && 2 * r <= cu;
+}
+
 // C = P P^T-style symmetric product of two n_pad x n_pad (or n_pad x K) operands.
 void set_sym(GemmArgs& g, const Plan& p, const void* P, const void* Q, int K, int64_t sPQ, int ld) {
   g.Mdim = g.Ndim = p.n_pad;
@@ -265,7 +283,13 @@ void set_sym(GemmArgs& g, const Plan& p, const void* P, const void* Q, int K, in
   g.sP = g.sQ = sPQ;
   g.ldp = g.ldq = ld;
   const int nt = p.n_pad / p.tile;
+  g.bn = kMfmaTile;
   g.ntiles = nt * (nt + 1) / 2;
+  if (p.op != kOpF32 && K <= kHalfTileMaxK && half_tiles_pay(static_cast<int64_t>(g.ntiles) * p.batch, p.cu)) {
+    // the lower triangle in 256 x 128 tiles: 2 I + 2 of them in tile row I
+    g.bn = kHalfTile;
+    g.ntiles = nt * (nt + 1);
+  }
   g.sO = static_cast<int64_t>(p.n_pad) * p.n_pad;
   g.ldo = p.n_pad;
   g.sE = g.sO;
@@ -284,6 +308,7 @@ void set_px(GemmArgs& g, const Plan& p, const void* P, const void* XT) {
   g.Q = XT;
   g.sQ = static_cast<int64_t>(p.m_pad) * p.n_pad;
   g.ldq = p.n_pad;
+  g.bn = kMfmaTile;
   g.ntiles = (p.n_pad / p.tile) * (p.m_pad / p.tile);
   g.sO = static_cast<int64_t>(p.n_pad) * p.m_pad;
   g.ldo = p.m_pad;
@@ -326,7 +351,7 @@ hipError_t gemm(const Plan& p, GemmArgs g, const char* role, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>(g.ntiles) * p.batch;
   g.full_blocks = static_cast<int>(tiles);
   g.kpieces = 1;
-  if (p.cu > 0) {
+  if (p.cu > 0 && g.bn == kMfmaTile) {
     int full = 0, pieces = 1;
     tail_split(tiles, g.K / 256, p.cu, &full, &pieces);
     if (pieces > 1 && (tiles - full) <= p.max_tail && (tiles - full) * pieces <= p.max_pieces) {
@@ -421,8 +446,6 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
   const int64_t snn = static_cast<int64_t>(p.n_pad) * p.n_pad;
   double* tp = reinterpret_cast<double*>(ws + p.tilepart);
   float* shift = reinterpret_cast<float*>(ws + p.shift);
-  const int nt = p.n_pad / p.tile;
-  const int ntri = nt * (nt + 1) / 2;
   int xc = 0;
   for (int t = 0; t < c.T; ++t) {
     const float a = c.c[t][0], b = c.c[t][1], cc = c.c[t][2];
@@ -431,6 +454,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
     g.out16 = ws + p.A16;
     g.part_out = c.shift ? tp : nullptr;
+    const int npart = g.ntiles;  // partials of A, one per tile of this launch
     MUON_LAUNCH(gemm(p, g, "XXt", s));
     // B' = c A A + b A + (a - a') I
     g = base_args(p, ws);
@@ -445,7 +469,7 @@ muon_status run_standard(const Plan& p, const Config& c, char* ws, const Final& 
     g.coef_c = cc;
     if (c.shift) {
       g.part_in = tp;
-      g.npart_in = ntri;
+      g.npart_in = npart;
       g.shift_out = shift;
     }
     g.out16 = ws + p.B16;
@@ -483,15 +507,15 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
   char* Z16 = ws + p.Z16;
   char* RZ16 = ws + p.RZ16;
   const int64_t snn = static_cast<int64_t>(p.n_pad) * p.n_pad;
-  const int nt = p.n_pad / p.tile;
-  const int ntri = nt * (nt + 1) / 2;
   int xc = 0, qc = 0;
+  int npart = 0;  // tiles (one partial each) of the launch that last wrote R
 
   auto gram_of_x = [&]() {  // R = X X^T + partials
     GemmArgs g = base_args(p, ws);
     set_sym(g, p, ws + p.XN, ws + p.XN, p.m_pad, sx, p.m_pad);
     g.out16 = R16;
     g.part_out = c.shift ? tp : nullptr;
+    npart = g.ntiles;
     return gemm(p, g, "XXt", s);
   };
   MUON_LAUNCH(gram_of_x());
@@ -511,7 +535,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
     g.coef_c = cc;
     if (c.shift) {
       g.part_in = tp;
-      g.npart_in = ntri;
+      g.npart_in = npart;
       g.shift_out = shift;
     }
     g.out16 = Z16;
@@ -559,6 +583,7 @@ muon_status run_gram(const Plan& p, const Config& c, char* ws, const Final& f, h
       g.shift_in = sh;
       g.out16 = R16;
       g.part_out = c.shift ? tp : nullptr;
+      npart = g.ntiles;
       MUON_LAUNCH(gemm(p, g, "ZRZ", s));
     }
   }

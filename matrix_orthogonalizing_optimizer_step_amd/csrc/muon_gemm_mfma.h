@@ -45,21 +45,37 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
   }
 }
 
-constexpr int kBM = kMfmaTile, kBN = kMfmaTile, kBK = 64;
+constexpr int kBM = kMfmaTile, kBK = 64;
 constexpr int kNW = 4, kNT = 64 * kNW;
 constexpr int kFM = kBM / kNW / 32;   // MFMA row blocks per wave (2)
-constexpr int kFN = kBN / 32;         // MFMA column blocks per wave (8)
 constexpr int kKS = kBK / 16;         // k-steps per slab (4)
 constexpr int kStages = 4;            // LDS ring depth for Q
-constexpr int kStageBytes = kBN * kBK * 2;   // 32 KB
-constexpr int kTN = kBN;              // epilogue: columns per wave
-constexpr int kLDE = kTN + 4;         // staged row length (floats)
-// each LDS stage array also holds one wave's 32-row epilogue staging block
-constexpr int kStageAlloc = kStageBytes > 32 * kLDE * 4 ? kStageBytes : 32 * kLDE * 4;
-// per-wave loads per slab: P: kFM row blocks x kKS fragments; Q: 8 row blocks / kNW waves x kKS
-constexpr int kLoadsA = kFM * kKS;
-constexpr int kLoadsB = (kBN / 32) / kNW * kKS;
-static_assert(kLoadsA == kLoadsB, "the vmcnt bookkeeping assumes equal A and B load groups");
+constexpr int kLDE = kMfmaTile + 4;   // last product: staged row length (floats)
+constexpr int kLoadsA = kFM * kKS;    // P loads per wave and slab
+
+// The block tile is 256 rows by BN columns.  BN = 256: one block per compute
+// unit, 2 x 8 MFMA blocks (256 accumulator registers) per wave, P three slabs
+// ahead in four register buffers.  BN = 128: two blocks per compute unit (two
+// waves per SIMD, so one wave's waits and barrier are covered by the other's
+// MFMAs), 2 x 4 MFMA blocks (128 accumulator registers) per wave, P one slab
+// ahead in two buffers; used for symmetric products with k = n (short), where
+// the finer tiles also fill the last round better.
+template <int BN>
+struct TileCfg {
+  static constexpr int kFN = BN / 32;          // MFMA column blocks per wave
+  static constexpr int kRBW = BN / 32 / kNW;   // Q row blocks each wave streams in per slab
+  static constexpr int kLoadsB = kRBW * kKS;   // Q loads per wave and slab
+  static constexpr int kStageBytes = BN * kBK * 2;
+  // the 256-wide stages also hold one wave's 32-row staging block of the last product
+  static constexpr int kStageAlloc = BN == 256 && kStageBytes < 32 * kLDE * 4 ? 32 * kLDE * 4 : kStageBytes;
+  static constexpr int kPBufs = BN == 256 ? 4 : 2;
+  // Loads a wave issues after its part of Q slab kt + 1 and before the
+  // barrier of slab kt: the P slabs kt + 1 .. kt + 3 (issued at the starts of
+  // slabs kt - 2 .. kt) and Q slabs kt + 2, kt + 3.  With P one slab ahead the
+  // oldest of those P groups would be slab kt - 1, already consumed, so the
+  // count leaves it out (which also makes it exact for the first slab).
+  static constexpr int kWaitBarrier = (kPBufs == 4 ? 3 : 2) * kLoadsA + 2 * kLoadsB;
+};
 
 // s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
 // (7 = no wait), lgkmcnt [11:8] (15 = no wait).
@@ -92,12 +108,14 @@ __device__ __forceinline__ void load_a_slab(uint4 (&buf)[kFM][kKS], __amdgpu_buf
           r, voff, __builtin_amdgcn_readfirstlane(sbase + f * rb_stride + kt * 4096 + s * 1024), 0));
 }
 
-// The Q slab kt into LDS stage `stage`: this wave's 2 row blocks x 4 fragments.
+// The Q slab kt into LDS stage `stage`: this wave's row blocks x 4 fragments.
+template <int BN>
 __device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t r, int voff, int sbase,
                                             int rb_stride, int kt, int wave) {
+  constexpr int RBW = TileCfg<BN>::kRBW;
 #pragma unroll
-  for (int f = 0; f < (kBN / 32) / kNW; ++f) {
-    const int rb = wave * ((kBN / 32) / kNW) + f;
+  for (int f = 0; f < RBW; ++f) {
+    const int rb = wave * RBW + f;
     // the 4 fragments of a row block are 1 KB apart both in memory and in
     // the stage, so they share the LDS base (M0) and the scalar offset and
     // differ only in the immediate offset, which applies to both addresses
@@ -112,21 +130,21 @@ __device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t
 }
 
 // MFMAs of one k-step with the Q fragments of the next k-step read in between.
-template <int OP>
-__device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], int s,
-                                      const uint4 (&bcur)[kFN], uint4 (&bnext)[kFN], const uint4* next_frags,
+template <int OP, int FN>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][FN], const uint4 (&a)[kFM][kKS], int s,
+                                      const uint4 (&bcur)[FN], uint4 (&bnext)[FN], const uint4* next_frags,
                                       bool read_next, int lane) {
   if (read_next) {
 #pragma unroll
-    for (int y = 0; y < kFN; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
+    for (int y = 0; y < FN; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
   }
 #pragma unroll
-  for (int y = 0; y < kFN; ++y)
+  for (int y = 0; y < FN; ++y)
 #pragma unroll
     for (int x = 0; x < kFM; ++x) acc[x][y] = mfma32<OP>(a[x][s], bcur[y], acc[x][y]);
   if (read_next) {
 #pragma unroll
-    for (int g = 0; g < kFN; ++g) {
+    for (int g = 0; g < FN; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
     }
@@ -135,18 +153,18 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[kFM][kFN], const uint4 (&a
 
 // Half a k-step: the MFMAs of columns Y0 .. Y0 + 3 with the reads of the
 // next k-step's fragments Y0 .. Y0 + 3 in between.
-template <int OP, int Y0>
-__device__ __forceinline__ void kstep_half(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], int s,
-                                           const uint4 (&bcur)[kFN], uint4 (&bnext)[kFN], const uint4* next_frags,
+template <int OP, int FN, int Y0>
+__device__ __forceinline__ void kstep_half(f32x16_t (&acc)[kFM][FN], const uint4 (&a)[kFM][kKS], int s,
+                                           const uint4 (&bcur)[FN], uint4 (&bnext)[FN], const uint4* next_frags,
                                            int lane) {
 #pragma unroll
-  for (int y = Y0; y < Y0 + kFN / 2; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
+  for (int y = Y0; y < Y0 + FN / 2; ++y) bnext[y] = next_frags[y * kKS * 64 + lane];
 #pragma unroll
-  for (int y = Y0; y < Y0 + kFN / 2; ++y)
+  for (int y = Y0; y < Y0 + FN / 2; ++y)
 #pragma unroll
     for (int x = 0; x < kFM; ++x) acc[x][y] = mfma32<OP>(a[x][s], bcur[y], acc[x][y]);
 #pragma unroll
-  for (int g = 0; g < kFN / 2; ++g) {
+  for (int g = 0; g < FN / 2; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
   }
@@ -158,23 +176,25 @@ __device__ __forceinline__ void kstep_half(f32x16_t (&acc)[kFM][kFN], const uint
 // the last slab: buffer loads are range-checked against the descriptor and
 // the data is never used, and straight-line code lets the compiler count
 // outstanding loads exactly.
-template <int OP>
-__device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][kFN], const uint4 (&a)[kFM][kKS], uint4 (&bf)[2][kFN],
-                                     uint4* cur, const uint4* nxt, __amdgpu_buffer_rsrc_t rQ, int voff, int sQ,
-                                     int qstride, int kt, int wave, int lane) {
-  kstep<OP>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
-  kstep<OP>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
-  kstep<OP>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
-  kstep_half<OP, 0>(acc, a, 3, bf[1], bf[0], nxt, lane);
+template <int OP, int BN>
+__device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][TileCfg<BN>::kFN], const uint4 (&a)[kFM][kKS],
+                                     uint4 (&bf)[2][TileCfg<BN>::kFN], uint4* cur, const uint4* nxt,
+                                     __amdgpu_buffer_rsrc_t rQ, int voff, int sQ, int qstride, int kt, int wave,
+                                     int lane) {
+  constexpr int kFN = TileCfg<BN>::kFN;
+  kstep<OP, kFN>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
+  kstep<OP, kFN>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
+  kstep<OP, kFN>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
+  kstep_half<OP, kFN, 0>(acc, a, 3, bf[1], bf[0], nxt, lane);
   // This wave's reads of slab kt (all older than the 4 reads of `nxt` just
   // issued) have landed and its part of slab kt + 1 is in LDS (the 5 load
   // groups issued after it may still be in flight); after the barrier the
   // whole slab kt + 1 is visible and nobody reads `cur`.
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * kLoadsB, kFN / 2));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(TileCfg<BN>::kWaitBarrier, kFN / 2));
   block_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  load_b_slab(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
-  kstep_half<OP, kFN / 2>(acc, a, 3, bf[1], bf[0], nxt, lane);
+  load_b_slab<BN>(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
+  kstep_half<OP, kFN, kFN / 2>(acc, a, 3, bf[1], bf[0], nxt, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -366,7 +386,7 @@ __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiStat
 // Whether final_rows_fast may take this block: inside the matrix and with
 // rows of W and O aligned to four elements.
 __device__ __forceinline__ bool final_fast_ok(const GemmArgs& a, const EpiState& st, int i0, int j0) {
-  if (i0 + 32 > a.n_real || j0 + kBN > a.m_real || (a.user_ld & 3) != 0) return false;
+  if (i0 + 32 > a.n_real || j0 + kMfmaTile > a.m_real || (a.user_ld & 3) != 0) return false;
   const uintptr_t wal = a.w_dtype == kF32 ? 15 : 7, oal = a.o_dtype == kF32 ? 15 : 7;
   return (reinterpret_cast<uintptr_t>(st.w) & wal) == 0 && (reinterpret_cast<uintptr_t>(st.o) & oal) == 0;
 }
@@ -475,12 +495,12 @@ struct EpiPtrs {
   int64_t rs_t, rs_n, rs_e16;
 };
 
-template <int KIND>
+template <int KIND, int BN>
 __device__ __forceinline__ EpiPtrs epi_ptrs(const GemmArgs& a, int b, int I, int J, int wave) {
   constexpr EpiSpec S = epi_spec(KIND);
   EpiPtrs p{};
   const int64_t ib5 = (I * kBM + wave * (kBM / kNW)) >> 5, ib6 = ib5 >> 1;
-  const int64_t jb5 = (J * kBN) >> 5, jb6 = jb5 >> 1;
+  const int64_t jb5 = (J * BN) >> 5, jb6 = jb5 >> 1;
   const int64_t bO = static_cast<int64_t>(b) * a.sO;
   if constexpr (!S.fin) {
     uint16_t* o16 = static_cast<uint16_t*>(a.out16) + bO;
@@ -615,76 +635,94 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
 
 // Block BLK + U of a group (see epi_run); recursion keeps every block index a
 // compile-time constant.
-template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int U>
+// dg = (first column block of the tile) - (first row block of the tile), in
+// 32-wide MFMA blocks; on tiles that meet the diagonal, block (x, y) of wave
+// w is a diagonal block when dg + y == 2 w + x and lies above the diagonal
+// (the mirror of an owned block, skipped) when dg + y > 2 w + x.
+template <int OP, int KIND, bool MAYDIAG, int FN, int G, int BLK, int U>
 __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
-                                         const f32x16_t (&acc)[kFM][kFN], const uint4 (&cur)[G][2], int I, int wave,
-                                         int lane, const uint4 (&id)[2], lds_f32* ep) {
-  constexpr int x = (BLK + U) / kFN, y = (BLK + U) % kFN;
-  const int rel = y - (2 * wave + x);  // diagonal tiles: > 0 is the mirror of an owned block
+                                         const f32x16_t (&acc)[kFM][FN], const uint4 (&cur)[G][2], int I, int dg,
+                                         int wave, int lane, const uint4 (&id)[2], lds_f32* ep) {
+  constexpr int x = (BLK + U) / FN, y = (BLK + U) % FN;
+  const int rel = dg + y - (2 * wave + x);
   if (!MAYDIAG || rel <= 0)
     epi_block<OP, KIND, MAYDIAG>(a, st, p, acc[x][y], cur[U], x, y, I * kBM + wave * (kBM / kNW) + 32 * x,
                                  MAYDIAG && rel == 0, lane, id, ep);
-  if constexpr (U + 1 < G) epi_unit<OP, KIND, MAYDIAG, G, BLK, U + 1>(a, st, p, acc, cur, I, wave, lane, id, ep);
+  if constexpr (U + 1 < G)
+    epi_unit<OP, KIND, MAYDIAG, FN, G, BLK, U + 1>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
 }
 
 // Blocks BLK .. BLK + G - 1 (block index 8 x + y) of the wave's register
 // epilogue with their inputs in `cur`; the inputs of the next group are
 // loaded first, so their latency overlaps this group's work.  All blocks are
 // named by template arguments: the accumulators stay in registers.
-template <int OP, int KIND, bool MAYDIAG, int G, int BLK, int END>
+template <int OP, int KIND, bool MAYDIAG, int FN, int G, int BLK, int END>
 __device__ __forceinline__ void epi_run(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
-                                        const f32x16_t (&acc)[kFM][kFN], uint4 (&cur)[G][2], int I, int wave,
+                                        const f32x16_t (&acc)[kFM][FN], uint4 (&cur)[G][2], int I, int dg, int wave,
                                         int lane, const uint4 (&id)[2], lds_f32* ep) {
   uint4 nxt[G][2];
   if constexpr (BLK + G < END) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int x = (BLK + G + u) / kFN, y = (BLK + G + u) % kFN;
-      if (!MAYDIAG || y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, nxt[u]);
+      const int x = (BLK + G + u) / FN, y = (BLK + G + u) % FN;
+      if (!MAYDIAG || dg + y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, nxt[u]);
     }
   }
-  epi_unit<OP, KIND, MAYDIAG, G, BLK, 0>(a, st, p, acc, cur, I, wave, lane, id, ep);
-  if constexpr (BLK + G < END) epi_run<OP, KIND, MAYDIAG, G, BLK + G, END>(a, st, p, acc, nxt, I, wave, lane, id, ep);
+  epi_unit<OP, KIND, MAYDIAG, FN, G, BLK, 0>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
+  if constexpr (BLK + G < END)
+    epi_run<OP, KIND, MAYDIAG, FN, G, BLK + G, END>(a, st, p, acc, nxt, I, dg, wave, lane, id, ep);
 }
 
-template <int OP, int KIND, bool MAYDIAG, int BEGIN, int END>
+template <int OP, int KIND, bool MAYDIAG, int FN, int BEGIN, int END>
 __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
-                                          const f32x16_t (&acc)[kFM][kFN], int I, int wave, int lane,
+                                          const f32x16_t (&acc)[kFM][FN], int I, int dg, int wave, int lane,
                                           const uint4 (&id)[2], lds_f32* ep) {
-  constexpr int G = 4;
+  constexpr int G = FN >= 8 ? 4 : 2;  // blocks per prefetch group (fewer registers with two blocks per CU)
   uint4 cur[G][2];
 #pragma unroll
   for (int u = 0; u < G; ++u) {
-    const int x = (BEGIN + u) / kFN, y = (BEGIN + u) % kFN;
-    if (!MAYDIAG || y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, cur[u]);
+    const int x = (BEGIN + u) / FN, y = (BEGIN + u) % FN;
+    if (!MAYDIAG || dg + y <= 2 * wave + x) load_ein<KIND>(p, x, y, lane, cur[u]);
   }
-  epi_run<OP, KIND, MAYDIAG, G, BEGIN, END>(a, st, p, acc, cur, I, wave, lane, id, ep);
+  epi_run<OP, KIND, MAYDIAG, FN, G, BEGIN, END>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
 }
 
-// The register epilogue of the wave's 64 x 256 sub-tile; the last product
-// stages O through LDS one 32-row block at a time so that the user's
-// row-major W is read and written along its rows.
-template <int OP, int KIND>
-__device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st, const f32x16_t (&acc)[kFM][kFN], int b,
-                                              int I, int J, int wave, int lane, lds_f32* ep) {
-  static_assert(kFM == 2 && kFN == 8, "the epilogue walks 2 x 8 MFMA blocks");
+// The register epilogue of the wave's 64 x BN sub-tile; the last product
+// (256-wide tiles only) stages O through LDS one 32-row block at a time so
+// that the user's row-major W is read and written along its rows.
+template <int OP, int KIND, int BN>
+__device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st,
+                                              const f32x16_t (&acc)[kFM][TileCfg<BN>::kFN], int b, int I, int J,
+                                              int wave, int lane, lds_f32* ep) {
+  constexpr int FN = TileCfg<BN>::kFN, NB = kFM * FN;
   constexpr EpiSpec S = epi_spec(KIND);
-  const EpiPtrs p = epi_ptrs<KIND>(a, b, I, J, wave);
+  const EpiPtrs p = epi_ptrs<KIND, BN>(a, b, I, J, wave);
   if constexpr (S.fin) {
+    static_assert(BN == kMfmaTile, "the last product uses 256-wide tiles");
     const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // no transposes here
-    epi_range<OP, KIND, false, 0, 8>(a, st, p, acc, I, wave, lane, id, ep);
+    epi_range<OP, KIND, false, FN, 0, FN>(a, st, p, acc, I, 0, wave, lane, id, ep);
     __syncthreads();
-    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * kBN, lane);
+    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * BN, lane);
     __syncthreads();
-    epi_range<OP, KIND, false, 8, 16>(a, st, p, acc, I, wave, lane, id, ep);
+    epi_range<OP, KIND, false, FN, FN, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
     __syncthreads();
-    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * kBN, lane);
+    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * BN, lane);
   } else {
     const uint4 id[2] = {ident_frag<OP>(0, lane), ident_frag<OP>(1, lane)};
-    if (S.sym && I == J)
-      epi_range<OP, KIND, S.sym, 0, 16>(a, st, p, acc, I, wave, lane, id, ep);
-    else
-      epi_range<OP, KIND, false, 0, 16>(a, st, p, acc, I, wave, lane, id, ep);
+    // a symmetric tile meets the diagonal when its column range overlaps its
+    // row range: tile J == I of the 256-wide tiles (dg = 0), tiles J == 2 I
+    // and 2 I + 1 of the 128-wide ones (dg = 0 and 4)
+    if constexpr (BN == kMfmaTile) {
+      if (S.sym && I == J)
+        epi_range<OP, KIND, S.sym, FN, 0, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
+      else
+        epi_range<OP, KIND, false, FN, 0, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
+    } else {
+      if (S.sym && J >= 2 * I)
+        epi_range<OP, KIND, S.sym, FN, 0, NB>(a, st, p, acc, I, 4 * (J - 2 * I), wave, lane, id, ep);
+      else
+        epi_range<OP, KIND, false, FN, 0, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
+    }
   }
 }
 
@@ -719,6 +757,17 @@ __device__ __forceinline__ int xcd_contiguous(int id, int n) {
   return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + slot;
 }
 
+// Tile t of the lower triangle in 256 x 128 tiles: row I (256 rows) holds
+// the tiles J = 0 .. 2 I + 1 (128 columns each), rows in order.
+__device__ __forceinline__ void tri_tile_half(int t, int& I, int& J) {
+  int i = static_cast<int>((sqrtf(4.0f * static_cast<float>(t) + 1.0f) - 1.0f) * 0.5f);
+  while ((i + 1) * (i + 2) <= t) ++i;
+  while (i * (i + 1) > t) --i;
+  I = i;
+  J = t - i * (i + 1);
+}
+
+template <int BN>
 __device__ __forceinline__ WorkItem work_item(const GemmArgs& a) {
   WorkItem w;
   const int hw = blockIdx.x, nfull = a.full_blocks;
@@ -743,9 +792,13 @@ __device__ __forceinline__ WorkItem work_item(const GemmArgs& a) {
   const int tile = t - w.b * a.ntiles;
   w.tile = tile;
   if (a.sym) {
-    tri_tile(tile, w.I, w.J);
+    if constexpr (BN == kMfmaTile) {
+      tri_tile(tile, w.I, w.J);
+    } else {
+      tri_tile_half(tile, w.I, w.J);
+    }
   } else {
-    const int ntm = a.Mdim / kBM, ntn = a.Ndim / kBN;
+    const int ntm = a.Mdim / kBM, ntn = a.Ndim / BN;
     constexpr int G = 8;
     const int grp = tile / (G * ntn);
     const int first = grp * G;
@@ -762,6 +815,7 @@ __device__ __forceinline__ WorkItem work_item(const GemmArgs& a) {
 // pieces, added in piece order (so the result does not depend on which piece
 // finishes last), in acc.  Partials are kept per wave as [x][y][g][lane]
 // float4 records (1 KB per store).  All threads of the block call this.
+template <int kFN>
 __device__ __forceinline__ bool tail_reduce(const GemmArgs& a, const WorkItem& w, f32x16_t (&acc)[kFM][kFN], int wave,
                                             int lane, int* flag) {
   constexpr int64_t kWaveFloats = kFM * kFN * 16 * 64;
@@ -821,14 +875,17 @@ __device__ __forceinline__ bool tail_reduce(const GemmArgs& a, const WorkItem& w
   return true;
 }
 
-template <int OP, int KIND>
-__global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
+template <int OP, int KIND, int BN>
+__global__ __launch_bounds__(kNT, BN == kMfmaTile ? 1 : 2) void gemm_nt_mfma(GemmArgs a) {
+  using C = TileCfg<BN>;
+  constexpr int kFN = C::kFN;
   // The Q ring is four separate arrays, each named statically at every access,
   // so the compiler's wait for an LDS read covers only the DMA into that stage.
-  __shared__ uint4 stg0[kStageAlloc / 16], stg1[kStageAlloc / 16], stg2[kStageAlloc / 16], stg3[kStageAlloc / 16];
+  __shared__ uint4 stg0[C::kStageAlloc / 16], stg1[C::kStageAlloc / 16], stg2[C::kStageAlloc / 16],
+      stg3[C::kStageAlloc / 16];
   __shared__ double red[2 * kNW];
   __shared__ int tail_flag;
-  const WorkItem w = work_item(a);
+  const WorkItem w = work_item<BN>(a);
   const int b = w.b, tile = w.tile, I = w.I, J = w.J;
   EpiState st;
   block_init<kNT>(a, b, tile, red, st);
@@ -844,7 +901,7 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   // byte offset of a row block = (row / 32) * (K / 64) * 4 KB
   const int pstride = (a.ldp >> 6) * 4096, qstride = (a.ldq >> 6) * 4096;
   const int sP = __builtin_amdgcn_readfirstlane((I * (kBM / 32) + wave * kFM) * pstride);
-  const int sQ = __builtin_amdgcn_readfirstlane(J * (kBN / 32) * qstride);
+  const int sQ = __builtin_amdgcn_readfirstlane(J * (BN / 32) * qstride);
 
   f32x16_t acc[kFM][kFN];
 #pragma unroll
@@ -857,47 +914,77 @@ __global__ __launch_bounds__(kNT) void gemm_nt_mfma(GemmArgs a) {
   // slabs k0 .. k1 - 1 (a multiple of 4 of them: every operand dimension is a
   // multiple of 256 and tail pieces are cut at multiples of 4 slabs)
   const int k0 = w.k0, k1 = w.k1;
-  uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS], abuf3[kFM][kKS];
   uint4 bf[2][kFN];
-  // prologue: Q slabs k0 .. k0 + 3 into the ring, P slabs k0 .. k0 + 2 into
-  // registers, issued in the order the loop itself issues them (P slab j + 3
-  // at the start of slab j, Q slab j + 4 in its middle), so the outstanding
-  // loads at the loop head look the same on entry and on every trip and the
-  // compiler's waits for the P registers stay exact.
-  load_b_slab(stg0, rQ, voff, sQ, qstride, k0, wave);
-  load_a_slab(abuf0, rP, voff, sP, pstride, k0);
-  load_b_slab(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
-  load_a_slab(abuf1, rP, voff, sP, pstride, k0 + 1);
-  load_b_slab(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
-  load_a_slab(abuf2, rP, voff, sP, pstride, k0 + 2);
-  load_b_slab(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(6 * kLoadsB, 15));  // Q slab 0 landed
-  block_barrier();
+  if constexpr (C::kPBufs == 4) {
+    uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS], abuf3[kFM][kKS];
+    // prologue: Q slabs k0 .. k0 + 3 into the ring, P slabs k0 .. k0 + 2 into
+    // registers, issued in the order the loop itself issues them (P slab j + 3
+    // at the start of slab j, Q slab j + 4 in its middle), so the outstanding
+    // loads at the loop head look the same on entry and on every trip and the
+    // compiler's waits for the P registers stay exact.
+    load_b_slab<BN>(stg0, rQ, voff, sQ, qstride, k0, wave);
+    load_a_slab(abuf0, rP, voff, sP, pstride, k0);
+    load_b_slab<BN>(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
+    load_a_slab(abuf1, rP, voff, sP, pstride, k0 + 1);
+    load_b_slab<BN>(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
+    load_a_slab(abuf2, rP, voff, sP, pstride, k0 + 2);
+    load_b_slab<BN>(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsA + 3 * C::kLoadsB, 15));  // Q slab 0 landed
+    block_barrier();
 #pragma unroll
-  for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
+    for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
 
-  // 4 slabs per trip (the 4 LDS stages and the 4 P register buffers, which
-  // are loaded three slabs ahead).
+    // 4 slabs per trip (the 4 LDS stages and the 4 P register buffers, which
+    // are loaded three slabs ahead).
 #define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
   load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 3);                                             \
-  slab<OP>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
-  for (int kt = k0; kt < k1; kt += 4) {
-    MUON_SLAB(0, abuf0, abuf3, stg0, stg1)
-    MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
-    MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
-    MUON_SLAB(3, abuf3, abuf2, stg3, stg0)
-  }
+  slab<OP, BN>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
+    for (int kt = k0; kt < k1; kt += 4) {
+      MUON_SLAB(0, abuf0, abuf3, stg0, stg1)
+      MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+      MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+      MUON_SLAB(3, abuf3, abuf2, stg3, stg0)
+    }
 #undef MUON_SLAB
+  } else {
+    uint4 abuf0[kFM][kKS], abuf1[kFM][kKS];
+    // prologue: Q slabs k0 .. k0 + 3, P slab k0 (the loop loads P slab j + 1
+    // at the start of slab j); the barrier count of the loop then holds from
+    // its first slab on
+    load_b_slab<BN>(stg0, rQ, voff, sQ, qstride, k0, wave);
+    load_b_slab<BN>(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
+    load_b_slab<BN>(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
+    load_a_slab(abuf0, rP, voff, sP, pstride, k0);
+    load_b_slab<BN>(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoadsA + 3 * C::kLoadsB, 15));  // Q slab 0 landed
+    block_barrier();
+#pragma unroll
+    for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
+
+    // 4 slabs per trip (the 4 LDS stages; the 2 P buffers alternate)
+#define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
+  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 1);                                             \
+  slab<OP, BN>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
+    for (int kt = k0; kt < k1; kt += 4) {
+      MUON_SLAB(0, abuf0, abuf1, stg0, stg1)
+      MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
+      MUON_SLAB(2, abuf0, abuf1, stg2, stg3)
+      MUON_SLAB(3, abuf1, abuf0, stg3, stg0)
+    }
+#undef MUON_SLAB
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   block_barrier();
-  if (w.piece >= 0 && !tail_reduce(a, w, acc, wave, lane, &tail_flag)) return;
+  if constexpr (BN == kMfmaTile) {
+    if (w.piece >= 0 && !tail_reduce<kFN>(a, w, acc, wave, lane, &tail_flag)) return;
+  }
 
   // The epilogue runs from registers; the last product stages O through this
   // wave's LDS stage.  It reads the launch arguments afresh, so they are not
   // held in scalar registers through the main loop.
   const GemmArgs ea = reload_args();
   lds_f32* ep = (lds_f32*)(wave == 0 ? stg0 : (wave == 1 ? stg1 : (wave == 2 ? stg2 : stg3)));
-  epilogue_mfma<OP, KIND>(ea, st, acc, b, I, J, wave, lane, ep);
+  epilogue_mfma<OP, KIND, BN>(ea, st, acc, b, I, J, wave, lane, ep);
   block_partials<kNT>(ea, b, tile, red, st);
 }
 
@@ -905,14 +992,25 @@ template <int OP>
 hipError_t launch_gemm_mfma(const GemmArgs& a, int batch, int kind, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>(a.ntiles) * batch;
   const dim3 grid(static_cast<unsigned>(a.full_blocks + (tiles - a.full_blocks) * a.kpieces)), block(kNT);
+  if (a.bn == kHalfTile) {  // symmetric products without the last-product or tail-split paths
+    if (!a.sym || a.kpieces != 1) return hipErrorInvalidValue;
+    switch (kind) {
+      case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym, kHalfTile>), grid, block, 0, s, a); break;
+      case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16, kHalfTile>), grid, block, 0, s, a); break;
+      case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q, kHalfTile>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (a.bn != kMfmaTile) return hipErrorInvalidValue;
   switch (kind) {
-    case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym>), grid, block, 0, s, a); break;
-    case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16>), grid, block, 0, s, a); break;
-    case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q>), grid, block, 0, s, a); break;
-    case kEpiGen: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGen>), grid, block, 0, s, a); break;
-    case kEpiGenE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGenE16>), grid, block, 0, s, a); break;
-    case kEpiFin: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFin>), grid, block, 0, s, a); break;
-    case kEpiFinE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFinE16>), grid, block, 0, s, a); break;
+    case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiGen: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGen, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiGenE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiGenE16, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiFin: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFin, kMfmaTile>), grid, block, 0, s, a); break;
+    case kEpiFinE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFinE16, kMfmaTile>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

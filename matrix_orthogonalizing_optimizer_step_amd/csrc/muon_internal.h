@@ -22,7 +22,8 @@ constexpr int kNormBlocks = 512;
 
 // Block tile edges of the MFMA kernels (16-bit operands) and of the fp32
 // check path.
-constexpr int kMfmaTile = 256;
+constexpr int kMfmaTile = 256;   // MFMA block tile: 256 rows by 256 (or kHalfTile) columns
+constexpr int kHalfTile = 128;   // the narrow tile of short symmetric products
 constexpr int kCheckTile = 64;
 
 // One GEMM launch over a batch: C[i][j] = sum_k P[i][k] * Q[j][k] (both
@@ -34,6 +35,7 @@ struct GemmArgs {
   int n_real;          // real n: the diagonal term and the partial sums stop here
   int sym;             // 1: C symmetric, only lower tiles are computed and mirrored
   int ntiles;          // tiles per matrix in this launch
+  int bn;              // MFMA kernels: block tile width, kMfmaTile or kHalfTile
 
   const void* P; int64_t sP; int ldp;  // row i of matrix b at P + b*sP + i*ldp
   const void* Q; int64_t sQ; int ldq;
