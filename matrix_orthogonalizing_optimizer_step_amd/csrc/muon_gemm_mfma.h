@@ -9,12 +9,14 @@ namespace muon {
 // ---------------------------------------------------------------------------
 // 16-bit MFMA kernel on packed operands.
 //
-// Block tile 256 (i) x 256 (j), 4 waves; wave w owns rows i0 + 64 w .. + 64
-// against all 256 columns (2 x 8 MFMA 32x32x16 blocks, 256 accumulator
-// registers).  k runs in slabs of 64 (4 MFMA k-steps):
+// Block tile 256 (i) x BN (j) with BN = 256 or 128 (TileCfg below), 4 waves;
+// wave w owns rows i0 + 64 w .. + 64 against all BN columns (2 x BN/32 MFMA
+// 32x32x16 blocks, 2 BN accumulator registers).  k runs in slabs of 64 (4
+// MFMA k-steps):
 //  * the P rows of a wave are private to it, so its P fragments go straight
 //    from global memory (L2) into registers with one contiguous 1 KB load per
-//    fragment, three slabs ahead (four register slab buffers);
+//    fragment, three slabs ahead in four register slab buffers (BN = 256) or
+//    one slab ahead in two (BN = 128, whose register budget is half);
 //  * the Q tile is shared by all waves: it is streamed into a 4-stage LDS
 //    ring with buffer_load ... lds (1 KB per instruction, lane l landing at
 //    byte 16 l), three slabs ahead, and each fragment is read back with one
@@ -484,7 +486,7 @@ constexpr EpiSpec epi_spec(int k) {
 }
 
 // This wave's output and input addresses, in elements, at MFMA block (0, 0)
-// of its 64 x 256 sub-tile (rows ib0 = 256 I + 64 w, columns jb0 = 256 J).
+// of its 64 x BN sub-tile (rows ib0 = 256 I + 64 w, columns jb0 = BN J).
 // In the packed layout the fragments of block (x, y), half h, sit at
 //   T (rows i, k = j):  t16 + x rs_t + 2048 (y / 2) + 512 (2 (y % 2) + h)
 //   N (rows j, k = i):  n16 + y rs_n + 512 (2 x + h)
@@ -652,7 +654,7 @@ __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const 
     epi_unit<OP, KIND, MAYDIAG, FN, G, BLK, U + 1>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
 }
 
-// Blocks BLK .. BLK + G - 1 (block index 8 x + y) of the wave's register
+// Blocks BLK .. BLK + G - 1 (block index FN x + y) of the wave's register
 // epilogue with their inputs in `cur`; the inputs of the next group are
 // loaded first, so their latency overlaps this group's work.  All blocks are
 // named by template arguments: the accumulators stay in registers.
