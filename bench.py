@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profile summary of the dominant kernel from three rocprofv3 output "
                          "directories (--stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "BENCH_JSON"),
+                    help="write the MFMA counter summary (--pmc MfmaUtil MfmaFlopsF16) of every GEMM kernel, "
+                         "with the algorithmic FLOPs from the same run's bench.py line, to --out and exit")
     ap.add_argument("--kernel", default=None, help="kernel name for --summarize-counters")
     ap.add_argument("--out", default=None, help="output file for --summarize-counters")
     ap.add_argument("--command", default="", help="the profiled command, recorded by --summarize-counters")
@@ -165,10 +168,49 @@ def summarize_counters(args):
     print("\n".join(lines))
 
 
+def summarize_mfma(args):
+    """Per GEMM kernel: MFMA FLOPs counted by the hardware (MfmaFlopsF16) and
+    the MFMA busy fraction of all SIMDs during the dispatch (MfmaUtil), against
+    the algorithmic FLOPs per launch the bench.py line of the same run reports."""
+    rows = _csv_rows(args.summarize_mfma[0], "counter_collection.csv")
+    with open(args.summarize_mfma[1]) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "gemm_nt_mfma" not in name:
+            continue
+        short = name.replace("void ", "").split("(muon::")[0].replace("muon::", "")
+        d = per.setdefault(short, {"MfmaFlopsF16": [], "MfmaUtil": []})
+        if r["Counter_Name"] in d:
+            dur = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            d[r["Counter_Name"]].append((float(r["Counter_Value"]), dur))
+    out = [f"command: {args.command}", f"source_sha256: {source_digest()}",
+           "mfma_busy_pct: MFMA-busy share of all SIMD cycles during the dispatches, weighted by dispatch time",
+           "kernel                          dispatches  hw_mfma_gflop  alg_gflop  hw/alg  mfma_busy_pct"]
+    for k in sorted(per):
+        d = per[k]
+        if not d["MfmaFlopsF16"]:
+            continue
+        hw = sum(v for v, _ in d["MfmaFlopsF16"]) / len(d["MfmaFlopsF16"])
+        tot = sum(t for _, t in d["MfmaUtil"])
+        util = sum(v * t for v, t in d["MfmaUtil"]) / tot if tot > 0 else float("nan")
+        kb = line["kernels"].get(k)
+        alg = kb["tflops"] * 1e12 * kb["avg_launch_ms"] / 1e3 if kb and kb["tflops"] else float("nan")
+        out.append(f"{k:32s} {len(d['MfmaFlopsF16']):10d} {hw / 1e9:14.1f} {alg / 1e9:10.1f} {hw / alg:7.3f} "
+                   f"{util:14.1f}")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the step shards by "
