@@ -1,0 +1,255 @@
+"""Pins of the low-bit-state oracle (oracle/grasp_oracle.py) against what
+fixes the answer independently of its formulas: brute-force searches over
+every code, hand-computed bytes, exact invariants of the quantisers, numpy's
+QR as a second route to the Q factor, and closed forms of the power
+iteration on matrices of known rank."""
+import numpy as np
+import pytest
+
+from oracle import grasp_oracle as go
+from oracle import muon_oracle as mo
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def outlier_matrix(seed, rows, cols):
+    """Gaussian entries with a few rows and columns scaled up (outliers in
+    both directions, the situation the grid is for)."""
+    r = rng(seed)
+    x = r.standard_normal((rows, cols)).astype(np.float32)
+    x[r.choice(rows, max(1, rows // 32), replace=False), :] *= 20
+    x[:, r.choice(cols, max(1, cols // 32), replace=False)] *= 20
+    return x.astype(np.float32)
+
+
+# ------------------------------------------------------------ grid quantisation
+def test_grid_scales_by_loops():
+    """Scales of a ragged 130 x 260 matrix (blocks 2 x 3, edge blocks partial)
+    recomputed with plain Python loops."""
+    x = rng(1).standard_normal((130, 260)).astype(np.float32)
+    sr, sc = go.grid_scales(x)
+    assert sr.shape == (130, 3) and sc.shape == (2, 260)
+    for i in range(130):
+        for bc in range(3):
+            assert sr[i, bc] == max(abs(float(v)) for v in x[i, bc * 128:min(260, bc * 128 + 128)])
+    for br in range(2):
+        for j in range(0, 260, 7):
+            assert sc[br, j] == max(abs(float(v)) for v in x[br * 128:min(130, br * 128 + 128), j])
+
+
+def brute_code(x, m, levels):
+    """Nearest of the 2 L + 1 reconstruction points q m / L (ties to the even
+    code), found by trying them all in exact rational arithmetic."""
+    from fractions import Fraction
+    if not (m > 0 and np.isfinite(m)):
+        return 0
+    X, Mf = Fraction(float(x)), Fraction(float(m))
+    best = None
+    for q in range(-levels, levels + 1):
+        d = abs(X - q * Mf / levels)
+        if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+            best = (d, q)
+    return best[1]
+
+
+def test_grid_codes_brute_force():
+    x = outlier_matrix(2, 40, 150)
+    q, sr, sc = go.grid_quantize(x)
+    m = go.grid_min_scale(sr, sc, *x.shape)
+    for i in range(0, 40, 3):
+        for j in range(150):
+            assert q[i, j] == brute_code(x[i, j], m[i, j], 7), (i, j)
+
+
+def test_grid_ties_round_to_even():
+    """x = m/2 gives 7/2 -> 4; x = 5m/14 gives 5/2 -> 2; x = -m/2 -> -4."""
+    m = np.float32(1.75)
+    x = np.zeros((1, 4), np.float32)
+    x[0] = [m, m / 2, np.float32(5 * 1.75 / 14), -m / 2]
+    q, sr, sc = go.grid_quantize(x)
+    # one row: the row scale is m; each column scale is |x|, so use a second row
+    # that lifts every column scale to m to make min(row, column) = m
+    x2 = np.vstack([x, np.full((1, 4), m, np.float32)])
+    q, sr, sc = go.grid_quantize(x2)
+    assert list(q[0]) == [7, 4, 2, -4]
+
+
+def test_grid_error_bound_and_exact_extremes():
+    """|x - x^| <= m / 14 for every entry, m = min(row, column scale) <= both
+    scales; the largest magnitude of every block row and block column is
+    reproduced exactly (code +-7)."""
+    x = outlier_matrix(3, 300, 200)
+    q, sr, sc = go.grid_quantize(x)
+    xh = go.grid_dequantize(q, sr, sc)
+    m = go.grid_min_scale(sr, sc, *x.shape).astype(np.float64)
+    assert np.all(np.abs(x - xh) <= m / 14 * (1 + 1e-12))
+    assert np.all(np.abs(q) <= 7)
+    for bi in range(3):
+        for bj in range(2):
+            blk = x[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            bh = xh[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            r = np.abs(blk).argmax(axis=1)
+            c = np.abs(blk).argmax(axis=0)
+            assert np.array_equal(bh[np.arange(blk.shape[0]), r], blk[np.arange(blk.shape[0]), r])
+            assert np.array_equal(bh[c, np.arange(blk.shape[1])], blk[c, np.arange(blk.shape[1])])
+
+
+def test_grid_zero_block_and_scale_covariance():
+    x = outlier_matrix(4, 256, 256)
+    x[:128, 128:] = 0
+    q, sr, sc = go.grid_quantize(x)
+    assert np.all(q[:128, 128:] == 0) and np.all(sr[:128, 1] == 0) and np.all(sc[0, 128:] == 0)
+    assert np.all(go.grid_dequantize(q, sr, sc)[:128, 128:] == 0)
+    q2, sr2, sc2 = go.grid_quantize((x * np.float32(2.0 ** -20)).astype(np.float32))
+    assert np.array_equal(q, q2)
+    assert np.array_equal(sr2, sr * np.float32(2.0 ** -20)) and np.array_equal(sc2, sc * np.float32(2.0 ** -20))
+
+
+def test_grid_beats_row_groups_on_two_sided_outliers():
+    """[GRASP] key design 2: with outliers along rows and columns, the grid's
+    per-entry bound min(row, column scale) beats per-row groups of 128 (whose
+    bound is the row scale alone); the notes report about half the loss."""
+    x = outlier_matrix(5, 512, 512)
+    q, sr, sc = go.grid_quantize(x)
+    e_grid = np.linalg.norm(go.grid_dequantize(q, sr, sc) - x)
+    # plain per-row groups of 128 with the same 4-bit code
+    s = np.repeat(sr, 128, axis=1)[:, :512].astype(np.float64)
+    e_group = np.linalg.norm(np.rint(7 * x / s) * s / 7 - x)
+    assert e_grid < 0.75 * e_group
+
+
+def test_nibble_packing():
+    q = np.array([[-1, 3, 7, -7, 0]], np.int8)
+    b = go.pack_nibbles(q)
+    assert list(b[0]) == [0x3F, 0x97, 0x00]
+    assert np.array_equal(go.unpack_nibbles(b, 5), q)
+    q = rng(6).integers(-7, 8, size=(9, 33)).astype(np.int8)
+    assert np.array_equal(go.unpack_nibbles(go.pack_nibbles(q), 33), q)
+
+
+# ------------------------------------------------------------ 8-bit groups
+def test_group8_codes_brute_force_and_bound():
+    x = outlier_matrix(7, 20, 300)  # 3 groups per row, the last 44 wide
+    q, s = go.group8_quantize(x)
+    assert s.shape == (20, 3)
+    for i in range(0, 20, 4):
+        for j in range(0, 300, 5):
+            assert q[i, j] == brute_code(x[i, j], s[i, j // 128], 127)
+        for g in range(3):
+            assert s[i, g] == np.abs(x[i, g * 128:(g + 1) * 128]).max()
+    xh = go.group8_dequantize(q, s)
+    bound = np.repeat(s, 128, axis=1)[:, :300] / 254.0
+    assert np.all(np.abs(xh - x) <= bound * (1 + 1e-12))
+
+
+# ------------------------------------------------------------ QR and the power iteration
+def test_orthonormalize_matches_numpy_qr():
+    """Second route: numpy's Householder QR with the signs fixed so that the
+    triangular factor has a positive diagonal."""
+    P = rng(8).standard_normal((200, 24)) @ np.diag(np.geomspace(1, 1e-3, 24))
+    Q = go.orthonormalize_columns(P)
+    q, r = np.linalg.qr(P)
+    q = q * np.sign(np.diag(r))[None, :]
+    np.testing.assert_allclose(Q, q, atol=1e-10)
+    np.testing.assert_allclose(Q.T @ Q, np.eye(24), atol=1e-12)
+
+
+def test_orthonormalize_zero_and_dependent_columns():
+    P = rng(9).standard_normal((50, 6))
+    P[:, 2] = 0
+    P[:, 4] = 2 * P[:, 0] - P[:, 1]
+    Q = go.orthonormalize_columns(P)
+    assert np.all(Q[:, 2] == 0) and np.all(Q[:, 4] == 0)
+    keep = [0, 1, 3, 5]
+    np.testing.assert_allclose(Q[:, keep].T @ Q[:, keep], np.eye(4), atol=1e-12)
+
+
+def test_power_iteration_exact_on_rank_k():
+    """M of rank k with R_prev spanning its row space: P P^T M = M, so the
+    residual vanishes."""
+    r = rng(10)
+    U = r.standard_normal((96, 5))
+    V = r.standard_normal((140, 5))
+    M = U @ V.T
+    R_prev = V @ r.standard_normal((5, 5))
+    P, R = go.power_iteration(M, R_prev)
+    assert np.linalg.norm(M - P @ R.T) < 1e-10 * np.linalg.norm(M)
+
+
+def test_power_iteration_column_scaling_invariance():
+    """Q_t = unit columns of R_{t-1}; any positive column scaling of R_{t-1}
+    leaves P (QR Q factor with positive diagonal) and R unchanged."""
+    r = rng(11)
+    M = r.standard_normal((80, 120))
+    R_prev = r.standard_normal((120, 8))
+    P1, R1 = go.power_iteration(M, R_prev)
+    P2, R2 = go.power_iteration(M, R_prev * np.geomspace(1e-3, 1e3, 8)[None, :])
+    np.testing.assert_allclose(P1, P2, atol=1e-10)
+    np.testing.assert_allclose(R1, R2, atol=1e-9)
+
+
+def test_warm_start_tracks_the_top_subspace():
+    """[GRASP] key design 1: consecutive momenta are close, so one warm-started
+    step from R_{t-1} recovers the top-k part (the notes measure a relative
+    error of about 0.01).  Checked against the SVD's best rank-k part on a
+    momentum with a decaying spectrum and a small new gradient."""
+    r = rng(12)
+    m, n, k = 128, 256, 8
+    U, _ = np.linalg.qr(r.standard_normal((m, m)))
+    V, _ = np.linalg.qr(r.standard_normal((n, m)))
+    M_prev = (U * np.arange(1, m + 1) ** -1.0) @ V.T
+    _, R_prev = go.power_iteration(M_prev, V[:, :k] + 0.01 * r.standard_normal((n, k)))
+    M = 0.95 * M_prev + 0.002 * r.standard_normal((m, n))
+    P, R = go.power_iteration(M, R_prev)
+    u, s, vt = np.linalg.svd(M)
+    top = (u[:, :k] * s[:k]) @ vt[:k]
+    warm = np.linalg.norm(P @ R.T - top) / np.linalg.norm(top)
+    assert warm < 0.03  # 0.020 here: the same order as the notes' figure
+    # a cold start (random R) is far worse after one step
+    P0, R0 = go.power_iteration(M, r.standard_normal((n, k)))
+    assert np.linalg.norm(P0 @ R0.T - top) / np.linalg.norm(top) > 10 * warm
+
+
+# ------------------------------------------------------------ the step
+def test_step_without_subspace_is_quantised_momentum():
+    """k = 0: M_t = mu deq(state) + G rounded to fp32; the new state is the
+    grid code of M_t; O is the plain Newton-Schulz of M_t."""
+    r = rng(13)
+    G = r.standard_normal((64, 192)).astype(np.float32)
+    st = go.new_state(64, 192, 0)
+    W = np.zeros((64, 192))
+    _, st1, O, M1, _ = go.grasp_step(W, st, G, 0.9, 0.01)
+    assert np.array_equal(M1, G.astype(np.float64))  # zero state: M_1 = G exactly
+    q, sr, sc = go.grid_quantize(G)
+    assert np.array_equal(st1["res_codes"], q) and np.array_equal(st1["res_sr"], sr)
+    np.testing.assert_allclose(O, mo.newton_schulz(M1), rtol=0, atol=1e-13)
+    G2 = np.zeros_like(G)
+    _, _, _, M2, _ = go.grasp_step(W, st1, G2, 0.5, 0.01)
+    assert np.array_equal(M2, (0.5 * go.grid_dequantize(q, sr, sc)).astype(np.float32).astype(np.float64))
+
+
+def test_step_with_subspace_reconstruction():
+    """k > 0: the stored state rebuilds M_t up to the codec bounds: the 4-bit
+    residual error is at most m / 14 per entry, and the rest is the 8-bit
+    error of P R^T."""
+    r = rng(14)
+    m, n, k = 130, 260, 8
+    G = (r.standard_normal((m, k)) @ r.standard_normal((k, n)) + 0.1 * r.standard_normal((m, n))).astype(np.float32)
+    st = go.new_state(m, n, k, R_init=r.standard_normal((n, k)))
+    _, st1, O, M1, det = go.grasp_step(np.zeros((m, n)), st, G, 0.95, 0.01)
+    assert np.array_equal(M1, G.astype(np.float64))
+    res_h = go.grid_dequantize(st1["res_codes"], st1["res_sr"], st1["res_sc"])
+    mm = go.grid_min_scale(st1["res_sr"], st1["res_sc"], m, n)
+    assert np.all(np.abs(res_h - det["M_res"]) <= mm / 14 * (1 + 1e-12))
+    Ph = go.group8_dequantize(st1["P_codes"], st1["P_scales"])
+    Rh = go.group8_dequantize(st1["R_codes"], st1["R_scales"])
+    rec = res_h + Ph @ Rh.T
+    err = np.linalg.norm(rec - M1) / np.linalg.norm(M1)
+    # the residual is much smaller than M_t, so its 4-bit error stays small
+    assert np.linalg.norm(det["M_res"]) < 0.5 * np.linalg.norm(M1)
+    assert err < 0.05
+    # and the subspace helps: quantising M_t directly is worse
+    q, sr, sc = go.grid_quantize(G)
+    assert err < np.linalg.norm(go.grid_dequantize(q, sr, sc) - M1) / np.linalg.norm(M1)
