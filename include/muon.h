@@ -16,6 +16,10 @@
  *   [MuonBlog] "Muon Optimizer" blog post, §1: Muon is for 2-D matrices;
  *           §5 (Muon is no drop-in AdamW replacement) item 4: weight decay and
  *           a per-parameter update scale.
+ *   [GRASP] also: key design 1 (top subspace P R^T kept in 8 bit, found by a
+ *           warm-started power-iteration step), key design 2 (grid
+ *           quantisation), the full example (the per-step flow) and the
+ *           training strategy (INT4 / INT8, group and grid size 128).
  *
  * Conventions shared by every entry point:
  *
@@ -49,9 +53,10 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 #define MUON_MAX_T 16
 #define MUON_MAX_DIM (1 << 20)
+#define MUON_GRASP_MAX_K 1024
 
 /* Element types.  F32 = IEEE binary32, BF16 = bfloat16, F16 = IEEE binary16. */
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1, MUON_F16 = 2 } muon_dtype;
@@ -179,6 +184,98 @@ muon_status muon_step(int batch, int rows, int cols,
                       muon_ns_variant variant, const muon_ns_config *cfg,
                       void *const *O_out, muon_dtype o_dtype,
                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Low-bit momentum state of 4-bit-Muon-GRASP ([GRASP] overall framework, key
+ * designs 1 and 2, full example, training strategy).  The momentum of a
+ * rows x cols weight is kept as M = M_res + P R^T with
+ *
+ *   M_res  4-bit grid code: the matrix is cut into 128 x 128 blocks (edge
+ *          blocks cover the real rows and columns only); each block has a
+ *          scale per row and per column, the largest magnitude of that row or
+ *          column inside the block (NaN propagating).  An entry x is stored as
+ *          q = rint(7 x / m), m = min(row scale, column scale), evaluated in
+ *          fp64 from fp32 values, ties to even, q in -7..7 (q = 0 when m is 0,
+ *          NaN or infinite), and restored as q m / 7.
+ *   P, R   rows x k and cols x k factors of the top-k part in 8-bit group
+ *          code: each row is cut into groups of 128 consecutive entries (the
+ *          last one shorter) with scale = largest magnitude of the group; q =
+ *          rint(127 x / scale) in fp64, restored as q scale / 127.
+ *
+ * Every field is a DEVICE array of `batch` device pointers, one per matrix:
+ *   res_codes       uint8 [rows][(cols + 1) / 2]: two codes per byte along a
+ *                   row, the even column in the low nibble (two's complement).
+ *   res_row_scales  float [rows][ceil(cols / 128)]
+ *   res_col_scales  float [ceil(rows / 128)][cols]
+ *   P_codes         int8 [rows][k]     P_scales  float [rows][ceil(k / 128)]
+ *   R_codes         int8 [cols][k]     R_scales  float [cols][ceil(k / 128)]
+ * (the P and R fields are ignored when k = 0).  The caller owns the state.
+ * Before the first step, the residual and P are zero (codes and scales) and R
+ * holds the code of any cols x k start matrix, e.g. a Gaussian one (with P
+ * zero, M_{-1} = 0 whatever R is, and R starts the power iteration).
+ */
+typedef struct muon_grasp_state {
+  void *const *res_codes;
+  void *const *res_row_scales;
+  void *const *res_col_scales;
+  void *const *P_codes;
+  void *const *P_scales;
+  void *const *R_codes;
+  void *const *R_scales;
+} muon_grasp_state;
+
+/* Workspace bytes of muon_grasp_step (0 for invalid arguments). */
+size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_variant variant,
+                                 const muon_ns_config *cfg);
+
+/*
+ * One Muon step whose momentum lives in the low-bit state ([GRASP] full
+ * example), for a batch of same-shape weights:
+ *   M_{t-1} = deq(M_res) + deq(P) deq(R)^T
+ *   M_t     = mu M_{t-1} + G      (fp64, rounded once to fp32)
+ *   k > 0:  Q = R_{t-1} with unit columns (zero columns stay zero);
+ *           P = QR Q factor of M_t Q (positive diagonal; a column dependent
+ *           on the earlier ones, or zero, becomes zero); R = M_t^T P;
+ *           P and R are stored in 8-bit code, M_res = M_t - P R^T in 4-bit
+ *           grid code (P and R at full precision in the residual).
+ *   k = 0:  no subspace: M_t itself is stored in 4-bit grid code.
+ *   O = NS(M_t) (variant, cfg as for muon_step), W <- W - lr (update_scale O
+ *   + weight_decay W).
+ *
+ *   k        subspace rank, 0 <= k <= min(rows, cols), k <= MUON_GRASP_MAX_K
+ *            ([GRASP] uses rank / 16).
+ *   state    see muon_grasp_state; updated in place.
+ *   G        gradients (F32, BF16 or F16).  W: F32 or BF16, updated in place.
+ *   O_out    NULL or outputs for O (F32 or BF16).
+ *   M_out    NULL or F32 outputs that receive M_t (for checking).
+ * The products with fp32 operands (M_t Q, M_t^T P, P U^{-1}, P R^T) run on
+ * the bf16 MFMA with each operand split into two bf16 parts (about 16
+ * significant bits per product); the Gram matrix and its Cholesky factor are
+ * fp64.  Errors as for muon_step.
+ */
+muon_status muon_grasp_step(int batch, int rows, int cols, int k,
+                            void *const *W, muon_dtype w_dtype,
+                            const muon_grasp_state *state,
+                            const void *const *G, muon_dtype g_dtype,
+                            float mu, float lr, float weight_decay, float update_scale,
+                            muon_ns_variant variant, const muon_ns_config *cfg,
+                            void *const *O_out, muon_dtype o_dtype, void *const *M_out,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The two codes on their own ([GRASP] key design 2, training strategy), with
+ * the layouts above; device arrays of device pointers, fp32 values.  Grid
+ * code: X and Y are rows x cols; group code: X and Y are rows x k.
+ */
+muon_status muon_grid_quantize(int batch, int rows, int cols, const void *const *X, void *const *codes,
+                               void *const *row_scales, void *const *col_scales, void *stream);
+muon_status muon_grid_dequantize(int batch, int rows, int cols, const void *const *codes,
+                                 const void *const *row_scales, const void *const *col_scales,
+                                 void *const *Y, void *stream);
+muon_status muon_group8_quantize(int batch, int rows, int k, const void *const *X, void *const *codes,
+                                 void *const *scales, void *stream);
+muon_status muon_group8_dequantize(int batch, int rows, int k, const void *const *codes,
+                                   const void *const *scales, void *const *Y, void *stream);
 
 /*
  * Per-iteration coefficient schedule in the manner of the Polar Express

@@ -44,6 +44,11 @@ class _Config(ctypes.Structure):
                 ("restart_mask", ctypes.c_uint32), ("compute", ctypes.c_int), ("shift", ctypes.c_int32)]
 
 
+class _GraspState(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes", "R_scales")]
+
+
 _lib = None
 
 
@@ -83,6 +88,18 @@ def load_library():
     lib.muon_quintic_schedule.argtypes = [i32, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_double)]
     lib.muon_quintic_schedule.restype = i32
+    lib.muon_grasp_workspace_size.argtypes = [i32, i32, i32, i32, i32, cfgp]
+    lib.muon_grasp_workspace_size.restype = sz
+    lib.muon_grasp_step.argtypes = [i32, i32, i32, i32, vp, i32, ctypes.POINTER(_GraspState), vp, i32,
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, i32, cfgp,
+                                    vp, i32, vp, vp, sz, vp]
+    lib.muon_grasp_step.restype = i32
+    for name in ("muon_grid_quantize", "muon_grid_dequantize"):
+        getattr(lib, name).argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        getattr(lib, name).restype = i32
+    for name in ("muon_group8_quantize", "muon_group8_dequantize"):
+        getattr(lib, name).argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        getattr(lib, name).restype = i32
     _lib = lib
     return lib
 
@@ -290,3 +307,137 @@ def trace_collect():
         if n > cap:
             raise MuonError(1, f"trace held {n} records, more than {cap}")
         return recs
+
+
+# --------------------------------------------------------------------------
+# low-bit momentum state (muon_grasp_state and muon_grasp_step in include/muon.h)
+# --------------------------------------------------------------------------
+GRID = 128  # grid block edge and 8-bit group length
+
+
+def _nb(x: int) -> int:
+    return (x + GRID - 1) // GRID
+
+
+def grid_quantize(X, stream=None):
+    """4-bit grid code of fp32 matrices: returns (codes, row_scales, col_scales) lists."""
+    lib = load_library()
+    rows, cols, dt = _batch(X, "X")
+    if dt != F32:
+        raise ValueError("X must be float32")
+    dev = X[0].device
+    codes = [torch.empty(rows, (cols + 1) // 2, dtype=torch.uint8, device=dev) for _ in X]
+    sr = [torch.empty(rows, _nb(cols), dtype=torch.float32, device=dev) for _ in X]
+    sc = [torch.empty(_nb(rows), cols, dtype=torch.float32, device=dev) for _ in X]
+    _check(lib.muon_grid_quantize(len(X), rows, cols, pointer_array(X).data_ptr(), pointer_array(codes).data_ptr(),
+                                  pointer_array(sr).data_ptr(), pointer_array(sc).data_ptr(), _stream(stream)))
+    return codes, sr, sc
+
+
+def grid_dequantize(codes, row_scales, col_scales, cols: int, stream=None):
+    """fp32 values q m / 7 of 4-bit grid codes (rows x cols each)."""
+    lib = load_library()
+    rows = codes[0].shape[0]
+    dev = codes[0].device
+    Y = [torch.empty(rows, cols, dtype=torch.float32, device=dev) for _ in codes]
+    _check(lib.muon_grid_dequantize(len(codes), rows, cols, pointer_array(codes).data_ptr(),
+                                    pointer_array(row_scales).data_ptr(), pointer_array(col_scales).data_ptr(),
+                                    pointer_array(Y).data_ptr(), _stream(stream)))
+    return Y
+
+
+def group8_quantize(X, stream=None):
+    """8-bit group code (groups of 128 along rows) of fp32 matrices: (codes, scales)."""
+    lib = load_library()
+    rows, k, dt = _batch(X, "X")
+    if dt != F32:
+        raise ValueError("X must be float32")
+    dev = X[0].device
+    codes = [torch.empty(rows, k, dtype=torch.int8, device=dev) for _ in X]
+    scales = [torch.empty(rows, _nb(k), dtype=torch.float32, device=dev) for _ in X]
+    _check(lib.muon_group8_quantize(len(X), rows, k, pointer_array(X).data_ptr(), pointer_array(codes).data_ptr(),
+                                    pointer_array(scales).data_ptr(), _stream(stream)))
+    return codes, scales
+
+
+def group8_dequantize(codes, scales, stream=None):
+    lib = load_library()
+    rows, k = codes[0].shape
+    Y = [torch.empty(rows, k, dtype=torch.float32, device=codes[0].device) for _ in codes]
+    _check(lib.muon_group8_dequantize(len(codes), rows, k, pointer_array(codes).data_ptr(),
+                                      pointer_array(scales).data_ptr(), pointer_array(Y).data_ptr(), _stream(stream)))
+    return Y
+
+
+class GraspState:
+    """Device buffers of the low-bit momentum state of ``batch`` rows x cols
+    matrices with subspace rank k (layout of muon_grasp_state).  The residual
+    and P start at zero; R starts as the 8-bit code of ``R_init`` (a list of
+    fp32 cols x k tensors), required when k > 0."""
+
+    def __init__(self, batch: int, rows: int, cols: int, k: int, device, R_init=None):
+        z = lambda *shape, dt: torch.zeros(*shape, dtype=dt, device=device)  # noqa: E731
+        self.rows, self.cols, self.k, self.batch = rows, cols, k, batch
+        self.res_codes = [z(rows, (cols + 1) // 2, dt=torch.uint8) for _ in range(batch)]
+        self.res_row_scales = [z(rows, _nb(cols), dt=torch.float32) for _ in range(batch)]
+        self.res_col_scales = [z(_nb(rows), cols, dt=torch.float32) for _ in range(batch)]
+        self.P_codes = self.P_scales = self.R_codes = self.R_scales = None
+        if k > 0:
+            if R_init is None or len(R_init) != batch:
+                raise ValueError("k > 0 needs one cols x k start matrix R_init per matrix")
+            self.P_codes = [z(rows, k, dt=torch.int8) for _ in range(batch)]
+            self.P_scales = [z(rows, _nb(k), dt=torch.float32) for _ in range(batch)]
+            self.R_codes, self.R_scales = group8_quantize([r.to(device, torch.float32).contiguous() for r in R_init])
+
+    def c_struct(self):
+        st = _GraspState()
+        keep = []
+        for name in ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes", "R_scales"):
+            lst = getattr(self, name)
+            if lst is not None:
+                arr = pointer_array(lst)
+                keep.append(arr)
+                setattr(st, name, arr.data_ptr())
+        return st, keep
+
+
+def grasp_workspace_size(batch: int, rows: int, cols: int, k: int, variant="standard",
+                         cfg: Optional[NSConfig] = None) -> int:
+    lib = load_library()
+    v = _variant(variant)
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    n = lib.muon_grasp_workspace_size(batch, rows, cols, k, v, ctypes.byref(c))
+    if n == 0:
+        raise MuonError(1, "invalid arguments for the workspace size")
+    return int(n)
+
+
+def grasp_step(W, state: GraspState, G, mu: float, lr: float, weight_decay: float = 0.0, variant="standard",
+               cfg: Optional[NSConfig] = None, O_out=None, M_out=None, workspace=None, stream=None,
+               update_scale: float = 1.0):
+    """One Muon step whose momentum lives in ``state`` (updated in place with W)."""
+    lib = load_library()
+    v = _variant(variant)
+    rows, cols, wdt = _batch(W, "W")
+    r3, c3, gdt = _batch(G, "G")
+    if (r3, c3) != (rows, cols) or (state.rows, state.cols) != (rows, cols) or not (len(W) == len(G) == state.batch):
+        raise ValueError("W, G and the state must match")
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    need = lib.muon_grasp_workspace_size(len(W), rows, cols, state.k, v, ctypes.byref(c))
+    if need == 0:
+        raise MuonError(1, "invalid arguments for the workspace size")
+    if workspace is None:
+        workspace = globals()["workspace"](need, W[0].device)
+    po, odt = None, F32
+    if O_out is not None:
+        _, _, odt = _batch(O_out, "O_out")
+        po = pointer_array(O_out)
+    pm = pointer_array(M_out) if M_out is not None else None
+    st, _keep_st = state.c_struct()
+    st_ = lib.muon_grasp_step(len(W), rows, cols, state.k, pointer_array(W).data_ptr(), wdt, ctypes.byref(st),
+                              pointer_array(G).data_ptr(), gdt, float(mu), float(lr), float(weight_decay),
+                              float(update_scale), v, ctypes.byref(c),
+                              po.data_ptr() if po is not None else None, odt,
+                              pm.data_ptr() if pm is not None else None,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st_)

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "../../include/muon.h"
+#include "muon_grasp.h"
 #include "muon_internal.h"
 
 using namespace muon;
@@ -617,6 +618,344 @@ muon_status orthogonalize(muon_ns_variant v, int batch, int rows, int cols, cons
   return v == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// low-bit momentum state ([GRASP] overall framework and full example)
+// ---------------------------------------------------------------------------
+constexpr int kGraspMaxPieces = 8;  // k pieces of the two long power-iteration products
+
+int nblk(int x, int b) { return (x + b - 1) / b; }
+
+// Workspace after the Newton-Schulz part: M_t and its pointer table, then
+// (k > 0) the power-iteration buffers.
+struct GraspLayout {
+  size_t ptrs, mt, q, colpart, ppart, ptil, spart, S, V64, uinv, P, rpart, R, total;
+  int nch_n, nch_m;
+};
+
+bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout* g) {
+  memset(g, 0, sizeof(*g));
+  const size_t B = static_cast<size_t>(batch), r = rows, c = cols, kk = k;
+  size_t off = round_up(base, 256);
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  g->ptrs = take(B * sizeof(void*));
+  g->mt = take(B * r * c * 4);
+  if (k > 0) {
+    g->nch_n = nblk(cols, 256);
+    g->nch_m = nblk(rows, 256);
+    g->q = take(B * c * kk * 4);
+    g->colpart = take(B * g->nch_n * kk * 8);
+    g->ppart = take(B * kGraspMaxPieces * r * kk * 4);
+    g->ptil = take(B * r * kk * 4);
+    g->spart = take(B * g->nch_m * kk * kk * 8);
+    g->S = take(B * kk * kk * 8);
+    g->V64 = take(B * kk * kk * 8);
+    g->uinv = take(B * kk * kk * 4);
+    g->P = take(B * r * kk * 4);
+    g->rpart = take(B * kGraspMaxPieces * c * kk * 4);
+    g->R = take(B * c * kk * 4);
+  }
+  g->total = off;
+  return true;
+}
+
+// k pieces for a product with `tiles` output tiles and K of length `K`: enough
+// blocks for about two rounds on the device, each piece at least 256 long.
+void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
+  const int cu = device_cus();
+  int pcs = tiles >= 2 * cu ? 1 : static_cast<int>((2 * cu + tiles - 1) / tiles);
+  pcs = pcs < kGraspMaxPieces ? pcs : kGraspMaxPieces;
+  const int maxp = K / 256 > 1 ? K / 256 : 1;
+  pcs = pcs < maxp ? pcs : maxp;
+  int chunk = static_cast<int>(round_up(static_cast<size_t>((K + pcs - 1) / pcs), 32));
+  *kchunk = chunk;
+  *pieces = (K + chunk - 1) / chunk;
+}
+
+bool grasp_state_ok(const muon_grasp_state* st, int k) {
+  if (st == nullptr || st->res_codes == nullptr || st->res_row_scales == nullptr || st->res_col_scales == nullptr)
+    return false;
+  if (k > 0 && (st->P_codes == nullptr || st->P_scales == nullptr || st->R_codes == nullptr || st->R_scales == nullptr))
+    return false;
+  return true;
+}
+
+// Momentum, power iteration and the new state; M_t ends in the workspace
+// (pointer table at lay.ptrs) for the Newton-Schulz part.
+muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_grasp_state* st, const void* const* G,
+                            int g_dtype, double mu, void* const* M_out, char* ws, const GraspLayout& lay,
+                            hipStream_t s) {
+  const double elems = static_cast<double>(rows) * cols * batch;
+  const double gsz = g_dtype == kF32 ? 4.0 : 2.0;
+  float* mt = reinterpret_cast<float*>(ws + lay.mt);
+  const int64_t s_mt = static_cast<int64_t>(rows) * cols;
+  MUON_LAUNCH(launch_ptr_table(mt, s_mt, batch, reinterpret_cast<float**>(ws + lay.ptrs), s));
+  if (k == 0) {
+    GridArgs a{};
+    a.rows = rows;
+    a.cols = cols;
+    a.codes = st->res_codes;
+    a.sr = st->res_row_scales;
+    a.sc = st->res_col_scales;
+    a.G = G;
+    a.g_dtype = g_dtype;
+    a.mu = mu;
+    a.Y = M_out;
+    a.mt = mt;
+    a.s_mt = s_mt;
+    const double bytes = elems * (1.0 + gsz + 4.0 + (M_out != nullptr ? 4.0 : 0.0));
+    MUON_LAUNCH(traced(s, "grid_kernel<1>", "gridq_momentum", 0.0, bytes,
+                       [&] { return launch_grid(a, 1, batch, s); }));
+    return MUON_OK;
+  }
+  const double kd = k;
+  // 1. M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G
+  {
+    ReconArgs a{};
+    a.rows = rows;
+    a.cols = cols;
+    a.k = k;
+    a.res_codes = st->res_codes;
+    a.res_sr = st->res_row_scales;
+    a.res_sc = st->res_col_scales;
+    a.P_codes = st->P_codes;
+    a.P_scales = st->P_scales;
+    a.R_codes = st->R_codes;
+    a.R_scales = st->R_scales;
+    a.G = G;
+    a.g_dtype = g_dtype;
+    a.mu = mu;
+    a.mt = mt;
+    a.s_mt = s_mt;
+    a.Y = M_out;
+    const double bytes = elems * (0.5 + gsz + 4.0 + (M_out != nullptr ? 4.0 : 0.0)) + (rows + cols) * kd * batch;
+    MUON_LAUNCH(traced(s, "recon_kernel", "grasp_momentum", 2.0 * elems * kd, bytes,
+                       [&] { return launch_recon(a, batch, s); }));
+  }
+  // 2. Q = unit columns of deq(R_{t-1})
+  float* Q = reinterpret_cast<float*>(ws + lay.q);
+  {
+    UnitArgs a{};
+    a.n = cols;
+    a.k = k;
+    a.nchunk = lay.nch_n;
+    a.codes = st->R_codes;
+    a.scales = st->R_scales;
+    a.part = reinterpret_cast<double*>(ws + lay.colpart);
+    a.Q = Q;
+    a.sQ = static_cast<int64_t>(cols) * k;
+    MUON_LAUNCH(traced(s, "unit_columns_kernel", "grasp_Q", 0.0, cols * kd * batch * 6.0,
+                       [&] { return launch_unit_columns(a, batch, s); }));
+  }
+  // 3. P~ = M_t Q (split along k when the tiles alone do not fill the device)
+  float* ptil = reinterpret_cast<float*>(ws + lay.ptil);
+  {
+    TallArgs a{};
+    a.M = rows;
+    a.N = k;
+    a.K = cols;
+    a.A = mt;
+    a.sA = s_mt;
+    a.a_row = cols;
+    a.a_k = 1;
+    a.B = Q;
+    a.sB = static_cast<int64_t>(cols) * k;
+    a.b_row = 1;
+    a.b_k = k;
+    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &a.pieces, &a.kchunk);
+    a.sC = static_cast<int64_t>(rows) * k;
+    a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.ppart) : ptil;
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 0>", "grasp_MQ", 2.0 * elems * kd,
+                       elems * 4.0 + (cols + rows * a.pieces) * kd * 4.0 * batch,
+                       [&] { return launch_tall(a, true, false, batch, s); }));
+    if (a.pieces > 1)
+      MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MQ_sum", 0.0, rows * kd * batch * 4.0 * (a.pieces + 1),
+                         [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, ptil, batch, s); }));
+  }
+  // 4. CholeskyQR: S = P~^T P~ = U^T U, U^{-1}
+  float* uinv = reinterpret_cast<float*>(ws + lay.uinv);
+  {
+    CholArgs a{};
+    a.m = rows;
+    a.k = k;
+    a.nchunk = lay.nch_m;
+    a.P = ptil;
+    a.sP = static_cast<int64_t>(rows) * k;
+    a.spart = reinterpret_cast<double*>(ws + lay.spart);
+    a.S = reinterpret_cast<double*>(ws + lay.S);
+    a.Vinv64 = reinterpret_cast<double*>(ws + lay.V64);
+    a.Uinv = uinv;
+    MUON_LAUNCH(traced(s, "gram64+chol_inv_kernel", "grasp_cholqr", rows * kd * kd * batch, rows * kd * 4.0 * batch,
+                       [&] { return launch_cholqr(a, batch, s); }));
+  }
+  // 5. P = P~ U^{-1}, then its 8-bit code
+  float* P = reinterpret_cast<float*>(ws + lay.P);
+  {
+    TallArgs a{};
+    a.M = rows;
+    a.N = k;
+    a.K = k;
+    a.A = ptil;
+    a.sA = static_cast<int64_t>(rows) * k;
+    a.a_row = k;
+    a.a_k = 1;
+    a.B = uinv;
+    a.sB = static_cast<int64_t>(k) * k;
+    a.b_row = 1;
+    a.b_k = k;
+    a.pieces = 1;
+    a.kchunk = k;
+    a.C = P;
+    a.sC = static_cast<int64_t>(rows) * k;
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 0>", "grasp_PUinv", 2.0 * rows * kd * kd * batch,
+                       rows * kd * 8.0 * batch, [&] { return launch_tall(a, true, false, batch, s); }));
+    Group8Args q{};
+    q.rows = rows;
+    q.k = k;
+    q.Xs = P;
+    q.sX = a.sC;
+    q.codes = st->P_codes;
+    q.scales = st->P_scales;
+    MUON_LAUNCH(traced(s, "group8_kernel<0>", "grasp_P_code", 0.0, rows * kd * 5.0 * batch,
+                       [&] { return launch_group8(q, false, batch, s); }));
+  }
+  // 6. R = M_t^T P, then its 8-bit code
+  float* R = reinterpret_cast<float*>(ws + lay.R);
+  {
+    TallArgs a{};
+    a.M = cols;
+    a.N = k;
+    a.K = rows;
+    a.A = mt;
+    a.sA = s_mt;
+    a.a_row = 1;
+    a.a_k = cols;
+    a.B = P;
+    a.sB = static_cast<int64_t>(rows) * k;
+    a.b_row = 1;
+    a.b_k = k;
+    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &a.pieces, &a.kchunk);
+    a.sC = static_cast<int64_t>(cols) * k;
+    a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.rpart) : R;
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel<0, 0>", "grasp_MtP", 2.0 * elems * kd,
+                       elems * 4.0 + (rows + cols * a.pieces) * kd * 4.0 * batch,
+                       [&] { return launch_tall(a, false, false, batch, s); }));
+    if (a.pieces > 1)
+      MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MtP_sum", 0.0, cols * kd * batch * 4.0 * (a.pieces + 1),
+                         [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, R, batch, s); }));
+    Group8Args q{};
+    q.rows = cols;
+    q.k = k;
+    q.Xs = R;
+    q.sX = a.sC;
+    q.codes = st->R_codes;
+    q.scales = st->R_scales;
+    MUON_LAUNCH(traced(s, "group8_kernel<0>", "grasp_R_code", 0.0, cols * kd * 5.0 * batch,
+                       [&] { return launch_group8(q, false, batch, s); }));
+  }
+  // 7. grid code of M_res = M_t - P R^T
+  {
+    ResidualArgs a{};
+    a.rows = rows;
+    a.cols = cols;
+    a.prod.M = rows;
+    a.prod.N = cols;
+    a.prod.K = k;
+    a.prod.A = P;
+    a.prod.sA = static_cast<int64_t>(rows) * k;
+    a.prod.a_row = k;
+    a.prod.a_k = 1;
+    a.prod.B = R;
+    a.prod.sB = static_cast<int64_t>(cols) * k;
+    a.prod.b_row = k;
+    a.prod.b_k = 1;
+    a.prod.pieces = 1;
+    a.prod.kchunk = k;
+    a.mt = mt;
+    a.s_mt = s_mt;
+    a.codes = st->res_codes;
+    a.sr = st->res_row_scales;
+    a.sc = st->res_col_scales;
+    MUON_LAUNCH(traced(s, "residual_kernel", "grasp_residual", 2.0 * elems * kd,
+                       elems * 4.5 + (rows + cols) * kd * 4.0 * batch,
+                       [&] { return launch_residual(a, batch, s); }));
+  }
+  return MUON_OK;
+}
+
+muon_status grasp_step(int batch, int rows, int cols, int k, void* const* W, muon_dtype w_dtype,
+                       const muon_grasp_state* state, const void* const* G, muon_dtype g_dtype, float mu, float lr,
+                       float weight_decay, float update_scale, muon_ns_variant variant, const muon_ns_config* cfg,
+                       void* const* O_out, muon_dtype o_dtype, void* const* M_out, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
+  Config c;
+  muon_status st = make_config(cfg, variant, &c);
+  if (st != MUON_OK) return st;
+  Plan p;
+  if (!make_plan(batch, rows, cols, variant, c, &p)) return MUON_ERR_INVALID_ARG;
+  const int kmax = rows < cols ? rows : cols;
+  if (k < 0 || k > kmax || k > MUON_GRASP_MAX_K) return MUON_ERR_INVALID_ARG;
+  if (W == nullptr || G == nullptr || !grasp_state_ok(state, k)) return MUON_ERR_INVALID_ARG;
+  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay) || !isfinite(update_scale)) return MUON_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_dtype(g_dtype)) return MUON_ERR_INVALID_ARG;
+  if (w_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
+  if (O_out != nullptr && o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
+  GraspLayout lay;
+  grasp_layout(p.total, batch, rows, cols, k, &lay);
+  if (workspace == nullptr || ws_bytes < lay.total) return MUON_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = run_grasp_state(batch, rows, cols, k, state, G, g_dtype, static_cast<double>(mu), M_out, ws, lay, s);
+  if (st != MUON_OK) return st;
+  st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(ws + lay.ptrs), kF32, nullptr, nullptr, 0.0, s);
+  if (st != MUON_OK) return st;
+  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
+  return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+}
+
+muon_status grid_codec(int mode, int batch, int rows, int cols, const void* const* X, void* const* codes,
+                       void* const* sr, void* const* sc, void* const* Y, void* stream) {
+  if (batch < 1 || rows < 1 || cols < 1 || rows > MUON_MAX_DIM || cols > MUON_MAX_DIM) return MUON_ERR_INVALID_ARG;
+  if (codes == nullptr || sr == nullptr || sc == nullptr) return MUON_ERR_INVALID_ARG;
+  if ((mode == 0 && X == nullptr) || (mode == 2 && Y == nullptr)) return MUON_ERR_INVALID_ARG;
+  GridArgs a{};
+  a.rows = rows;
+  a.cols = cols;
+  a.X = X;
+  a.codes = codes;
+  a.sr = sr;
+  a.sc = sc;
+  a.Y = Y;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const double elems = static_cast<double>(rows) * cols * batch;
+  MUON_LAUNCH(traced(s, mode == 0 ? "grid_kernel<0>" : "grid_kernel<2>", mode == 0 ? "grid_quantize" : "grid_dequantize",
+                     0.0, elems * 4.5, [&] { return launch_grid(a, mode, batch, s); }));
+  return MUON_OK;
+}
+
+muon_status group8_codec(bool dequantize, int batch, int rows, int k, void* const* X, void* const* codes,
+                         void* const* scales, void* stream) {
+  if (batch < 1 || rows < 1 || k < 1 || rows > MUON_MAX_DIM || k > MUON_MAX_DIM) return MUON_ERR_INVALID_ARG;
+  if (X == nullptr || codes == nullptr || scales == nullptr) return MUON_ERR_INVALID_ARG;
+  Group8Args a{};
+  a.rows = rows;
+  a.k = k;
+  a.Xp = X;
+  a.codes = codes;
+  a.scales = scales;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MUON_LAUNCH(traced(s, dequantize ? "group8_kernel<1>" : "group8_kernel<0>",
+                     dequantize ? "group8_dequantize" : "group8_quantize", 0.0,
+                     static_cast<double>(rows) * k * batch * 5.0, [&] { return launch_group8(a, dequantize, batch, s); }));
+  return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -684,6 +1023,51 @@ muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype 
   if (st != MUON_OK) return st;
   Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
   return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+}
+
+size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_variant variant,
+                                 const muon_ns_config* cfg) {
+  Config c;
+  if (make_config(cfg, variant, &c) != MUON_OK) return 0;
+  Plan p;
+  if (!make_plan(batch, rows, cols, variant, c, &p)) return 0;
+  const int kmax = rows < cols ? rows : cols;
+  if (k < 0 || k > kmax || k > MUON_GRASP_MAX_K) return 0;
+  GraspLayout lay;
+  grasp_layout(p.total, batch, rows, cols, k, &lay);
+  return lay.total;
+}
+
+muon_status muon_grasp_step(int batch, int rows, int cols, int k, void* const* W, muon_dtype w_dtype,
+                            const muon_grasp_state* state, const void* const* G, muon_dtype g_dtype, float mu,
+                            float lr, float weight_decay, float update_scale, muon_ns_variant variant,
+                            const muon_ns_config* cfg, void* const* O_out, muon_dtype o_dtype, void* const* M_out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  return grasp_step(batch, rows, cols, k, W, w_dtype, state, G, g_dtype, mu, lr, weight_decay, update_scale, variant,
+                    cfg, O_out, o_dtype, M_out, workspace, ws_bytes, stream);
+}
+
+muon_status muon_grid_quantize(int batch, int rows, int cols, const void* const* X, void* const* codes,
+                               void* const* row_scales, void* const* col_scales, void* stream) {
+  return grid_codec(0, batch, rows, cols, X, codes, row_scales, col_scales, nullptr, stream);
+}
+
+muon_status muon_grid_dequantize(int batch, int rows, int cols, const void* const* codes,
+                                 const void* const* row_scales, const void* const* col_scales, void* const* Y,
+                                 void* stream) {
+  return grid_codec(2, batch, rows, cols, nullptr, const_cast<void* const*>(codes),
+                    const_cast<void* const*>(row_scales), const_cast<void* const*>(col_scales), Y, stream);
+}
+
+muon_status muon_group8_quantize(int batch, int rows, int k, const void* const* X, void* const* codes,
+                                 void* const* scales, void* stream) {
+  return group8_codec(false, batch, rows, k, const_cast<void* const*>(X), codes, scales, stream);
+}
+
+muon_status muon_group8_dequantize(int batch, int rows, int k, const void* const* codes, const void* const* scales,
+                                   void* const* Y, void* stream) {
+  return group8_codec(true, batch, rows, k, Y, const_cast<void* const*>(codes), const_cast<void* const*>(scales),
+                      stream);
 }
 
 double muon_ns_flops(int rows, int cols, muon_ns_variant variant, const muon_ns_config* cfg,

@@ -1,0 +1,91 @@
+// Internal declarations of the low-bit momentum state kernels (muon_grasp.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kGridBlock = 128;  // grid block edge and 8-bit group length
+
+// 4-bit grid code over 128 x 128 blocks; matrix arguments are device arrays of
+// per-matrix device pointers, except the fp32 M_t buffer (strided).
+struct GridArgs {
+  int rows, cols;
+  const void* const* X;                         // mode 0: fp32 input
+  void* const* codes;                           // uint8 rows x (cols + 1) / 2
+  void* const* sr;                              // fp32 rows x ceil(cols / 128)
+  void* const* sc;                              // fp32 ceil(rows / 128) x cols
+  const void* const* G; int g_dtype; double mu; // mode 1
+  void* const* Y;                               // mode 1: optional copy of M_t; mode 2: output
+  float* mt; int64_t s_mt;                      // mode 1: M_t of matrix b at mt + b * s_mt
+};
+
+// 8-bit groups of 128 along the rows of a rows x k matrix.
+struct Group8Args {
+  int rows, k;
+  void* const* Xp; float* Xs; int64_t sX;       // fp32 values: pointer array, or strided if Xp is null
+  void* const* codes;                           // int8 rows x k
+  void* const* scales;                          // fp32 rows x ceil(k / 128)
+};
+
+// Q = unit columns of the decoded R_{t-1} (n x k).
+struct UnitArgs {
+  int n, k, nchunk;                             // nchunk = ceil(n / 256)
+  const void* const* codes; const void* const* scales;
+  double* part;                                 // batch x nchunk x k
+  float* Q; int64_t sQ;
+};
+
+// C[b] (M x N, row-major, fp32) = A[b] B[b]; A element (row, k) at
+// A + b sA + row a_row + k a_k, B element (col, k) at B + b sB + col b_row + k b_k.
+// With pieces > 1, block z = b * pieces + p covers k in [p kchunk, (p + 1) kchunk)
+// and writes C + z sC (partial products, summed by launch_sum_pieces).
+struct TallArgs {
+  int M, N, K;
+  const float* A; int64_t sA, a_row, a_k;
+  const float* B; int64_t sB, b_row, b_k;
+  float* C; int64_t sC;
+  int pieces, kchunk;
+};
+
+// M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G.
+struct ReconArgs {
+  int rows, cols, k;
+  const void* const* res_codes; const void* const* res_sr; const void* const* res_sc;
+  const void* const* P_codes; const void* const* P_scales;
+  const void* const* R_codes; const void* const* R_scales;
+  const void* const* G; int g_dtype; double mu;
+  float* mt; int64_t s_mt;
+  void* const* Y;                               // optional copy of M_t
+};
+
+// New grid code of M_t - P R^T (prod: A = P, B = R, both k-contiguous).
+struct ResidualArgs {
+  int rows, cols;
+  TallArgs prod;
+  const float* mt; int64_t s_mt;
+  void* const* codes; void* const* sr; void* const* sc;
+};
+
+// CholeskyQR of P~ (m x k): partial Gram matrices, their sum S, U^{-1}.
+struct CholArgs {
+  int m, k, nchunk;                             // nchunk = ceil(m / 256)
+  const float* P; int64_t sP;
+  double* spart;                                // batch x nchunk x k x k
+  double* S;                                    // batch x k x k (becomes U)
+  double* Vinv64;                               // batch x k x k scratch
+  float* Uinv;                                  // batch x k x k
+};
+
+hipError_t launch_grid(const GridArgs& a, int mode, int batch, hipStream_t s);
+hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStream_t s);
+hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s);
+hipError_t launch_tall(const TallArgs& a, bool a_kcontig, bool b_kcontig, int batch, hipStream_t s);
+hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float* out, int batch, hipStream_t s);
+hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s);
+hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s);
+hipError_t launch_cholqr(const CholArgs& a, int batch, hipStream_t s);
+hipError_t launch_ptr_table(float* base, int64_t stride, int batch, float** out, hipStream_t s);
+
+}  // namespace muon

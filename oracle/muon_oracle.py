@@ -60,7 +60,7 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to bfloat16 (8 significant bits, fp32 exponent
     range), ties to even, returned as float64.  Done directly on the float64
     bit pattern so there is exactly one rounding."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.ascontiguousarray(x, dtype=np.float64)  # ravel() below must be a view
     out = np.empty_like(x)
     flat = x.ravel()
     o = out.ravel()

@@ -166,3 +166,15 @@ def random_matrix(seed: int, rows: int, cols: int, std: float = 1.0, dtype: str 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a CPU or device tensor's stored values."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def random_codes(seed: int, shape, levels: int) -> np.ndarray:
+    """Uniform integers in [-levels, levels] (int8): an arbitrary stored code."""
+    r = _rng(9500 + seed, 0, 0)
+    return r.integers(-levels, levels + 1, size=shape).astype(np.int8)
+
+
+def random_scales(seed: int, shape, scale: float = 1.0) -> np.ndarray:
+    """Positive float32 values exp(N(0, 1/4)) * scale: arbitrary stored scales."""
+    r = _rng(9600 + seed, 0, 0)
+    return (np.exp(0.5 * r.standard_normal(shape)) * scale).astype(np.float32)

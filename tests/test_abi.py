@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert mu.abi_version() == 2
+    assert mu.abi_version() == 3
 
 
 def test_status_strings():
@@ -131,3 +131,33 @@ def test_binding_rejects_bad_batches():
         bd._batch([torch.zeros(3, 3), torch.zeros(3, 4)], "M")
     with pytest.raises(ValueError):
         bd._batch([torch.zeros(3, 3)], "M")  # not a device tensor
+
+
+def test_invalid_grasp_calls():
+    """Argument checks of the low-bit-state entry points (no device work)."""
+    lib = mu.load_library()
+    assert mu.grasp_workspace_size(1, 300, 200, 12) > mu.grasp_workspace_size(1, 300, 200, 0) > mu.workspace_size(1, 300, 200)
+    for args in [(1, 8, 8, 9), (1, 8, 8, -1), (1, 2048, 2048, 1025), (0, 8, 8, 0)]:
+        with pytest.raises(bd.MuonError):
+            mu.grasp_workspace_size(*args)
+    ws = mu.grasp_workspace_size(1, 8, 8, 2)
+    full = bd._GraspState(*([16] * 7))
+
+    def call(k=2, st=full, W=1, wdt=0, G=2, gdt=1, mu_=0.9, s=1.0, v=0, odt=0, O=None, wsb=ws, w=256):
+        return lib.muon_grasp_step(1, 8, 8, k, W, wdt, ctypes.byref(st) if st is not None else None, G, gdt,
+                                   mu_, 0.1, 0.0, s, v, None, O, odt, None, w, wsb, None)
+
+    assert call(st=None) == 1
+    assert call(st=bd._GraspState(16, 16, 16, None, None, None, None)) == 1   # k > 0 needs P and R
+    assert call(k=9) == 1 and call(k=-1) == 1
+    assert call(W=None) == 1 and call(G=None) == 1
+    assert call(mu_=float("nan")) == 1 and call(s=float("inf")) == 1
+    assert call(gdt=5) == 1 and call(v=3) == 1
+    assert call(wdt=2) == 2 and call(O=4, odt=2) == 2
+    assert call(wsb=ws - 1) == 3 and call(w=256 + 16) == 3
+    assert lib.muon_grid_quantize(0, 8, 8, 1, 2, 3, 4, None) == 1
+    assert lib.muon_grid_quantize(1, 8, 8, None, 2, 3, 4, None) == 1
+    assert lib.muon_grid_dequantize(1, 8, 0, 1, 2, 3, 4, None) == 1
+    assert lib.muon_grid_dequantize(1, 8, 8, 1, 2, 3, None, None) == 1
+    assert lib.muon_group8_quantize(1, 8, 0, 1, 2, 3, None) == 1
+    assert lib.muon_group8_dequantize(1, 8, 8, 1, None, 3, None) == 1

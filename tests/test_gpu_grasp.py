@@ -1,0 +1,276 @@
+"""GPU parity of the low-bit momentum state (through the C ABI) against the
+fp64 oracle in oracle/grasp_oracle.py.
+
+* The two codes on their own are bit-exact: the same fp32 input gives the
+  same codes and scales, and decoding gives the fp32 rounding of the
+  oracle's fp64 value.
+* k = 0 (no subspace): M_t and the new 4-bit state are bit-exact.
+* k > 0: M_t from a given state agrees to fp32 rounding; the power
+  iteration's P and R (8-bit) and the residual (4-bit) are computed from
+  products near fp32 accuracy on the GPU and in fp64 by the oracle, so a code
+  may differ by one where the oracle's unrounded value L x / m lies near a
+  rounding boundary.  The Q factor of M_t Q moves by about cond(M_t Q) times
+  the relative error of the product (a property of QR, not of the method used),
+  so the reach grows with the conditioning: the test allows a 1 % share of
+  codes that differ by one, each within 0.75 of the oracle's unrounded value
+  (one of the two nearest codes), and compares the decoded state and O at
+  relative Frobenius error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import matrix_orthogonalizing_optimizer_step_amd as mu
+from oracle import grasp_oracle as go
+from oracle import muon_oracle as orc
+from synth import inputs as syn
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MU, LR = float(np.float32(0.95)), float(np.float32(0.02))
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(DEV) if dtype is None else t.to(DEV, dtype)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def seeded(seed, rows, cols, std=1.0):
+    return syn.to_f64(syn.random_matrix(seed, rows, cols, std)).astype(np.float32)
+
+
+# ------------------------------------------------------------ the codes alone
+@pytest.mark.parametrize("rows,cols", [(130, 260), (1, 1), (257, 3), (128, 128), (3, 515)])
+def test_grid_code_bitexact(rows, cols):
+    x = seeded(rows * 7 + cols, rows, cols)
+    x[::5, ::3] *= 40  # two-sided outliers
+    if rows >= 128 and cols >= 128:
+        x[:64, :64] = 0                                    # a zero corner of a block
+        x[100, 7] = np.float32(3.0) * np.abs(x[100]).max()  # a row/column extreme
+    q, sr, sc = go.grid_quantize(x)
+    codes, gsr, gsc = mu.grid_quantize([dev(x)])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes[0]), go.pack_nibbles(q))
+    assert np.array_equal(host(gsr[0]), sr) and np.array_equal(host(gsc[0]), sc)
+    y = mu.grid_dequantize(codes, gsr, gsc, cols)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y[0]), go.grid_dequantize(q, sr, sc).astype(np.float32))
+
+
+def test_grid_code_ties_nan_inf():
+    m = np.float32(1.75)
+    x = np.zeros((3, 6), np.float32)
+    x[0, :4] = [m, m / 2, np.float32(5 * 1.75 / 14), -m / 2]
+    x[1, :4] = m
+    x[2, 4] = np.nan
+    x[0, 5] = np.inf
+    q, sr, sc = go.grid_quantize(x)
+    codes, gsr, gsc = mu.grid_quantize([dev(x)])
+    torch.cuda.synchronize()
+    assert list(q[0, :4]) == [7, 4, 2, -4]
+    assert np.array_equal(host(codes[0]), go.pack_nibbles(q))
+    np.testing.assert_array_equal(host(gsr[0]), sr)  # NaN in the same places
+    np.testing.assert_array_equal(host(gsc[0]), sc)
+
+
+@pytest.mark.parametrize("rows,k", [(300, 224), (5, 1), (17, 300), (64, 128)])
+def test_group8_code_bitexact(rows, k):
+    x = seeded(rows + 11 * k, rows, k)
+    x[:, ::7] *= 30
+    q, s = go.group8_quantize(x)
+    codes, scales = mu.group8_quantize([dev(x)])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes[0]), q) and np.array_equal(host(scales[0]), s)
+    y = mu.group8_dequantize(codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y[0]), go.group8_dequantize(q, s).astype(np.float32))
+
+
+# ------------------------------------------------------------ helpers for the step
+def gpu_state_from(st, rows, cols, k):
+    """Device copy of an oracle-layout state (codes unpacked -> packed bytes)."""
+    gs = mu.GraspState(1, rows, cols, 0, DEV)
+    gs.k = k
+    gs.res_codes = [dev(go.pack_nibbles(st["res_codes"]))]
+    gs.res_row_scales = [dev(st["res_sr"])]
+    gs.res_col_scales = [dev(st["res_sc"])]
+    if k > 0:
+        gs.P_codes, gs.P_scales = [dev(st["P_codes"])], [dev(st["P_scales"])]
+        gs.R_codes, gs.R_scales = [dev(st["R_codes"])], [dev(st["R_scales"])]
+    return gs
+
+
+def random_state(seed, rows, cols, k, res_scale=0.1, f_scale=0.05):
+    """An arbitrary valid state from seeded random codes and scales."""
+    nb = lambda n: (n + 127) // 128  # noqa: E731
+    st = dict(res_codes=syn.random_codes(seed, (rows, cols), 7),
+              res_sr=syn.random_scales(seed + 1, (rows, nb(cols)), res_scale),
+              res_sc=syn.random_scales(seed + 2, (nb(rows), cols), res_scale))
+    if k > 0:
+        st["P_codes"] = syn.random_codes(seed + 3, (rows, k), 127)
+        st["P_scales"] = syn.random_scales(seed + 4, (rows, nb(k)), f_scale)
+        st["R_codes"] = syn.random_codes(seed + 5, (cols, k), 127)
+        st["R_scales"] = syn.random_scales(seed + 6, (cols, nb(k)), f_scale)
+    return st
+
+
+def near_tie_mismatch(q_gpu, q_or, x_or, m, levels, share=0.01, reach=0.75):
+    """Codes equal except a small share that differ by one, each of them
+    within ``reach`` of the oracle's unrounded L x / m (one of the two codes
+    nearest to the exact value)."""
+    q_gpu = q_gpu.astype(np.int32)
+    q_or = q_or.astype(np.int32)
+    diff = q_gpu != q_or
+    if not diff.any():
+        return 0.0
+    assert np.abs(q_gpu - q_or).max() == 1
+    t = levels * np.asarray(x_or, np.float64)[diff] / np.asarray(m, np.float64)[diff]
+    assert np.all(np.abs(t - q_gpu[diff]) < reach), "a code differs away from a rounding boundary"
+    frac = diff.mean()
+    assert frac <= share, frac
+    return frac
+
+
+def close_scales(got, want):
+    """Scales (largest magnitudes) agree to the products' accuracy: relative
+    2e-3, or 1e-3 of the matrix's largest scale (a residual of a momentum with
+    a strong top subspace is small, and its error is set by the size of M_t;
+    a CPU emulation of the split-bf16 products reproduces the GPU's figures)."""
+    np.testing.assert_allclose(got, want, rtol=2e-3, atol=1e-3 * float(np.abs(want).max()))
+
+
+def compare_state(gs, st, det, rows, cols, k):
+    torch.cuda.synchronize()
+    q_gpu = go.unpack_nibbles(host(gs.res_codes[0]), cols)
+    sr, sc = host(gs.res_row_scales[0]), host(gs.res_col_scales[0])
+    close_scales(sr, st["res_sr"])
+    close_scales(sc, st["res_sc"])
+    m_or = go.grid_min_scale(st["res_sr"], st["res_sc"], rows, cols)
+    f_res = near_tie_mismatch(q_gpu, st["res_codes"], det["M_res"], m_or, 7)
+    rec_gpu = go.grid_dequantize(q_gpu, sr, sc)
+    rec_or = go.grid_dequantize(st["res_codes"], st["res_sr"], st["res_sc"])
+    if k > 0:
+        for name, key in (("P", "P"), ("R", "R")):
+            qg, sg = host(getattr(gs, name + "_codes")[0]), host(getattr(gs, name + "_scales")[0])
+            close_scales(sg, st[name + "_scales"])
+            mo_ = np.repeat(st[name + "_scales"], 128, axis=1)[:, :k]
+            near_tie_mismatch(qg, st[name + "_codes"], det[key].astype(np.float32), mo_, 127)
+        Pg = go.group8_dequantize(host(gs.P_codes[0]), host(gs.P_scales[0]))
+        Rg = go.group8_dequantize(host(gs.R_codes[0]), host(gs.R_scales[0]))
+        Po = go.group8_dequantize(st["P_codes"], st["P_scales"])
+        Ro = go.group8_dequantize(st["R_codes"], st["R_scales"])
+        rec_gpu = rec_gpu + Pg @ Rg.T
+        rec_or = rec_or + Po @ Ro.T
+    assert orc.relative_frobenius(rec_gpu, rec_or) < 1e-2
+    return f_res
+
+
+def run_both(W, st_or, gs, G, k, variant, M_out=True):
+    rows, cols = G.shape
+    Wd, Gd = [dev(W)], [dev(G)]
+    O = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)]
+    Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)] if M_out else None
+    mu.grasp_step(Wd, gs, Gd, MU, LR, 0.0, variant, O_out=O, M_out=Mt)
+    torch.cuda.synchronize()
+    W1, st1, O1, M1, det = go.grasp_step(W.astype(np.float64), st_or, G, MU, LR, 0.0, variant)
+    return (host(Wd[0]), host(O[0]), host(Mt[0]) if M_out else None), (W1, st1, O1, M1, det)
+
+
+# ------------------------------------------------------------ the step
+@pytest.mark.parametrize("rows,cols", [(300, 520), (520, 300), (129, 1)])
+def test_grasp_step_without_subspace_bitexact(rows, cols):
+    """k = 0, two steps from the zero state: M_t and the state bit for bit."""
+    st = go.new_state(rows, cols, 0)
+    gs = mu.GraspState(1, rows, cols, 0, DEV)
+    W = seeded(1, rows, cols)
+    for step in range(2):
+        G = seeded(10 + step, rows, cols, 0.01)
+        (Wg, Og, Mg), (W1, st, O1, M1, det) = run_both(W, st, gs, G, 0, "standard")
+        assert np.array_equal(Mg, M1.astype(np.float32)), step
+        assert np.array_equal(go.unpack_nibbles(host(gs.res_codes[0]), cols), st["res_codes"])
+        assert np.array_equal(host(gs.res_row_scales[0]), st["res_sr"])
+        assert np.array_equal(host(gs.res_col_scales[0]), st["res_sc"])
+        if min(rows, cols) > 1:
+            assert orc.relative_frobenius(Og, O1) < 2e-2
+        assert orc.relative_frobenius(Wg - W, W1 - W) < 2e-2 + 1e-4
+
+
+@pytest.mark.parametrize("rows,cols,k,variant", [
+    (300, 520, 20, "standard"),
+    (520, 300, 20, "gram"),
+    (384, 640, 130, "standard"),   # two 8-bit groups per row of P and R
+    (256, 4096, 16, "gram"),      # M_t Q split along k
+    (4096, 256, 16, "standard"),  # M_t^T P split along k
+    (200, 150, 1, "standard"),
+])
+def test_grasp_step_from_a_random_state(rows, cols, k, variant):
+    """One step from an arbitrary state: M_t to fp32 rounding, the new state
+    up to near-tie codes, O and W at the 16-bit tolerance."""
+    st = random_state(rows + cols + k, rows, cols, k)
+    gs = gpu_state_from(st, rows, cols, k)
+    W = seeded(2, rows, cols)
+    G = seeded(3, rows, cols, 0.01)
+    (Wg, Og, Mg), (W1, st1, O1, M1, det) = run_both(W, st, gs, G, k, variant)
+    err = np.abs(Mg.astype(np.float64) - M1)
+    assert np.all(err <= 1.2e-7 * np.abs(M1) + 1e-12 * np.abs(M1).max())
+    f = compare_state(gs, st1, det, rows, cols, k)
+    assert orc.relative_frobenius(Og, O1) < 2e-2
+    assert orc.relative_frobenius(Wg - W, W1 - W) < 2e-2 + 1e-4
+    print(f"{rows}x{cols} k={k} {variant}: residual codes off by one {f:.2e}")
+
+
+def test_grasp_first_steps_with_a_low_rank_momentum():
+    """From the start state (zero residual and P, Gaussian R): two steps on a
+    gradient of rank k plus noise; after the warm-started second step the
+    subspace holds the low-rank part, the residual is small and the decoded
+    state tracks M_t."""
+    rows, cols, k = 320, 448, 12
+    U = seeded(20, rows, k)
+    V = seeded(21, k, cols)
+    R0 = seeded(22, cols, k)
+    st = go.new_state(rows, cols, k, R_init=R0)
+    gs = mu.GraspState(1, rows, cols, k, DEV, R_init=[dev(R0)])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gs.R_codes[0]), st["R_codes"]) and np.array_equal(host(gs.R_scales[0]), st["R_scales"])
+    W = seeded(23, rows, cols)
+    for step in range(2):
+        G = (U @ V + 0.05 * seeded(30 + step, rows, cols)).astype(np.float32)
+        (Wg, Og, Mg), (W1, st_next, O1, M1, det) = run_both(W, st, gs, G, k, "gram")
+        if step == 0:
+            assert np.array_equal(Mg, M1.astype(np.float32))  # M_{-1} = 0
+            compare_state(gs, st_next, det, rows, cols, k)
+        else:
+            # each side now runs on its own state, so the two M_t differ by the
+            # near-tie codes of step 0: compare the two M_t, and what each side
+            # stored with its own M_t
+            assert orc.relative_frobenius(Mg, M1) < 1e-2
+            torch.cuda.synchronize()
+            rec_g = go.grid_dequantize(go.unpack_nibbles(host(gs.res_codes[0]), cols), host(gs.res_row_scales[0]),
+                                       host(gs.res_col_scales[0])) + \
+                go.group8_dequantize(host(gs.P_codes[0]), host(gs.P_scales[0])) @ \
+                go.group8_dequantize(host(gs.R_codes[0]), host(gs.R_scales[0])).T
+            rec_o = go.reconstruct(st_next)
+            assert orc.relative_frobenius(rec_g, Mg) < 2e-2 and orc.relative_frobenius(rec_o, M1) < 2e-2
+        # a cold start (random R) leaves about a fifth; the warm start about 1 %
+        assert np.linalg.norm(det["M_res"]) < (0.3 if step == 0 else 0.03) * np.linalg.norm(M1)
+        if step == 0:  # later, O = NS(M_t) magnifies the small state differences in the weak directions
+            assert orc.relative_frobenius(Og, O1) < 2e-2
+        st = st_next  # each side keeps its own state; W is the same seeded matrix every step
+
+
+def test_grasp_zero_column_of_R():
+    """A zero column of R_{t-1} gives a zero column of Q, hence of P and R."""
+    rows, cols, k = 160, 200, 6
+    st = random_state(77, rows, cols, k)
+    st["R_codes"][:, 3] = 0
+    gs = gpu_state_from(st, rows, cols, k)
+    G = seeded(5, rows, cols, 0.01)
+    (Wg, Og, Mg), (W1, st1, O1, M1, det) = run_both(seeded(6, rows, cols), st, gs, G, k, "standard")
+    assert np.all(host(gs.P_codes[0])[:, 3] == 0) and np.all(st1["P_codes"][:, 3] == 0)
+    assert np.all(host(gs.R_codes[0])[:, 3] == 0)
+    compare_state(gs, st1, det, rows, cols, k)
