@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--compute", default=None, help="operand type override: bf16, f16 or f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
+    ap.add_argument("--no-low-bit", action="store_true",
+                    help="skip timing the step with the low-bit (4-bit grid / 8-bit subspace) momentum state")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--one-stream", action="store_true",
@@ -411,6 +413,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    low_bit = None if args.no_low_bit else time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev)
+
     # ------------------------------------------------ CPU baseline: the fp64 oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -449,6 +453,7 @@ def main():
         "traced_ms_per_step": traced_sec * 1e3,
         "traced_note": "traced steps run the groups serially on one stream (per-kernel event timing)",
         "cpu_baseline": cpu,
+        "low_bit_state": low_bit,
         "pages_context": {
             "gram_ns_optimizer_time_saving": "up to 50% (Kimi K2, hardware not stated)",
             "ns_runtime_reduction": "40-50% (Kimi K2, hardware not stated)",
@@ -457,6 +462,85 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
+
+
+def time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev):
+    """The same step with the momentum kept in the low-bit state
+    (muon_grasp_step): k = 0 (4-bit grid code of M_t, no subspace) and k =
+    min(rows, cols) / 16 (8-bit top subspace from one warm-started power
+    iteration, 4-bit grid residual).  Each group on its own stream as in the
+    main step; then one traced serial pass for the per-kernel times of the
+    state kernels."""
+    import torch
+    variant = args.variant
+    main = torch.cuda.current_stream()
+    out = {}
+    for label in ("k0", "rank_over_16"):
+        for gi, x in enumerate(groups):
+            g = x["g"]
+            k = 0 if label == "k0" else max(1, min(g.rows, g.cols) // 16)
+            R0 = [syn.random_matrix(100 + gi * 64 + i, g.cols, k).to(dev) for i in range(g.count)] if k else None
+            x["gs"] = mu.GraspState(g.count, g.rows, g.cols, k, dev, R_init=R0)
+            x["gws"] = torch.empty(mu.grasp_workspace_size(g.count, g.rows, g.cols, k, variant, cfg_for(variant)),
+                                   dtype=torch.uint8, device=dev)
+
+        def gstep(serial=False):
+            serial = serial or args.one_stream
+            if not serial:
+                ev = torch.cuda.Event()
+                ev.record(main)
+            for x in groups:
+                if not serial:
+                    x["stream"].wait_event(ev)
+                mu.grasp_step(x["W"], x["gs"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant),
+                              workspace=x["gws"], stream=main if serial else x["stream"])
+            if not serial:
+                for x in groups:
+                    done = torch.cuda.Event()
+                    done.record(x["stream"])
+                    main.wait_event(done)
+
+        for _ in range(args.warmup):
+            gstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            gstep()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        mu.trace_enable(True)
+        gstep(serial=True)
+        torch.cuda.synchronize()
+        recs = mu.trace_collect()
+        mu.trace_enable(False)
+        kern = {}
+        for r in recs:
+            kk = kern.setdefault(r["role"], dict(ms=0.0, flops=0.0, bytes=0.0))
+            kk["ms"] += r["ms"]
+            kk["flops"] += r["flops"]
+            kk["bytes"] += r["bytes"]
+        state_roles = {k: {"ms": v["ms"],
+                           "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None,
+                           "gbs": v["bytes"] / (v["ms"] / 1e3) / 1e9}
+                       for k, v in kern.items() if k.startswith("grasp") or k.startswith("grid")}
+        out[label] = {
+            "ms_per_step": sec * 1e3,
+            "ns_tflops_algorithmic": flops_for(variant, True) / sec / 1e12,
+            "k": {x["g"].name: x["gs"].k for x in groups},
+            "state_bytes": sum(sum(t.numel() * t.element_size() for name in
+                                   ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes",
+                                    "R_scales") for t in (getattr(x["gs"], name) or [])) for x in groups),
+            "serial_state_kernels": state_roles,
+            "serial_state_ms": sum(v["ms"] for v in state_roles.values()),
+        }
+        log(f"[bench] low-bit state {label}: {sec * 1e3:.3f} ms/step, state kernels (serial) "
+            f"{out[label]['serial_state_ms']:.3f} ms")
+        for x in groups:
+            del x["gs"], x["gws"]
+    out["note"] = ("muon_grasp_step on the same workload and variant; M_t is rebuilt from the stored state, "
+                   "orthogonalised, and stored again; state_bytes counts codes and scales (fp32 momentum: "
+                   f"{4 * wl.elements} bytes)")
+    return out
 
 
 CPU_SAMPLE_SECONDS = 10.0

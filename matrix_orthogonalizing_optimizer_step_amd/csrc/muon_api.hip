@@ -629,8 +629,8 @@ int nblk(int x, int b) { return (x + b - 1) / b; }
 // Workspace after the Newton-Schulz part: M_t and its pointer table, then
 // (k > 0) the power-iteration buffers.
 struct GraspLayout {
-  size_t ptrs, mt, q, colpart, ppart, ptil, spart, S, V64, uinv, P, rpart, R, total;
-  int nch_n, nch_m;
+  size_t ptrs, mt, q, colpart, colinv, ppart, ptil, spart, S, dead, P, rpart, R, total;
+  int nch_n, nch_m, gchunk;
 };
 
 bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout* g) {
@@ -645,16 +645,17 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
   g->ptrs = take(B * sizeof(void*));
   g->mt = take(B * r * c * 4);
   if (k > 0) {
-    g->nch_n = nblk(cols, 256);
-    g->nch_m = nblk(rows, 256);
+    g->nch_n = nblk(cols, kUnitRows);
+    g->gchunk = gram_chunk_rows(rows, batch);
+    g->nch_m = nblk(rows, g->gchunk);
     g->q = take(B * c * kk * 4);
     g->colpart = take(B * g->nch_n * kk * 8);
+    g->colinv = take(B * kk * 8);
     g->ppart = take(B * kGraspMaxPieces * r * kk * 4);
     g->ptil = take(B * r * kk * 4);
     g->spart = take(B * g->nch_m * kk * kk * 8);
     g->S = take(B * kk * kk * 8);
-    g->V64 = take(B * kk * kk * 8);
-    g->uinv = take(B * kk * kk * 4);
+    g->dead = take(B * kk * 4);
     g->P = take(B * r * kk * 4);
     g->rpart = take(B * kGraspMaxPieces * c * kk * 4);
     g->R = take(B * c * kk * 4);
@@ -746,6 +747,7 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.codes = st->R_codes;
     a.scales = st->R_scales;
     a.part = reinterpret_cast<double*>(ws + lay.colpart);
+    a.inv = reinterpret_cast<double*>(ws + lay.colinv);
     a.Q = Q;
     a.sQ = static_cast<int64_t>(cols) * k;
     MUON_LAUNCH(traced(s, "unit_columns_kernel", "grasp_Q", 0.0, cols * kd * batch * 6.0,
@@ -776,48 +778,31 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MQ_sum", 0.0, rows * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, ptil, batch, s); }));
   }
-  // 4. CholeskyQR: S = P~^T P~ = U^T U, U^{-1}
-  float* uinv = reinterpret_cast<float*>(ws + lay.uinv);
+  // 4. CholeskyQR: S = P~^T P~ = U^T U, P = P~ U^{-1}, then its 8-bit code
+  float* P = reinterpret_cast<float*>(ws + lay.P);
   {
     CholArgs a{};
     a.m = rows;
     a.k = k;
     a.nchunk = lay.nch_m;
+    a.chunk = lay.gchunk;
     a.P = ptil;
     a.sP = static_cast<int64_t>(rows) * k;
     a.spart = reinterpret_cast<double*>(ws + lay.spart);
     a.S = reinterpret_cast<double*>(ws + lay.S);
-    a.Vinv64 = reinterpret_cast<double*>(ws + lay.V64);
-    a.Uinv = uinv;
-    MUON_LAUNCH(traced(s, "gram64+chol_inv_kernel", "grasp_cholqr", rows * kd * kd * batch, rows * kd * 4.0 * batch,
-                       [&] { return launch_cholqr(a, batch, s); }));
-  }
-  // 5. P = P~ U^{-1}, then its 8-bit code
-  float* P = reinterpret_cast<float*>(ws + lay.P);
-  {
-    TallArgs a{};
-    a.M = rows;
-    a.N = k;
-    a.K = k;
-    a.A = ptil;
-    a.sA = static_cast<int64_t>(rows) * k;
-    a.a_row = k;
-    a.a_k = 1;
-    a.B = uinv;
-    a.sB = static_cast<int64_t>(k) * k;
-    a.b_row = 1;
-    a.b_k = k;
-    a.pieces = 1;
-    a.kchunk = k;
-    a.C = P;
-    a.sC = static_cast<int64_t>(rows) * k;
-    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 0>", "grasp_PUinv", 2.0 * rows * kd * kd * batch,
-                       rows * kd * 8.0 * batch, [&] { return launch_tall(a, true, false, batch, s); }));
+    a.dead = reinterpret_cast<int*>(ws + lay.dead);
+    a.Pout = P;
+    MUON_LAUNCH(traced(s, "gram64_kernel+gram_sum", "grasp_gram", rows * kd * kd * batch, rows * kd * 4.0 * batch,
+                       [&] { return launch_gram(a, batch, s); }));
+    MUON_LAUNCH(traced(s, "chol_panel_kernel", "grasp_cholesky", kd * kd * kd / 3.0 * batch, kd * kd * 16.0 * batch,
+                       [&] { return launch_chol(a, batch, s); }));
+    MUON_LAUNCH(traced(s, "row_solve_kernel", "grasp_row_solve", rows * kd * kd * batch, rows * kd * 8.0 * batch,
+                       [&] { return launch_row_solve(a, batch, s); }));
     Group8Args q{};
     q.rows = rows;
     q.k = k;
     q.Xs = P;
-    q.sX = a.sC;
+    q.sX = a.sP;
     q.codes = st->P_codes;
     q.scales = st->P_scales;
     MUON_LAUNCH(traced(s, "group8_kernel<0>", "grasp_P_code", 0.0, rows * kd * 5.0 * batch,

@@ -30,10 +30,12 @@ struct Group8Args {
 };
 
 // Q = unit columns of the decoded R_{t-1} (n x k).
+constexpr int kUnitRows = 64;  // rows per chunk of the column sums
 struct UnitArgs {
-  int n, k, nchunk;                             // nchunk = ceil(n / 256)
+  int n, k, nchunk;                             // nchunk = ceil(n / kUnitRows)
   const void* const* codes; const void* const* scales;
   double* part;                                 // batch x nchunk x k
+  double* inv;                                  // batch x k: 1 / column norm
   float* Q; int64_t sQ;
 };
 
@@ -68,15 +70,26 @@ struct ResidualArgs {
   void* const* codes; void* const* sr; void* const* sc;
 };
 
-// CholeskyQR of P~ (m x k): partial Gram matrices, their sum S, U^{-1}.
+// CholeskyQR of P~ (m x k): partial Gram matrices, their sum S, the factor U
+// (in place of S) and P = P~ U^{-1}.
 struct CholArgs {
-  int m, k, nchunk;                             // nchunk = ceil(m / 256)
-  const float* P; int64_t sP;
+  int m, k, nchunk, chunk;                      // Gram partials over chunks of `chunk` rows
+  const float* P; int64_t sP;                   // P~ (input)
   double* spart;                                // batch x nchunk x k x k
   double* S;                                    // batch x k x k (becomes U)
-  double* Vinv64;                               // batch x k x k scratch
-  float* Uinv;                                  // batch x k x k
+  int* dead;                                    // batch x k: 1 for a dependent or zero column
+  float* Pout;                                  // P (m x k, same strides as P~)
+  int panel;                                    // Cholesky panel rows (set by the launcher)
 };
+
+// Largest subspace rank the kernels take.
+constexpr int kMaxRankK = 1024;
+
+// Rows per Gram partial: 64, or more when the batch alone gives ~1024 blocks.
+inline int gram_chunk_rows(int m, int batch) {
+  const int64_t per = (static_cast<int64_t>(m) * batch + 1023) / 1024;
+  return static_cast<int>((per + 63) / 64 * 64);
+}
 
 hipError_t launch_grid(const GridArgs& a, int mode, int batch, hipStream_t s);
 hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStream_t s);
@@ -85,7 +98,9 @@ hipError_t launch_tall(const TallArgs& a, bool a_kcontig, bool b_kcontig, int ba
 hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float* out, int batch, hipStream_t s);
 hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s);
 hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s);
-hipError_t launch_cholqr(const CholArgs& a, int batch, hipStream_t s);
+hipError_t launch_gram(const CholArgs& a, int batch, hipStream_t s);
+hipError_t launch_chol(const CholArgs& a, int batch, hipStream_t s);
+hipError_t launch_row_solve(const CholArgs& a, int batch, hipStream_t s);
 hipError_t launch_ptr_table(float* base, int64_t stride, int batch, float** out, hipStream_t s);
 
 }  // namespace muon

@@ -61,42 +61,97 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Grid code of one 128 x 128 block (bi, bj).  Thread (wave w, lane l) holds
-// rows bi*128 + w + 4 s (s < 32) and columns j = bj*128 + 2 l, j + 1; entries
-// outside the matrix are 0 and are neither stored nor able to raise a scale.
-// All threads of the block must call this (it synchronises once).  The
-// caller has read every old scale it needs before the call.
+// Thread layout of the grid-code kernels on block (bi, bj): thread t holds
+// columns j0 = bj*128 + 8 (t % 16) .. j0 + 7 of rows bi*128 + t / 16 + 16 s
+// (s < 8), so a row's 128 columns sit in 16 lanes of one wave and its codes
+// are 4 bytes per thread.  `vec`: cols % 8 == 0, every 8-column run is whole
+// and aligned (16-byte loads of G, 32-byte stores of M_t, 4-byte code words).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void encode_block(const float (&x0)[32], const float (&x1)[32], float cm0, float cm1,
-                                             uint8_t* codes, float* sr, float* sc, int rows, int cols, int bi,
-                                             int bj, float (*cpart)[kGB]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int j = bj * kGB + 2 * lane;
-  cpart[w][2 * lane] = cm0;
-  cpart[w][2 * lane + 1] = cm1;
-  __syncthreads();
-  float c0 = cpart[0][2 * lane], c1 = cpart[0][2 * lane + 1];
+__device__ __forceinline__ void load8_f32(const void* p, int64_t e, int dtype, bool vec, int n, float (&v)[8]) {
+  if (vec) {
+    if (dtype == 0) {
+      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + e);
+      const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + e + 4);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + e);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int v = 1; v < 4; ++v) {
-    c0 = nan_max(c0, cpart[v][2 * lane]);
-    c1 = nan_max(c1, cpart[v][2 * lane + 1]);
+      for (int q = 0; q < 4; ++q) {
+        const uint16_t lo = static_cast<uint16_t>(w[q] & 0xffffu), hi = static_cast<uint16_t>(w[q] >> 16);
+        v[2 * q] = dtype == 1 ? bf16_to_f32(lo) : f16_to_f32(lo);
+        v[2 * q + 1] = dtype == 1 ? bf16_to_f32(hi) : f16_to_f32(hi);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = c < n ? load_as_f32(p, e + c, dtype) : 0.0f;
   }
+}
+
+__device__ __forceinline__ void store8_f32(float* p, bool vec, int n, const float (&v)[8]) {
+  if (vec) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < n) p[c] = v[c];
+  }
+}
+
+// Grid code of block (bi, bj) from the values x[s][c] of this thread (0
+// outside the matrix).  All threads of the block call this; it synchronises
+// once, and the caller has read every old scale it needs before the call.
+__device__ __forceinline__ void encode_block(const float (&x)[8][8], uint8_t* codes, float* sr, float* sc, int rows,
+                                             int cols, int bi, int bj, bool vec, float (*cpart)[kGB]) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, cg = t & 15, rs = t >> 4;
+  const int j0 = bj * kGB + 8 * cg, n = min(8, cols - j0);
   const int nbc = (cols + kGB - 1) / kGB;
   const int64_t cb = (cols + 1) / 2;
-  if (w == 0) {
-    if (j < cols) sc[static_cast<int64_t>(bi) * cols + j] = c0;
-    if (j + 1 < cols) sc[static_cast<int64_t>(bi) * cols + j + 1] = c1;
-  }
+  float cm[8];
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const int i = bi * kGB + w + 4 * s;
-    const float r = wave_max(nan_max(fabsf(x0[s]), fabsf(x1[s])));
-    if (i < rows) {
-      if (lane == 0) sr[static_cast<int64_t>(i) * nbc + bj] = r;
-      if (j < cols) {
-        const int q0 = encode(x0[s], nan_min(r, c0), 7.0);
-        const int q1 = j + 1 < cols ? encode(x1[s], nan_min(r, c1), 7.0) : 0;
-        codes[static_cast<int64_t>(i) * cb + (j >> 1)] = static_cast<uint8_t>((q0 & 15) | ((q1 & 15) << 4));
+  for (int c = 0; c < 8; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) m = nan_max(m, fabsf(x[s][c]));
+    m = nan_max(m, __shfl_xor(m, 16));
+    cm[c] = nan_max(m, __shfl_xor(m, 32));
+  }
+  if (lane < 16)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) cpart[w][8 * cg + c] = cm[c];
+  __syncthreads();
+  float cs[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    cs[c] = nan_max(nan_max(cpart[0][8 * cg + c], cpart[1][8 * cg + c]), nan_max(cpart[2][8 * cg + c], cpart[3][8 * cg + c]));
+  if (t < 16)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c < n) sc[static_cast<int64_t>(bi) * cols + j0 + c] = cs[c];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int i = bi * kGB + rs + 16 * s;
+    float r = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r = nan_max(r, fabsf(x[s][c]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) r = nan_max(r, __shfl_xor(r, o));
+    if (i < rows && n > 0) {
+      if (cg == 0) sr[static_cast<int64_t>(i) * nbc + bj] = r;
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int q = c < n ? encode(x[s][c], nan_min(r, cs[c]), 7.0) : 0;
+        word |= static_cast<uint32_t>(q & 15) << (4 * c);
+      }
+      uint8_t* dst = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
+      if (vec) {
+        *reinterpret_cast<uint32_t*>(dst) = word;
+      } else {
+        for (int q = 0; 2 * q < n; ++q) dst[q] = static_cast<uint8_t>(word >> (8 * q));
       }
     }
   }
@@ -109,63 +164,65 @@ template <int MODE>
 __global__ __launch_bounds__(kGT) void grid_kernel(GridArgs a) {
   __shared__ float cpart[4][kGB];
   const int b = blockIdx.z, bi = blockIdx.y, bj = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
   const int rows = a.rows, cols = a.cols;
-  const int j = bj * kGB + 2 * lane;
-  const bool in0 = j < cols, in1 = j + 1 < cols;
+  const int j0 = bj * kGB + 8 * cg, n = min(8, cols - j0);
   const int nbc = (cols + kGB - 1) / kGB;
   const int64_t cb = (cols + 1) / 2;
   uint8_t* codes = static_cast<uint8_t*>(a.codes[b]);
   float* sr = static_cast<float*>(a.sr[b]);
   float* sc = static_cast<float*>(a.sc[b]);
-  float oc0 = 0.0f, oc1 = 0.0f;
-  if constexpr (MODE != 0) {
-    if (in0) oc0 = sc[static_cast<int64_t>(bi) * cols + j];
-    if (in1) oc1 = sc[static_cast<int64_t>(bi) * cols + j + 1];
-  }
-  float x0[32], x1[32];
-  float cm0 = 0.0f, cm1 = 0.0f;
+  // vector accesses need cols % 8 == 0 and aligned bases (user pointers may be offset)
+  uintptr_t mis = reinterpret_cast<uintptr_t>(codes) & 3u;
+  if (MODE == 0) mis |= reinterpret_cast<uintptr_t>(a.X[b]) & 15u;
+  if (MODE == 1) mis |= (reinterpret_cast<uintptr_t>(a.G[b]) | reinterpret_cast<uintptr_t>(a.mt + static_cast<int64_t>(b) * a.s_mt)) & 15u;
+  if (MODE != 0 && a.Y != nullptr) mis |= reinterpret_cast<uintptr_t>(a.Y[b]) & 15u;
+  const bool vec = (cols & 7) == 0 && mis == 0;
+  float oc[8];
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const int i = bi * kGB + w + 4 * s;
-    float v0 = 0.0f, v1 = 0.0f;
-    if (i < rows && in0) {
-      const int64_t e = static_cast<int64_t>(i) * cols + j;
+  for (int c = 0; c < 8; ++c) oc[c] = (MODE != 0 && c < n) ? sc[static_cast<int64_t>(bi) * cols + j0 + c] : 0.0f;
+  float x[8][8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int i = bi * kGB + rs + 16 * s;
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+    if (i < rows && n > 0) {
+      const int64_t e = static_cast<int64_t>(i) * cols + j0;
       if constexpr (MODE == 0) {
-        const float* X = static_cast<const float*>(a.X[b]);
-        v0 = X[e];
-        if (in1) v1 = X[e + 1];
+        load8_f32(a.X[b], e, 0, vec, n, v);
       } else {
         const float r = sr[static_cast<int64_t>(i) * nbc + bj];
-        const uint32_t byte = codes[static_cast<int64_t>(i) * cb + (j >> 1)];
-        const double d0 = decode(sext4(byte & 15u), nan_min(r, oc0), 7.0);
-        const double d1 = in1 ? decode(sext4(byte >> 4), nan_min(r, oc1), 7.0) : 0.0;
-        if constexpr (MODE == 2) {
-          float* Y = static_cast<float*>(a.Y[b]);
-          Y[e] = static_cast<float>(d0);
-          if (in1) Y[e + 1] = static_cast<float>(d1);
+        const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
+        uint32_t word = 0;
+        if (vec) {
+          word = *reinterpret_cast<const uint32_t*>(src);
         } else {
-          const double g0 = load_as_f32(a.G[b], e, a.g_dtype);
-          const double g1 = in1 ? static_cast<double>(load_as_f32(a.G[b], e + 1, a.g_dtype)) : 0.0;
-          v0 = static_cast<float>(__dadd_rn(__dmul_rn(a.mu, d0), g0));
-          v1 = in1 ? static_cast<float>(__dadd_rn(__dmul_rn(a.mu, d1), g1)) : 0.0f;
-          float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
-          mt[e] = v0;
-          if (in1) mt[e + 1] = v1;
-          if (a.Y != nullptr) {
-            float* Y = static_cast<float*>(a.Y[b]);
-            Y[e] = v0;
-            if (in1) Y[e + 1] = v1;
-          }
+          for (int q = 0; 2 * q < n; ++q) word |= static_cast<uint32_t>(src[q]) << (8 * q);
+        }
+        double d[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) d[c] = c < n ? decode(sext4((word >> (4 * c)) & 15u), nan_min(r, oc[c]), 7.0) : 0.0;
+        if constexpr (MODE == 2) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = static_cast<float>(d[c]);
+          store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
+        } else {
+          float g[8];
+          load8_f32(a.G[b], e, a.g_dtype, vec, n, g);
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            v[c] = c < n ? static_cast<float>(__dadd_rn(__dmul_rn(a.mu, d[c]), static_cast<double>(g[c]))) : 0.0f;
+          store8_f32(a.mt + static_cast<int64_t>(b) * a.s_mt + e, vec, n, v);
+          if (a.Y != nullptr) store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
         }
       }
     }
-    x0[s] = v0;
-    x1[s] = v1;
-    cm0 = nan_max(cm0, fabsf(v0));
-    cm1 = nan_max(cm1, fabsf(v1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[s][c] = v[c];
   }
-  if constexpr (MODE != 2) encode_block(x0, x1, cm0, cm1, codes, sr, sc, rows, cols, bi, bj, cpart);
+  if constexpr (MODE != 2) encode_block(x, codes, sr, sc, rows, cols, bi, bj, vec, cpart);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,17 +257,17 @@ __global__ __launch_bounds__(kGT) void group8_kernel(Group8Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Q = unit columns of deq(R_{t-1}) (n x k, fp32).  Stage 1: per chunk of 256
-// rows, the fp64 sum of squares of every column.  Stage 2: every block sums
-// the chunk partials in chunk order (so all blocks agree), then scales its
-// rows; a zero column stays zero.
+// Q = unit columns of the decoded R_{t-1} (n x k, fp32).  Stage 1: per chunk
+// of kUnitRows rows, the fp64 sum of squares of every column.  Stage 2 (one
+// block per matrix): 1 / norm per column from the chunk partials summed in
+// chunk order (0 for a zero column).  Stage 3: the scaled rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGT) void colsq_kernel(UnitArgs a) {
   const int b = blockIdx.y, ch = blockIdx.x;
   const int k = a.k, ng = (k + kGB - 1) / kGB;
   const int8_t* q = static_cast<const int8_t*>(a.codes[b]);
   const float* sc = static_cast<const float*>(a.scales[b]);
-  const int i0 = ch * kGT, i1 = min(a.n, i0 + kGT);
+  const int i0 = ch * kUnitRows, i1 = min(a.n, i0 + kUnitRows);
   for (int c = threadIdx.x; c < k; c += kGT) {
     double ss = 0.0;
     for (int i = i0; i < i1; ++i) {
@@ -221,20 +278,23 @@ __global__ __launch_bounds__(kGT) void colsq_kernel(UnitArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGT) void unit_columns_kernel(UnitArgs a) {
-  extern __shared__ double inv[];  // k entries
-  const int b = blockIdx.y, ch = blockIdx.x;
-  const int k = a.k, ng = (k + kGB - 1) / kGB;
+__global__ __launch_bounds__(kGT) void colinv_kernel(UnitArgs a) {
+  const int b = blockIdx.x, k = a.k;
   for (int c = threadIdx.x; c < k; c += kGT) {
     double ss = 0.0;
     for (int p = 0; p < a.nchunk; ++p) ss += a.part[(static_cast<int64_t>(b) * a.nchunk + p) * k + c];
-    inv[c] = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+    a.inv[static_cast<int64_t>(b) * k + c] = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
   }
-  __syncthreads();
+}
+
+__global__ __launch_bounds__(kGT) void unit_columns_kernel(UnitArgs a) {
+  const int b = blockIdx.y, ch = blockIdx.x;
+  const int k = a.k, ng = (k + kGB - 1) / kGB;
   const int8_t* q = static_cast<const int8_t*>(a.codes[b]);
   const float* sc = static_cast<const float*>(a.scales[b]);
+  const double* inv = a.inv + static_cast<int64_t>(b) * k;
   float* Q = a.Q + static_cast<int64_t>(b) * a.sQ;
-  const int i0 = ch * kGT, i1 = min(a.n, i0 + kGT);
+  const int i0 = ch * kUnitRows, i1 = min(a.n, i0 + kUnitRows);
   for (int64_t e = static_cast<int64_t>(i0) * k + threadIdx.x; e < static_cast<int64_t>(i1) * k; e += kGT) {
     const int i = static_cast<int>(e / k), c = static_cast<int>(e - static_cast<int64_t>(i) * k);
     Q[e] = static_cast<float>(decode(q[e], sc[static_cast<int64_t>(i) * ng + c / kGB], 127.0) * inv[c]);
@@ -263,11 +323,12 @@ __device__ __forceinline__ void load_f32(const float* base, int64_t s_row, int64
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = threadIdx.x + kGT * p;
-    const int rr = KC ? (e >> 3) : (e & 31) * 4, kk = KC ? (e & 7) * 4 : (e >> 5);
+    // KC: 8 threads per row, 16 bytes each; row-contiguous: a row per thread
+    // (consecutive threads on consecutive rows), 4 scalar loads along k
+    const int rr = KC ? (e >> 3) : (e & 127), kk = KC ? (e & 7) * 4 : (e >> 7) * 4;
     const int row = row0 + rr, k = k0 + kk;
     const float* src = base + static_cast<int64_t>(row) * s_row + static_cast<int64_t>(k) * s_k;
-    const bool full = KC ? (row < nrows && k + 3 < K) : (row + 3 < nrows && k < K);
-    if (full && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+    if (KC && row < nrows && k + 3 < K && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
       const float4 x = *reinterpret_cast<const float4*>(src);
       r.v[4 * p] = x.x;
       r.v[4 * p + 1] = x.y;
@@ -275,10 +336,7 @@ __device__ __forceinline__ void load_f32(const float* base, int64_t s_row, int64
       r.v[4 * p + 3] = x.w;
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = KC ? (row < nrows && k + q < K) : (row + q < nrows && k < K);
-        r.v[4 * p + q] = ok ? src[q] : 0.0f;
-      }
+      for (int q = 0; q < 4; ++q) r.v[4 * p + q] = (row < nrows && k + q < K) ? src[static_cast<int64_t>(q) * s_k] : 0.0f;
     }
   }
 }
@@ -289,7 +347,7 @@ __device__ __forceinline__ void store_split(const TileRegs& r, uint16_t* hi, uin
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = threadIdx.x + kGT * p;
-    const int rr = KC ? (e >> 3) : (e & 31) * 4, kk = KC ? (e & 7) * 4 : (e >> 5);
+    const int rr = KC ? (e >> 3) : (e & 127), kk = KC ? (e & 7) * 4 : (e >> 7) * 4;
     uint16_t h[4], l[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -297,19 +355,11 @@ __device__ __forceinline__ void store_split(const TileRegs& r, uint16_t* hi, uin
       h[q] = f32_to_bf16(x);
       l[q] = SPLIT ? f32_to_bf16(x - bf16_to_f32(h[q])) : 0;
     }
-    if (KC) {
-      *reinterpret_cast<uint2*>(hi + rr * kTL + kk) =
-          make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
-      if (SPLIT)
-        *reinterpret_cast<uint2*>(lo + rr * kTL + kk) =
-            make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hi[(rr + q) * kTL + kk] = h[q];
-        if (SPLIT) lo[(rr + q) * kTL + kk] = l[q];
-      }
-    }
+    *reinterpret_cast<uint2*>(hi + rr * kTL + kk) =
+        make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
+    if (SPLIT)
+      *reinterpret_cast<uint2*>(lo + rr * kTL + kk) =
+          make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
   }
 }
 
@@ -460,57 +510,75 @@ __global__ __launch_bounds__(kGT) void sum_pieces_kernel(const float* part, int 
 }
 
 // ---------------------------------------------------------------------------
-// M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G for one 128 x 128 grid block.
-// The code product runs group by group (128 k each) as exact integer sums in
-// the fp32 accumulator and is scaled in fp64 by sP sR / 127^2.
+// M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G for a 64 x 128 tile (half a
+// grid block: small enough per wave, 1 x 2 MFMA blocks, to keep several waves
+// per SIMD for the bandwidth-bound epilogue).  The code product runs group
+// by group (128 k each) as exact integer sums in the fp32 accumulator and is
+// scaled in fp64 by sP sR / 127^2; the 4-bit residual decodes in fp64.  Both
+// scalings multiply by fp64 reciprocals of 7 and 127^2 (within an fp64 ulp of
+// the quotients, far below the fp32 rounding of M_t).
 // ---------------------------------------------------------------------------
+constexpr int kRecRows = 64;
+
 __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
-  __shared__ __align__(16) uint16_t smem[2 * kStageHalves];
-  const int b = blockIdx.z, bi = blockIdx.y, bj = blockIdx.x;
-  const int row0 = bi * kTT, col0 = bj * kTT;
+  __shared__ __align__(16) uint16_t smem[(kRecRows + kTT) * kTL];
+  const int b = blockIdx.z, bj = blockIdx.x;
+  const int row0 = blockIdx.y * kRecRows, col0 = bj * kTT, bi = row0 / kGB;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wr = 32 * (w >> 1), wc = 64 * (w & 1);
   const int k = a.k, ng = (k + kGB - 1) / kGB;
   const int8_t* Pc = static_cast<const int8_t*>(a.P_codes[b]);
   const int8_t* Rc = static_cast<const int8_t*>(a.R_codes[b]);
   const float* Ps = static_cast<const float*>(a.P_scales[b]);
   const float* Rs = static_cast<const float*>(a.R_scales[b]);
-  uint16_t *Ah = smem, *Bh = smem + kStageHalves;
-  double pr[2][2][16];
+  uint16_t *Ah = smem, *Bh = smem + kRecRows * kTL;
+  const int arows = min(a.rows, row0 + kRecRows);
+  constexpr double kInvL8sq = 1.0 / 16129.0, kInv7 = 1.0 / 7.0;
+  double pr[2][16];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int y = 0; y < 2; ++y)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pr[y][v] = 0.0;
+  for (int g = 0; g < ng; ++g) {
+    const int kbeg = g * kGB, kend = min(k, kbeg + kGB);
+    gq_f32x16 acc[2];
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pr[x][y][v] = 0.0;
-  for (int g = 0; g < ng; ++g) {
-    const int kbeg = g * kGB, kend = min(k, kbeg + kGB);
-    gq_f32x16 acc[2][2];
-    zero_acc(acc);
+      for (int v = 0; v < 16; ++v) acc[y][v] = 0.0f;
     CodeRegs ra, rb;
-    load_i8(Pc, k, row0, kbeg, a.rows, kend, ra);
+    load_i8(Pc, k, row0, kbeg, arows, kend, ra);
     load_i8(Rc, k, col0, kbeg, a.cols, kend, rb);
     for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-      store_i8(ra, Ah);
+      if (threadIdx.x < 2 * kRecRows) store_i8(ra, Ah);
       store_i8(rb, Bh);
       __syncthreads();
       if (k0 + kTK < kend) {
-        load_i8(Pc, k, row0, k0 + kTK, a.rows, kend, ra);
+        load_i8(Pc, k, row0, k0 + kTK, arows, kend, ra);
         load_i8(Rc, k, col0, k0 + kTK, a.cols, kend, rb);
       }
-      mma_stage<false>(Ah, nullptr, Bh, nullptr, acc);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int kk = 16 * s + 8 * (lane >> 5);
+        const uint4 av = *reinterpret_cast<const uint4*>(Ah + (wr + (lane & 31)) * kTL + kk);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(Bh + (wc + 32 * y + (lane & 31)) * kTL + kk);
+          acc[y] = mfma(av, bv, acc[y]);
+        }
+      }
       __syncthreads();
     }
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const int col = col0 + acc_col(y);
-      const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) : 0.0;
+      const int col = col0 + wc + 32 * y + (lane & 31);
+      const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row0 + acc_row(x, v);
-          const double sP = row < a.rows ? static_cast<double>(Ps[static_cast<int64_t>(row) * ng + g]) : 0.0;
-          pr[x][y][v] += (static_cast<double>(acc[x][y][v]) * (sP * sR)) / 16129.0;
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int row = row0 + wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const double sP = row < a.rows ? static_cast<double>(Ps[static_cast<int64_t>(row) * ng + g]) : 0.0;
+        pr[y][v] = fma(static_cast<double>(acc[y][v]), sP * sR, pr[y][v]);
+      }
     }
   }
   const uint8_t* codes = static_cast<const uint8_t*>(a.res_codes[b]);
@@ -522,24 +590,23 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   float* Y = a.Y != nullptr ? static_cast<float*>(a.Y[b]) : nullptr;
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
-    const int col = col0 + acc_col(y);
+    const int col = col0 + wc + 32 * y + (lane & 31);
     if (col >= a.cols) continue;
     const float cs = sc[static_cast<int64_t>(bi) * a.cols + col];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row0 + acc_row(x, v);
-        if (row >= a.rows) continue;
-        const int64_t e = static_cast<int64_t>(row) * a.cols + col;
-        const uint32_t byte = codes[static_cast<int64_t>(row) * cb + (col >> 1)];
-        const int q = sext4((col & 1) ? (byte >> 4) : (byte & 15u));
-        const double res = decode(q, nan_min(sr[static_cast<int64_t>(row) * nbc + bj], cs), 7.0);
-        const double g = load_as_f32(a.G[b], e, a.g_dtype);
-        const float m = static_cast<float>(__dadd_rn(__dmul_rn(a.mu, __dadd_rn(res, pr[x][y][v])), g));
-        mt[e] = m;
-        if (Y != nullptr) Y[e] = m;
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int row = row0 + wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (row >= a.rows) continue;
+      const int64_t e = static_cast<int64_t>(row) * a.cols + col;
+      const uint32_t byte = codes[static_cast<int64_t>(row) * cb + (col >> 1)];
+      const int q = sext4((col & 1) ? (byte >> 4) : (byte & 15u));
+      const double res =
+          static_cast<double>(q) * static_cast<double>(nan_min(sr[static_cast<int64_t>(row) * nbc + bj], cs)) * kInv7;
+      const double g = load_as_f32(a.G[b], e, a.g_dtype);
+      const float m = static_cast<float>(fma(a.mu, res + pr[y][v], g));
+      mt[e] = m;
+      if (Y != nullptr) Y[e] = m;
+    }
   }
 }
 
@@ -569,38 +636,37 @@ __global__ __launch_bounds__(kGT) void residual_kernel(ResidualArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) tile[acc_row(x, v) * kRL + acc_col(y)] = acc[x][y][v];
   __syncthreads();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
   const int rows = a.rows, cols = a.cols;
-  const int j = col0 + 2 * lane;
+  const int j0 = col0 + 8 * cg, n = min(8, cols - j0);
   const float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
-  float x0[32], x1[32];
-  float cm0 = 0.0f, cm1 = 0.0f;
+  const bool vec = (cols & 7) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.codes[b]) & 3u) | (reinterpret_cast<uintptr_t>(mt) & 15u)) == 0;
+  float x[8][8];
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const int r = w + 4 * s, i = row0 + r;
-    float v0 = 0.0f, v1 = 0.0f;
-    if (i < rows && j < cols) {
-      const int64_t e = static_cast<int64_t>(i) * cols + j;
-      v0 = mt[e] - tile[r * kRL + 2 * lane];
-      if (j + 1 < cols) v1 = mt[e + 1] - tile[r * kRL + 2 * lane + 1];
+  for (int s = 0; s < 8; ++s) {
+    const int r = rs + 16 * s, i = row0 + r;
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+    if (i < rows && n > 0) {
+      load8_f32(mt, static_cast<int64_t>(i) * cols + j0, 0, vec, n, v);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < n) v[c] -= tile[r * kRL + 8 * cg + c];
     }
-    x0[s] = v0;
-    x1[s] = v1;
-    cm0 = nan_max(cm0, fabsf(v0));
-    cm1 = nan_max(cm1, fabsf(v1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[s][c] = v[c];
   }
-  encode_block(x0, x1, cm0, cm1, static_cast<uint8_t*>(a.codes[b]), static_cast<float*>(a.sr[b]),
-               static_cast<float*>(a.sc[b]), rows, cols, bi, bj, cpart);
+  encode_block(x, static_cast<uint8_t*>(a.codes[b]), static_cast<float*>(a.sr[b]), static_cast<float*>(a.sc[b]), rows,
+               cols, bi, bj, vec, cpart);
 }
 
 // ---------------------------------------------------------------------------
-// CholeskyQR.  Stage 1: fp64 partial Gram matrices S_c = P~_c^T P~_c over
-// chunks of 256 rows (upper triangle, 4 x 4 register blocks, 8 rows at a
-// time through LDS).  Stage 2: the partials summed in chunk order.  Stage 3
-// (one block per matrix): S = U^T U by right-looking Cholesky on the upper
-// triangle in fp64, then U^{-1} column by column; a pivot at or below 1e-12
-// of its original diagonal (a column dependent on the earlier ones, or
-// zero) gives a zero column of U^{-1}, hence of P.
+// CholeskyQR: P = P~ U^{-1} with P~^T P~ = U^T U.  Stage 1: fp64 partial
+// Gram matrices over chunks of 256 rows (upper triangle, 4 x 4 register
+// blocks, 8 rows at a time through LDS).  Stage 2: the partials summed in
+// chunk order.  Stages 3 and 4 below: the Cholesky factor and the solve.
 // ---------------------------------------------------------------------------
 constexpr int kGramRows = 8;
 
@@ -611,7 +677,7 @@ __global__ __launch_bounds__(kGT) void gram64_kernel(CholArgs a) {
   const int npairs = nb * (nb + 1) / 2;
   const float* P = a.P + static_cast<int64_t>(b) * a.sP;
   double* out = a.spart + (static_cast<int64_t>(b) * a.nchunk + ch) * k * k;
-  const int i0 = ch * kGT, i1 = min(a.m, i0 + kGT);
+  const int i0 = ch * a.chunk, i1 = min(a.m, i0 + a.chunk);
   for (int base = 0; base < npairs; base += 4 * kGT) {
     double acc[4][16];
     int pa[4], pb[4];
@@ -685,52 +751,172 @@ __global__ __launch_bounds__(kGT) void gram_sum_kernel(CholArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGT) void chol_inv_kernel(CholArgs a) {
-  extern __shared__ double lds[];  // urow[k] | diag0[k] | dead flags (as doubles)[k]
-  const int b = blockIdx.x, k = a.k;
-  double* U = a.S + static_cast<int64_t>(b) * k * k;  // in place: upper triangle S -> U
-  double* urow = lds;
-  double* diag0 = lds + k;
-  double* dead = lds + 2 * k;
+// Stage 3, one block per matrix: blocked right-looking Cholesky S = U^T U
+// on the upper triangle (fp64, in place).  A panel of W rows (W k <= 7168
+// doubles, 56 KB of LDS) is loaded, factored row by row in LDS, written back,
+// and applied to the trailing rows in global memory.  A pivot at or below
+// 1e-12 of its original diagonal (or a non-positive diagonal) marks a dead
+// column: its row of U becomes e_j (U_jj = 1, the rest 0), so it takes
+// nothing from later columns, and the solve below zeroes its column of P.
+constexpr int kPanelElems = 7168;
+
+__global__ __launch_bounds__(kGT) void chol_panel_kernel(CholArgs a) {
+  extern __shared__ double buf[];        // W x k panel rows (columns p0.. at offset c - p0)
+  __shared__ double diag0[kMaxRankK];
+  const int b = blockIdx.x, k = a.k, W = a.panel;
+  const int lane = threadIdx.x & 63;
+  double* U = a.S + static_cast<int64_t>(b) * k * k;
+  int* dead = a.dead + static_cast<int64_t>(b) * k;
   for (int c = threadIdx.x; c < k; c += kGT) diag0[c] = U[static_cast<int64_t>(c) * k + c];
   __syncthreads();
-  for (int j = 0; j < k; ++j) {
-    const double d = U[static_cast<int64_t>(j) * k + j];
-    const bool is_dead = !(d > 1e-12 * diag0[j]) || !(diag0[j] > 0.0);
-    const double piv = is_dead ? 1.0 : sqrt(d);
-    for (int c = j + threadIdx.x; c < k; c += kGT) {
-      const double u = c == j ? piv : (is_dead ? 0.0 : U[static_cast<int64_t>(j) * k + c] / piv);
-      urow[c] = u;
-      U[static_cast<int64_t>(j) * k + c] = u;
+  for (int p0 = 0; p0 < k; p0 += W) {
+    const int pw = min(W, k - p0), wid = k - p0;
+    for (int e = threadIdx.x; e < pw * wid; e += kGT) {
+      const int r = e / wid, c = e - r * wid;
+      buf[e] = c >= r ? U[static_cast<int64_t>(p0 + r) * k + p0 + c] : 0.0;
     }
-    if (threadIdx.x == 0) dead[j] = is_dead ? 1.0 : 0.0;
     __syncthreads();
-    if (!is_dead) {
-      // S[r][c] -= U[j][r] U[j][c] for j < r <= c
-      const int t = k - j - 1;
-      for (int e = threadIdx.x; e < t * t; e += kGT) {
-        const int r = e / t, c = e - r * t;
-        if (c < r) continue;
-        const int rr = j + 1 + r, cc = j + 1 + c;
-        U[static_cast<int64_t>(rr) * k + cc] -= urow[rr] * urow[cc];
+    if (threadIdx.x < 64) {
+      // wave 0 factors the panel alone; wavefront-scope fences order its LDS
+      // accesses between the phases of a row
+      for (int jj = 0; jj < pw; ++jj) {
+        const int j = p0 + jj;
+        const double d = buf[jj * wid + jj];
+        const bool is_dead = !(diag0[j] > 0.0) || !(d > 1e-12 * diag0[j]);
+        const double piv = is_dead ? 1.0 : sqrt(d);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (int c = jj + lane; c < wid; c += 64)
+          buf[jj * wid + c] = c == jj ? piv : (is_dead ? 0.0 : buf[jj * wid + c] / piv);
+        if (lane == 0) dead[j] = is_dead ? 1 : 0;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (!is_dead) {
+          // rows jj+1.. of the panel, 8 at a time so the loads of a batch issue together
+          for (int c0 = lane; c0 < wid; c0 += 64) {
+            const double uc = buf[jj * wid + c0];
+            for (int r0 = jj + 1; r0 < pw; r0 += 8) {
+              double v[8], ur[8];
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = r0 + q;
+                const bool ok = r < pw && c0 >= r;
+                ur[q] = ok ? buf[jj * wid + r] : 0.0;
+                v[q] = ok ? buf[r * wid + c0] : 0.0;
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                const int r = r0 + q;
+                if (r < pw && c0 >= r) buf[r * wid + c0] = v[q] - ur[q] * uc;
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       }
     }
     __syncthreads();
-  }
-  // U^{-1} (upper): column c by one thread, bottom-up; fp32 output, zero for dead columns.
-  double* V = a.Vinv64 + static_cast<int64_t>(b) * k * k;  // scratch, row-major
-  float* out = a.Uinv + static_cast<int64_t>(b) * k * k;
-  for (int c = threadIdx.x; c < k; c += kGT) {
-    for (int i = c + 1; i < k; ++i) V[static_cast<int64_t>(i) * k + c] = 0.0;
-    V[static_cast<int64_t>(c) * k + c] = 1.0 / U[static_cast<int64_t>(c) * k + c];
-    for (int i = c - 1; i >= 0; --i) {
-      double s = 0.0;
-      for (int l = i + 1; l <= c; ++l) s = fma(U[static_cast<int64_t>(i) * k + l], V[static_cast<int64_t>(l) * k + c], s);
-      V[static_cast<int64_t>(i) * k + c] = -s / U[static_cast<int64_t>(i) * k + i];
+    for (int e = threadIdx.x; e < pw * wid; e += kGT) {
+      const int r = e / wid, c = e - r * wid;
+      if (c >= r) U[static_cast<int64_t>(p0 + r) * k + p0 + c] = buf[e];
     }
-    const bool zero = dead[c] != 0.0;
-    for (int i = 0; i < k; ++i)
-      out[static_cast<int64_t>(i) * k + c] = zero ? 0.0f : static_cast<float>(V[static_cast<int64_t>(i) * k + c]);
+    // trailing rows r >= p0 + pw: S[r][c] -= sum over the panel of U[j][r] U[j][c],
+    // in 4 x 4 blocks (R <= C) of the trailing upper triangle
+    const int t = k - p0 - pw, nb = (t + 3) / 4;
+    const int npairs = nb * (nb + 1) / 2;
+    for (int pidx = threadIdx.x; pidx < npairs; pidx += kGT) {
+      int R = 0, rem = pidx, len = nb;
+      while (rem >= len) {
+        rem -= len;
+        ++R;
+        --len;
+      }
+      const int C = R + rem;
+      double acc[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+      for (int jj = 0; jj < pw; ++jj) {
+        const double* row = buf + jj * wid + pw;
+        double x[4], y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[u] = 4 * R + u < t ? row[4 * R + u] : 0.0;
+          y[u] = 4 * C + u < t ? row[4 * C + u] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * R + u, c = 4 * C + v;
+          if (r < t && c < t && c >= r) U[static_cast<int64_t>(p0 + pw + r) * k + p0 + pw + c] -= acc[u][v];
+        }
+    }
+    __syncthreads();  // the trailing rows are final before the next panel loads them
+  }
+}
+
+// P = P~ U^{-1} by forward substitution along each row (P U = P~).  A block
+// of 4 waves takes 4 RPW rows; column block jb (64 columns, lane l owning
+// column j = 64 jb + l) first takes the finished columns of earlier blocks
+// (their fp64 values in LDS times rows of U read from L2), then stages U's
+// 64 x 64 diagonal block in LDS and finishes its columns one at a time, each
+// broadcast from the lane that owns it.  Dead columns are zero.  fp64
+// arithmetic, fp32 result.
+template <int RPW>
+__global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
+  extern __shared__ double lds[];  // U block 64 x 64 | rows: 4 waves x RPW x k
+  double* ub = lds;
+  const int b = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = a.k;
+  double* prow = lds + 64 * 64 + static_cast<int64_t>(w) * RPW * k;
+  const double* U = a.S + static_cast<int64_t>(b) * k * k;
+  const int* dead = a.dead + static_cast<int64_t>(b) * k;
+  const int r0 = (blockIdx.x * 4 + w) * RPW;
+  const float* Pt = a.P + static_cast<int64_t>(b) * a.sP;
+  float* Po = a.Pout + static_cast<int64_t>(b) * a.sP;
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    const int j = j0 + lane, nb = min(64, k - j0);
+    const bool in = j < k;
+    double acc[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const int r = r0 + q;
+      acc[q] = in && r < a.m ? static_cast<double>(Pt[static_cast<int64_t>(r) * k + j]) : 0.0;
+    }
+#pragma unroll 4
+    for (int l = 0; l < j0; ++l) {
+      const double u = in ? U[static_cast<int64_t>(l) * k + j] : 0.0;
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) acc[q] = fma(-prow[q * k + l], u, acc[q]);
+    }
+    __syncthreads();  // the previous U block is no longer read
+    for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
+      const int rr = e >> 6, cc = e & 63;
+      ub[rr * 64 + cc] = (rr < nb && cc < nb && cc >= rr) ? U[static_cast<int64_t>(j0 + rr) * k + j0 + cc] : 0.0;
+    }
+    __syncthreads();
+    for (int q = 0; q < nb; ++q) {
+      const int l = j0 + q;
+      const bool dl = dead[l] != 0;
+      const double diag = ub[q * 64 + q], u = ub[q * 64 + lane];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const double mine = (lane == q && !dl) ? acc[rr] / diag : 0.0;
+        const double pl = __shfl(mine, q);
+        if (lane > q) acc[rr] = fma(-pl, u, acc[rr]);
+        if (lane == q) prow[rr * k + l] = pl;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const int r = r0 + q;
+      if (in && r < a.m) Po[static_cast<int64_t>(r) * k + j] = static_cast<float>(prow[q * k + j]);
+    }
   }
 }
 
@@ -768,7 +954,10 @@ hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL(colsq_kernel, g, dim3(kGT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unit_columns_kernel, g, dim3(kGT), static_cast<size_t>(a.k) * sizeof(double), s, a);
+  hipLaunchKernelGGL(colinv_kernel, dim3(batch), dim3(kGT), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(unit_columns_kernel, g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -790,7 +979,8 @@ hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float
 }
 
 hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(recon_kernel, grid_blocks(a.rows, a.cols, batch), dim3(kGT), 0, s, a);
+  const dim3 g((a.cols + kTT - 1) / kTT, (a.rows + kRecRows - 1) / kRecRows, batch);
+  hipLaunchKernelGGL(recon_kernel, g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -799,7 +989,7 @@ hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cholqr(const CholArgs& a, int batch, hipStream_t s) {
+hipError_t launch_gram(const CholArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL(gram64_kernel, dim3(a.nchunk, batch), dim3(kGT),
                      static_cast<size_t>(kGramRows) * a.k * sizeof(double), s, a);
   hipError_t e = hipGetLastError();
@@ -807,9 +997,25 @@ hipError_t launch_cholqr(const CholArgs& a, int batch, hipStream_t s) {
   int64_t blocks = (static_cast<int64_t>(a.k) * a.k + kGT - 1) / kGT;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(gram_sum_kernel, dim3(static_cast<unsigned>(blocks), batch), dim3(kGT), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(kGT), static_cast<size_t>(3) * a.k * sizeof(double), s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chol(const CholArgs& a, int batch, hipStream_t s) {
+  CholArgs c = a;
+  c.panel = 32;
+  while (c.panel > 1 && c.panel * a.k > kPanelElems) c.panel >>= 1;
+  hipLaunchKernelGGL(chol_panel_kernel, dim3(batch), dim3(kGT), static_cast<size_t>(c.panel) * a.k * sizeof(double), s,
+                     c);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_solve(const CholArgs& a, int batch, hipStream_t s) {
+  // rows per wave: 4 while the rows' fp64 values fit beside the U block (64 KB)
+  const int rpw = a.k <= 224 ? 4 : 1;
+  const size_t lds = (64 * 64 + static_cast<size_t>(4) * rpw * a.k) * sizeof(double);  // <= 64 KB
+  const dim3 grid((a.m + 4 * rpw - 1) / (4 * rpw), batch);
+  if (rpw == 4) hipLaunchKernelGGL(row_solve_kernel<4>, grid, dim3(kGT), lds, s, a);
+  else hipLaunchKernelGGL(row_solve_kernel<1>, grid, dim3(kGT), lds, s, a);
   return hipGetLastError();
 }
 
