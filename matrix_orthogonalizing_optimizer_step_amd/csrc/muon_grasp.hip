@@ -752,17 +752,26 @@ __global__ __launch_bounds__(kGT) void gram_sum_kernel(CholArgs a) {
 }
 
 // Stage 3, one block per matrix: blocked right-looking Cholesky S = U^T U
-// on the upper triangle (fp64, in place).  A panel of W rows (W k <= 7168
-// doubles, 56 KB of LDS) is loaded, factored row by row in LDS, written back,
-// and applied to the trailing rows in global memory.  A pivot at or below
-// 1e-12 of its original diagonal (or a non-positive diagonal) marks a dead
-// column: its row of U becomes e_j (U_jj = 1, the rest 0), so it takes
-// nothing from later columns, and the solve below zeroes its column of P.
+// on the upper triangle (fp64, in place), panels of W <= 32 rows (W k <= 7168
+// doubles, 56 KB of LDS).  Per panel: wave 0 factors the W x W diagonal block
+// in registers (lane c holds column c; row j of U is broadcast lane by lane),
+// all waves solve for the rest of the panel rows (U11^T U12 = S12, a column
+// per thread, U11 read as LDS broadcasts), and all waves apply the panel to
+// the trailing rows in global memory.  A pivot at or below 1e-12 of its
+// original diagonal (or a non-positive diagonal) marks a dead column: its row
+// of U becomes e_j (U_jj = 1, the rest 0), so it takes nothing from later
+// columns, and the solve below zeroes its column of P.
 constexpr int kPanelElems = 7168;
 
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const int2 v = __builtin_bit_cast(int2, x);
+  return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(v.x, l), __builtin_amdgcn_readlane(v.y, l)));
+}
+
 __global__ __launch_bounds__(kGT) void chol_panel_kernel(CholArgs a) {
-  extern __shared__ double buf[];        // W x k panel rows (columns p0.. at offset c - p0)
+  extern __shared__ double buf[];        // W x (k - p0) panel rows, column c - p0
   __shared__ double diag0[kMaxRankK];
+  __shared__ int pdead[32];
   const int b = blockIdx.x, k = a.k, W = a.panel;
   const int lane = threadIdx.x & 63;
   double* U = a.S + static_cast<int64_t>(b) * k * k;
@@ -776,49 +785,62 @@ __global__ __launch_bounds__(kGT) void chol_panel_kernel(CholArgs a) {
       buf[e] = c >= r ? U[static_cast<int64_t>(p0 + r) * k + p0 + c] : 0.0;
     }
     __syncthreads();
+    // 1. the pw x pw diagonal block by wave 0 in registers: lane c holds column c
     if (threadIdx.x < 64) {
-      // wave 0 factors the panel alone; wavefront-scope fences order its LDS
-      // accesses between the phases of a row
-      for (int jj = 0; jj < pw; ++jj) {
-        const int j = p0 + jj;
-        const double d = buf[jj * wid + jj];
-        const bool is_dead = !(diag0[j] > 0.0) || !(d > 1e-12 * diag0[j]);
-        const double piv = is_dead ? 1.0 : sqrt(d);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        for (int c = jj + lane; c < wid; c += 64)
-          buf[jj * wid + c] = c == jj ? piv : (is_dead ? 0.0 : buf[jj * wid + c] / piv);
-        if (lane == 0) dead[j] = is_dead ? 1 : 0;
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        if (!is_dead) {
-          // rows jj+1.. of the panel, 8 at a time so the loads of a batch issue together
-          for (int c0 = lane; c0 < wid; c0 += 64) {
-            const double uc = buf[jj * wid + c0];
-            for (int r0 = jj + 1; r0 < pw; r0 += 8) {
-              double v[8], ur[8];
+      const int c = lane;
+      double d[32];
 #pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const int r = r0 + q;
-                const bool ok = r < pw && c0 >= r;
-                ur[q] = ok ? buf[jj * wid + r] : 0.0;
-                v[q] = ok ? buf[r * wid + c0] : 0.0;
-              }
+      for (int r = 0; r < 32; ++r) d[r] = (c < pw && r <= c) ? buf[r * wid + c] : 0.0;
 #pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const int r = r0 + q;
-                if (r < pw && c0 >= r) buf[r * wid + c0] = v[q] - ur[q] * uc;
+      for (int j = 0; j < 32; ++j) {
+        if (j < pw) {
+          const double djj = readlane_f64(d[j], j);
+          const bool is_dead = !(diag0[p0 + j] > 0.0) || !(djj > 1e-12 * diag0[p0 + j]);
+          const double piv = is_dead ? 1.0 : sqrt(djj);
+          if (c == j) d[j] = piv;
+          else if (c > j) d[j] = is_dead ? 0.0 : d[j] / piv;
+          if (lane == 0) pdead[j] = is_dead ? 1 : 0;
+          if (!is_dead) {
+#pragma unroll
+            for (int r = j + 1; r < 32; ++r) {
+              if (r < pw) {
+                const double ujr = readlane_f64(d[j], r);
+                if (c >= r) d[r] = fma(-ujr, d[j], d[r]);
               }
             }
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       }
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        if (c < pw && r <= c) buf[r * wid + c] = d[r];
     }
+    __syncthreads();
+    // 2. the panel rows right of the block: U11^T U12 = S12, column by column
+    for (int cc = pw + threadIdx.x; cc < wid; cc += kGT) {
+      double x[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) x[r] = r < pw ? buf[r * wid + cc] : 0.0;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        if (r < pw) {
+          double acc = x[r];
+#pragma unroll
+          for (int l = 0; l < r; ++l) acc = fma(-buf[l * wid + r], x[l], acc);
+          x[r] = pdead[r] ? 0.0 : acc / buf[r * wid + r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        if (r < pw) buf[r * wid + cc] = x[r];
+    }
+    if (threadIdx.x < pw) dead[p0 + threadIdx.x] = pdead[threadIdx.x];
     __syncthreads();
     for (int e = threadIdx.x; e < pw * wid; e += kGT) {
       const int r = e / wid, c = e - r * wid;
       if (c >= r) U[static_cast<int64_t>(p0 + r) * k + p0 + c] = buf[e];
     }
-    // trailing rows r >= p0 + pw: S[r][c] -= sum over the panel of U[j][r] U[j][c],
+    // 3. trailing rows r >= p0 + pw: S[r][c] -= sum over the panel of U[j][r] U[j][c],
     // in 4 x 4 blocks (R <= C) of the trailing upper triangle
     const int t = k - p0 - pw, nb = (t + 3) / 4;
     const int npairs = nb * (nb + 1) / 2;
