@@ -274,3 +274,25 @@ def test_grasp_zero_column_of_R():
     assert np.all(host(gs.P_codes[0])[:, 3] == 0) and np.all(st1["P_codes"][:, 3] == 0)
     assert np.all(host(gs.R_codes[0])[:, 3] == 0)
     compare_state(gs, st1, det, rows, cols, k)
+
+
+@pytest.mark.parametrize("rows,cols,k", [(3584, 18944, 224), (3584, 512, 32)], ids=["qwen-mlp", "qwen-kv"])
+def test_grasp_state_full_size(rows, cols, k):
+    """Full-size matrices of the Qwen2.5-7B layer set at rank / 16, from a
+    random state: M_t to fp32 rounding and the new state as in the smaller
+    cases (the oracle computes the momentum and the state only; its fp64
+    Newton-Schulz at this size would take minutes, and O is covered by the
+    step tests above and by the full-size Newton-Schulz tests)."""
+    st = random_state(rows // 7 + k, rows, cols, k)
+    gs = gpu_state_from(st, rows, cols, k)
+    G = seeded(40, rows, cols, 1e-3)
+    Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)]
+    mu.grasp_step([dev(seeded(41, rows, cols))], gs, [dev(G)], MU, LR, 0.0, "gram", M_out=Mt)
+    torch.cuda.synchronize()
+    Mg = host(Mt[0])
+    M1 = go.momentum(st, G, MU)
+    err = np.abs(Mg.astype(np.float64) - M1)
+    assert np.all(err <= 1.2e-7 * np.abs(M1) + 1e-12 * np.abs(M1).max())
+    st1, det = go.compress(M1, st)
+    f = compare_state(gs, st1, det, rows, cols, k)
+    print(f"{rows}x{cols} k={k}: residual codes off by one {f:.2e}")
