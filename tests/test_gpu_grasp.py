@@ -296,3 +296,44 @@ def test_grasp_state_full_size(rows, cols, k):
     st1, det = go.compress(M1, st)
     f = compare_state(gs, st1, det, rows, cols, k)
     print(f"{rows}x{cols} k={k}: residual codes off by one {f:.2e}")
+
+
+@pytest.mark.parametrize("k", [0, 12])
+def test_grasp_step_in_a_hip_graph(k):
+    """The low-bit step also launches kernels only (no memsets or copies), so
+    it can be captured once and replayed: each replay, with the program's own
+    eager work and synchronisations between replays, advances the state
+    exactly as an eager step does (bit for bit: every reduction has a fixed
+    order)."""
+    rows, cols = 320, 448
+    R0 = [dev(seeded(50, cols, k))] if k else None
+    sg = mu.GraspState(1, rows, cols, k, DEV, R_init=R0)
+    se = mu.GraspState(1, rows, cols, k, DEV, R_init=R0)
+    Wg = [dev(seeded(51, rows, cols))]
+    We = [Wg[0].clone()]
+    G = [dev(seeded(52, rows, cols, 0.01))]
+    ws = torch.empty(mu.grasp_workspace_size(1, rows, cols, k, "gram"), dtype=torch.uint8, device=DEV)
+    names = ["res_codes", "res_row_scales", "res_col_scales"] + (["P_codes", "P_scales", "R_codes", "R_scales"] if k else [])
+
+    def same():
+        torch.cuda.synchronize()
+        assert torch.equal(Wg[0], We[0])
+        for n in names:
+            assert torch.equal(getattr(sg, n)[0], getattr(se, n)[0]), n
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture (caches the pointer arrays)
+        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    mu.grasp_step(We, se, G, MU, LR, 0.0, "gram")
+    same()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws)
+    for rep in range(3):
+        g.replay()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        mu.grasp_step(We, se, G, MU, LR, 0.0, "gram")
+        assert float(junk) == float(junk)
+        same()
