@@ -475,10 +475,12 @@ def time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev):
     variant = args.variant
     main = torch.cuda.current_stream()
     out = {}
-    for label in ("k0", "rank_over_16"):
+    for label in ("k0", "rank_over_16", "rank_over_16_aux_stream"):
+        aux = label.endswith("aux_stream")
         for gi, x in enumerate(groups):
             g = x["g"]
             k = 0 if label == "k0" else max(1, min(g.rows, g.cols) // 16)
+            x["aux"] = torch.cuda.Stream(device=dev) if aux else None
             R0 = [syn.random_matrix(100 + gi * 64 + i, g.cols, k).to(dev) for i in range(g.count)] if k else None
             x["gs"] = mu.GraspState(g.count, g.rows, g.cols, k, dev, R_init=R0)
             x["gws"] = torch.empty(mu.grasp_workspace_size(g.count, g.rows, g.cols, k, variant, cfg_for(variant)),
@@ -493,7 +495,8 @@ def time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev):
                 if not serial:
                     x["stream"].wait_event(ev)
                 mu.grasp_step(x["W"], x["gs"], x["G"], 0.95, 0.02, 0.0, variant, cfg_for(variant),
-                              workspace=x["gws"], stream=main if serial else x["stream"])
+                              workspace=x["gws"], stream=main if serial else x["stream"],
+                              aux_stream=None if serial else x["aux"])
             if not serial:
                 for x in groups:
                     done = torch.cuda.Event()
@@ -539,7 +542,8 @@ def time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev):
             del x["gs"], x["gws"]
     out["note"] = ("muon_grasp_step on the same workload and variant; M_t is rebuilt from the stored state, "
                    "orthogonalised, and stored again; state_bytes counts codes and scales (fp32 momentum: "
-                   f"{4 * wl.elements} bytes)")
+                   f"{4 * wl.elements} bytes); *_aux_stream: the state update of each group on a second stream "
+                   "beside its Newton-Schulz (the serial per-kernel pass uses one stream)")
     return out
 
 

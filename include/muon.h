@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 #define MUON_MAX_T 16
 #define MUON_MAX_DIM (1 << 20)
 #define MUON_GRASP_MAX_K 1024
@@ -248,6 +248,13 @@ size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_v
  *   G        gradients (F32, BF16 or F16).  W: F32 or BF16, updated in place.
  *   O_out    NULL or outputs for O (F32 or BF16).
  *   M_out    NULL or F32 outputs that receive M_t (for checking).
+ *   aux_stream  NULL, or a second stream of the caller's on the same device:
+ *            with k > 0 the update of the state (everything after M_t: the
+ *            power iteration, the codes of P and R, the residual) then runs
+ *            there, beside Newton-Schulz on `stream`, from an event recorded
+ *            on `stream`; the call ends by making `stream` wait for it, so the
+ *            whole step is complete when `stream` passes the call.  Other work
+ *            on aux_stream must not touch the state or the workspace meanwhile.
  * The products with fp32 operands (M_t Q, M_t^T P, P U^{-1}, P R^T) run on
  * the bf16 MFMA with each operand split into two bf16 parts (about 16
  * significant bits per product); the Gram matrix and its Cholesky factor are
@@ -260,7 +267,7 @@ muon_status muon_grasp_step(int batch, int rows, int cols, int k,
                             float mu, float lr, float weight_decay, float update_scale,
                             muon_ns_variant variant, const muon_ns_config *cfg,
                             void *const *O_out, muon_dtype o_dtype, void *const *M_out,
-                            void *workspace, size_t ws_bytes, void *stream);
+                            void *workspace, size_t ws_bytes, void *stream, void *aux_stream);
 
 /*
  * The two codes on their own ([GRASP] key design 2, training strategy), with

@@ -92,7 +92,7 @@ def load_library():
     lib.muon_grasp_workspace_size.restype = sz
     lib.muon_grasp_step.argtypes = [i32, i32, i32, i32, vp, i32, ctypes.POINTER(_GraspState), vp, i32,
                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, i32, cfgp,
-                                    vp, i32, vp, vp, sz, vp]
+                                    vp, i32, vp, vp, sz, vp, vp]
     lib.muon_grasp_step.restype = i32
     for name in ("muon_grid_quantize", "muon_grid_dequantize"):
         getattr(lib, name).argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
@@ -414,8 +414,10 @@ def grasp_workspace_size(batch: int, rows: int, cols: int, k: int, variant="stan
 
 def grasp_step(W, state: GraspState, G, mu: float, lr: float, weight_decay: float = 0.0, variant="standard",
                cfg: Optional[NSConfig] = None, O_out=None, M_out=None, workspace=None, stream=None,
-               update_scale: float = 1.0):
-    """One Muon step whose momentum lives in ``state`` (updated in place with W)."""
+               update_scale: float = 1.0, aux_stream=None):
+    """One Muon step whose momentum lives in ``state`` (updated in place with W).
+    ``aux_stream``: a second stream on which the state update runs beside
+    Newton-Schulz (joined back into ``stream`` at the end of the call)."""
     lib = load_library()
     v = _variant(variant)
     rows, cols, wdt = _batch(W, "W")
@@ -439,5 +441,6 @@ def grasp_step(W, state: GraspState, G, mu: float, lr: float, weight_decay: floa
                               float(update_scale), v, ctypes.byref(c),
                               po.data_ptr() if po is not None else None, odt,
                               pm.data_ptr() if pm is not None else None,
-                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream),
+                              _stream(aux_stream) if aux_stream is not None else None)
     _check(st_)

@@ -689,7 +689,7 @@ bool grasp_state_ok(const muon_grasp_state* st, int k) {
 // (pointer table at lay.ptrs) for the Newton-Schulz part.
 muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_grasp_state* st, const void* const* G,
                             int g_dtype, double mu, void* const* M_out, char* ws, const GraspLayout& lay,
-                            hipStream_t s) {
+                            hipStream_t s, hipStream_t s2, hipEvent_t* join) {
   const double elems = static_cast<double>(rows) * cols * batch;
   const double gsz = g_dtype == kF32 ? 4.0 : 2.0;
   float* mt = reinterpret_cast<float*>(ws + lay.mt);
@@ -736,6 +736,16 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     const double bytes = elems * (0.5 + gsz + 4.0 + (M_out != nullptr ? 4.0 : 0.0)) + (rows + cols) * kd * batch;
     MUON_LAUNCH(traced(s, "recon_kernel", "grasp_momentum", 2.0 * elems * kd, bytes,
                        [&] { return launch_recon(a, batch, s); }));
+  }
+  // The rest reads M_t and the old R only: with a second stream it runs there,
+  // beside Newton-Schulz on the call's stream, and joins back at the end.
+  if (s2 != s) {
+    hipEvent_t fork = nullptr;
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return MUON_ERR_HIP;
+    const bool ok = hipEventRecord(fork, s) == hipSuccess && hipStreamWaitEvent(s2, fork, 0) == hipSuccess;
+    (void)hipEventDestroy(fork);
+    if (!ok) return MUON_ERR_HIP;
+    s = s2;
   }
   // 2. Q = unit columns of deq(R_{t-1})
   float* Q = reinterpret_cast<float*>(ws + lay.q);
@@ -869,6 +879,10 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
                        elems * 4.5 + (rows + cols) * kd * 4.0 * batch,
                        [&] { return launch_residual(a, batch, s); }));
   }
+  if (join != nullptr && s == s2) {
+    if (hipEventCreateWithFlags(join, hipEventDisableTiming) != hipSuccess) return MUON_ERR_HIP;
+    if (hipEventRecord(*join, s2) != hipSuccess) return MUON_ERR_HIP;
+  }
   return MUON_OK;
 }
 
@@ -876,7 +890,7 @@ muon_status grasp_step(int batch, int rows, int cols, int k, void* const* W, muo
                        const muon_grasp_state* state, const void* const* G, muon_dtype g_dtype, float mu, float lr,
                        float weight_decay, float update_scale, muon_ns_variant variant, const muon_ns_config* cfg,
                        void* const* O_out, muon_dtype o_dtype, void* const* M_out, void* workspace,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, void* aux_stream) {
   if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
   Config c;
   muon_status st = make_config(cfg, variant, &c);
@@ -896,12 +910,21 @@ muon_status grasp_step(int batch, int rows, int cols, int k, void* const* W, muo
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  st = run_grasp_state(batch, rows, cols, k, state, G, g_dtype, static_cast<double>(mu), M_out, ws, lay, s);
-  if (st != MUON_OK) return st;
-  st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(ws + lay.ptrs), kF32, nullptr, nullptr, 0.0, s);
-  if (st != MUON_OK) return st;
-  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
-  return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+  hipStream_t s2 = aux_stream != nullptr && k > 0 ? static_cast<hipStream_t>(aux_stream) : s;
+  hipEvent_t join = nullptr;
+  st = run_grasp_state(batch, rows, cols, k, state, G, g_dtype, static_cast<double>(mu), M_out, ws, lay, s, s2,
+                       s2 != s ? &join : nullptr);
+  if (st == MUON_OK)
+    st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(ws + lay.ptrs), kF32, nullptr, nullptr, 0.0, s);
+  if (st == MUON_OK) {
+    Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
+    st = variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+  }
+  if (join != nullptr) {  // the call ends on `stream` with the state update done
+    if (hipStreamWaitEvent(s, join, 0) != hipSuccess && st == MUON_OK) st = MUON_ERR_HIP;
+    (void)hipEventDestroy(join);
+  }
+  return st;
 }
 
 muon_status grid_codec(int mode, int batch, int rows, int cols, const void* const* X, void* const* codes,
@@ -1027,9 +1050,9 @@ muon_status muon_grasp_step(int batch, int rows, int cols, int k, void* const* W
                             const muon_grasp_state* state, const void* const* G, muon_dtype g_dtype, float mu,
                             float lr, float weight_decay, float update_scale, muon_ns_variant variant,
                             const muon_ns_config* cfg, void* const* O_out, muon_dtype o_dtype, void* const* M_out,
-                            void* workspace, size_t ws_bytes, void* stream) {
+                            void* workspace, size_t ws_bytes, void* stream, void* aux_stream) {
   return grasp_step(batch, rows, cols, k, W, w_dtype, state, G, g_dtype, mu, lr, weight_decay, update_scale, variant,
-                    cfg, O_out, o_dtype, M_out, workspace, ws_bytes, stream);
+                    cfg, O_out, o_dtype, M_out, workspace, ws_bytes, stream, aux_stream);
 }
 
 muon_status muon_grid_quantize(int batch, int rows, int cols, const void* const* X, void* const* codes,

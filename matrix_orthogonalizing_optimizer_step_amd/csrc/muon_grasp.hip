@@ -363,9 +363,10 @@ __device__ __forceinline__ void store_split(const TileRegs& r, uint16_t* hi, uin
   }
 }
 
-// int8 codes (k contiguous) -> registers (16 per thread) -> LDS as exact bf16.
+// int8 codes (k contiguous) -> registers (16 bytes per thread, packed) -> LDS
+// as exact bf16.
 struct CodeRegs {
-  int v[16];
+  uint4 v;
 };
 
 __device__ __forceinline__ void load_i8(const int8_t* base, int64_t s_row, int row0, int k0, int nrows, int K,
@@ -374,22 +375,26 @@ __device__ __forceinline__ void load_i8(const int8_t* base, int64_t s_row, int r
   const int row = row0 + rr, k = k0 + kk;
   const int8_t* src = base + static_cast<int64_t>(row) * s_row + k;
   if (row < nrows && k + 15 < K && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-    const uint4 x = *reinterpret_cast<const uint4*>(src);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int q = 0; q < 16; ++q) r.v[q] = static_cast<int8_t>((w[q >> 2] >> (8 * (q & 3))) & 0xffu);
+    r.v = *reinterpret_cast<const uint4*>(src);
   } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 16; ++q) r.v[q] = (row < nrows && k + q < K) ? src[q] : 0;
+    for (int q = 0; q < 16; ++q)
+      if (row < nrows && k + q < K) w[q >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(src[q])) << (8 * (q & 3));
+    r.v = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 __device__ __forceinline__ void store_i8(const CodeRegs& r, uint16_t* hi) {
   const int rr = threadIdx.x >> 1, kk = (threadIdx.x & 1) * 16;
+  const uint32_t in[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
   uint32_t w[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    w[q] = f32x2_to_bf16x2(static_cast<float>(r.v[2 * q]), static_cast<float>(r.v[2 * q + 1]));
+  for (int q = 0; q < 8; ++q) {
+    const int lo = static_cast<int8_t>((in[q >> 1] >> (16 * (q & 1))) & 0xffu);
+    const int hi8 = static_cast<int8_t>((in[q >> 1] >> (16 * (q & 1) + 8)) & 0xffu);
+    w[q] = f32x2_to_bf16x2(static_cast<float>(lo), static_cast<float>(hi8));
+  }
   *reinterpret_cast<uint4*>(hi + rr * kTL + kk) = make_uint4(w[0], w[1], w[2], w[3]);
   *reinterpret_cast<uint4*>(hi + rr * kTL + kk + 8) = make_uint4(w[4], w[5], w[6], w[7]);
 }
@@ -520,8 +525,11 @@ __global__ __launch_bounds__(kGT) void sum_pieces_kernel(const float* part, int 
 // ---------------------------------------------------------------------------
 constexpr int kRecRows = 64;
 
-__global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
-  __shared__ __align__(16) uint16_t smem[(kRecRows + kTT) * kTL];
+__global__ __launch_bounds__(kGT, 2) void recon_kernel(ReconArgs a) {
+  // LDS: the operand staging during the products, then the fp64 product tile
+  __shared__ __align__(16) double tile[kRecRows * kTT];
+  static_assert(sizeof(double) * kRecRows * kTT >= sizeof(uint16_t) * (kRecRows + kTT) * kTL, "staging fits");
+  uint16_t* smem = reinterpret_cast<uint16_t*>(tile);
   const int b = blockIdx.z, bj = blockIdx.x;
   const int row0 = blockIdx.y * kRecRows, col0 = bj * kTT, bi = row0 / kGB;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -581,6 +589,18 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
       }
     }
   }
+  // the product tile into LDS (the last loop iteration ended with a barrier)
+#pragma unroll
+  for (int y = 0; y < 2; ++y)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      tile[(wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kTT + wc + 32 * y + (lane & 31)] = pr[y][v];
+  __syncthreads();
+  // epilogue in the grid-code layout: thread t holds columns col0 + 8 (t % 16) .. + 7
+  // of rows row0 + t / 16 + 16 s (s < 4), with vector loads and stores where aligned
+  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int j0 = col0 + 8 * cg, n = min(8, a.cols - j0);
+  if (n <= 0) return;  // no barrier follows
   const uint8_t* codes = static_cast<const uint8_t*>(a.res_codes[b]);
   const float* sr = static_cast<const float*>(a.res_sr[b]);
   const float* sc = static_cast<const float*>(a.res_sc[b]);
@@ -588,25 +608,36 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   const int64_t cb = (a.cols + 1) / 2;
   float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
   float* Y = a.Y != nullptr ? static_cast<float*>(a.Y[b]) : nullptr;
+  uintptr_t mis = (reinterpret_cast<uintptr_t>(codes) & 3u) |
+                  ((reinterpret_cast<uintptr_t>(a.G[b]) | reinterpret_cast<uintptr_t>(mt)) & 15u);
+  if (Y != nullptr) mis |= reinterpret_cast<uintptr_t>(Y) & 15u;
+  const bool vec = (a.cols & 7) == 0 && mis == 0;
+  float cs[8];
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int col = col0 + wc + 32 * y + (lane & 31);
-    if (col >= a.cols) continue;
-    const float cs = sc[static_cast<int64_t>(bi) * a.cols + col];
+  for (int c = 0; c < 8; ++c) cs[c] = c < n ? sc[static_cast<int64_t>(bi) * a.cols + j0 + c] : 0.0f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = row0 + wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row >= a.rows) continue;
-      const int64_t e = static_cast<int64_t>(row) * a.cols + col;
-      const uint32_t byte = codes[static_cast<int64_t>(row) * cb + (col >> 1)];
-      const int q = sext4((col & 1) ? (byte >> 4) : (byte & 15u));
-      const double res =
-          static_cast<double>(q) * static_cast<double>(nan_min(sr[static_cast<int64_t>(row) * nbc + bj], cs)) * kInv7;
-      const double g = load_as_f32(a.G[b], e, a.g_dtype);
-      const float m = static_cast<float>(fma(a.mu, res + pr[y][v], g));
-      mt[e] = m;
-      if (Y != nullptr) Y[e] = m;
+  for (int s = 0; s < kRecRows / 16; ++s) {
+    const int r = rs + 16 * s, i = row0 + r;
+    if (i >= a.rows) break;
+    const float rsc = sr[static_cast<int64_t>(i) * nbc + bj];
+    const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
+    uint32_t word = 0;
+    if (vec) {
+      word = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+      for (int q = 0; 2 * q < n; ++q) word |= static_cast<uint32_t>(src[q]) << (8 * q);
     }
+    const int64_t e = static_cast<int64_t>(i) * a.cols + j0;
+    float g[8], m[8];
+    load8_f32(a.G[b], e, a.g_dtype, vec, n, g);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int q = sext4((word >> (4 * c)) & 15u);
+      const double res = static_cast<double>(q) * static_cast<double>(nan_min(rsc, cs[c])) * kInv7;
+      m[c] = static_cast<float>(fma(a.mu, res + tile[r * kTT + 8 * cg + c], static_cast<double>(g[c])));
+    }
+    store8_f32(mt + e, vec, n, m);
+    if (Y != nullptr) store8_f32(Y + e, vec, n, m);
   }
 }
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert mu.abi_version() == 3
+    assert mu.abi_version() == 4
 
 
 def test_status_strings():
@@ -145,7 +145,7 @@ def test_invalid_grasp_calls():
 
     def call(k=2, st=full, W=1, wdt=0, G=2, gdt=1, mu_=0.9, s=1.0, v=0, odt=0, O=None, wsb=ws, w=256):
         return lib.muon_grasp_step(1, 8, 8, k, W, wdt, ctypes.byref(st) if st is not None else None, G, gdt,
-                                   mu_, 0.1, 0.0, s, v, None, O, odt, None, w, wsb, None)
+                                   mu_, 0.1, 0.0, s, v, None, O, odt, None, w, wsb, None, None)
 
     assert call(st=None) == 1
     assert call(st=bd._GraspState(16, 16, 16, None, None, None, None)) == 1   # k > 0 needs P and R

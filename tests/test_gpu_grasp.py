@@ -170,12 +170,13 @@ def compare_state(gs, st, det, rows, cols, k):
     return f_res
 
 
-def run_both(W, st_or, gs, G, k, variant, M_out=True):
+def run_both(W, st_or, gs, G, k, variant, M_out=True, aux=False):
     rows, cols = G.shape
     Wd, Gd = [dev(W)], [dev(G)]
     O = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)]
     Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)] if M_out else None
-    mu.grasp_step(Wd, gs, Gd, MU, LR, 0.0, variant, O_out=O, M_out=Mt)
+    mu.grasp_step(Wd, gs, Gd, MU, LR, 0.0, variant, O_out=O, M_out=Mt,
+                  aux_stream=torch.cuda.Stream() if aux else None)
     torch.cuda.synchronize()
     W1, st1, O1, M1, det = go.grasp_step(W.astype(np.float64), st_or, G, MU, LR, 0.0, variant)
     return (host(Wd[0]), host(O[0]), host(Mt[0]) if M_out else None), (W1, st1, O1, M1, det)
@@ -200,6 +201,7 @@ def test_grasp_step_without_subspace_bitexact(rows, cols):
         assert orc.relative_frobenius(Wg - W, W1 - W) < 2e-2 + 1e-4
 
 
+@pytest.mark.parametrize("aux", [False, True], ids=["one-stream", "aux-stream"])
 @pytest.mark.parametrize("rows,cols,k,variant", [
     (300, 520, 20, "standard"),
     (520, 300, 20, "gram"),
@@ -208,14 +210,15 @@ def test_grasp_step_without_subspace_bitexact(rows, cols):
     (4096, 256, 16, "standard"),  # M_t^T P split along k
     (200, 150, 1, "standard"),
 ])
-def test_grasp_step_from_a_random_state(rows, cols, k, variant):
+def test_grasp_step_from_a_random_state(rows, cols, k, variant, aux):
     """One step from an arbitrary state: M_t to fp32 rounding, the new state
-    up to near-tie codes, O and W at the 16-bit tolerance."""
+    up to near-tie codes, O and W at the 16-bit tolerance; with an aux stream
+    the state update runs beside Newton-Schulz and must give the same."""
     st = random_state(rows + cols + k, rows, cols, k)
     gs = gpu_state_from(st, rows, cols, k)
     W = seeded(2, rows, cols)
     G = seeded(3, rows, cols, 0.01)
-    (Wg, Og, Mg), (W1, st1, O1, M1, det) = run_both(W, st, gs, G, k, variant)
+    (Wg, Og, Mg), (W1, st1, O1, M1, det) = run_both(W, st, gs, G, k, variant, aux=aux)
     err = np.abs(Mg.astype(np.float64) - M1)
     assert np.all(err <= 1.2e-7 * np.abs(M1) + 1e-12 * np.abs(M1).max())
     f = compare_state(gs, st1, det, rows, cols, k)
@@ -298,8 +301,9 @@ def test_grasp_state_full_size(rows, cols, k):
     print(f"{rows}x{cols} k={k}: residual codes off by one {f:.2e}")
 
 
+@pytest.mark.parametrize("aux", [False, True], ids=["one-stream", "aux-stream"])
 @pytest.mark.parametrize("k", [0, 12])
-def test_grasp_step_in_a_hip_graph(k):
+def test_grasp_step_in_a_hip_graph(k, aux):
     """The low-bit step also launches kernels only (no memsets or copies), so
     it can be captured once and replayed: each replay, with the program's own
     eager work and synchronisations between replays, advances the state
@@ -321,16 +325,17 @@ def test_grasp_step_in_a_hip_graph(k):
         for n in names:
             assert torch.equal(getattr(sg, n)[0], getattr(se, n)[0]), n
 
+    ax = torch.cuda.Stream() if aux else None  # captured too: it joins the capture through the fork event
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up outside the capture (caches the pointer arrays)
-        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws)
+        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws, aux_stream=ax)
     torch.cuda.current_stream().wait_stream(side)
     mu.grasp_step(We, se, G, MU, LR, 0.0, "gram")
     same()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws)
+        mu.grasp_step(Wg, sg, G, MU, LR, 0.0, "gram", workspace=ws, aux_stream=ax)
     for rep in range(3):
         g.replay()
         junk = torch.randn(1 << 20, device=DEV).sum()
