@@ -342,3 +342,38 @@ def test_grasp_step_in_a_hip_graph(k, aux):
         mu.grasp_step(We, se, G, MU, LR, 0.0, "gram")
         assert float(junk) == float(junk)
         same()
+
+
+@pytest.mark.parametrize("rows,cols,k", [(300, 520, 20), (2048, 256, 16)], ids=["300x520-k20", "2048x256-k16"])
+def test_grasp_step_batched(rows, cols, k):
+    """A batch of 3 matrices in one call, each with its own random state:
+    every matrix matches the oracle on its own (per-matrix pointers, strided
+    workspace slices, split products over the batch)."""
+    n = 3
+    sts = [random_state(1000 + 37 * i + k, rows, cols, k) for i in range(n)]
+    gs = mu.GraspState(n, rows, cols, 0, DEV)
+    gs.k = k
+    gs.res_codes = [dev(go.pack_nibbles(st["res_codes"])) for st in sts]
+    gs.res_row_scales = [dev(st["res_sr"]) for st in sts]
+    gs.res_col_scales = [dev(st["res_sc"]) for st in sts]
+    gs.P_codes = [dev(st["P_codes"]) for st in sts]
+    gs.P_scales = [dev(st["P_scales"]) for st in sts]
+    gs.R_codes = [dev(st["R_codes"]) for st in sts]
+    gs.R_scales = [dev(st["R_scales"]) for st in sts]
+    Ws = [seeded(60 + i, rows, cols) for i in range(n)]
+    Gs = [seeded(70 + i, rows, cols, 0.01) for i in range(n)]
+    Wd = [dev(w) for w in Ws]
+    O = [torch.empty(rows, cols, dtype=torch.float32, device=DEV) for _ in range(n)]
+    Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV) for _ in range(n)]
+    mu.grasp_step(Wd, gs, [dev(g) for g in Gs], MU, LR, 0.0, "gram", O_out=O, M_out=Mt)
+    torch.cuda.synchronize()
+    for i in range(n):
+        W1, st1, O1, M1, det = go.grasp_step(Ws[i].astype(np.float64), sts[i], Gs[i], MU, LR, 0.0, "gram")
+        Mg = host(Mt[i])
+        assert np.all(np.abs(Mg.astype(np.float64) - M1) <= 1.2e-7 * np.abs(M1) + 1e-12 * np.abs(M1).max()), i
+        one = mu.GraspState(1, rows, cols, 0, DEV)
+        one.k = k
+        for name in ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes", "R_scales"):
+            setattr(one, name, [getattr(gs, name)[i]])
+        compare_state(one, st1, det, rows, cols, k)
+        assert orc.relative_frobenius(host(O[i]), O1) < 2e-2, i
