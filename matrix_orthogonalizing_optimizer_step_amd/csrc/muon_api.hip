@@ -626,6 +626,23 @@ constexpr int kGraspMaxPieces = 8;  // k pieces of the two long power-iteration 
 
 int nblk(int x, int b) { return (x + b - 1) / b; }
 
+// k pieces for a product with `tiles` output tiles and K of length `K`: enough
+// blocks for about two rounds on the device, each piece at least 256 long.
+// Planned for the 256 compute units of the MI355X so that the workspace size
+// depends on the shapes only.
+constexpr int kGraspPlanCUs = 256;
+
+void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
+  const int cu = kGraspPlanCUs;
+  int pcs = tiles >= 2 * cu ? 1 : static_cast<int>((2 * cu + tiles - 1) / tiles);
+  pcs = pcs < kGraspMaxPieces ? pcs : kGraspMaxPieces;
+  const int maxp = K / 256 > 1 ? K / 256 : 1;
+  pcs = pcs < maxp ? pcs : maxp;
+  int chunk = static_cast<int>(round_up(static_cast<size_t>((K + pcs - 1) / pcs), 32));
+  *kchunk = chunk;
+  *pieces = (K + chunk - 1) / chunk;
+}
+
 // Workspace after the Newton-Schulz part: M_t and its pointer table, then
 // (k > 0) the power-iteration buffers.
 struct GraspLayout {
@@ -651,30 +668,20 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->q = take(B * c * kk * 4);
     g->colpart = take(B * g->nch_n * kk * 8);
     g->colinv = take(B * kk * 8);
-    g->ppart = take(B * kGraspMaxPieces * r * kk * 4);
+    int pcs = 1, chunk = 0;
+    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &pcs, &chunk);
+    g->ppart = take(pcs > 1 ? B * pcs * r * kk * 4 : 0);
     g->ptil = take(B * r * kk * 4);
     g->spart = take(B * g->nch_m * kk * kk * 8);
     g->S = take(B * kk * kk * 8);
     g->dead = take(B * kk * 4);
     g->P = take(B * r * kk * 4);
-    g->rpart = take(B * kGraspMaxPieces * c * kk * 4);
+    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &pcs, &chunk);
+    g->rpart = take(pcs > 1 ? B * pcs * c * kk * 4 : 0);
     g->R = take(B * c * kk * 4);
   }
   g->total = off;
   return true;
-}
-
-// k pieces for a product with `tiles` output tiles and K of length `K`: enough
-// blocks for about two rounds on the device, each piece at least 256 long.
-void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
-  const int cu = device_cus();
-  int pcs = tiles >= 2 * cu ? 1 : static_cast<int>((2 * cu + tiles - 1) / tiles);
-  pcs = pcs < kGraspMaxPieces ? pcs : kGraspMaxPieces;
-  const int maxp = K / 256 > 1 ? K / 256 : 1;
-  pcs = pcs < maxp ? pcs : maxp;
-  int chunk = static_cast<int>(round_up(static_cast<size_t>((K + pcs - 1) / pcs), 32));
-  *kchunk = chunk;
-  *pieces = (K + chunk - 1) / chunk;
 }
 
 bool grasp_state_ok(const muon_grasp_state* st, int k) {
