@@ -243,11 +243,12 @@ size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_v
  *   + weight_decay W).
  *
  *   k        subspace rank, 0 <= k <= min(rows, cols), k <= MUON_GRASP_MAX_K
- *            ([GRASP] uses rank / 16).
+ *            ([GRASP] uses rank / 16).  batch <= 8191.
  *   state    see muon_grasp_state; updated in place.
  *   G        gradients (F32, BF16 or F16).  W: F32 or BF16, updated in place.
  *   O_out    NULL or outputs for O (F32 or BF16).
  *   M_out    NULL or F32 outputs that receive M_t (for checking).
+ * W, G, O_out and M_out must be distinct arrays (MUON_ERR_INVALID_ARG).
  *   aux_stream  NULL, or a second stream of the caller's on the same device:
  *            with k > 0 the update of the state (everything after M_t: the
  *            power iteration, the codes of P and R, the residual) then runs
@@ -272,7 +273,7 @@ muon_status muon_grasp_step(int batch, int rows, int cols, int k,
 /*
  * The two codes on their own ([GRASP] key design 2, training strategy), with
  * the layouts above; device arrays of device pointers, fp32 values.  Grid
- * code: X and Y are rows x cols; group code: X and Y are rows x k.
+ * code: X and Y are rows x cols; group code: X and Y are rows x k.  batch <= 65535.
  */
 muon_status muon_grid_quantize(int batch, int rows, int cols, const void *const *X, void *const *codes,
                                void *const *row_scales, void *const *col_scales, void *stream);

@@ -623,6 +623,7 @@ muon_status orthogonalize(muon_ns_variant v, int batch, int rows, int cols, cons
 // low-bit momentum state ([GRASP] overall framework and full example)
 // ---------------------------------------------------------------------------
 constexpr int kGraspMaxPieces = 8;  // k pieces of the two long power-iteration products
+constexpr int kGraspMaxBatch = 65535 / kGraspMaxPieces;  // the state kernels put (batch x pieces) in grid z
 
 int nblk(int x, int b) { return (x + b - 1) / b; }
 
@@ -907,6 +908,13 @@ muon_status grasp_step(int batch, int rows, int cols, int k, void* const* W, muo
   const int kmax = rows < cols ? rows : cols;
   if (k < 0 || k > kmax || k > MUON_GRASP_MAX_K) return MUON_ERR_INVALID_ARG;
   if (W == nullptr || G == nullptr || !grasp_state_ok(state, k)) return MUON_ERR_INVALID_ARG;
+  if (batch > kGraspMaxBatch) return MUON_ERR_INVALID_ARG;
+  {
+    const void* arrays[4] = {W, G, O_out, M_out};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (arrays[i] != nullptr && arrays[i] == arrays[j]) return MUON_ERR_INVALID_ARG;
+  }
   if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay) || !isfinite(update_scale)) return MUON_ERR_INVALID_ARG;
   if (!valid_dtype(w_dtype) || !valid_dtype(g_dtype)) return MUON_ERR_INVALID_ARG;
   if (w_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
@@ -937,6 +945,7 @@ muon_status grasp_step(int batch, int rows, int cols, int k, void* const* W, muo
 muon_status grid_codec(int mode, int batch, int rows, int cols, const void* const* X, void* const* codes,
                        void* const* sr, void* const* sc, void* const* Y, void* stream) {
   if (batch < 1 || rows < 1 || cols < 1 || rows > MUON_MAX_DIM || cols > MUON_MAX_DIM) return MUON_ERR_INVALID_ARG;
+  if (batch > 65535) return MUON_ERR_INVALID_ARG;
   if (codes == nullptr || sr == nullptr || sc == nullptr) return MUON_ERR_INVALID_ARG;
   if ((mode == 0 && X == nullptr) || (mode == 2 && Y == nullptr)) return MUON_ERR_INVALID_ARG;
   GridArgs a{};
@@ -957,6 +966,7 @@ muon_status grid_codec(int mode, int batch, int rows, int cols, const void* cons
 muon_status group8_codec(bool dequantize, int batch, int rows, int k, void* const* X, void* const* codes,
                          void* const* scales, void* stream) {
   if (batch < 1 || rows < 1 || k < 1 || rows > MUON_MAX_DIM || k > MUON_MAX_DIM) return MUON_ERR_INVALID_ARG;
+  if (batch > 65535) return MUON_ERR_INVALID_ARG;
   if (X == nullptr || codes == nullptr || scales == nullptr) return MUON_ERR_INVALID_ARG;
   Group8Args a{};
   a.rows = rows;

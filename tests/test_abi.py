@@ -155,6 +155,10 @@ def test_invalid_grasp_calls():
     assert call(gdt=5) == 1 and call(v=3) == 1
     assert call(wdt=2) == 2 and call(O=4, odt=2) == 2
     assert call(wsb=ws - 1) == 3 and call(w=256 + 16) == 3
+    assert call(G=1) == 1                                  # G aliases W
+    assert lib.muon_grasp_step(8192, 8, 8, 0, 1, 0, ctypes.byref(full), 2, 1, 0.9, 0.1, 0.0, 1.0, 0, None, None, 0,
+                               None, 256, 1 << 40, None, None) == 1   # batch over the limit
+    assert lib.muon_grid_quantize(65536, 8, 8, 1, 2, 3, 4, None) == 1
     assert lib.muon_grid_quantize(0, 8, 8, 1, 2, 3, 4, None) == 1
     assert lib.muon_grid_quantize(1, 8, 8, None, 2, 3, 4, None) == 1
     assert lib.muon_grid_dequantize(1, 8, 0, 1, 2, 3, 4, None) == 1
