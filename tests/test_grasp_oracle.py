@@ -253,3 +253,49 @@ def test_step_with_subspace_reconstruction():
     # and the subspace helps: quantising M_t directly is worse
     q, sr, sc = go.grid_quantize(G)
     assert err < np.linalg.norm(go.grid_dequantize(q, sr, sc) - M1) / np.linalg.norm(M1)
+
+
+def test_nibbles_are_twos_complement():
+    """Every byte decodes to two 4-bit two's-complement values (0x8 is -8)."""
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = go.unpack_nibbles(b, 512)
+    lo, hi = q[0, 0::2].astype(int), q[0, 1::2].astype(int)
+    want = lambda v: v - 16 if v >= 8 else v  # noqa: E731
+    assert all(lo[i] == want(i & 15) and hi[i] == want(i >> 4) for i in range(256))
+
+
+def test_reconstruction_by_loops():
+    """M_{t-1} = deq(M_res) + deq(P) deq(R)^T, entry by entry with exact
+    rationals, on a small state with two 8-bit groups per row."""
+    from fractions import Fraction as F
+    r = rng(15)
+    rows, cols, k = 5, 7, 130
+    st = dict(res_codes=r.integers(-7, 8, (rows, cols)).astype(np.int8),
+              res_sr=r.random((rows, 1)).astype(np.float32) + 0.5,
+              res_sc=r.random((1, cols)).astype(np.float32) + 0.5,
+              P_codes=r.integers(-127, 128, (rows, k)).astype(np.int8),
+              P_scales=r.random((rows, 2)).astype(np.float32),
+              R_codes=r.integers(-127, 128, (cols, k)).astype(np.int8),
+              R_scales=r.random((cols, 2)).astype(np.float32))
+    M = go.reconstruct(st)
+    for i in range(rows):
+        for j in range(cols):
+            m = min(F(float(st["res_sr"][i, 0])), F(float(st["res_sc"][0, j])))
+            v = int(st["res_codes"][i, j]) * m / 7
+            for l in range(k):
+                g = l // 128
+                v += (int(st["P_codes"][i, l]) * F(float(st["P_scales"][i, g])) / 127) * \
+                     (int(st["R_codes"][j, l]) * F(float(st["R_scales"][j, g])) / 127)
+            assert abs(M[i, j] - float(v)) <= 1e-12 * max(1.0, abs(float(v)))
+
+
+def test_nearly_dependent_column_is_kept():
+    """A column at relative distance 1e-3 from the span of the earlier ones is
+    independent (squared ratio 1e-6, far above 1e-12): kept, and equal to
+    numpy's QR factor."""
+    r = rng(16)
+    P = r.standard_normal((60, 4))
+    P[:, 2] = P[:, 0] + 1e-3 * r.standard_normal(60)
+    Q = go.orthonormalize_columns(P)
+    q, rr = np.linalg.qr(P)
+    np.testing.assert_allclose(Q, q * np.sign(np.diag(rr))[None, :], atol=1e-8)
