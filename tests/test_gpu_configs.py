@@ -63,3 +63,38 @@ def test_llama1b_layer0(gi, count, variant):
 @pytest.mark.parametrize("gi,count", [(0, 6), (1, 3)], ids=["up_gate-7168x2048", "down-2048x7168"])
 def test_moe_three_experts_gram(gi, count):
     check_group(syn.WORKLOADS["moe-64x"], gi, count, "gram")
+
+
+@pytest.mark.parametrize("wkey,gi,count", [("moe-64x", 0, 2), ("llama-130m", 0, 4)],
+                         ids=["moe-up_gate-7168x2048", "llama130m-attn-768x768"])
+def test_low_bit_state_first_step(wkey, gi, count):
+    """The low-bit momentum state on a workload's own shapes and gradients
+    (k = rank / 16), from the start state (zero residual and P, a seeded
+    Gaussian R): M_t = G bit for bit, then the new state against the oracle's
+    (codes off by one only at near-ties) and O at the 16-bit tolerance, one
+    batched call per group."""
+    from oracle import grasp_oracle as go
+    from tests.test_gpu_grasp import compare_state
+    wl = syn.WORKLOADS[wkey]
+    Ws, _, Gs = syn.group_inputs(wl, gi, count=count)
+    rows, cols = Ws[0].shape
+    k = min(rows, cols) // 16
+    R0 = [syn.random_matrix(500 + i, cols, k) for i in range(count)]
+    gs = mu.GraspState(count, rows, cols, k, DEV, R_init=[r.to(DEV) for r in R0])
+    W = [w.to(DEV) for w in Ws]
+    O = [torch.empty(rows, cols, dtype=torch.float32, device=DEV) for _ in Ws]
+    Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV) for _ in Ws]
+    mu.grasp_step(W, gs, [g.to(DEV) for g in Gs], MU, LR, 0.0, "gram", O_out=O, M_out=Mt)
+    torch.cuda.synchronize()
+    mu32, lr32 = float(np.float32(MU)), float(np.float32(LR))
+    for i in range(count):
+        st = go.new_state(rows, cols, k, R_init=syn.to_f64(R0[i]).astype(np.float32))
+        G = syn.to_f64(Gs[i]).astype(np.float32)
+        W1, st1, O1, M1, det = go.grasp_step(syn.to_f64(Ws[i]), st, G, mu32, lr32, 0.0, "gram")
+        assert np.array_equal(syn.to_f64(Mt[i]), M1), i
+        one = mu.GraspState(1, rows, cols, 0, DEV)
+        one.k = k
+        for name in ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes", "R_scales"):
+            setattr(one, name, [getattr(gs, name)[i]])
+        compare_state(one, st1, det, rows, cols, k, M_ref=M1)
+        assert orc.relative_frobenius(syn.to_f64(O[i]), O1) < TOL, i
