@@ -388,3 +388,26 @@ def test_grasp_step_batched(rows, cols, k):
             setattr(one, name, [getattr(gs, name)[i]])
         compare_state(one, st1, det, rows, cols, k)
         assert orc.relative_frobenius(host(O[i]), O1) < 2e-2, i
+
+
+def test_grasp_step_with_offset_buffers():
+    """User buffers need not be aligned: a bf16 gradient two bytes off and a
+    code buffer one byte off (views into larger allocations) take the
+    element-wise paths and still give M_t and the state bit for bit."""
+    rows, cols = 64, 256
+    g = seeded(80, rows, cols, 0.01)
+    gbuf = torch.empty(rows * cols + 1, dtype=torch.bfloat16, device=DEV)
+    G = gbuf[1:].view(rows, cols)
+    G.copy_(torch.from_numpy(g).to(DEV, torch.bfloat16))
+    gs = mu.GraspState(1, rows, cols, 0, DEV)
+    cbuf = torch.zeros(rows * cols // 2 + 1, dtype=torch.uint8, device=DEV)
+    gs.res_codes = [cbuf[1:].view(rows, cols // 2)]
+    Mt = [torch.empty(rows, cols, dtype=torch.float32, device=DEV)]
+    mu.grasp_step([dev(seeded(81, rows, cols))], gs, [G], MU, LR, 0.0, "standard", M_out=Mt)
+    torch.cuda.synchronize()
+    g_stored = syn.to_f64(G).astype(np.float32)  # the bf16 values the kernel read
+    _, st1, _, M1, _ = go.grasp_step(seeded(81, rows, cols).astype(np.float64), go.new_state(rows, cols, 0),
+                                     g_stored, MU, LR)
+    assert np.array_equal(host(Mt[0]), M1.astype(np.float32))
+    assert np.array_equal(go.unpack_nibbles(host(gs.res_codes[0]), cols), st1["res_codes"])
+    assert np.array_equal(host(gs.res_row_scales[0]), st1["res_sr"])
