@@ -515,17 +515,17 @@ __global__ __launch_bounds__(kGT) void sum_pieces_kernel(const float* part, int 
 }
 
 // ---------------------------------------------------------------------------
-// M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G for a 64 x 128 tile (half a
-// grid block: small enough per wave, 1 x 2 MFMA blocks, to keep several waves
-// per SIMD for the bandwidth-bound epilogue).  The code product runs group
+// M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G for a 32 x 128 tile (a quarter
+// of a grid block: one 32 x 32 MFMA block per wave, so that several waves per
+// SIMD hide the latency of the bandwidth-bound epilogue).  The code product runs group
 // by group (128 k each) as exact integer sums in the fp32 accumulator and is
 // scaled in fp64 by sP sR / 127^2; the 4-bit residual decodes in fp64.  Both
 // scalings multiply by fp64 reciprocals of 7 and 127^2 (within an fp64 ulp of
 // the quotients, far below the fp32 rounding of M_t).
 // ---------------------------------------------------------------------------
-constexpr int kRecRows = 64;
+constexpr int kRecRows = 32;
 
-__global__ __launch_bounds__(kGT, 2) void recon_kernel(ReconArgs a) {
+__global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   // LDS: the operand staging during the products, then the fp64 product tile
   __shared__ __align__(16) double tile[kRecRows * kTT];
   static_assert(sizeof(double) * kRecRows * kTT >= sizeof(uint16_t) * (kRecRows + kTT) * kTL, "staging fits");
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(kGT, 2) void recon_kernel(ReconArgs a) {
   const int b = blockIdx.z, bj = blockIdx.x;
   const int row0 = blockIdx.y * kRecRows, col0 = bj * kTT, bi = row0 / kGB;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wr = 32 * (w >> 1), wc = 64 * (w & 1);
+  const int wc = 32 * w;  // wave w: the 32 x 32 block at columns wc..
   const int k = a.k, ng = (k + kGB - 1) / kGB;
   const int8_t* Pc = static_cast<const int8_t*>(a.P_codes[b]);
   const int8_t* Rc = static_cast<const int8_t*>(a.R_codes[b]);
@@ -542,18 +542,14 @@ __global__ __launch_bounds__(kGT, 2) void recon_kernel(ReconArgs a) {
   uint16_t *Ah = smem, *Bh = smem + kRecRows * kTL;
   const int arows = min(a.rows, row0 + kRecRows);
   constexpr double kInvL8sq = 1.0 / 16129.0, kInv7 = 1.0 / 7.0;
-  double pr[2][16];
+  double pr[16];
 #pragma unroll
-  for (int y = 0; y < 2; ++y)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) pr[y][v] = 0.0;
+  for (int v = 0; v < 16; ++v) pr[v] = 0.0;
   for (int g = 0; g < ng; ++g) {
     const int kbeg = g * kGB, kend = min(k, kbeg + kGB);
-    gq_f32x16 acc[2];
+    gq_f32x16 acc;
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[y][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
     CodeRegs ra, rb;
     load_i8(Pc, k, row0, kbeg, arows, kend, ra);
     load_i8(Rc, k, col0, kbeg, a.cols, kend, rb);
@@ -568,36 +564,27 @@ __global__ __launch_bounds__(kGT, 2) void recon_kernel(ReconArgs a) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int kk = 16 * s + 8 * (lane >> 5);
-        const uint4 av = *reinterpret_cast<const uint4*>(Ah + (wr + (lane & 31)) * kTL + kk);
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(Bh + (wc + 32 * y + (lane & 31)) * kTL + kk);
-          acc[y] = mfma(av, bv, acc[y]);
-        }
+        const uint4 av = *reinterpret_cast<const uint4*>(Ah + (lane & 31) * kTL + kk);
+        const uint4 bv = *reinterpret_cast<const uint4*>(Bh + (wc + (lane & 31)) * kTL + kk);
+        acc = mfma(av, bv, acc);
       }
       __syncthreads();
     }
+    const int col = col0 + wc + (lane & 31);
+    const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int col = col0 + wc + 32 * y + (lane & 31);
-      const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row0 + wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const double sP = row < a.rows ? static_cast<double>(Ps[static_cast<int64_t>(row) * ng + g]) : 0.0;
-        pr[y][v] = fma(static_cast<double>(acc[y][v]), sP * sR, pr[y][v]);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int row = row0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const double sP = row < a.rows ? static_cast<double>(Ps[static_cast<int64_t>(row) * ng + g]) : 0.0;
+      pr[v] = fma(static_cast<double>(acc[v]), sP * sR, pr[v]);
     }
   }
   // the product tile into LDS (the last loop iteration ended with a barrier)
 #pragma unroll
-  for (int y = 0; y < 2; ++y)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      tile[(wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kTT + wc + 32 * y + (lane & 31)] = pr[y][v];
+  for (int v = 0; v < 16; ++v) tile[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kTT + wc + (lane & 31)] = pr[v];
   __syncthreads();
   // epilogue in the grid-code layout: thread t holds columns col0 + 8 (t % 16) .. + 7
-  // of rows row0 + t / 16 + 16 s (s < 4), with vector loads and stores where aligned
+  // of rows row0 + t / 16 + 16 s (s < 2), with vector loads and stores where aligned
   const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
   const int j0 = col0 + 8 * cg, n = min(8, a.cols - j0);
   if (n <= 0) return;  // no barrier follows
