@@ -529,6 +529,7 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   // LDS: the operand staging during the products, then the fp64 product tile
   __shared__ __align__(16) double tile[kRecRows * kTT];
   static_assert(sizeof(double) * kRecRows * kTT >= sizeof(uint16_t) * (kRecRows + kTT) * kTL, "staging fits");
+  __shared__ float psc[kRecRows * (kMaxRankK / kGB)];  // P's group scales for the tile's rows
   uint16_t* smem = reinterpret_cast<uint16_t*>(tile);
   const int b = blockIdx.z, bj = blockIdx.x;
   const int row0 = blockIdx.y * kRecRows, col0 = bj * kTT, bi = row0 / kGB;
@@ -542,6 +543,12 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   uint16_t *Ah = smem, *Bh = smem + kRecRows * kTL;
   const int arows = min(a.rows, row0 + kRecRows);
   constexpr double kInvL8sq = 1.0 / 16129.0, kInv7 = 1.0 / 7.0;
+  // P's scales for the tile's rows, read from LDS by the fold (the k-loop's
+  // barriers order these stores before the first read)
+  for (int e = threadIdx.x; e < kRecRows * ng; e += kGT) {
+    const int r = e / ng;
+    psc[e] = row0 + r < a.rows ? Ps[static_cast<int64_t>(row0) * ng + e] : 0.0f;
+  }
   double pr[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) pr[v] = 0.0;
@@ -574,8 +581,7 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
     const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = row0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const double sP = row < a.rows ? static_cast<double>(Ps[static_cast<int64_t>(row) * ng + g]) : 0.0;
+      const double sP = psc[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * ng + g];
       pr[v] = fma(static_cast<double>(acc[v]), sP * sR, pr[v]);
     }
   }
@@ -596,12 +602,12 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
   float* Y = a.Y != nullptr ? static_cast<float*>(a.Y[b]) : nullptr;
   uintptr_t mis = (reinterpret_cast<uintptr_t>(codes) & 3u) |
-                  ((reinterpret_cast<uintptr_t>(a.G[b]) | reinterpret_cast<uintptr_t>(mt)) & 15u);
+                  ((reinterpret_cast<uintptr_t>(a.G[b]) | reinterpret_cast<uintptr_t>(mt) |
+                    reinterpret_cast<uintptr_t>(sc)) & 15u);
   if (Y != nullptr) mis |= reinterpret_cast<uintptr_t>(Y) & 15u;
   const bool vec = (a.cols & 7) == 0 && mis == 0;
   float cs[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) cs[c] = c < n ? sc[static_cast<int64_t>(bi) * a.cols + j0 + c] : 0.0f;
+  load8_f32(sc, static_cast<int64_t>(bi) * a.cols + j0, 0, vec, n, cs);
 #pragma unroll
   for (int s = 0; s < kRecRows / 16; ++s) {
     const int r = rs + 16 * s, i = row0 + r;
