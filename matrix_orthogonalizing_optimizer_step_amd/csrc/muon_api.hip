@@ -647,7 +647,7 @@ void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
 // Workspace after the Newton-Schulz part: M_t and its pointer table, then
 // (k > 0) the power-iteration buffers.
 struct GraspLayout {
-  size_t ptrs, mt, q, colpart, colinv, ppart, ptil, spart, S, dead, P, rpart, R, total;
+  size_t ptrs, mt, q, qs, colpart, colinv, ppart, ptil, spart, S, dead, P, ps, rpart, R, total;
   int nch_n, nch_m, gchunk;
 };
 
@@ -667,6 +667,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->gchunk = gram_chunk_rows(rows, batch);
     g->nch_m = nblk(rows, g->gchunk);
     g->q = take(B * c * kk * 4);
+    g->qs = take(B * c * kk * 4);  // Q^T split into bf16 hi and lo planes
     g->colpart = take(B * g->nch_n * kk * 8);
     g->colinv = take(B * kk * 8);
     int pcs = 1, chunk = 0;
@@ -677,6 +678,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->S = take(B * kk * kk * 8);
     g->dead = take(B * kk * 4);
     g->P = take(B * r * kk * 4);
+    g->ps = take(B * r * kk * 4);  // P^T split into bf16 hi and lo planes
     grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &pcs, &chunk);
     g->rpart = take(pcs > 1 ? B * pcs * c * kk * 4 : 0);
     g->R = take(B * c * kk * 4);
@@ -771,6 +773,13 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     MUON_LAUNCH(traced(s, "unit_columns_kernel", "grasp_Q", 0.0, cols * kd * batch * 6.0,
                        [&] { return launch_unit_columns(a, batch, s); }));
   }
+  // Q^T as bf16 hi / lo planes, split once for all row tiles of M_t Q
+  uint16_t* qs = reinterpret_cast<uint16_t*>(ws + lay.qs);
+  const int64_t s_qs = static_cast<int64_t>(cols) * k * 2;
+  MUON_LAUNCH(traced(s, "split_t_kernel", "grasp_Q_split", 0.0, cols * kd * batch * 8.0, [&] {
+    return launch_split_t(Q, static_cast<int64_t>(cols) * k, cols, k, qs, qs + static_cast<int64_t>(cols) * k, s_qs,
+                          batch, s);
+  }));
   // 3. P~ = M_t Q (split along k when the tiles alone do not fill the device)
   float* ptil = reinterpret_cast<float*>(ws + lay.ptil);
   {
@@ -782,16 +791,16 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.sA = s_mt;
     a.a_row = cols;
     a.a_k = 1;
-    a.B = Q;
-    a.sB = static_cast<int64_t>(cols) * k;
-    a.b_row = 1;
-    a.b_k = k;
+    a.Bh = qs;
+    a.Bl = qs + static_cast<int64_t>(cols) * k;
+    a.sB = s_qs;
+    a.b_row = cols;
     grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(rows) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.ppart) : ptil;
-    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 0>", "grasp_MQ", 2.0 * elems * kd,
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 1, 1>", "grasp_MQ", 2.0 * elems * kd,
                        elems * 4.0 + (cols + rows * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, true, false, batch, s); }));
+                       [&] { return launch_tall(a, true, true, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MQ_sum", 0.0, rows * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, ptil, batch, s); }));
@@ -826,8 +835,14 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     MUON_LAUNCH(traced(s, "group8_kernel<0>", "grasp_P_code", 0.0, rows * kd * 5.0 * batch,
                        [&] { return launch_group8(q, false, batch, s); }));
   }
-  // 6. R = M_t^T P, then its 8-bit code
+  // 6. R = M_t^T P (P^T split once into bf16 planes), then its 8-bit code
   float* R = reinterpret_cast<float*>(ws + lay.R);
+  uint16_t* ps = reinterpret_cast<uint16_t*>(ws + lay.ps);
+  const int64_t s_ps = static_cast<int64_t>(rows) * k * 2;
+  MUON_LAUNCH(traced(s, "split_t_kernel", "grasp_P_split", 0.0, rows * kd * batch * 8.0, [&] {
+    return launch_split_t(P, static_cast<int64_t>(rows) * k, rows, k, ps, ps + static_cast<int64_t>(rows) * k, s_ps,
+                          batch, s);
+  }));
   {
     TallArgs a{};
     a.M = cols;
@@ -837,16 +852,16 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.sA = s_mt;
     a.a_row = 1;
     a.a_k = cols;
-    a.B = P;
-    a.sB = static_cast<int64_t>(rows) * k;
-    a.b_row = 1;
-    a.b_k = k;
+    a.Bh = ps;
+    a.Bl = ps + static_cast<int64_t>(rows) * k;
+    a.sB = s_ps;
+    a.b_row = rows;
     grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(cols) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.rpart) : R;
-    MUON_LAUNCH(traced(s, "tall_gemm_kernel<0, 0>", "grasp_MtP", 2.0 * elems * kd,
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel<0, 1, 1>", "grasp_MtP", 2.0 * elems * kd,
                        elems * 4.0 + (rows + cols * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, false, false, batch, s); }));
+                       [&] { return launch_tall(a, false, true, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MtP_sum", 0.0, cols * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, R, batch, s); }));

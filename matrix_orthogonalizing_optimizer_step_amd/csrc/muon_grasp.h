@@ -43,12 +43,16 @@ struct UnitArgs {
 // A + b sA + row a_row + k a_k, B element (col, k) at B + b sB + col b_row + k b_k.
 // With pieces > 1, block z = b * pieces + p covers k in [p kchunk, (p + 1) kchunk)
 // and writes C + z sC (partial products, summed by launch_sum_pieces).
+// Bh / Bl non-null: B comes pre-split into bf16 planes (hi, lo), element
+// (col, k) at + b sB + col b_row + k (k contiguous); B and b_k are unused.
 struct TallArgs {
   int M, N, K;
   const float* A; int64_t sA, a_row, a_k;
   const float* B; int64_t sB, b_row, b_k;
   float* C; int64_t sC;
   int pieces, kchunk;
+  const uint16_t* Bh = nullptr;
+  const uint16_t* Bl = nullptr;
 };
 
 // M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G.
@@ -95,6 +99,8 @@ hipError_t launch_grid(const GridArgs& a, int mode, int batch, hipStream_t s);
 hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStream_t s);
 hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s);
 hipError_t launch_tall(const TallArgs& a, bool a_kcontig, bool b_kcontig, int batch, hipStream_t s);
+hipError_t launch_split_t(const float* X, int64_t sX, int rows, int k, uint16_t* hi, uint16_t* lo, int64_t sT,
+                          int batch, hipStream_t s);
 hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float* out, int batch, hipStream_t s);
 hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s);
 hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s);

@@ -447,25 +447,112 @@ __device__ __forceinline__ void zero_acc(gq_f32x16 (&acc)[2][2]) {
 
 // acc += A[row0.., kbeg..kend) B[kbeg..kend), col0..] for fp32 operands
 // (split).  smem: 4 planes of kStageHalves bf16.
-template <bool AKC, bool BKC>
+// An operand already split into bf16 planes (hi, lo), k contiguous: the
+// thread's four runs of 4 consecutive k, 8 bytes per plane each.
+struct PairRegs {
+  uint2 h[4], l[4];
+};
+
+__device__ __forceinline__ void load_pair(const uint16_t* hi, const uint16_t* lo, int64_t s_row, int row0, int k0,
+                                          int nrows, int K, PairRegs& r) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = threadIdx.x + kGT * p;
+    const int row = row0 + (e >> 3), k = k0 + (e & 7) * 4;
+    const int64_t off = static_cast<int64_t>(row) * s_row + k;
+    if (row < nrows && k + 3 < K && ((reinterpret_cast<uintptr_t>(hi + off) | reinterpret_cast<uintptr_t>(lo + off)) & 7u) == 0) {
+      r.h[p] = *reinterpret_cast<const uint2*>(hi + off);
+      r.l[p] = *reinterpret_cast<const uint2*>(lo + off);
+    } else {
+      uint32_t h[2] = {0u, 0u}, l[2] = {0u, 0u};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row < nrows && k + q < K) {
+          h[q >> 1] |= static_cast<uint32_t>(hi[off + q]) << (16 * (q & 1));
+          l[q >> 1] |= static_cast<uint32_t>(lo[off + q]) << (16 * (q & 1));
+        }
+      r.h[p] = make_uint2(h[0], h[1]);
+      r.l[p] = make_uint2(l[0], l[1]);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_pair(const PairRegs& r, uint16_t* hi, uint16_t* lo) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = threadIdx.x + kGT * p;
+    const int rr = e >> 3, kk = (e & 7) * 4;
+    *reinterpret_cast<uint2*>(hi + rr * kTL + kk) = r.h[p];
+    *reinterpret_cast<uint2*>(lo + rr * kTL + kk) = r.l[p];
+  }
+}
+
+// acc += A B over k in [kbeg, kend).  BPS: B comes pre-split (a.Bh, a.Bl:
+// planes of bf16 hi / lo, element (col, k) at col * b_row + k).
+template <bool AKC, bool BKC, bool BPS = false>
 __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, int col0, int kbeg, int kend,
                                           uint16_t* smem, gq_f32x16 (&acc)[2][2]) {
   const float* A = a.A + static_cast<int64_t>(b) * a.sA;
-  const float* B = a.B + static_cast<int64_t>(b) * a.sB;
   uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
-  TileRegs ra, rb;
+  TileRegs ra;
   load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
-  load_f32<BKC>(B, a.b_row, a.b_k, col0, kbeg, a.N, kend, rb);
-  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-    store_split<AKC, true>(ra, Ah, Al);
-    store_split<BKC, true>(rb, Bh, Bl);
-    __syncthreads();
-    if (k0 + kTK < kend) {
-      load_f32<AKC>(A, a.a_row, a.a_k, row0, k0 + kTK, a.M, kend, ra);
-      load_f32<BKC>(B, a.b_row, a.b_k, col0, k0 + kTK, a.N, kend, rb);
+  if constexpr (BPS) {
+    const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
+    const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
+    PairRegs rb;
+    load_pair(Bhi, Blo, a.b_row, col0, kbeg, a.N, kend, rb);
+    for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+      store_split<AKC, true>(ra, Ah, Al);
+      store_pair(rb, Bh, Bl);
+      __syncthreads();
+      if (k0 + kTK < kend) {
+        load_f32<AKC>(A, a.a_row, a.a_k, row0, k0 + kTK, a.M, kend, ra);
+        load_pair(Bhi, Blo, a.b_row, col0, k0 + kTK, a.N, kend, rb);
+      }
+      mma_stage<true>(Ah, Al, Bh, Bl, acc);
+      __syncthreads();
     }
-    mma_stage<true>(Ah, Al, Bh, Bl, acc);
-    __syncthreads();
+  } else {
+    const float* B = a.B + static_cast<int64_t>(b) * a.sB;
+    TileRegs rb;
+    load_f32<BKC>(B, a.b_row, a.b_k, col0, kbeg, a.N, kend, rb);
+    for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+      store_split<AKC, true>(ra, Ah, Al);
+      store_split<BKC, true>(rb, Bh, Bl);
+      __syncthreads();
+      if (k0 + kTK < kend) {
+        load_f32<AKC>(A, a.a_row, a.a_k, row0, k0 + kTK, a.M, kend, ra);
+        load_f32<BKC>(B, a.b_row, a.b_k, col0, k0 + kTK, a.N, kend, rb);
+      }
+      mma_stage<true>(Ah, Al, Bh, Bl, acc);
+      __syncthreads();
+    }
+  }
+}
+
+// X (rows x k fp32, matrix b at X + b sX) -> planes hi, lo of X^T (k x rows,
+// bf16, matrix b at + b sT): the split of an operand done once, through a
+// 64 x 64 LDS tile so that both sides are coalesced.
+__global__ __launch_bounds__(kGT) void split_t_kernel(const float* X, int64_t sX, int rows, int k, uint16_t* hi,
+                                                      uint16_t* lo, int64_t sT) {
+  __shared__ float t[64][65];
+  const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const float* Xm = X + static_cast<int64_t>(b) * sX;
+  for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
+    const int r = e >> 6, c = e & 63;
+    t[r][c] = (r0 + r < rows && c0 + c < k) ? Xm[static_cast<int64_t>(r0 + r) * k + c0 + c] : 0.0f;
+  }
+  __syncthreads();
+  uint16_t* H = hi + static_cast<int64_t>(b) * sT;
+  uint16_t* L = lo + static_cast<int64_t>(b) * sT;
+  for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
+    const int c = e >> 6, r = e & 63;
+    if (c0 + c < k && r0 + r < rows) {
+      const float x = t[r][c];
+      const uint16_t h = f32_to_bf16(x);
+      H[static_cast<int64_t>(c0 + c) * rows + r0 + r] = h;
+      L[static_cast<int64_t>(c0 + c) * rows + r0 + r] = f32_to_bf16(x - bf16_to_f32(h));
+    }
   }
 }
 
@@ -480,7 +567,7 @@ __device__ __forceinline__ int acc_col(int y) {
 }
 
 // C (or a k-piece of C) = A B, stored fp32.  grid: (N tiles, M tiles, batch * pieces).
-template <bool AKC, bool BKC>
+template <bool AKC, bool BKC, bool BPS>
 __global__ __launch_bounds__(kGT) void tall_gemm_kernel(TallArgs a) {
   __shared__ __align__(16) uint16_t smem[4 * kStageHalves];
   const int b = blockIdx.z / a.pieces, piece = blockIdx.z - b * a.pieces;
@@ -488,7 +575,7 @@ __global__ __launch_bounds__(kGT) void tall_gemm_kernel(TallArgs a) {
   const int kbeg = piece * a.kchunk, kend = min(a.K, kbeg + a.kchunk);
   gq_f32x16 acc[2][2];
   zero_acc(acc);
-  tall_loop<AKC, BKC>(a, b, row0, col0, kbeg, kend, smem, acc);
+  tall_loop<AKC, BKC, BPS>(a, b, row0, col0, kbeg, kend, smem, acc);
   float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.sC;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -1009,10 +1096,25 @@ hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s) {
 
 hipError_t launch_tall(const TallArgs& a, bool akc, bool bkc, int batch, hipStream_t s) {
   const dim3 g((a.N + kTT - 1) / kTT, (a.M + kTT - 1) / kTT, batch * a.pieces);
-  if (akc && bkc) hipLaunchKernelGGL((tall_gemm_kernel<true, true>), g, dim3(kGT), 0, s, a);
-  else if (akc) hipLaunchKernelGGL((tall_gemm_kernel<true, false>), g, dim3(kGT), 0, s, a);
-  else if (bkc) hipLaunchKernelGGL((tall_gemm_kernel<false, true>), g, dim3(kGT), 0, s, a);
-  else hipLaunchKernelGGL((tall_gemm_kernel<false, false>), g, dim3(kGT), 0, s, a);
+  if (a.Bh != nullptr) {  // B pre-split (k contiguous)
+    if (akc) hipLaunchKernelGGL((tall_gemm_kernel<true, true, true>), g, dim3(kGT), 0, s, a);
+    else hipLaunchKernelGGL((tall_gemm_kernel<false, true, true>), g, dim3(kGT), 0, s, a);
+  } else if (akc && bkc) {
+    hipLaunchKernelGGL((tall_gemm_kernel<true, true, false>), g, dim3(kGT), 0, s, a);
+  } else if (akc) {
+    hipLaunchKernelGGL((tall_gemm_kernel<true, false, false>), g, dim3(kGT), 0, s, a);
+  } else if (bkc) {
+    hipLaunchKernelGGL((tall_gemm_kernel<false, true, false>), g, dim3(kGT), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((tall_gemm_kernel<false, false, false>), g, dim3(kGT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_t(const float* X, int64_t sX, int rows, int k, uint16_t* hi, uint16_t* lo, int64_t sT,
+                          int batch, hipStream_t s) {
+  const dim3 g((k + 63) / 64, (rows + 63) / 64, batch);
+  hipLaunchKernelGGL(split_t_kernel, g, dim3(kGT), 0, s, X, sX, rows, k, hi, lo, sT);
   return hipGetLastError();
 }
 
