@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from collections import OrderedDict
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -149,20 +150,43 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-_ptr_cache: dict = {}
+_ptr_cache: "OrderedDict[tuple, torch.Tensor]" = OrderedDict()  # least recently used first
+_ptr_pinned: dict = {}  # arrays a captured graph reads: kept for the life of the process
+_PTR_CACHE_MAX = 256
 
 
 def pointer_array(tensors: Sequence[torch.Tensor]) -> torch.Tensor:
-    """A device array holding the data pointers of ``tensors`` (cached)."""
+    """A device array holding the data pointers of ``tensors``.
+
+    Arrays are cached (least recently used evicted past 256 entries, after a
+    device synchronisation, as a kernel on another stream may still read it).  Making
+    one is a host-to-device copy, which a stream under graph capture does not
+    allow: call once with the same tensors before capturing.  An array used
+    during a capture is kept for the life of the process, since the graph
+    reads it at every replay."""
     ptrs = tuple(int(t.data_ptr()) for t in tensors)
     dev = tensors[0].device
     key = (str(dev), ptrs)
+    capturing = dev.type == "cuda" and torch.cuda.is_current_stream_capturing()
+    arr = _ptr_pinned.get(key)
+    if arr is not None:
+        return arr
     arr = _ptr_cache.get(key)
     if arr is None:
-        if len(_ptr_cache) > 256:
-            _ptr_cache.clear()
+        if capturing:
+            raise MuonError("pointer array not cached for these tensors: under graph capture, "
+                            "call once with the same tensors before capturing")
+        if len(_ptr_cache) >= _PTR_CACHE_MAX:
+            if dev.type == "cuda":  # a kernel on any stream may still read the array: wait before freeing it
+                torch.cuda.synchronize(dev)
+            while len(_ptr_cache) >= _PTR_CACHE_MAX:
+                _ptr_cache.popitem(last=False)
         arr = torch.tensor(ptrs, dtype=torch.int64).to(dev)
         _ptr_cache[key] = arr
+    else:
+        _ptr_cache.move_to_end(key)
+    if capturing:
+        _ptr_pinned[key] = _ptr_cache.pop(key)
     return arr
 
 

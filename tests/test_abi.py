@@ -165,3 +165,22 @@ def test_invalid_grasp_calls():
     assert lib.muon_grid_dequantize(1, 8, 8, 1, 2, 3, None, None) == 1
     assert lib.muon_group8_quantize(1, 8, 0, 1, 2, 3, None) == 1
     assert lib.muon_group8_dequantize(1, 8, 8, 1, None, 3, None) == 1
+
+
+def test_pointer_array_cache_evicts_least_recently_used():
+    """The pointer-array cache drops the least recently used entry, so an array
+    used just before a graph capture is still cached when the capture needs it."""
+    import torch
+    bd._ptr_cache.clear()
+    keep = [torch.zeros(2)]
+    first = bd.pointer_array(keep)
+    others = [[torch.zeros(1)] for _ in range(bd._PTR_CACHE_MAX + 40)]
+    for i, o in enumerate(others):
+        bd.pointer_array(o)
+        if i % 8 == 0:
+            assert bd.pointer_array(keep) is first  # a hit moves it to the back
+    assert len(bd._ptr_cache) <= bd._PTR_CACHE_MAX
+    assert bd.pointer_array(keep) is first
+    assert bd.pointer_array(keep).tolist() == [keep[0].data_ptr()]
+    assert (str(keep[0].device), (others[0][0].data_ptr(),)) not in bd._ptr_cache
+    bd._ptr_cache.clear()
