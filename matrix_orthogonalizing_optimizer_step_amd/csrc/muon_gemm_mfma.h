@@ -59,8 +59,8 @@ constexpr int kLoadsA = kFM * kKS;    // P loads per wave and slab
 // unit, 2 x 8 MFMA blocks (256 accumulator registers) per wave, P three slabs
 // ahead in four register buffers.  BN = 128: two blocks per compute unit (two
 // waves per SIMD, so one wave's waits and barrier are covered by the other's
-// MFMAs), 2 x 4 MFMA blocks (128 accumulator registers) per wave, P one slab
-// ahead in two buffers; used for symmetric products with k = n (short), where
+// MFMAs), 2 x 4 MFMA blocks (128 accumulator registers) per wave, P two slabs
+// ahead in three buffers; used for symmetric products with k = n (short), where
 // the finer tiles also fill the last round better.
 template <int BN>
 struct TileCfg {
@@ -70,13 +70,12 @@ struct TileCfg {
   static constexpr int kStageBytes = BN * kBK * 2;
   // the 256-wide stages also hold one wave's 32-row staging block of the last product
   static constexpr int kStageAlloc = BN == 256 && kStageBytes < 32 * kLDE * 4 ? 32 * kLDE * 4 : kStageBytes;
-  static constexpr int kPBufs = BN == 256 ? 4 : 2;
+  static constexpr int kPBufs = BN == 256 ? 4 : 3;
   // Loads a wave issues after its part of Q slab kt + 1 and before the
-  // barrier of slab kt: the P slabs kt + 1 .. kt + 3 (issued at the starts of
-  // slabs kt - 2 .. kt) and Q slabs kt + 2, kt + 3.  With P one slab ahead the
-  // oldest of those P groups would be slab kt - 1, already consumed, so the
-  // count leaves it out (which also makes it exact for the first slab).
-  static constexpr int kWaitBarrier = (kPBufs == 4 ? 3 : 2) * kLoadsA + 2 * kLoadsB;
+  // barrier of slab kt: three P slab groups (issued at the starts of slabs
+  // kt - 2 .. kt: slabs kt + 1 .. kt + 3 with P three slabs ahead, kt .. kt + 2
+  // with P two ahead) and Q slabs kt + 2, kt + 3.
+  static constexpr int kWaitBarrier = 3 * kLoadsA + 2 * kLoadsB;
 };
 
 // s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
@@ -949,29 +948,43 @@ __global__ __launch_bounds__(kNT, BN == kMfmaTile ? 1 : 2) void gemm_nt_mfma(Gem
     }
 #undef MUON_SLAB
   } else {
-    uint4 abuf0[kFM][kKS], abuf1[kFM][kKS];
-    // prologue: Q slabs k0 .. k0 + 3, P slab k0 (the loop loads P slab j + 1
-    // at the start of slab j); the barrier count of the loop then holds from
-    // its first slab on
+    uint4 abuf0[kFM][kKS], abuf1[kFM][kKS], abuf2[kFM][kKS];
+    // prologue: Q slabs k0 .. k0 + 3 and P slabs k0, k0 + 1, in the order the
+    // loop issues them (P slab j + 2 at the start of slab j, Q slab j + 4 in
+    // its middle), so the compiler's waits for the P registers stay exact
     load_b_slab<BN>(stg0, rQ, voff, sQ, qstride, k0, wave);
     load_b_slab<BN>(stg1, rQ, voff, sQ, qstride, k0 + 1, wave);
-    load_b_slab<BN>(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
     load_a_slab(abuf0, rP, voff, sP, pstride, k0);
+    load_b_slab<BN>(stg2, rQ, voff, sQ, qstride, k0 + 2, wave);
+    load_a_slab(abuf1, rP, voff, sP, pstride, k0 + 1);
     load_b_slab<BN>(stg3, rQ, voff, sQ, qstride, k0 + 3, wave);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoadsA + 3 * C::kLoadsB, 15));  // Q slab 0 landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsA + 3 * C::kLoadsB, 15));  // Q slab 0 landed
     block_barrier();
 #pragma unroll
     for (int y = 0; y < kFN; ++y) bf[0][y] = stg0[y * kKS * 64 + lane];
 
-    // 4 slabs per trip (the 4 LDS stages; the 2 P buffers alternate)
+    // 12 slabs per trip (the 4 LDS stages against the 3 P buffers, loaded two
+    // slabs ahead); the slab count is a multiple of 4, so the trip may end
+    // after its 4th or 8th slab
 #define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
-  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 1);                                             \
+  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 2);                                             \
   slab<OP, BN>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
-    for (int kt = k0; kt < k1; kt += 4) {
-      MUON_SLAB(0, abuf0, abuf1, stg0, stg1)
+    for (int kt = k0;; kt += 12) {
+      MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
       MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
-      MUON_SLAB(2, abuf0, abuf1, stg2, stg3)
-      MUON_SLAB(3, abuf1, abuf0, stg3, stg0)
+      MUON_SLAB(2, abuf2, abuf1, stg2, stg3)
+      MUON_SLAB(3, abuf0, abuf2, stg3, stg0)
+      if (kt + 4 >= k1) break;
+      MUON_SLAB(4, abuf1, abuf0, stg0, stg1)
+      MUON_SLAB(5, abuf2, abuf1, stg1, stg2)
+      MUON_SLAB(6, abuf0, abuf2, stg2, stg3)
+      MUON_SLAB(7, abuf1, abuf0, stg3, stg0)
+      if (kt + 8 >= k1) break;
+      MUON_SLAB(8, abuf2, abuf1, stg0, stg1)
+      MUON_SLAB(9, abuf0, abuf2, stg1, stg2)
+      MUON_SLAB(10, abuf1, abuf0, stg2, stg3)
+      MUON_SLAB(11, abuf2, abuf1, stg3, stg0)
+      if (kt + 12 >= k1) break;
     }
 #undef MUON_SLAB
   }
