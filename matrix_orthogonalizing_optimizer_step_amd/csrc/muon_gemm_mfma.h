@@ -52,7 +52,6 @@ constexpr int kNW = 4, kNT = 64 * kNW;
 constexpr int kFM = kBM / kNW / 32;   // MFMA row blocks per wave (2)
 constexpr int kKS = kBK / 16;         // k-steps per slab (4)
 constexpr int kStages = 4;            // LDS ring depth for Q
-constexpr int kLDE = kMfmaTile + 4;   // last product: staged row length (floats)
 constexpr int kLoadsA = kFM * kKS;    // P loads per wave and slab
 
 // The block tile is 256 rows by BN columns.  BN = 256: one block per compute
@@ -68,8 +67,8 @@ struct TileCfg {
   static constexpr int kRBW = BN / 32 / kNW;   // Q row blocks each wave streams in per slab
   static constexpr int kLoadsB = kRBW * kKS;   // Q loads per wave and slab
   static constexpr int kStageBytes = BN * kBK * 2;
-  // the 256-wide stages also hold one wave's 32-row staging block of the last product
-  static constexpr int kStageAlloc = BN == 256 && kStageBytes < 32 * kLDE * 4 ? 32 * kLDE * 4 : kStageBytes;
+  // a stage also holds one wave's 32-row staging block of the last product (rows of BN + 4 floats)
+  static constexpr int kStageAlloc = kStageBytes < 32 * (BN + 4) * 4 ? 32 * (BN + 4) * 4 : kStageBytes;
   static constexpr int kPBufs = BN == 256 ? 4 : 3;
   // Loads a wave issues after its part of Q slab kt + 1 and before the
   // barrier of slab kt: three P slab groups (issued at the starts of slabs
@@ -321,14 +320,16 @@ __device__ __forceinline__ void st4(void* p, int64_t off, const float4& v) {
   }
 }
 
-// The final update for a staged 32 x 256 block of O that lies wholly inside
-// the user's matrix, whose rows are aligned to four elements: W of dtype WD
-// and O of dtype OD (-1: absent).  Loads of W for 16 rows (or columns) are
-// issued together; there are no per-element range checks.
-template <int WD, int OD, int LDE>
+// The final update for a staged 32 x BW block of O (BW = 256 or 128) that
+// lies wholly inside the user's matrix, whose rows are aligned to four
+// elements: W of dtype WD and O of dtype OD (-1: absent).  Loads of W for R
+// rows (or columns) are issued together; there are no per-element range
+// checks.
+template <int WD, int OD, int LDE, int BW>
 __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
                                                 int lane) {
-  constexpr int R = 16;
+  constexpr int R = BW == 256 ? 16 : 8;
+  constexpr int LPR = BW / 4, RS = 64 / LPR;  // lanes per row of the block, rows per step
   constexpr int wsz = WD == kF32 ? 4 : 2, osz = OD == kF32 ? 4 : 2;
   void* w = st.w;
   void* o = st.o;
@@ -340,22 +341,23 @@ __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiStat
     nw.z -= lr * (os * ov.z + wd * nw.z);
     nw.w -= lr * (os * ov.w + wd * nw.w);
   };
-  if (!a.transposed) {  // W[i][j .. j + 3], lane -> columns j0 + 4 lane
-    const int64_t base = static_cast<int64_t>(i0) * ld + j0 + 4 * lane;
+  if (!a.transposed) {  // W[i][j .. j + 3], lane -> columns j0 + 4 (lane % LPR) of rows RS r + lane / LPR
+    const int sub = lane / LPR, cl = 4 * (lane % LPR);
+    const int64_t base = static_cast<int64_t>(i0 + sub) * ld + j0 + cl;
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += R) {
+    for (int r0 = 0; r0 < 32; r0 += R * RS) {
       float4 wv[R];
       if constexpr (WD >= 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) wv[r] = ld4<WD>(w, (base + (r0 + r) * ld) * wsz);
+        for (int r = 0; r < R; ++r) wv[r] = ld4<WD>(w, (base + (r0 + RS * r) * ld) * wsz);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float4 ov = lds_load4(ep + (r0 + r) * LDE + 4 * lane);
-        if constexpr (OD >= 0) st4<OD>(o, (base + (r0 + r) * ld) * osz, ov);
+        const float4 ov = lds_load4(ep + (r0 + RS * r + sub) * LDE + cl);
+        if constexpr (OD >= 0) st4<OD>(o, (base + (r0 + RS * r) * ld) * osz, ov);
         if constexpr (WD >= 0) {
           update(wv[r], ov);
-          st4<WD>(w, (base + (r0 + r) * ld) * wsz, wv[r]);
+          st4<WD>(w, (base + (r0 + RS * r) * ld) * wsz, wv[r]);
         }
       }
     }
@@ -363,7 +365,7 @@ __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiStat
     const int r4 = (lane & 7) * 4;
     const int64_t base = static_cast<int64_t>(j0 + (lane >> 3)) * ld + i0 + r4;
 #pragma unroll
-    for (int c0 = 0; c0 < 256; c0 += 8 * R) {
+    for (int c0 = 0; c0 < BW; c0 += 8 * R) {
       float4 wv[R];
       if constexpr (WD >= 0) {
 #pragma unroll
@@ -384,70 +386,73 @@ __device__ __forceinline__ void final_rows_fast(const GemmArgs& a, const EpiStat
   }
 }
 
-// Whether final_rows_fast may take this block: inside the matrix and with
-// rows of W and O aligned to four elements.
+// Whether final_rows_fast may take this 32 x BW block: inside the matrix and
+// with rows of W and O aligned to four elements.
+template <int BW>
 __device__ __forceinline__ bool final_fast_ok(const GemmArgs& a, const EpiState& st, int i0, int j0) {
-  if (i0 + 32 > a.n_real || j0 + kMfmaTile > a.m_real || (a.user_ld & 3) != 0) return false;
+  if (i0 + 32 > a.n_real || j0 + BW > a.m_real || (a.user_ld & 3) != 0) return false;
   const uintptr_t wal = a.w_dtype == kF32 ? 15 : 7, oal = a.o_dtype == kF32 ? 15 : 7;
   return (reinterpret_cast<uintptr_t>(st.w) & wal) == 0 && (reinterpret_cast<uintptr_t>(st.o) & oal) == 0;
 }
 
-template <int LDE>
+template <int LDE, int BW>
 __device__ __forceinline__ void final_rows_any(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
                                                int lane);
 
-// The update of one staged block: the fast form for the dtype pair, or the
-// general one (ragged edges, unaligned rows).
-template <int LDE>
+// The update of one staged 32 x BW block: the fast form for the dtype pair,
+// or the general one (ragged edges, unaligned rows).
+template <int LDE, int BW>
 __device__ __forceinline__ void final_block(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
                                             int lane) {
-  if (final_fast_ok(a, st, i0, j0)) {
+  if (final_fast_ok<BW>(a, st, i0, j0)) {
     const int wdt = st.w != nullptr ? a.w_dtype : -1, odt = st.o != nullptr ? a.o_dtype : -1;
 #define MUON_FAST(WD, OD)                                               \
   if (wdt == WD && odt == OD) {                                         \
-    final_rows_fast<WD, OD, LDE>(a, st, ep, i0, j0, lane);              \
+    final_rows_fast<WD, OD, LDE, BW>(a, st, ep, i0, j0, lane);          \
     return;                                                             \
   }
     MUON_FAST(kF32, -1) MUON_FAST(kBF16, -1) MUON_FAST(-1, kF32) MUON_FAST(-1, kBF16)
     MUON_FAST(kF32, kF32) MUON_FAST(kF32, kBF16) MUON_FAST(kBF16, kF32) MUON_FAST(kBF16, kBF16)
 #undef MUON_FAST
   }
-  final_rows_any<LDE>(a, st, ep, i0, j0, lane);
+  final_rows_any<LDE, BW>(a, st, ep, i0, j0, lane);
 }
 
 // Final product, general form (ragged edges, unaligned rows): W <- W -
 // lr (O + wd W) and the optional store of O, for rows i0 .. i0 + 31 and
-// columns j0 .. j0 + 255 of O staged in LDS (row-major, LDE floats per row),
-// with per-element range checks.
-template <int LDE>
+// columns j0 .. j0 + BW - 1 of O staged in LDS (row-major, LDE floats per
+// row), with per-element range checks.
+template <int LDE, int BW>
 __device__ __forceinline__ void final_rows_any(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
                                                int lane) {
-  constexpr int R = 16;
-  if (!a.transposed) {  // W is n x m: lane -> columns j .. j + 3 of every row
-    const int j = j0 + 4 * lane;
+  constexpr int R = BW == 256 ? 16 : 8;
+  constexpr int LPR = BW / 4, RS = 64 / LPR;  // lanes per row of the block, rows per step
+  if (!a.transposed) {  // W is n x m: lane -> columns j .. j + 3 of rows RS r + lane / LPR
+    const int sub = lane / LPR, cl = 4 * (lane % LPR);
+    const int j = j0 + cl;
     const int valid = a.m_real - j;
-    for (int r0 = 0; r0 < 32; r0 += R) {
+    for (int r0 = 0; r0 < 32; r0 += R * RS) {
       float4 w[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int i = i0 + r0 + r;
+        const int i = i0 + r0 + RS * r + sub;
         w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (st.w != nullptr && i < a.n_real && valid > 0)
           w[r] = user_load4(st.w, static_cast<int64_t>(i) * a.user_ld + j, a.w_dtype, valid);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int i = i0 + r0 + r;
+        const int i = i0 + r0 + RS * r + sub;
         if (i < a.n_real)
           final_update4(a, st, static_cast<int64_t>(i) * a.user_ld + j, valid,
-                        lds_load4(ep + (r0 + r) * LDE + 4 * lane), w[r]);
+                        lds_load4(ep + (r0 + RS * r + sub) * LDE + cl), w[r]);
       }
     }
   } else {  // W is m x n: lane -> W[j][i .. i + 3] for 32 columns j of O
     const int r4 = (lane & 7) * 4;
     const int i = i0 + r4;
     const int valid = a.n_real - i;
-    for (int c0 = 0; c0 < 256; c0 += 8 * R) {
+    for (int c0 = 0; c0 < BW; c0 += 8 * R) {
       float4 w[R];
 #pragma unroll
       for (int t = 0; t < R; ++t) {
@@ -567,9 +572,9 @@ __device__ __forceinline__ void store_tn(uint16_t* t, uint16_t* n, const float (
 // v = alpha C + beta E + gamma [i == j < n_real] in arrangement A, then its
 // stores and partial sums.  MAYDIAG: the tile is on the diagonal of a
 // symmetric product and dblk says whether this block is (ib == jb).  Final
-// kinds write v to the wave's LDS staging area ep (row-major, kLDE floats per
+// kinds write v to the wave's LDS staging area ep (row-major, BN + 4 floats per
 // row) for the update of W.
-template <int OP, int KIND, bool MAYDIAG>
+template <int OP, int KIND, bool MAYDIAG, int FN>
 __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const EpiPtrs& p, const f32x16_t& c,
                                           const uint4 (&ein)[2], int x, int y, int ib, bool dblk, int lane,
                                           const uint4 (&id)[2], lds_f32* ep) {
@@ -596,7 +601,7 @@ __device__ __forceinline__ void epi_block(const GemmArgs& a, EpiState& st, const
   }
   if constexpr (S.fin) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + ir0 + (r & 3)) * kLDE + 32 * y + jr] = v[r];
+    for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + ir0 + (r & 3)) * (32 * FN + 4) + 32 * y + jr] = v[r];
     return;
   }
   if constexpr (S.sym) {
@@ -647,7 +652,7 @@ __device__ __forceinline__ void epi_unit(const GemmArgs& a, EpiState& st, const 
   constexpr int x = (BLK + U) / FN, y = (BLK + U) % FN;
   const int rel = dg + y - (2 * wave + x);
   if (!MAYDIAG || rel <= 0)
-    epi_block<OP, KIND, MAYDIAG>(a, st, p, acc[x][y], cur[U], x, y, I * kBM + wave * (kBM / kNW) + 32 * x,
+    epi_block<OP, KIND, MAYDIAG, FN>(a, st, p, acc[x][y], cur[U], x, y, I * kBM + wave * (kBM / kNW) + 32 * x,
                                  MAYDIAG && rel == 0, lane, id, ep);
   if constexpr (U + 1 < G)
     epi_unit<OP, KIND, MAYDIAG, FN, G, BLK, U + 1>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
@@ -699,15 +704,14 @@ __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st,
   constexpr EpiSpec S = epi_spec(KIND);
   const EpiPtrs p = epi_ptrs<KIND, BN>(a, b, I, J, wave);
   if constexpr (S.fin) {
-    static_assert(BN == kMfmaTile, "the last product uses 256-wide tiles");
     const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // no transposes here
     epi_range<OP, KIND, false, FN, 0, FN>(a, st, p, acc, I, 0, wave, lane, id, ep);
     __syncthreads();
-    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW), J * BN, lane);
+    final_block<BN + 4, BN>(a, st, ep, I * kBM + wave * (kBM / kNW), J * BN, lane);
     __syncthreads();
     epi_range<OP, KIND, false, FN, FN, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
     __syncthreads();
-    final_block<kLDE>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * BN, lane);
+    final_block<BN + 4, BN>(a, st, ep, I * kBM + wave * (kBM / kNW) + 32, J * BN, lane);
   } else {
     const uint4 id[2] = {ident_frag<OP>(0, lane), ident_frag<OP>(1, lane)};
     // a symmetric tile meets the diagonal when its column range overlaps its
@@ -1007,12 +1011,16 @@ template <int OP>
 hipError_t launch_gemm_mfma(const GemmArgs& a, int batch, int kind, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>(a.ntiles) * batch;
   const dim3 grid(static_cast<unsigned>(a.full_blocks + (tiles - a.full_blocks) * a.kpieces)), block(kNT);
-  if (a.bn == kHalfTile) {  // symmetric products without the last-product or tail-split paths
-    if (!a.sym || a.kpieces != 1) return hipErrorInvalidValue;
+  if (a.bn == kHalfTile) {  // short symmetric products and last products, without the tail split
+    if (a.kpieces != 1) return hipErrorInvalidValue;
+    const bool fin = kind == kEpiFin || kind == kEpiFinE16;
+    if (fin ? a.sym != 0 : a.sym == 0) return hipErrorInvalidValue;
     switch (kind) {
       case kEpiSym: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSym, kHalfTile>), grid, block, 0, s, a); break;
       case kEpiSymE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16, kHalfTile>), grid, block, 0, s, a); break;
       case kEpiSymE16Q: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiSymE16Q, kHalfTile>), grid, block, 0, s, a); break;
+      case kEpiFin: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFin, kHalfTile>), grid, block, 0, s, a); break;
+      case kEpiFinE16: hipLaunchKernelGGL((gemm_nt_mfma<OP, kEpiFinE16, kHalfTile>), grid, block, 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
