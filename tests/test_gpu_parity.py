@@ -235,6 +235,42 @@ def test_muon_step_transposed_bf16_weights():
     assert np.all(err <= 0.05 * np.abs(syn.to_f64(O1[0]) - Or) + np.abs(Wr) * 2.0 ** -8 + 1e-6)
 
 
+@pytest.mark.parametrize("variant", ["standard", "gram"])
+@pytest.mark.parametrize("shape,w_bf16", [((300, 1100), False), ((1100, 300), True), ((512, 1536), True),
+                                          ((768, 512), False)])
+def test_last_product_same_update_for_every_output_choice(variant, shape, w_bf16):
+    """The last product updates W from its fp32 result staged on chip, so W
+    and M come out bit for bit the same whether O is also written (fp32 or
+    bf16) or not, and the bf16 O is the fp32 O rounded to nearest even.  This
+    covers each (W, O) dtype pair of the fused update, both orientations and
+    ragged edges; the run without O (the usual training call) is also checked
+    against the oracle."""
+    r, c = shape
+    W0 = syn.random_matrix(70, r, c, dtype="bf16" if w_bf16 else "f32")
+    M0 = syn.random_matrix(71, r, c, std=1e-3, dtype="bf16")
+    G0 = syn.random_matrix(72, r, c, std=1e-3, dtype="bf16")
+    res = {}
+    for odt in (None, torch.float32, torch.bfloat16):
+        W, M, G = W0.to(DEV), M0.to(DEV), G0.to(DEV)
+        O = None if odt is None else [torch.empty(r, c, dtype=odt, device=DEV)]
+        mu.muon_step([W], [M], [G], 0.95, 0.02, 0.01, variant, None, O_out=O)
+        torch.cuda.synchronize()
+        res[odt] = (W.cpu(), M.cpu(), None if O is None else O[0].cpu())
+    for odt in (torch.float32, torch.bfloat16):
+        assert torch.equal(res[odt][0], res[None][0]) and torch.equal(res[odt][1], res[None][1]), odt
+    assert torch.equal(res[torch.bfloat16][2], res[torch.float32][2].to(torch.bfloat16))
+    mu32, lr32, wd32 = (float(np.float32(v)) for v in (0.95, 0.02, 0.01))
+    Wr, Mr, Or = orc.muon_step(syn.to_f64(W0), syn.to_f64(M0), syn.to_f64(G0), mu32, lr32, wd32, variant,
+                               state_dtype="bf16", w_dtype="f64")
+    assert np.array_equal(syn.to_f64(res[None][1]), Mr)
+    assert relF(syn.to_f64(res[torch.float32][2]), Or) < 2e-2
+    dW = syn.to_f64(res[None][0]) - syn.to_f64(W0)
+    # bf16 weights: the update also carries one bf16 rounding of W per element
+    bound = 2e-2 + (np.abs(syn.to_f64(W0)).max() * 2.0 ** -8 * np.sqrt(r * c) / np.linalg.norm(Wr - syn.to_f64(W0))
+                    if w_bf16 else 1e-4)
+    assert relF(dW, Wr - syn.to_f64(W0)) < bound
+
+
 @pytest.mark.parametrize("variant,compute", [("standard", "bf16"), ("gram", "f16"), ("standard", "f32")])
 @pytest.mark.parametrize("shape", [(256, 700), (300, 200)])
 def test_muon_step_update_scale_and_weight_decay(variant, compute, shape):
