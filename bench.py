@@ -72,14 +72,40 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_step_amd", "csrc")
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed
+    (string and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest() -> str:
-    """sha256 over the HIP sources: a traffic figure holds only for the code it was taken on."""
+    """sha256 over the code of the HIP sources (comments and layout left out):
+    a traffic figure holds only for the code it was taken on."""
     import hashlib
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
     return h.hexdigest()
 
 

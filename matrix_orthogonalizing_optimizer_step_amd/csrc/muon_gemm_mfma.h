@@ -60,7 +60,8 @@ constexpr int kLoadsA = kFM * kKS;    // P loads per wave and slab
 // waves per SIMD, so one wave's waits and barrier are covered by the other's
 // MFMAs), 2 x 4 MFMA blocks (128 accumulator registers) per wave, P two slabs
 // ahead in three buffers; used for symmetric products with k = n (short), where
-// the finer tiles also fill the last round better.
+// the finer tiles also fill the last round better, and for the last product
+// (k = n), where one block's update of W overlaps the other block's MFMAs.
 template <int BN>
 struct TileCfg {
   static constexpr int kFN = BN / 32;          // MFMA column blocks per wave
@@ -694,7 +695,7 @@ __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const
 }
 
 // The register epilogue of the wave's 64 x BN sub-tile; the last product
-// (256-wide tiles only) stages O through LDS one 32-row block at a time so
+// stages O through LDS one 32-row block (32 x BN) at a time so
 // that the user's row-major W is read and written along its rows.
 template <int OP, int KIND, int BN>
 __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st,
