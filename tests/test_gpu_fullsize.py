@@ -15,7 +15,9 @@ about 2e12 fp64 FLOPs, seconds on the host's BLAS).  For the 3584x18944
 group O is also checked through properties that hold at any size: its
 singular values lie in the band the quintic coefficients imply, and Gram and
 standard Newton-Schulz on the GPU agree (they are equal in exact
-arithmetic).
+arithmetic).  Standard Newton-Schulz (bf16 operands), the bench's other
+variant, is compared with the oracle in full on the q/o and 3584x18944
+groups the same way.
 """
 import numpy as np
 import pytest
@@ -91,3 +93,21 @@ def test_fullsize_mlp_group_against_oracle_and_properties():
     rel = lambda a, b: (torch.linalg.matrix_norm((a - b).double()) / torch.linalg.matrix_norm(b.double())).item()
     assert rel(Og, O0) < 1e-3
     assert rel(Os, Og) < 3e-2
+
+
+@pytest.mark.parametrize("gi", [0, 2], ids=["qo-3584x3584", "mlp-3584x18944"])
+def test_fullsize_standard_ns_against_oracle(gi):
+    """Standard Newton-Schulz (bf16 operands, T = 5), the bench's other
+    variant, on a whole same-shape group in one call: the first matrix against
+    the fp64 oracle element by element, and the momentum bit for bit."""
+    Ws, Ms, G0 = syn.group_inputs(WL, gi)
+    W = [w.to(DEV) for w in Ws]
+    M = [m.to(DEV) for m in Ms]
+    O = [torch.empty(w.shape, dtype=torch.float32, device=DEV) for w in W]
+    mu.muon_step(W, M, [g.to(DEV) for g in G0], MU, LR, 0.0, "standard", O_out=O)
+    torch.cuda.synchronize()
+    mu32 = float(np.float32(MU))
+    expect = orc.round_bf16(mu32 * syn.to_f64(Ms[0]) + syn.to_f64(G0[0]))
+    assert np.array_equal(syn.to_f64(M[0]), expect)
+    ref = orc.newton_schulz(syn.to_f64(M[0]))
+    assert orc.relative_frobenius(syn.to_f64(O[0]), ref) < 2e-2
