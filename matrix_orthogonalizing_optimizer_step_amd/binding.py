@@ -174,8 +174,8 @@ def pointer_array(tensors: Sequence[torch.Tensor]) -> torch.Tensor:
     arr = _ptr_cache.get(key)
     if arr is None:
         if capturing:
-            raise MuonError("pointer array not cached for these tensors: under graph capture, "
-                            "call once with the same tensors before capturing")
+            raise MuonError(1, "pointer array not cached for these tensors: under graph capture, "
+                               "call once with the same tensors before capturing")  # MUON_ERR_INVALID_ARG
         if len(_ptr_cache) >= _PTR_CACHE_MAX:
             if dev.type == "cuda":  # a kernel on any stream may still read the array: wait before freeing it
                 torch.cuda.synchronize(dev)

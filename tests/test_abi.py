@@ -184,3 +184,28 @@ def test_pointer_array_cache_evicts_least_recently_used():
     assert bd.pointer_array(keep).tolist() == [keep[0].data_ptr()]
     assert (str(keep[0].device), (others[0][0].data_ptr(),)) not in bd._ptr_cache
     bd._ptr_cache.clear()
+
+
+def test_pointer_array_miss_under_capture_is_a_muon_error(monkeypatch):
+    """Under graph capture an uncached pointer array is refused with the
+    library's invalid-argument status (checked on the CPU by faking the
+    capture state; no device work)."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+
+    class FakeDev:
+        type = "cuda"
+
+        def __str__(self):
+            return "cuda:99"
+
+    class FakeTensor:
+        device = FakeDev()
+
+        def data_ptr(self):
+            return 0x1234500
+
+    bd._ptr_cache.clear()
+    with pytest.raises(bd.MuonError, match="before capturing") as e:
+        bd.pointer_array([FakeTensor()])
+    assert e.value.status == 1

@@ -360,6 +360,33 @@ def test_muon_step_in_a_hip_graph(variant):
             assert torch.equal(a, b), rep
 
 
+def test_capture_without_a_prior_call_raises_cleanly():
+    """Pointer arrays are made by a host-to-device copy, which a capturing
+    stream does not allow: capturing a step on tensors never used before
+    raises MuonError before anything is enqueued, and the device stays usable
+    (a normal step afterwards matches one on a copy of the inputs)."""
+    W = [syn.random_matrix(80, 256, 512).to(DEV)]
+    M = [torch.zeros(256, 512, dtype=torch.bfloat16, device=DEV)]
+    G = [syn.random_matrix(81, 256, 512, std=1e-3, dtype="bf16").to(DEV)]
+    ws = torch.empty(mu.workspace_size(1, 256, 512, "gram"), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    # the allocator may hand out addresses an earlier test's arrays were keyed on
+    from matrix_orthogonalizing_optimizer_step_amd import binding as bd
+    for lst in (W, M, G):
+        key = (str(lst[0].device), tuple(int(t.data_ptr()) for t in lst))
+        bd._ptr_cache.pop(key, None)
+        bd._ptr_pinned.pop(key, None)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(mu.MuonError, match="before capturing"):
+        with torch.cuda.graph(g):
+            mu.muon_step(W, M, G, 0.95, 0.02, 0.0, "gram", None, workspace=ws)
+    We, Me = [w.clone() for w in W], [m.clone() for m in M]
+    mu.muon_step(W, M, G, 0.95, 0.02, 0.0, "gram", None, workspace=ws)
+    mu.muon_step(We, Me, G, 0.95, 0.02, 0.0, "gram", None)
+    torch.cuda.synchronize()
+    assert torch.equal(W[0], We[0]) and torch.equal(M[0], Me[0])
+
+
 @pytest.mark.parametrize("variant", ["standard", "gram"])
 def test_narrow_and_wide_tiles_agree_bitwise(variant):
     """A batch of one 512x1536 matrix runs its symmetric products in 256x128
