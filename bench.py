@@ -605,7 +605,43 @@ def cpu_baseline(wl, variant, mu, syn):
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} pass(es) of one Muon step ({variant} NS, fp64 numpy) on one matrix of each group: "
                       + ", ".join(names),
-            "seconds": sec, "host_cpus": os.cpu_count()}
+            "seconds": sec, "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "single_thread": single_thread_oracle(mu, syn)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_oracle(mu, syn):
+    """The oracle's standard-NS step on one 256x512 fp32 matrix with one BLAS
+    thread (whole passes, about one second)."""
+    import numpy as np
+
+    from oracle import muon_oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    rows, cols = 256, 512
+    W, M, G = (syn.to_f64(syn.random_matrix(90 + i, rows, cols)) for i in range(3))
+    flops, passes = mu.ns_flops(rows, cols, "standard", mu.NSConfig(), True), 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while passes == 0 or (passes < 50 and time.perf_counter() - t0 < 1.0):
+            orc.muon_step(W, M, G, float(np.float32(0.95)), float(np.float32(0.02)), 0.0, "standard",
+                          state_dtype="f32", w_dtype="f32")
+            passes += 1
+        sec = time.perf_counter() - t0
+    return {"value": flops * passes / sec / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "sample": f"{passes} pass(es) of one Muon step (standard NS, fp64 numpy) on one 256x512 matrix"}
 
 
 if __name__ == "__main__":
