@@ -109,6 +109,15 @@ __device__ __forceinline__ void load_a_slab(uint4 (&buf)[kFM][kKS], __amdgpu_buf
           r, voff, __builtin_amdgcn_readfirstlane(sbase + f * rb_stride + kt * 4096 + s * 1024), 0));
 }
 
+// The P fragments of k-step s of slab kt for this wave (kFM loads).
+__device__ __forceinline__ void load_a_part(uint4 (&buf)[kFM][kKS], __amdgpu_buffer_rsrc_t r, int voff, int sbase,
+                                            int rb_stride, int kt, int s) {
+#pragma unroll
+  for (int f = 0; f < kFM; ++f)
+    buf[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+        r, voff, __builtin_amdgcn_readfirstlane(sbase + f * rb_stride + kt * 4096 + s * 1024), 0));
+}
+
 // The Q slab kt into LDS stage `stage`: this wave's row blocks x 4 fragments.
 template <int BN>
 __device__ __forceinline__ void load_b_slab(uint4* stage, __amdgpu_buffer_rsrc_t r, int voff, int sbase,
@@ -191,6 +200,30 @@ __device__ __forceinline__ void slab(f32x16_t (&acc)[kFM][TileCfg<BN>::kFN], con
   // issued) have landed and its part of slab kt + 1 is in LDS (the 5 load
   // groups issued after it may still be in flight); after the barrier the
   // whole slab kt + 1 is visible and nobody reads `cur`.
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(TileCfg<BN>::kWaitBarrier, kFN / 2));
+  block_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_b_slab<BN>(cur, rQ, voff, sQ, qstride, kt + kStages, wave);
+  kstep_half<OP, kFN, kFN / 2>(acc, a, 3, bf[1], bf[0], nxt, lane);
+}
+
+// slab() with the P fragments of slab ktp loaded into `anext` a k-step at a
+// time (all before the barrier, so the barrier's count is unchanged).
+template <int OP, int BN>
+__device__ __forceinline__ void slab_spread(f32x16_t (&acc)[kFM][TileCfg<BN>::kFN], const uint4 (&a)[kFM][kKS],
+                                            uint4 (&bf)[2][TileCfg<BN>::kFN], uint4* cur, const uint4* nxt,
+                                            uint4 (&anext)[kFM][kKS], __amdgpu_buffer_rsrc_t rP, int sP, int pstride,
+                                            int ktp, __amdgpu_buffer_rsrc_t rQ, int voff, int sQ, int qstride, int kt,
+                                            int wave, int lane) {
+  constexpr int kFN = TileCfg<BN>::kFN;
+  load_a_part(anext, rP, voff, sP, pstride, ktp, 0);
+  kstep<OP, kFN>(acc, a, 0, bf[0], bf[1], cur + 1 * 64, true, lane);
+  load_a_part(anext, rP, voff, sP, pstride, ktp, 1);
+  kstep<OP, kFN>(acc, a, 1, bf[1], bf[0], cur + 2 * 64, true, lane);
+  load_a_part(anext, rP, voff, sP, pstride, ktp, 2);
+  kstep<OP, kFN>(acc, a, 2, bf[0], bf[1], cur + 3 * 64, true, lane);
+  load_a_part(anext, rP, voff, sP, pstride, ktp, 3);
+  kstep_half<OP, kFN, 0>(acc, a, 3, bf[1], bf[0], nxt, lane);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(TileCfg<BN>::kWaitBarrier, kFN / 2));
   block_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -972,8 +1005,8 @@ __global__ __launch_bounds__(kNT, BN == kMfmaTile ? 1 : 2) void gemm_nt_mfma(Gem
     // slabs ahead); the slab count is a multiple of 4, so the trip may end
     // after its 4th or 8th slab
 #define MUON_SLAB(U, BUF, NEXTBUF, CUR, NXT)                                                           \
-  load_a_slab(NEXTBUF, rP, voff, sP, pstride, kt + U + 2);                                             \
-  slab<OP, BN>(acc, BUF, bf, CUR, NXT, rQ, voff, sQ, qstride, kt + U, wave, lane);
+  slab_spread<OP, BN>(acc, BUF, bf, CUR, NXT, NEXTBUF, rP, sP, pstride, kt + U + 2, rQ, voff, sQ, qstride,      \
+                      kt + U, wave, lane);
     for (int kt = k0;; kt += 12) {
       MUON_SLAB(0, abuf0, abuf2, stg0, stg1)
       MUON_SLAB(1, abuf1, abuf0, stg1, stg2)
