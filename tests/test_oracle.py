@@ -64,6 +64,46 @@ def test_bf16_rounding_matches_torch_on_float32_values():
     np.testing.assert_array_equal(orc.round_bf16(x.astype(np.float64)), ref)
 
 
+def test_bf16_rounding_of_non_contiguous_input():
+    # a transposed view and a strided slice give the rounding of their own
+    # elements in their own positions (an element-order slip would scramble them)
+    one, ulp = 1.0, 2.0 ** -7
+    A = np.array([[one + ulp / 2, 3.0, -(one + 1.5 * ulp)],
+                  [0.0, one + ulp / 2 + 2.0 ** -40, 5.0e-39]])
+    want = np.array([[one, 3.0, -(one + 2 * ulp)],
+                     [0.0, one + ulp, np.round(5.0e-39 / 2.0 ** -133) * 2.0 ** -133]])
+    np.testing.assert_array_equal(orc.round_bf16(A.T), want.T)
+    np.testing.assert_array_equal(orc.round_bf16(A[:, ::2]), want[:, ::2])
+    x = rng(7).standard_normal((37, 53)).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(np.ascontiguousarray(x.T)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_bf16(x.T), ref)
+    np.testing.assert_array_equal(orc.round_bf16(x[::3, 1::2]), orc.round_bf16(x)[::3, 1::2])
+
+
+def test_relative_frobenius_hand_values():
+    # ||x - ref||_F / ||ref||_F with values worked out by hand; pairs of equal
+    # norm and nonzero difference rule out a comparison of norms alone
+    I4 = np.eye(4)
+    assert orc.relative_frobenius(-I4, I4) == pytest.approx(2.0, abs=1e-15)
+    assert orc.relative_frobenius(I4, I4) == 0.0
+    E = np.array([[0.0, 1.0, 0.0, 0.0], [0.0, 0.0, 0.0, 2.0], [0.0, 0.0, 0.0, 0.0], [2.0, 0.0, 0.0, 0.0]])
+    assert orc.relative_frobenius(I4 + E, I4) == pytest.approx(3.0 / 2.0, abs=1e-15)  # ||E|| = 3, ||I4|| = 2
+    # a permutation of the entries: same norm, distance sqrt(2) of the norm
+    a, b = np.array([[1.0, 0.0], [0.0, 0.0]]), np.array([[0.0, 1.0], [0.0, 0.0]])
+    assert orc.relative_frobenius(a, b) == pytest.approx(np.sqrt(2.0), abs=1e-15)
+    # the reference is the second argument: the metric is not symmetric
+    assert orc.relative_frobenius(np.array([[3.0]]), np.array([[1.0]])) == pytest.approx(2.0)
+    assert orc.relative_frobenius(np.array([[1.0]]), np.array([[3.0]])) == pytest.approx(2.0 / 3.0)
+    # a rotation by 90 degrees of a 2-vector: |x| = |ref| = 5, |x - ref| = 5 sqrt(2)
+    assert orc.relative_frobenius(np.array([[-4.0, 3.0]]), np.array([[3.0, 4.0]])) == pytest.approx(np.sqrt(2.0))
+    # an all-zero reference: the plain norm of the difference
+    assert orc.relative_frobenius(np.array([[3.0, 4.0]]), np.zeros((1, 2))) == pytest.approx(5.0)
+    # transposed inputs compare position by position
+    x = np.array([[1.0, 2.0, 0.0]])
+    assert orc.relative_frobenius(x.T, x.T.copy()) == 0.0
+    assert orc.relative_frobenius(x[:, ::-1], x) == pytest.approx(np.sqrt(2.0 / 5.0))  # [0, 2, 1] - [1, 2, 0]
+
+
 def test_round_to_idempotent_and_dtypes():
     x = rng(1).standard_normal(1000)
     for dt in ("f32", "bf16", "f16"):
