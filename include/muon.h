@@ -89,7 +89,13 @@ typedef enum {
  *   compute      MFMA operand type: MUON_BF16 (standard default), MUON_F16
  *                (Gram default: [GNS §3.3] casts to float16), or MUON_F32 for
  *                the slow fp32 check path (fp32 operands, fp64 accumulation).
- *                Products always accumulate in fp32 or wider.
+ *                Products always accumulate in fp32 or wider.  MUON_BF16 is
+ *                accepted for the standard variant with the fixed quintic
+ *                only; with the Gram variant or any other coefficient table
+ *                every entry point returns MUON_ERR_UNSUPPORTED (and
+ *                muon_workspace_size 0): bf16's 8-bit significand exceeds
+ *                the 2e-2 relative error of the 16-bit path there, where
+ *                MUON_F16, at the same MFMA rate, stays within it.
  *   shift        1 (default): each iteration splits its a_t I term into a
  *                diagonal shift a' (the mean of a_t + b_t l + c_t l^2 over the
  *                eigenvalues l of the Gram matrix, from its trace and

@@ -157,13 +157,24 @@ muon_status make_config(const muon_ns_config* user, muon_ns_variant v, Config* o
   if (!valid_dtype(cfg.compute)) return MUON_ERR_INVALID_ARG;
   if (v == MUON_NS_GRAM && (cfg.restart_mask >> (cfg.T - 1)) != 0u) return MUON_ERR_INVALID_ARG;
   out->T = cfg.T;
+  bool quintic = true;  // the fixed quintic for every t
   for (int t = 0; t < cfg.T; ++t) {
     for (int k = 0; k < 3; ++k) {
       const float x = cfg.coeffs != nullptr ? cfg.coeffs[3 * t + k] : kQuintic[k];
       if (!isfinite(x)) return MUON_ERR_INVALID_ARG;
       out->c[t][k] = x;
+      quintic = quintic && x == kQuintic[k];
     }
   }
+  // bf16 operands (8 significant bits) stay within the 2e-2 relative error
+  // of the 16-bit path only for standard NS with the fixed quintic.  Gram NS
+  // computes in float16 ([GNS §3.3], [GNS §3.4 Alg.2]): with bf16 operands
+  // square matrices (singular values down to ~n^-1.5 of the norm) measure
+  // 2-3.5e-2.  Steep per-iteration polynomials (a_1 ~ 8.5 in the derived
+  // minimax schedules) amplify bf16 rounding past the tolerance as well
+  // (up to 2.6e-2 standard, 1.05e-1 Gram); float16 operands, at the same
+  // MFMA rate, hold both.
+  if (cfg.compute == MUON_BF16 && (v == MUON_NS_GRAM || !quintic)) return MUON_ERR_UNSUPPORTED;
   out->eps = cfg.eps;
   out->restart_mask = v == MUON_NS_GRAM ? cfg.restart_mask : 0u;
   out->op = cfg.compute == MUON_F32 ? kOpF32 : (cfg.compute == MUON_BF16 ? kOpBF16 : kOpF16);

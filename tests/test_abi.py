@@ -100,6 +100,42 @@ def test_invalid_calls_fail_before_any_device_work():
     assert _call_orth(lib, cfg=ctypes.byref(bad)) == 1
 
 
+def test_bf16_refused_for_gram_and_for_other_coefficient_tables():
+    """bf16 operands are accepted for standard NS with the fixed quintic only:
+    Gram NS computes in float16 (Gram NS notes, section 3.3) and other
+    coefficient tables amplify bf16 rounding past the 16-bit tolerance.  The
+    refusal is MUON_ERR_UNSUPPORTED, returned before any device work (bogus
+    pointers are safe), and the workspace size is 0 for such a config."""
+    lib = mu.load_library()
+
+    def cfg_of(variant, compute, coeffs=None, T=5):
+        c, keep = bd.NSConfig(T=T, compute=compute, coeffs=coeffs).to_c(variant)
+        return c, keep
+
+    quintic = [orc.QUINTIC] * 5
+    cases = [(bd.GRAM, "bf16", None, 5, 2), (bd.GRAM, "bf16", quintic, 5, 2),
+             (bd.STANDARD, "bf16", [(1.0, 0.0, 0.0)], 1, 2), (bd.STANDARD, "bf16", quintic[:4] + [(3.0, -3.2, 1.2)], 5, 2),
+             (bd.STANDARD, "bf16", None, 5, 0), (bd.STANDARD, "bf16", quintic, 5, 0), (bd.STANDARD, "bf16", None, 3, 0),
+             (bd.STANDARD, "f16", [(1.0, 0.0, 0.0)], 1, 0), (bd.GRAM, "f16", None, 5, 0), (bd.GRAM, "f32", None, 5, 0)]
+    for variant, compute, coeffs, T, code in cases:
+        c, keep = cfg_of(variant, compute, coeffs, T)
+        if variant == bd.GRAM and T < 3:
+            c.restart_mask = 0
+        fn = lib.ns_orthogonalize if variant == bd.STANDARD else lib.gram_ns_orthogonalize
+        ws = lib.muon_workspace_size(1, 4, 4, variant, ctypes.byref(c))
+        if code == 0:
+            assert ws > 0, (variant, compute, coeffs)
+        else:
+            assert ws == 0, (variant, compute, coeffs)
+            assert fn(1, 4, 4, 1, 0, 2, 0, ctypes.byref(c), 256, 1 << 30, None) == code
+            assert lib.muon_step(1, 4, 4, 1, 0, 2, 3, 1, 0.9, 0.1, 0.0, 1.0, variant, ctypes.byref(c), None, 0,
+                                 256, 1 << 30, None) == code
+            assert lib.muon_grasp_step(1, 8, 8, 0, 1, 0, ctypes.byref(bd._GraspState(*([16] * 7))), 2, 1, 0.9, 0.1,
+                                       0.0, 1.0, variant, ctypes.byref(c), None, 0, None, 256, 1 << 30, None,
+                                       None) == code
+        del keep
+
+
 def test_invalid_muon_step_calls():
     lib = mu.load_library()
     ws = mu.workspace_size(1, 4, 4)

@@ -52,6 +52,11 @@ def test_one_iteration_with_probe_coefficients(compute, shape, abc):
     """T = 1 isolates the products: (1,0,0) is the normalisation alone,
     (0,1,0) is X X^T X, (0,0,1) is (X X^T)^2 X."""
     M = syn.random_matrix(1, *shape)
+    if compute == "bf16":  # bf16 operands take the fixed quintic only
+        with pytest.raises(mu.MuonError) as e:
+            gpu_orth("standard", [M], compute, T=1, coeffs=[abc])
+        assert e.value.status == 2
+        return
     for shift in (True, False):
         got = gpu_orth("standard", [M], compute, T=1, coeffs=[abc], shift=shift)[0]
         ref = oracle_orth("standard", M, T=1, coeffs=[abc])
@@ -76,9 +81,12 @@ def test_standard_ns_parity(compute, shape):
 @pytest.mark.parametrize("restarts", [(2,), (), (1, 2, 3, 4)])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_gram_ns_parity(compute, restarts, shape):
-    if compute == "bf16" and shape[0] == shape[1]:
-        pytest.skip("bf16 Gram NS on square matrices is outside 2e-2; fp16 is the Gram compute type")
     M = syn.random_matrix(3, *shape, std=1e-3, dtype="bf16")
+    if compute == "bf16":  # Gram NS computes in float16; bf16 is refused (outside 2e-2 on squares)
+        with pytest.raises(mu.MuonError) as e:
+            gpu_orth("gram", [M], compute, restarts=restarts)
+        assert e.value.status == 2
+        return
     got = gpu_orth("gram", [M], compute, restarts=restarts)[0]
     ref = oracle_orth("gram", M, restarts=restarts)
     assert relF(got, ref) < TOL[compute], relF(got, ref)
@@ -91,9 +99,10 @@ def test_quintic_schedule_parity(variant, compute, f):
     """Per-iteration minimax quintics from the library's schedule (ell = 1e-3,
     with and without the safety factor), restart after iteration 2 for Gram,
     against the oracle run with the same fp32 coefficients.  The steep first
-    polynomials amplify operand rounding: bf16 operands measure up to 2.6e-2
-    on 700 x 256, over the 16-bit tolerance, so the 16-bit case runs with the
-    fp16 operands that the Gram NS notes recommend (section 3.3)."""
+    polynomials amplify operand rounding: bf16 operands measured up to 2.6e-2
+    on 700 x 256, over the 16-bit tolerance, so the library refuses bf16 with
+    such a table and the 16-bit case runs with the fp16 operands that the Gram
+    NS notes recommend (section 3.3)."""
     coeffs, _ = mu.quintic_schedule(5, 1e-3, f)
     for shape in ((300, 1100), (700, 256)):
         M = syn.random_matrix(50, *shape, std=1e-3, dtype="bf16")
