@@ -163,6 +163,31 @@ def random_matrix(seed: int, rows: int, cols: int, std: float = 1.0, dtype: str 
     return gaussian(9000 + seed, 0, 0, rows, cols, std, dtype)
 
 
+def dyadic_matrix(seed: int, n: int, m: int, dtype: str = "bf16"):
+    """An n x m matrix (n a power of two, n <= m) whose entries all come from
+    one seeded Gaussian vector g of length n (stored in ``dtype``): the n x n
+    block D[r][c] = g[r XOR c] sits in n columns chosen by a seeded
+    permutation, each with a seeded sign; the other m - n columns are zero.
+    Returns (matrix as a CPU tensor, g, the column of D for every output
+    column or -1, the column signs).  Only random draws and index shuffling
+    happen here."""
+    if n & (n - 1) or n > m:
+        raise ValueError("n must be a power of two and at most m")
+    r = _rng(9700 + seed, n, m)
+    g = r.standard_normal(n).astype(np.float32)
+    g = _store(g[None, :], dtype).to(torch.float64).numpy()[0]
+    perm = r.permutation(m)
+    src = np.full(m, -1, dtype=np.int64)
+    src[perm[:n]] = np.arange(n)
+    signs = np.where(r.random(m) < 0.5, -1.0, 1.0)
+    idx = np.arange(n, dtype=np.int32)
+    D = g[np.bitwise_xor.outer(idx, idx)].astype(np.float32)
+    out = np.zeros((n, m), dtype=np.float32)
+    cols = perm[:n]
+    out[:, cols] = D * signs[cols][None, :].astype(np.float32)
+    return _store(out, dtype), g, src, signs
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a CPU or device tensor's stored values."""
     return t.detach().to("cpu", torch.float64).numpy()

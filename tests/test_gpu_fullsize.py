@@ -16,8 +16,8 @@ group O is also checked through properties that hold at any size: its
 singular values lie in the band the quintic coefficients imply, and Gram and
 standard Newton-Schulz on the GPU agree (they are equal in exact
 arithmetic).  Standard Newton-Schulz (bf16 operands), the bench's other
-variant, is compared with the oracle in full on the q/o and 3584x18944
-groups the same way.
+variant, is compared with the oracle in full on every group the same way
+(k/v is iterated transposed: n = 512, m = 3584).
 """
 import numpy as np
 import pytest
@@ -95,7 +95,7 @@ def test_fullsize_mlp_group_against_oracle_and_properties():
     assert rel(Os, Og) < 3e-2
 
 
-@pytest.mark.parametrize("gi", [0, 2], ids=["qo-3584x3584", "mlp-3584x18944"])
+@pytest.mark.parametrize("gi", [0, 1, 2], ids=["qo-3584x3584", "kv-3584x512", "mlp-3584x18944"])
 def test_fullsize_standard_ns_against_oracle(gi):
     """Standard Newton-Schulz (bf16 operands, T = 5), the bench's other
     variant, on a whole same-shape group in one call: the first matrix against

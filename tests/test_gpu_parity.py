@@ -166,6 +166,33 @@ def test_zero_matrix_gives_zero():
         assert np.all(O == 0)
 
 
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")], ids=["nan", "inf"])
+@pytest.mark.parametrize("variant", ["standard", "gram"])
+def test_non_finite_momentum_propagates(variant, bad):
+    """A NaN or Inf in the gradient propagates: the stored momentum holds it
+    at its own position only (bit for bit against the oracle's rounding), and
+    the norm, hence every entry of O and of the updated W, becomes NaN, as the
+    fp64 oracle's IEEE arithmetic gives (Inf / ||M|| = Inf / Inf).  The
+    device stays usable: a finite step right after matches the oracle."""
+    r, c = 300, 520
+    W = syn.random_matrix(95, r, c)
+    G = syn.random_matrix(96, r, c, std=1e-3, dtype="bf16")
+    G[17, 401] = bad
+    Mp = torch.zeros(r, c, dtype=torch.bfloat16)
+    W1, M1, O1 = run_step([W], [Mp], [G], 0.95, 0.02, 0.0, variant)
+    Wr, Mr, Or = orc.muon_step(syn.to_f64(W), syn.to_f64(Mp), syn.to_f64(G), float(np.float32(0.95)),
+                               float(np.float32(0.02)), 0.0, variant, state_dtype="bf16", w_dtype="f64")
+    assert np.array_equal(syn.to_f64(M1[0]), Mr, equal_nan=True)
+    assert np.isnan(Or).all() and np.isnan(Wr).all()
+    assert torch.isnan(O1[0]).all() and torch.isnan(W1[0]).all()
+    G[17, 401] = 0.0
+    W2, M2, O2 = run_step([W], [Mp], [G], 0.95, 0.02, 0.0, variant)
+    Wr, Mr, Or = orc.muon_step(syn.to_f64(W), syn.to_f64(Mp), syn.to_f64(G), float(np.float32(0.95)),
+                               float(np.float32(0.02)), 0.0, variant, state_dtype="bf16", w_dtype="f64")
+    assert np.array_equal(syn.to_f64(M2[0]), Mr)
+    assert relF(syn.to_f64(O2[0]), Or) < 2e-2
+
+
 def test_bf16_output():
     M = syn.random_matrix(21, 256, 512, dtype="bf16")
     got = gpu_orth("standard", [M], "bf16", odt=torch.bfloat16)[0]
