@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 #define MUON_MAX_T 16
 #define MUON_MAX_DIM (1 << 20)
 #define MUON_GRASP_MAX_K 1024
@@ -190,6 +190,33 @@ muon_status muon_step(int batch, int rows, int cols,
                       muon_ns_variant variant, const muon_ns_config *cfg,
                       void *const *O_out, muon_dtype o_dtype,
                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * muon_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It runs the same kernels as muon_step, with its
+ * scratch memory in a fixed device array of MUON_FIXED_SCRATCH_BYTES inside
+ * the library: one copy per device, allocated when the library's code is
+ * loaded on that device and held until the process ends.  The call itself
+ * allocates nothing; the caller still passes every input and output.
+ *
+ *   Arguments, checks and results as muon_step.  A problem whose workspace
+ *   (muon_workspace_size for the same batch, shape, variant and cfg) exceeds
+ *   MUON_FIXED_SCRATCH_BYTES is rejected with MUON_ERR_WORKSPACE before any
+ *   device work.  The first call on a device looks up the array's address
+ *   there (MUON_ERR_HIP if that fails).
+ *   Every call on one device shares that device's array and leaves its
+ *   contents behind: calls that overlap on one device (on different streams
+ *   or from different threads without ordering) race and give wrong results.
+ *   Order them on one stream, or use muon_step with separate workspaces.
+ */
+#define MUON_FIXED_SCRATCH_BYTES ((size_t)64 << 20)
+muon_status muon_step_fixed_scratch(int batch, int rows, int cols,
+                                    void *const *W, muon_dtype w_dtype,
+                                    void *const *M, const void *const *G, muon_dtype state_dtype,
+                                    float mu, float lr, float weight_decay, float update_scale,
+                                    muon_ns_variant variant, const muon_ns_config *cfg,
+                                    void *const *O_out, muon_dtype o_dtype, void *stream);
 
 /*
  * Low-bit momentum state of 4-bit-Muon-GRASP ([GRASP] overall framework, key

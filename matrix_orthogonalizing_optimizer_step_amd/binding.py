@@ -76,6 +76,9 @@ def load_library():
     lib.muon_step.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, ctypes.c_float,
                               ctypes.c_float, ctypes.c_float, i32, cfgp, vp, i32, vp, sz, vp]
     lib.muon_step.restype = i32
+    lib.muon_step_fixed_scratch.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, ctypes.c_float, ctypes.c_float,
+                                            ctypes.c_float, ctypes.c_float, i32, cfgp, vp, i32, vp]
+    lib.muon_step_fixed_scratch.restype = i32
     lib.muon_ns_flops.argtypes = [i32, i32, i32, cfgp, i32]
     lib.muon_ns_flops.restype = ctypes.c_double
     lib.muon_status_string.argtypes = [i32]
@@ -283,6 +286,37 @@ def muon_step(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant=
                        float(mu), float(lr), float(weight_decay), float(update_scale), v, ctypes.byref(c),
                        po.data_ptr() if po is not None else None, odt,
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+
+
+FIXED_SCRATCH_BYTES = 64 << 20  # MUON_FIXED_SCRATCH_BYTES
+
+
+def muon_step_fixed_scratch(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant="standard",
+                            cfg: Optional[NSConfig] = None, O_out=None, stream=None, update_scale: float = 1.0):
+    """muon_step with the library's fixed device scratch instead of a
+    workspace (for callers that cannot allocate; problems whose workspace
+    exceeds FIXED_SCRATCH_BYTES are refused).  Calls that overlap on one
+    device race on that scratch."""
+    lib = load_library()
+    v = _variant(variant)
+    rows, cols, wdt = _batch(W, "W")
+    r2, c2, sdt = _batch(M, "M")
+    r3, c3, gdt = _batch(G, "G")
+    if (r2, c2) != (rows, cols) or (r3, c3) != (rows, cols) or gdt != sdt:
+        raise ValueError("W, M and G must share the shape; M and G the dtype")
+    if not (len(W) == len(M) == len(G)):
+        raise ValueError("W, M and G must have one tensor per matrix")
+    c, _keep = (cfg or NSConfig()).to_c(v)
+    po, odt = None, F32
+    if O_out is not None:
+        _, _, odt = _batch(O_out, "O_out")
+        po = pointer_array(O_out)
+    pw, pm, pg = pointer_array(W), pointer_array(M), pointer_array(G)
+    st = lib.muon_step_fixed_scratch(len(W), rows, cols, pw.data_ptr(), wdt, pm.data_ptr(), pg.data_ptr(), sdt,
+                                     float(mu), float(lr), float(weight_decay), float(update_scale), v,
+                                     ctypes.byref(c), po.data_ptr() if po is not None else None, odt,
+                                     _stream(stream))
     _check(st)
 
 

@@ -1016,6 +1016,73 @@ muon_status group8_codec(bool dequantize, int batch, int rows, int k, void* cons
   return MUON_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The step, with the caller's workspace or the fixed device scratch below.
+// ---------------------------------------------------------------------------
+}  // namespace
+
+// Scratch memory of muon_step_fixed_scratch, for callers that cannot
+// allocate: one copy per device, held until the process ends.  Host code
+// never uses this name as an address; it takes the device address from
+// hipGetSymbolAddress once per device (scratch_address below).
+static __device__ __align__(256) char scratch[MUON_FIXED_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there; null if the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+muon_status step(int batch, int rows, int cols, void* const* W, muon_dtype w_dtype, void* const* M,
+                 const void* const* G, muon_dtype state_dtype, float mu, float lr, float weight_decay,
+                 float update_scale, muon_ns_variant variant, const muon_ns_config* cfg, void* const* O_out,
+                 muon_dtype o_dtype, void* workspace, size_t ws_bytes, void* stream, bool fixed_scratch) {
+  if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
+  Config c;
+  muon_status st = make_config(cfg, variant, &c);
+  if (st != MUON_OK) return st;
+  Plan p;
+  if (!make_plan(batch, rows, cols, variant, c, &p)) return MUON_ERR_INVALID_ARG;
+  if (W == nullptr || M == nullptr || G == nullptr) return MUON_ERR_INVALID_ARG;
+  const void* arrays[4] = {W, M, G, O_out};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (arrays[i] != nullptr && arrays[i] == arrays[j]) return MUON_ERR_INVALID_ARG;
+  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay) || !isfinite(update_scale)) return MUON_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_dtype(state_dtype)) return MUON_ERR_INVALID_ARG;
+  if (w_dtype == MUON_F16 || state_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
+  if (O_out != nullptr && o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
+  if (fixed_scratch) {  // every check above passed: only now touch the device
+    if (p.total > MUON_FIXED_SCRATCH_BYTES) return MUON_ERR_WORKSPACE;
+    workspace = scratch_address();
+    if (workspace == nullptr) return MUON_ERR_HIP;
+    ws_bytes = MUON_FIXED_SCRATCH_BYTES;
+  }
+  if (workspace == nullptr || ws_bytes < p.total) return MUON_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(M), state_dtype, G, M,
+                    static_cast<double>(mu), s);
+  if (st != MUON_OK) return st;
+  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
+  return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1059,30 +1126,17 @@ muon_status muon_step(int batch, int rows, int cols, void* const* W, muon_dtype 
                       float weight_decay, float update_scale, muon_ns_variant variant, const muon_ns_config* cfg,
                       void* const* O_out, muon_dtype o_dtype, void* workspace, size_t ws_bytes,
                       void* stream) {
-  if (variant != MUON_NS_STANDARD && variant != MUON_NS_GRAM) return MUON_ERR_INVALID_ARG;
-  Config c;
-  muon_status st = make_config(cfg, variant, &c);
-  if (st != MUON_OK) return st;
-  Plan p;
-  if (!make_plan(batch, rows, cols, variant, c, &p)) return MUON_ERR_INVALID_ARG;
-  if (W == nullptr || M == nullptr || G == nullptr) return MUON_ERR_INVALID_ARG;
-  const void* arrays[4] = {W, M, G, O_out};
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (arrays[i] != nullptr && arrays[i] == arrays[j]) return MUON_ERR_INVALID_ARG;
-  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay) || !isfinite(update_scale)) return MUON_ERR_INVALID_ARG;
-  if (!valid_dtype(w_dtype) || !valid_dtype(state_dtype)) return MUON_ERR_INVALID_ARG;
-  if (w_dtype == MUON_F16 || state_dtype == MUON_F16) return MUON_ERR_UNSUPPORTED;
-  if (O_out != nullptr && o_dtype != MUON_F32 && o_dtype != MUON_BF16) return MUON_ERR_UNSUPPORTED;
-  if (workspace == nullptr || ws_bytes < p.total) return MUON_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MUON_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  st = run_prologue(p, c, ws, reinterpret_cast<const void* const*>(M), state_dtype, G, M,
-                    static_cast<double>(mu), s);
-  if (st != MUON_OK) return st;
-  Final f{W, w_dtype, O_out, o_dtype, lr, weight_decay, update_scale};
-  return variant == MUON_NS_STANDARD ? run_standard(p, c, ws, f, s) : run_gram(p, c, ws, f, s);
+  return step(batch, rows, cols, W, w_dtype, M, G, state_dtype, mu, lr, weight_decay, update_scale, variant, cfg,
+              O_out, o_dtype, workspace, ws_bytes, stream, false);
+}
+
+muon_status muon_step_fixed_scratch(int batch, int rows, int cols, void* const* W, muon_dtype w_dtype,
+                                    void* const* M, const void* const* G, muon_dtype state_dtype, float mu,
+                                    float lr, float weight_decay, float update_scale, muon_ns_variant variant,
+                                    const muon_ns_config* cfg, void* const* O_out, muon_dtype o_dtype,
+                                    void* stream) {
+  return step(batch, rows, cols, W, w_dtype, M, G, state_dtype, mu, lr, weight_decay, update_scale, variant, cfg,
+              O_out, o_dtype, nullptr, 0, stream, true);
 }
 
 size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_variant variant,

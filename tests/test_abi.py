@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert mu.abi_version() == 4
+    assert mu.abi_version() == 5
 
 
 def test_status_strings():
