@@ -153,44 +153,86 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-_ptr_cache: "OrderedDict[tuple, torch.Tensor]" = OrderedDict()  # least recently used first
+def _stream_obj(stream, device):
+    """The torch stream object for None (current), a torch stream or a raw handle."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+class _PtrArray:
+    """A cached pointer array: the device tensor, the stream its copy was
+    enqueued on, and an event recorded after that copy."""
+    __slots__ = ("arr", "stream", "ready")
+
+    def __init__(self, arr, stream, ready):
+        self.arr, self.stream, self.ready = arr, stream, ready
+
+
+_ptr_cache: "OrderedDict[tuple, _PtrArray]" = OrderedDict()  # least recently used first
 _ptr_pinned: dict = {}  # arrays a captured graph reads: kept for the life of the process
 _PTR_CACHE_MAX = 256
 
 
-def pointer_array(tensors: Sequence[torch.Tensor]) -> torch.Tensor:
-    """A device array holding the data pointers of ``tensors``.
+def pointer_array(tensors: Sequence[torch.Tensor], stream=None) -> torch.Tensor:
+    """A device array holding the data pointers of ``tensors``, for use on
+    ``stream`` (None = the current stream).
 
-    Arrays are cached (least recently used evicted past 256 entries, after a
-    device synchronisation, as a kernel on another stream may still read it).  Making
-    one is a host-to-device copy, which a stream under graph capture does not
-    allow: call once with the same tensors before capturing.  An array used
+    A new array is filled by an asynchronous copy from pinned host memory
+    enqueued on ``stream``, so the host never waits for the device.  Arrays
+    are cached by device and pointers (least recently used dropped past 256
+    entries).  Using a cached array on another stream first waits, on the
+    host, for the event after its copy (only if that copy has not finished,
+    which is rare) and records the stream with the caching allocator, so a
+    dropped array's memory is not reused while that stream may still read
+    it.  Making an array is a copy, which a stream under graph capture does
+    not take: call once with the same tensors before capturing.  An array used
     during a capture is kept for the life of the process, since the graph
     reads it at every replay."""
     ptrs = tuple(int(t.data_ptr()) for t in tensors)
     dev = tensors[0].device
     key = (str(dev), ptrs)
-    capturing = dev.type == "cuda" and torch.cuda.is_current_stream_capturing()
-    arr = _ptr_pinned.get(key)
-    if arr is not None:
-        return arr
-    arr = _ptr_cache.get(key)
-    if arr is None:
-        if capturing:
-            raise MuonError(1, "pointer array not cached for these tensors: under graph capture, "
-                               "call once with the same tensors before capturing")  # MUON_ERR_INVALID_ARG
-        if len(_ptr_cache) >= _PTR_CACHE_MAX:
-            if dev.type == "cuda":  # a kernel on any stream may still read the array: wait before freeing it
-                torch.cuda.synchronize(dev)
+    if dev.type != "cuda":  # host tensors (argument checks without a device)
+        ent = _ptr_cache.get(key)
+        if ent is None:
             while len(_ptr_cache) >= _PTR_CACHE_MAX:
                 _ptr_cache.popitem(last=False)
-        arr = torch.tensor(ptrs, dtype=torch.int64).to(dev)
-        _ptr_cache[key] = arr
-    else:
+            ent = _ptr_cache[key] = _PtrArray(torch.tensor(ptrs, dtype=torch.int64), None, None)
+        else:
+            _ptr_cache.move_to_end(key)
+        return ent.arr
+    capturing = torch.cuda.is_current_stream_capturing()
+    ent = _ptr_pinned.get(key)
+    if ent is None:
+        ent = _ptr_cache.get(key)
+        if ent is None:
+            if capturing:
+                raise MuonError(1, "pointer array not cached for these tensors: under graph capture, "
+                                   "call once with the same tensors before capturing")  # MUON_ERR_INVALID_ARG
+            while len(_ptr_cache) >= _PTR_CACHE_MAX:
+                _ptr_cache.popitem(last=False)  # its streams are recorded: freeing it is ordered after them
+            s = _stream_obj(stream, dev)
+            host = torch.tensor(ptrs, dtype=torch.int64).pin_memory()
+            with torch.cuda.stream(s):
+                arr = torch.empty(len(ptrs), dtype=torch.int64, device=dev)
+                arr.copy_(host, non_blocking=True)
+                ready = torch.cuda.Event()
+                ready.record(s)
+            ent = _ptr_cache[key] = _PtrArray(arr, s.cuda_stream, ready)
+            return ent.arr
         _ptr_cache.move_to_end(key)
-    if capturing:
-        _ptr_pinned[key] = _ptr_cache.pop(key)
-    return arr
+        if capturing:
+            _ptr_pinned[key] = _ptr_cache.pop(key)
+    if capturing:  # a capture starts with a device synchronisation: the copy has landed
+        return ent.arr
+    if _stream(stream) != ent.stream:
+        if not ent.ready.query():
+            ent.ready.synchronize()
+        if key not in _ptr_pinned:
+            ent.arr.record_stream(_stream_obj(stream, dev))
+    return ent.arr
 
 
 def _batch(tensors: Sequence[torch.Tensor], name: str):
@@ -209,7 +251,8 @@ def _batch(tensors: Sequence[torch.Tensor], name: str):
     return t0.shape[0], t0.shape[1], _DT[t0.dtype]
 
 
-_ws_cache: dict = {}
+_ws_cache: dict = {}   # (device, stream handle) -> buffer
+_ws_pinned: dict = {}  # buffers a captured graph uses: kept for the life of the process
 
 
 def workspace_size(batch: int, rows: int, cols: int, variant="standard", cfg: Optional[NSConfig] = None) -> int:
@@ -222,13 +265,27 @@ def workspace_size(batch: int, rows: int, cols: int, variant="standard", cfg: Op
     return int(n)
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A cached device byte buffer of at least ``nbytes`` (256-byte aligned)."""
-    key = str(torch.device(device))
+def workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """A cached device byte buffer of at least ``nbytes`` (256-byte aligned)
+    for calls on ``stream`` (None = the current stream).
+
+    One buffer per (device, stream): calls on different streams never share
+    scratch memory.  A buffer is allocated on its stream, so when a larger one
+    replaces it the caching allocator reuses its memory only in that stream's
+    order, after the calls that used it.  A buffer used during a graph
+    capture is kept for the life of the process (the graph uses it at every
+    replay) and never replaced: a larger need then gets a new buffer."""
+    dev = torch.device(device)
+    s = _stream_obj(stream, dev)
+    key = (str(dev), s.cuda_stream)
+    capturing = torch.cuda.is_current_stream_capturing()
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
+    if capturing:
+        _ws_pinned[buf.data_ptr()] = buf
     return buf
 
 
@@ -241,8 +298,8 @@ def _orthogonalize(fname, variant, M, O, cfg, ws, stream):
     c, _keep = (cfg or NSConfig()).to_c(variant)
     need = lib.muon_workspace_size(len(M), rows, cols, variant, ctypes.byref(c))
     if ws is None:
-        ws = workspace(need, M[0].device)
-    pm, po = pointer_array(M), pointer_array(O)
+        ws = workspace(need, M[0].device, stream)
+    pm, po = pointer_array(M, stream), pointer_array(O, stream)
     st = getattr(lib, fname)(len(M), rows, cols, pm.data_ptr(), mdt, po.data_ptr(), odt, ctypes.byref(c),
                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st)
@@ -276,12 +333,12 @@ def muon_step(W, M, G, mu: float, lr: float, weight_decay: float = 0.0, variant=
     c, _keep = (cfg or NSConfig()).to_c(v)
     need = lib.muon_workspace_size(len(W), rows, cols, v, ctypes.byref(c))
     if workspace is None:
-        workspace = globals()["workspace"](need, W[0].device)
+        workspace = globals()["workspace"](need, W[0].device, stream)
     po, odt = None, F32
     if O_out is not None:
         _, _, odt = _batch(O_out, "O_out")
-        po = pointer_array(O_out)
-    pw, pm, pg = pointer_array(W), pointer_array(M), pointer_array(G)
+        po = pointer_array(O_out, stream)
+    pw, pm, pg = pointer_array(W, stream), pointer_array(M, stream), pointer_array(G, stream)
     st = lib.muon_step(len(W), rows, cols, pw.data_ptr(), wdt, pm.data_ptr(), pg.data_ptr(), sdt,
                        float(mu), float(lr), float(weight_decay), float(update_scale), v, ctypes.byref(c),
                        po.data_ptr() if po is not None else None, odt,
@@ -311,8 +368,8 @@ def muon_step_fixed_scratch(W, M, G, mu: float, lr: float, weight_decay: float =
     po, odt = None, F32
     if O_out is not None:
         _, _, odt = _batch(O_out, "O_out")
-        po = pointer_array(O_out)
-    pw, pm, pg = pointer_array(W), pointer_array(M), pointer_array(G)
+        po = pointer_array(O_out, stream)
+    pw, pm, pg = pointer_array(W, stream), pointer_array(M, stream), pointer_array(G, stream)
     st = lib.muon_step_fixed_scratch(len(W), rows, cols, pw.data_ptr(), wdt, pm.data_ptr(), pg.data_ptr(), sdt,
                                      float(mu), float(lr), float(weight_decay), float(update_scale), v,
                                      ctypes.byref(c), po.data_ptr() if po is not None else None, odt,
@@ -387,8 +444,8 @@ def grid_quantize(X, stream=None):
     codes = [torch.empty(rows, (cols + 1) // 2, dtype=torch.uint8, device=dev) for _ in X]
     sr = [torch.empty(rows, _nb(cols), dtype=torch.float32, device=dev) for _ in X]
     sc = [torch.empty(_nb(rows), cols, dtype=torch.float32, device=dev) for _ in X]
-    _check(lib.muon_grid_quantize(len(X), rows, cols, pointer_array(X).data_ptr(), pointer_array(codes).data_ptr(),
-                                  pointer_array(sr).data_ptr(), pointer_array(sc).data_ptr(), _stream(stream)))
+    _check(lib.muon_grid_quantize(len(X), rows, cols, pointer_array(X, stream).data_ptr(), pointer_array(codes, stream).data_ptr(),
+                                  pointer_array(sr, stream).data_ptr(), pointer_array(sc, stream).data_ptr(), _stream(stream)))
     return codes, sr, sc
 
 
@@ -398,9 +455,9 @@ def grid_dequantize(codes, row_scales, col_scales, cols: int, stream=None):
     rows = codes[0].shape[0]
     dev = codes[0].device
     Y = [torch.empty(rows, cols, dtype=torch.float32, device=dev) for _ in codes]
-    _check(lib.muon_grid_dequantize(len(codes), rows, cols, pointer_array(codes).data_ptr(),
-                                    pointer_array(row_scales).data_ptr(), pointer_array(col_scales).data_ptr(),
-                                    pointer_array(Y).data_ptr(), _stream(stream)))
+    _check(lib.muon_grid_dequantize(len(codes), rows, cols, pointer_array(codes, stream).data_ptr(),
+                                    pointer_array(row_scales, stream).data_ptr(), pointer_array(col_scales, stream).data_ptr(),
+                                    pointer_array(Y, stream).data_ptr(), _stream(stream)))
     return Y
 
 
@@ -413,8 +470,8 @@ def group8_quantize(X, stream=None):
     dev = X[0].device
     codes = [torch.empty(rows, k, dtype=torch.int8, device=dev) for _ in X]
     scales = [torch.empty(rows, _nb(k), dtype=torch.float32, device=dev) for _ in X]
-    _check(lib.muon_group8_quantize(len(X), rows, k, pointer_array(X).data_ptr(), pointer_array(codes).data_ptr(),
-                                    pointer_array(scales).data_ptr(), _stream(stream)))
+    _check(lib.muon_group8_quantize(len(X), rows, k, pointer_array(X, stream).data_ptr(), pointer_array(codes, stream).data_ptr(),
+                                    pointer_array(scales, stream).data_ptr(), _stream(stream)))
     return codes, scales
 
 
@@ -422,8 +479,8 @@ def group8_dequantize(codes, scales, stream=None):
     lib = load_library()
     rows, k = codes[0].shape
     Y = [torch.empty(rows, k, dtype=torch.float32, device=codes[0].device) for _ in codes]
-    _check(lib.muon_group8_dequantize(len(codes), rows, k, pointer_array(codes).data_ptr(),
-                                      pointer_array(scales).data_ptr(), pointer_array(Y).data_ptr(), _stream(stream)))
+    _check(lib.muon_group8_dequantize(len(codes), rows, k, pointer_array(codes, stream).data_ptr(),
+                                      pointer_array(scales, stream).data_ptr(), pointer_array(Y, stream).data_ptr(), _stream(stream)))
     return Y
 
 
@@ -447,13 +504,13 @@ class GraspState:
             self.P_scales = [z(rows, _nb(k), dt=torch.float32) for _ in range(batch)]
             self.R_codes, self.R_scales = group8_quantize([r.to(device, torch.float32).contiguous() for r in R_init])
 
-    def c_struct(self):
+    def c_struct(self, stream=None):
         st = _GraspState()
         keep = []
         for name in ("res_codes", "res_row_scales", "res_col_scales", "P_codes", "P_scales", "R_codes", "R_scales"):
             lst = getattr(self, name)
             if lst is not None:
-                arr = pointer_array(lst)
+                arr = pointer_array(lst, stream)
                 keep.append(arr)
                 setattr(st, name, arr.data_ptr())
         return st, keep
@@ -487,15 +544,15 @@ def grasp_step(W, state: GraspState, G, mu: float, lr: float, weight_decay: floa
     if need == 0:
         raise MuonError(1, "invalid arguments for the workspace size")
     if workspace is None:
-        workspace = globals()["workspace"](need, W[0].device)
+        workspace = globals()["workspace"](need, W[0].device, stream)
     po, odt = None, F32
     if O_out is not None:
         _, _, odt = _batch(O_out, "O_out")
-        po = pointer_array(O_out)
-    pm = pointer_array(M_out) if M_out is not None else None
-    st, _keep_st = state.c_struct()
-    st_ = lib.muon_grasp_step(len(W), rows, cols, state.k, pointer_array(W).data_ptr(), wdt, ctypes.byref(st),
-                              pointer_array(G).data_ptr(), gdt, float(mu), float(lr), float(weight_decay),
+        po = pointer_array(O_out, stream)
+    pm = pointer_array(M_out, stream) if M_out is not None else None
+    st, _keep_st = state.c_struct(stream)
+    st_ = lib.muon_grasp_step(len(W), rows, cols, state.k, pointer_array(W, stream).data_ptr(), wdt,
+                              ctypes.byref(st), pointer_array(G, stream).data_ptr(), gdt, float(mu), float(lr), float(weight_decay),
                               float(update_scale), v, ctypes.byref(c),
                               po.data_ptr() if po is not None else None, odt,
                               pm.data_ptr() if pm is not None else None,

@@ -245,3 +245,39 @@ def test_pointer_array_miss_under_capture_is_a_muon_error(monkeypatch):
     with pytest.raises(bd.MuonError, match="before capturing") as e:
         bd.pointer_array([FakeTensor()])
     assert e.value.status == 1
+
+
+def test_implicit_workspace_per_stream_and_pinned_under_capture(monkeypatch):
+    """The binding's implicit workspace: one buffer per (device, stream),
+    grown in place of the old one, and kept for good once a capture used it
+    (checked on the CPU with stand-in streams and a faked capture state)."""
+    import contextlib
+
+    import torch
+
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    capturing = {"on": False}
+    monkeypatch.setattr(torch.cuda, "stream", lambda s: contextlib.nullcontext())
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: capturing["on"])
+    bd._ws_cache.clear()
+    bd._ws_pinned.clear()
+    s1, s2 = FakeStream(11), FakeStream(22)
+    a = bd.workspace(1000, "cpu", s1)
+    b = bd.workspace(1000, "cpu", s2)
+    assert a.data_ptr() != b.data_ptr()               # streams never share scratch
+    assert bd.workspace(500, "cpu", s1) is a          # reused while large enough
+    c = bd.workspace(4000, "cpu", s1)                 # grown: a new buffer replaces the old one
+    assert c is not a and c.numel() >= 4000 and bd.workspace(10, "cpu", s1) is c
+    capturing["on"] = True
+    d = bd.workspace(100, "cpu", s2)                  # used under capture: pinned
+    assert d is b and bd._ws_pinned[d.data_ptr()] is d
+    e = bd.workspace(8000, "cpu", s2)                 # a larger need under capture: new, also pinned
+    assert e is not d and bd._ws_pinned[e.data_ptr()] is e and bd._ws_pinned[d.data_ptr()] is d
+    capturing["on"] = False
+    f = bd.workspace(16000, "cpu", s2)                # after the capture: replaced in the cache, pinned ones kept
+    assert f is not e and bd._ws_pinned[e.data_ptr()] is e and f.data_ptr() not in bd._ws_pinned
+    bd._ws_cache.clear()
+    bd._ws_pinned.clear()

@@ -443,3 +443,47 @@ def test_narrow_and_wide_tiles_agree_bitwise(variant):
     assert torch.equal(outs[0], outs[1])
     ref = oracle_orth(variant, Ms[0])
     assert relF(syn.to_f64(outs[0]), ref) < 2e-2
+
+
+def test_fresh_tensors_make_no_host_stall_and_streams_stay_ordered():
+    """A step on tensors never seen before builds its pointer arrays with an
+    asynchronous copy: with the stream busy for a while, building them
+    returns at once (the host does not wait for the device).  Steps with
+    fresh gradients alternating between two streams, with no host
+    synchronisation, equal the same steps run on one stream."""
+    import time
+
+    from matrix_orthogonalizing_optimizer_step_amd import binding as bd
+    r, c = 300, 520
+    busy = torch.randn(4096, 4096, device=DEV)
+    torch.cuda.synchronize()
+    for _ in range(40):  # about 0.1 s of work queued on the current stream
+        busy = (busy @ busy) * 1e-4
+    fresh = [torch.empty(r, c, device=DEV) for _ in range(3)]
+    t0 = time.perf_counter()
+    arr = bd.pointer_array(fresh)
+    dt = time.perf_counter() - t0
+    still_busy = not torch.cuda.current_stream().query()
+    torch.cuda.synchronize()
+    assert arr.cpu().tolist() == [t.data_ptr() for t in fresh]
+    assert still_busy and dt < 0.03, (still_busy, dt)
+
+    W0 = syn.random_matrix(97, r, c)
+    Gs = [syn.random_matrix(98 + i, r, c, std=1e-3, dtype="bf16") for i in range(4)]
+    side = torch.cuda.Stream()
+    Wa, Ma = [W0.to(DEV)], [torch.zeros(r, c, dtype=torch.bfloat16, device=DEV)]
+    Wb, Mb = [W0.to(DEV)], [torch.zeros(r, c, dtype=torch.bfloat16, device=DEV)]
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    fresh_a = [G.to(DEV) for G in Gs]  # kept alive to the end: each step sees new addresses
+    fresh_b = [G.to(DEV) for G in Gs]
+    torch.cuda.synchronize()
+    for i in range(len(Gs)):
+        s = side if i % 2 else main
+        s.wait_stream(main if i % 2 else side)
+        with torch.cuda.stream(s):
+            mu.muon_step(Wa, Ma, [fresh_a[i]], 0.95, 0.02, 0.0, "gram")
+        mu.muon_step(Wb, Mb, [fresh_b[i]], 0.95, 0.02, 0.0, "gram")
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(Wa[0], Wb[0]) and torch.equal(Ma[0], Mb[0])
