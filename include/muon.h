@@ -333,6 +333,19 @@ muon_status muon_group8_dequantize(int batch, int rows, int k, const void *const
  * below 3e-6, under any 16-bit rounding).  The coefficients
  * are rounded to fp32, and the intervals follow the rounded polynomials.
  *
+ * Use with Gram NS: the schedule (T = 5, ell = 1e-3, f = 1 or 1.05) was
+ * checked with the Gram default, one restart after iteration 2.  By the
+ * diagnostics [GNS §3.2] judges restarts with (the smallest eigenvalue of
+ * every Gram matrix, the condition number of Q_t), with Gram matrices
+ * rounded to bf16 or holding a spurious eigenvalue of -1e-5 ([GNS §3.1]),
+ * that is the single restart point that keeps the eigenvalues above -0.4
+ * and gives the best-conditioned Q on square Gaussian inputs (cond below
+ * 100 there and on rectangular ones); without a restart the spurious
+ * eigenvalue grows past -1.  The steep first polynomial (a_1 ~ 8) can leave
+ * cond(Q_2) near 170 on inputs whose singular values fill [ell, 1] (e.g.
+ * sigma_i ~ i^-1/2), whatever the restart point.  bf16 operands refuse
+ * such a table (see muon_ns_config.compute); use MUON_F16.
+ *
  *   T       iterations, 1..MUON_MAX_T.
  *   ell     lower end of the singular values of X0, 0 < ell < 1 (e.g. 1e-3).
  *   safety  f, 1 <= f <= 2 (1 = none; [GNS §3.3] uses 1.05).

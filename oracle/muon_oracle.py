@@ -172,7 +172,7 @@ def newton_schulz(M, coeffs=None, T=5, eps=EPS, counter=None):
 # Gram Newton-Schulz ([GNS §2.3 Alg.1], [GNS §3.4 Alg.2])
 # --------------------------------------------------------------------------
 def gram_newton_schulz(M, coeffs=None, T=5, eps=EPS, restarts=(2,), counter=None,
-                       R0=None, trace=None):
+                       R0=None, trace=None, gram_round=None):
     """Gram Newton-Schulz with restarts.
 
     R = X X^T, Q = I; for t = 1..T: Z = b R + c R^2; Q <- Q Z + a Q; then
@@ -181,15 +181,26 @@ def gram_newton_schulz(M, coeffs=None, T=5, eps=EPS, restarts=(2,), counter=None
     whose R is never used).  Return Q X.
 
     ``R0`` replaces the initial Gram matrix (used to study a spurious negative
-    eigenvalue, [GNS §3.1 Prop.2]); ``trace`` (a list) receives (t, R, Q)
-    after every iteration for inspection."""
+    eigenvalue, [GNS §3.1 Prop.2]); ``trace`` (a list) receives (t, R, Q_t)
+    after every iteration t for inspection: R as it stands after the
+    iteration (the new Gram matrix after a restart) and Q_t as updated in
+    iteration t, before a restart resets it.  ``gram_round`` ('bf16' or
+    'f16') rounds every Gram matrix X X^T the iteration forms (the initial
+    one and each restart's) to that type, as a 16-bit Gram product stores it
+    ([GNS §3.1]: this rounding gives R_0 small negative eigenvalues); None
+    keeps them exact."""
     X, transposed = _orient(M)
     n = X.shape[0]
     table = _coeff_table(coeffs, T)
     restarts = set(int(t) for t in restarts)
     X = X / (np.linalg.norm(X) + eps)
     I = np.eye(n)
-    R = _mm(X, X.T, counter, "XXt", True) if R0 is None else np.array(R0, dtype=np.float64)
+
+    def gram(Y):
+        G = _mm(Y, Y.T, counter, "XXt", True)
+        return G if gram_round is None else round_to(G, gram_round)
+
+    R = gram(X) if R0 is None else np.array(R0, dtype=np.float64)
     Q = I
     fresh = True  # Q is the identity: the product Q Z needs no GEMM
     for t, (a, b, c) in enumerate(table, start=1):
@@ -199,18 +210,43 @@ def gram_newton_schulz(M, coeffs=None, T=5, eps=EPS, restarts=(2,), counter=None
         else:
             Q = _mm(Q, Z, counter, "QZ", True) + a * Q
         fresh = False
+        Q_t = Q
         if t < T and t in restarts:
             X = _mm(Q, X, counter, "QX", False)
-            R = _mm(X, X.T, counter, "XXt", True)
+            R = gram(X)
             Q = I
             fresh = True
         elif t < T:
             RZ = _mm(R, Z, counter, "RZ", True) + a * R
             R = _mm(Z, RZ, counter, "ZRZ", True) + a * RZ
         if trace is not None:
-            trace.append((t, R.copy(), Q.copy()))
+            trace.append((t, R.copy(), Q_t.copy()))
     O = _mm(Q, X, counter, "QX", False)
     return O.T if transposed else O
+
+
+def restart_diagnostics(M, coeffs=None, T=5, restarts=(2,), eps=EPS, gram_round=None, R0=None):
+    """The two quantities [GNS §3.2] judges a restart point by: the smallest
+    eigenvalue of every Gram matrix R the iteration forms (R_0, the R_t it
+    updates, and each restart's new X X^T; R at t = T is never formed) and
+    the condition number (largest over smallest singular value) of Q_t after
+    each iteration t = 1..T.  Gram matrices are rounded as ``gram_round``
+    says (see gram_newton_schulz); ``R0`` replaces the initial one (e.g. with
+    a spurious negative eigenvalue, [GNS §3.1]).  Returns (lambda_min list,
+    cond list)."""
+    if R0 is None:
+        X, _ = _orient(M)
+        X = X / (np.linalg.norm(X) + eps)
+        R0 = X @ X.T
+        if gram_round is not None:
+            R0 = round_to(R0, gram_round)
+    R0 = np.array(R0, dtype=np.float64)
+    trace = []
+    gram_newton_schulz(M, coeffs, T, eps, restarts, R0=R0, trace=trace, gram_round=gram_round)
+    lam = [float(np.linalg.eigvalsh(R0).min())]
+    lam += [float(np.linalg.eigvalsh(R).min()) for (t, R, _) in trace if t < T]
+    cond = [float(np.linalg.cond(Q)) for (_, _, Q) in trace]
+    return lam, cond
 
 
 # --------------------------------------------------------------------------
@@ -272,7 +308,7 @@ def relative_frobenius(x, ref):
 
 __all__ = [
     "QUINTIC", "EPS", "round_bf16", "round_to", "FlopCounter", "newton_schulz",
-    "gram_newton_schulz", "muon_step", "counted_flops", "relative_frobenius",
+    "gram_newton_schulz", "restart_diagnostics", "muon_step", "counted_flops", "relative_frobenius",
 ]
 
 if __name__ == "__main__":  # pragma: no cover - manual check

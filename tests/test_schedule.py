@@ -165,3 +165,107 @@ def test_library_schedule_rejects_bad_arguments():
     assert lib.muon_quintic_schedule(5, float("nan"), 1.0, buf, None) == 1
     assert lib.muon_quintic_schedule(5, 1e-3, 1.0, None, None) == 1
     assert lib.muon_quintic_schedule(16, 1e-7, 1.05, buf, None) == 0
+
+
+# ------------------------------------------------------------ restart diagnostics ([GNS §3.2])
+def _haar(rng_, n, k):
+    q, r = np.linalg.qr(rng_.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def _inputs():
+    """The workloads' input families at small size: rectangular and square
+    Gaussians, a transposed one, and a decaying spectrum sigma_i = i^-1/2."""
+    r = np.random.default_rng(2026)
+    U, V = _haar(r, 128, 128), _haar(r, 352, 128)
+    return {"gauss-128x512": r.standard_normal((128, 512)), "gauss-128x128": r.standard_normal((128, 128)),
+            "gauss-512x256": r.standard_normal((512, 256)),
+            "spectrum-128x352": (U * np.arange(1, 129) ** -0.5) @ V.T}
+
+
+def _with_spurious_eigenvalue(M, lam):
+    """The exact initial Gram matrix with its smallest eigenvalue set to lam."""
+    X = M if M.shape[0] <= M.shape[1] else M.T
+    X = X / (np.linalg.norm(X) + orc.EPS)
+    w, V = np.linalg.eigh(X @ X.T)
+    w[0] = lam
+    return (V * w) @ V.T
+
+
+SCHEDULES = {"quintic": None, "derived-f1": (5, 1e-3, 1.0), "derived-f1.05": (5, 1e-3, 1.05)}
+
+
+def _coeffs(key):
+    return None if SCHEDULES[key] is None else oracle_schedule(*SCHEDULES[key])[0]
+
+
+@pytest.mark.parametrize("restarts", [(), (2,), (1, 3)])
+@pytest.mark.parametrize("key", list(SCHEDULES))
+def test_restart_diagnostics_follow_the_scalar_form(key, restarts):
+    """For a diagonal input every Gram state is diagonal (Thm.1): R_t =
+    diag(x_t^2) and, within the phase that began at the last restart s,
+    Q_t = diag(x_t / x_s); so the diagnostics are the smallest x_t^2 and the
+    ratio of the largest to the smallest x_t / x_s, from the scalar map."""
+    coeffs = _coeffs(key) or [orc.QUINTIC] * 5
+    d = np.array([0.9, 0.6, 0.3, 0.1, 0.03, 0.01, 0.003, 0.5])
+    lam, cond = orc.restart_diagnostics(np.diag(d), coeffs, 5, restarts)
+    xs = [d / (np.linalg.norm(d) + orc.EPS)]
+    for c in coeffs:
+        xs.append(qs.quintic(c, xs[-1]))
+    start, want_cond = 0, []
+    for t in range(1, 6):
+        q = xs[t] / xs[start]
+        want_cond.append(q.max() / q.min())
+        if t in restarts:
+            start = t
+    want_lam = [float((x ** 2).min()) for x in xs[:5]]
+    np.testing.assert_allclose(lam, want_lam, rtol=1e-9)
+    np.testing.assert_allclose(cond, want_cond, rtol=1e-9)
+
+
+@pytest.mark.parametrize("name", list(_inputs()))
+def test_default_restart_meets_the_pages_bounds(name):
+    """The library's Gram default (fixed quintic, restart after iteration 2)
+    keeps the smallest Gram eigenvalue above -0.4 and cond(Q_t) below 100
+    ([GNS §3.2]) on the workloads' input families, with every Gram matrix
+    rounded to bf16 and with the page's spurious eigenvalue of -1e-5
+    injected ([GNS §3.1]); without a restart the condition number passes 100
+    once the spurious eigenvalue is there."""
+    M = _inputs()[name]
+    for kw in (dict(gram_round="bf16"), dict(R0=_with_spurious_eigenvalue(M, -1e-5))):
+        lam, cond = orc.restart_diagnostics(M, None, 5, (2,), **kw)
+        assert min(lam) > -0.4 and max(cond) < 100, (kw.keys(), min(lam), max(cond))
+    if name == "gauss-128x128":
+        _, cond = orc.restart_diagnostics(M, None, 5, (), R0=_with_spurious_eigenvalue(M, -1e-5))
+        assert max(cond) > 100
+
+
+@pytest.mark.parametrize("key", ["derived-f1", "derived-f1.05"])
+def test_restart_point_of_the_derived_schedules(key):
+    """The restart point for the derived schedules, chosen by the diagnostics
+    of [GNS §3.2]: a single restart that keeps the smallest Gram eigenvalue
+    above -0.4 with bf16 Gram rounding and with the injected -1e-5, and
+    among those the smallest largest cond(Q_t) on the square Gaussian input
+    with bf16 Gram rounding (the input whose tiny singular values make Q
+    worst conditioned).  That is the restart after iteration 2, the library's
+    default; without any restart the injected eigenvalue grows past -0.4
+    (Prop.2), and restarting after iteration 1 lets it reach -0.4 too in
+    bf16 (f = 1)."""
+    coeffs = _coeffs(key)
+    ins = _inputs()
+    M = ins["gauss-128x128"]
+    R0 = _with_spurious_eigenvalue(M, -1e-5)
+    lam, _ = orc.restart_diagnostics(M, coeffs, 5, (), R0=R0)
+    assert min(lam) < -0.4
+    scores = {}
+    for t in (1, 2, 3, 4):
+        lam_b, cond_b = orc.restart_diagnostics(M, coeffs, 5, (t,), gram_round="bf16")
+        lam_i, _ = orc.restart_diagnostics(M, coeffs, 5, (t,), R0=R0)
+        if min(lam_b) > -0.4 and min(lam_i) > -0.4:
+            scores[t] = max(cond_b)
+    assert min(scores, key=scores.get) == 2, scores
+    assert scores[2] < 100
+    # on rectangular Gaussians the restart after 2 meets both bounds as well
+    for name in ("gauss-128x512", "gauss-512x256"):
+        lam, cond = orc.restart_diagnostics(ins[name], coeffs, 5, (2,), gram_round="bf16")
+        assert min(lam) > -0.4 and max(cond) < 100
