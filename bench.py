@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-other-variant", action="store_true", help="skip timing the other NS variant")
     ap.add_argument("--no-low-bit", action="store_true",
                     help="skip timing the step with the low-bit (4-bit grid / 8-bit subspace) momentum state")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the compact timing of the other workloads (default run only)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the relative error against the fp64 oracle (one matrix per group) and the "
+                         "256x512 comparison with the SVD polar factor")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--one-stream", action="store_true",
@@ -441,6 +446,21 @@ def main():
 
     low_bit = None if args.no_low_bit else time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev)
 
+    # ------------------------------------------------ precision against the fp64 oracle
+    parity = None
+    if not args.no_parity:
+        parity = {"groups": group_parity(wl, variants, cfg_for, mu, syn, dev),
+                  "single_256x512_vs_svd_polar": polar_distance(mu, syn, dev)}
+
+    # ------------------------------------------------ the other workloads (compact)
+    others = None
+    if not args.no_other_workloads and args.workload == "qwen2.5-7b" and not args.one_stream:
+        for x in groups:  # free the headline workload's buffers first
+            for key in ("W", "M", "G", "O", "ws"):
+                x.pop(key, None)
+        torch.cuda.empty_cache()
+        others = {k: time_workload(syn.WORKLOADS[k], mu, syn, dev) for k in OTHER_WORKLOADS}
+
     # ------------------------------------------------ CPU baseline: the fp64 oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -479,6 +499,8 @@ def main():
         "traced_ms_per_step": traced_sec * 1e3,
         "traced_note": "traced steps run the groups serially on one stream (per-kernel event timing)",
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "other_workloads": others,
         "low_bit_state": low_bit,
         "pages_context": {
             "gram_ns_optimizer_time_saving": "up to 50% (Kimi K2, hardware not stated)",
@@ -570,6 +592,125 @@ def time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev):
                    "orthogonalised, and stored again; state_bytes counts codes and scales (fp32 momentum: "
                    f"{4 * wl.elements} bytes); *_aux_stream: the state update of each group on a second stream "
                    "beside its Newton-Schulz (the serial per-kernel pass uses one stream)")
+    return out
+
+
+OTHER_WORKLOADS = ("llama-130m", "llama-1.1b", "moe-64x")
+OTHER_WARMUP, OTHER_STEPS = 2, 5
+
+
+def time_workload(wl, mu, syn, dev):
+    """Gram and standard NS steps per second on another workload, compact:
+    each group holds one seeded matrix (W, M, G) replicated over its count
+    (MFMA timing does not depend on the values), one stream and workspace per
+    group as in the headline step, 2 warm-up and 5 timed steps."""
+    import torch
+    log(f"[bench] workload {wl.key}: {wl.matrices} matrices")
+    groups = []
+    for gi, g in enumerate(wl.groups):
+        Ws, Ms, Gs = syn.group_inputs(wl, gi, count=1)
+        rep = lambda t: [t.to(dev) for _ in range(g.count)]  # noqa: E731
+        nb = max(mu.workspace_size(g.count, g.rows, g.cols, v) for v in ("gram", "standard"))
+        groups.append(dict(g=g, W=rep(Ws[0]), M=rep(Ms[0]), G=rep(Gs[0]), stream=torch.cuda.Stream(device=dev),
+                           ws=torch.empty(nb, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+
+    def step(variant):
+        ev = torch.cuda.Event()
+        ev.record(main)
+        for x in groups:
+            x["stream"].wait_event(ev)
+            mu.muon_step(x["W"], x["M"], x["G"], 0.95, 0.02, 0.0, variant, None, workspace=x["ws"], stream=x["stream"])
+        for x in groups:
+            done = torch.cuda.Event()
+            done.record(x["stream"])
+            main.wait_event(done)
+
+    out = {"matrices": wl.matrices,
+           "groups": "; ".join(f"{g.count} x {g.rows}x{g.cols}" for g in wl.groups)}
+    for variant in ("gram", "standard"):
+        for _ in range(OTHER_WARMUP):
+            step(variant)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(OTHER_STEPS):
+            step(variant)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / OTHER_STEPS
+        alg = sum(g.count * mu.ns_flops(g.rows, g.cols, variant, None, True) for g in wl.groups)
+        out[variant] = {"ms_per_step": sec * 1e3, "tflops_algorithmic": alg / sec / 1e12,
+                        "pct_of_16bit_peak": 100.0 * alg / sec / 1e12 / PEAK_16BIT_TFLOPS,
+                        "matrices_per_s": wl.matrices / sec, "steps_per_s": 1.0 / sec}
+        log(f"[bench]   {variant}: {sec * 1e3:.2f} ms/step, {alg / sec / 1e12:.0f} TFLOP/s")
+    del groups
+    torch.cuda.empty_cache()
+    out["note"] = (f"{OTHER_WARMUP} warm-up and {OTHER_STEPS} timed steps; one seeded matrix per group replicated "
+                   "over the group (values do not change MFMA timing)")
+    return out
+
+
+def group_parity(wl, variants, cfg_for, mu, syn, dev):
+    """One Muon step on the first matrix of each group (its own seeded
+    inputs, a batch of one) against the fp64 oracle: the relative Frobenius
+    error of O and whether the stored momentum is bit for bit the oracle's."""
+    import numpy as np
+    import torch
+
+    from oracle import muon_oracle as orc
+    out = {}
+    for gi, g in enumerate(wl.groups):
+        Ws, Ms, Gs = syn.group_inputs(wl, gi, count=1)
+        for v in variants:
+            W, M = [Ws[0].to(dev)], [Ms[0].to(dev)]
+            O = [torch.empty(g.rows, g.cols, dtype=torch.float32, device=dev)]
+            mu.muon_step(W, M, [Gs[0].to(dev)], 0.95, 0.02, 0.0, v, cfg_for(v), O_out=O)
+            torch.cuda.synchronize()
+            _, Mr, Or = orc.muon_step(syn.to_f64(Ws[0]), syn.to_f64(Ms[0]), syn.to_f64(Gs[0]),
+                                      float(np.float32(0.95)), float(np.float32(0.02)), 0.0, v,
+                                      state_dtype=wl.state_dtype, w_dtype=wl.w_dtype)
+            out[f"{g.name} {g.rows}x{g.cols} {v}"] = {
+                "relF_O": float(orc.relative_frobenius(syn.to_f64(O[0]), Or)),
+                "momentum_bit_exact": bool(np.array_equal(syn.to_f64(M[0]), Mr))}
+    log("[bench] parity: " + ", ".join(f"{k} {v['relF_O']:.2e}" for k, v in out.items()))
+    return out
+
+
+def polar_distance(mu, syn, dev):
+    """The 256x512 fp32 configuration (one step, standard NS, T = 5): the
+    distance of O from the polar factor U V^T of the stored momentum (fp64
+    SVD), beside its exact value sqrt(sum (p_5(x_i) - 1)^2 / n) for the fixed
+    quintic p (x_i = sigma_i / (||M|| + eps)) and O's error against the
+    oracle.  Newton-Schulz at T = 5 is not the polar factor; the first
+    number must match the second up to O's own error."""
+    import numpy as np
+    import torch
+
+    from oracle import muon_oracle as orc
+    wl = syn.WORKLOADS["single-256x512"]
+    W0, M0, G0 = syn.matrix_inputs(wl, 0, 256, 512)
+    mu32, lr32 = float(np.float32(0.95)), float(np.float32(0.02))
+    _, Mr, Or = orc.muon_step(syn.to_f64(W0), syn.to_f64(M0), syn.to_f64(G0), mu32, lr32, 0.0, "standard",
+                              state_dtype="f32", w_dtype="f64")
+    U, sv, Vt = np.linalg.svd(Mr, full_matrices=False)
+    polar = U @ Vt
+    x = sv / (np.linalg.norm(Mr) + orc.EPS)
+    for _ in range(5):
+        a, b, c = orc.QUINTIC
+        x = a * x + b * x ** 3 + c * x ** 5
+    exact = float(np.sqrt(np.sum((x - 1.0) ** 2) / x.size))
+    out = {"exact_distance_of_ns_from_polar": exact,
+           "oracle_distance_from_polar": float(orc.relative_frobenius(Or, polar))}
+    for compute in ("f32", "bf16"):
+        W, M = [W0.to(dev)], [M0.to(dev)]
+        O = [torch.empty(256, 512, dtype=torch.float32, device=dev)]
+        mu.muon_step(W, M, [G0.to(dev)], 0.95, 0.02, 0.0, "standard", mu.NSConfig(compute=compute), O_out=O)
+        torch.cuda.synchronize()
+        Og = syn.to_f64(O[0])
+        out[compute] = {"distance_from_polar": float(orc.relative_frobenius(Og, polar)),
+                        "relF_vs_oracle": float(orc.relative_frobenius(Og, Or))}
+    log(f"[bench] 256x512 vs SVD polar: exact {exact:.4f}, f32 {out['f32']['distance_from_polar']:.4f}, "
+        f"bf16 {out['bf16']['distance_from_polar']:.4f}")
     return out
 
 

@@ -50,24 +50,26 @@ def _finish(proc: subprocess.Popen, what: str, verbose: bool) -> None:
         print(msgs, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles (one process per source, in parallel); writes
-    libmuon.so atomically and returns its path."""
+def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB, defines=()) -> str:
+    """Always recompiles (one process per source, in parallel); writes the
+    library (default libmuon.so next to this file) atomically and returns its
+    path.  ``csrc``, ``lib`` and ``defines`` (-D flags) build a variant."""
     objdir = tempfile.mkdtemp(prefix="muon_build_")
     try:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
-            procs.append((src, _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)))
+            procs.append((src, _run([hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-c", "-o", obj,
+                                     os.path.join(csrc, src)], verbose)))
         for src, proc in procs:
             _finish(proc, src, verbose)
-        tmp = LIB + ".tmp"
+        tmp = lib + ".tmp"
         _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose), "link", verbose)
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":

@@ -18,7 +18,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmuon.so")
+# MUON_LIBRARY selects another build of the library (e.g. for A/B timing)
+LIB_PATH = os.environ.get("MUON_LIBRARY") or os.path.join(_HERE, "libmuon.so")
 
 F32, BF16, F16 = 0, 1, 2
 STANDARD, GRAM = 0, 1
