@@ -40,28 +40,25 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return h;
 }
 
-// float64 -> bfloat16 with a single rounding: round the binary64 significand
-// to 8 bits first (the result is then exact in binary32 and in bfloat16).
+// float64 -> bfloat16 with a single rounding to nearest even, without
+// branches.  From magnitude 2^-126 up, x is rounded to binary32 by
+// round-to-odd (the hardware's nearest-even result, stepped one unit toward
+// zero if it went away from zero, with its last bit set whenever the
+// conversion was inexact), which keeps 16 bits below bfloat16's last place,
+// so rounding that value to nearest even (v_cvt_pk_bf16_f32) gives the same
+// result as rounding x itself; NaN stays NaN and infinities stay infinite.
+// Below 2^-126 bfloat16 has the fixed quantum 2^-133: x is rounded to a
+// multiple of it in binary64 (exact) and converted exactly.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-  uint64_t au = u & 0x7fffffffffffffffull;
-  if (au > 0x7ff0000000000000ull) return static_cast<uint16_t>(((u >> 48) & 0x8000u) | 0x7fc0u);
-  int e = static_cast<int>(au >> 52) - 1023;
-  float f;
-  if (au == 0x7ff0000000000000ull) {
-    f = static_cast<float>(x);
-  } else if (e >= -126) {
-    const uint64_t half = 1ull << 44;
-    uint64_t low = u & ((1ull << 45) - 1);
-    uint64_t keep = u >> 45;
-    if (low > half || (low == half && (keep & 1ull))) keep += 1;
-    f = static_cast<float>(__longlong_as_double(static_cast<long long>(keep << 45)));
-  } else {
-    // bfloat16 subnormals: a fixed quantum of 2^-133
-    double q = rint(x * 0x1p133);
-    f = static_cast<float>(q * 0x1p-133);
-  }
-  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+  const double ax = fabs(x);
+  const float f = static_cast<float>(x);
+  const double back = static_cast<double>(f);
+  const bool inexact = back != x;
+  uint32_t u = __float_as_uint(f);
+  u -= (inexact && fabs(back) > ax) ? 1u : 0u;
+  u |= inexact ? 1u : 0u;
+  const float tiny = static_cast<float>(rint(x * 0x1p133) * 0x1p-133);
+  return f32_to_bf16(ax < 0x1p-126 ? tiny : __uint_as_float(u));
 }
 
 // Storage dtype helpers for user buffers (0 = f32, 1 = bf16, 2 = f16).

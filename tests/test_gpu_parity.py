@@ -487,3 +487,47 @@ def test_fresh_tensors_make_no_host_stall_and_streams_stay_ordered():
     main.wait_stream(side)
     torch.cuda.synchronize()
     assert torch.equal(Wa[0], Wb[0]) and torch.equal(Ma[0], Mb[0])
+
+
+@pytest.mark.parametrize("mu_", [0.5, 0.95])
+def test_momentum_rounding_ties_and_extremes(mu_):
+    """The momentum M <- mu M + G is rounded once to bf16, bit for bit as the
+    oracle rounds the exact value: on exact ties and values just either side
+    of them (mu = 0.5 makes mu M exact, so M + G can sit exactly half-way
+    between two bf16 values), on bf16 subnormals (below 2^-126), near the
+    largest bf16 value and on overflow to infinity."""
+    r = np.random.default_rng(77)
+    n = 64 * 96
+    g = orc.round_bf16(r.standard_normal(n) * 2.0 ** r.integers(-20, 20, n))
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(g))) - 7)
+    kind = r.integers(0, 6, n)
+    # mu m lands at ulp/2 (a tie), or one step of m either side of it
+    m = np.where(kind == 0, ulp, np.where(kind == 1, ulp * (1 + 2.0 ** -7), ulp * (1 - 2.0 ** -8))) / (2 * mu_)
+    m = orc.round_bf16(m * np.where(r.random(n) < 0.5, -1.0, 1.0))
+    # bf16 subnormals and tiny values, huge values and overflow
+    m[kind == 3] = orc.round_bf16(r.standard_normal((kind == 3).sum()) * 2.0 ** -130)
+    g[kind == 3] = orc.round_bf16(r.standard_normal((kind == 3).sum()) * 2.0 ** -128)
+    k4 = (kind == 4).sum()
+    m[kind == 4] = orc.round_bf16(3.0e38 * np.sign(r.standard_normal(k4)))
+    g[kind == 4] = orc.round_bf16(3.0e38 * r.uniform(-1.0, 1.0, k4))  # same sign: overflow; opposite: near the top
+    # bf16 tensors made from their bit patterns: a host conversion may flush
+    # bf16 subnormals to zero
+    def to_bf16(x):
+        bits = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return torch.from_numpy(bits.view(np.int16).reshape(64, 96)).view(torch.bfloat16)
+
+    def from_bf16(t):
+        bits = t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64).ravel()
+
+    M, G = to_bf16(m), to_bf16(g)
+    assert np.array_equal(from_bf16(M), m) and np.array_equal(from_bf16(G), g)
+    W = torch.zeros(64, 96)
+    _, M1, _ = run_step([W], [M], [G], mu_, 0.0, 0.0, "standard", O=False)
+    want = orc.round_bf16(float(np.float32(mu_)) * m + g)
+    got = from_bf16(M1[0])
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:8]
+    assert np.isinf(want).any() and (np.abs(want[np.isfinite(want) & (want != 0)]) < 2.0 ** -126).any()
+    if mu_ == 0.5:  # exact ties are present
+        x = mu_ * m + g
+        assert (np.abs(x - want) == ulp / 2).sum() > 100
