@@ -72,6 +72,7 @@ def parse():
 
 
 COPY_PROBE_BYTES = 1 << 30
+TRACED_STEPS_MAX = 30  # steps of the serial, per-launch traced pass
 COPY_PROBE_REPS = 3
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_step_amd", "csrc")
@@ -389,12 +390,13 @@ def main():
     # ------------------------------------------------ per-kernel durations (HIP events)
     # The traced steps run the groups back to back on one stream so that each
     # launch's event pair measures that kernel alone on the GPU.
+    traced_steps = min(args.steps, TRACED_STEPS_MAX)
     mu.trace_enable(True)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(traced_steps):
         step(args.variant, serial=True)
     torch.cuda.synchronize()
-    traced_sec = (time.perf_counter() - t0) / args.steps
+    traced_sec = (time.perf_counter() - t0) / traced_steps
     recs = mu.trace_collect()
     mu.trace_enable(False)
     kern = {}
@@ -408,8 +410,8 @@ def main():
     for r in recs:
         key = f'{r["kernel"]}:{r["role"]}'
         k = roles.setdefault(key, dict(ms=0.0, flops=0.0, launches=0))
-        k["ms"] += r["ms"] / args.steps
-        k["flops"] += r["flops"] / args.steps
+        k["ms"] += r["ms"] / traced_steps
+        k["flops"] += r["flops"] / traced_steps
         k["launches"] += 1
     dom_name, dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
     avg_ms = dom["ms"] / dom["launches"]
@@ -419,7 +421,7 @@ def main():
         peak = PEAK_F32_TFLOPS if dom_name.endswith("f64acc") else PEAK_16BIT_TFLOPS
         roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                     "traffic": read_traffic(dom_name, wl.key), "kernel": dom_name,
-                    "launches_per_step": dom["launches"] // args.steps,
+                    "launches_per_step": dom["launches"] // traced_steps,
                     "avg_launch_ms": avg_ms, "flops_per_launch": dom["flops"] / dom["launches"],
                     "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"]}
     else:
@@ -427,7 +429,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(dom_name, wl.key), "kernel": dom_name,
                     "avg_launch_ms": avg_ms}
-    kernels = {k: {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] // args.steps,
+    kernels = {k: {"ms_per_step": v["ms"] / traced_steps, "launches_per_step": v["launches"] // traced_steps,
                    "avg_launch_ms": v["ms"] / v["launches"],
                    "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None,
                    "gbs": v["bytes"] / (v["ms"] / 1e3) / 1e9} for k, v in kern.items()}
@@ -497,6 +499,7 @@ def main():
         "kernels": kernels,
         "roles": role_tab,
         "traced_ms_per_step": traced_sec * 1e3,
+        "traced_steps": traced_steps,
         "traced_note": "traced steps run the groups serially on one stream (per-kernel event timing)",
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -412,17 +412,15 @@ def trace_enable(on: bool = True) -> bool:
 def trace_collect():
     """Wait for the traced launches and return them as dicts (oldest first)."""
     lib = load_library()
-    cap = 4096
-    while True:
-        buf = (TraceRecord * cap)()
-        n = lib.muon_trace_collect(buf, cap)
-        if n < 0:
-            raise MuonError(4, "trace event query failed")
-        recs = [dict(kernel=buf[i].kernel.decode(), role=buf[i].role.decode(), flops=buf[i].flops,
-                     bytes=buf[i].bytes, ms=float(buf[i].ms)) for i in range(min(n, cap))]
-        if n > cap:
-            raise MuonError(1, f"trace held {n} records, more than {cap}")
-        return recs
+    cap = 1 << 16
+    buf = (TraceRecord * cap)()
+    n = lib.muon_trace_collect(buf, cap)
+    if n < 0:
+        raise MuonError(4, "trace event query failed")
+    if n > cap:
+        raise MuonError(1, f"trace held {n} records, more than {cap}")
+    return [dict(kernel=buf[i].kernel.decode(), role=buf[i].role.decode(), flops=buf[i].flops,
+                 bytes=buf[i].bytes, ms=float(buf[i].ms)) for i in range(n)]
 
 
 # --------------------------------------------------------------------------
