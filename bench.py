@@ -56,24 +56,25 @@ def parse():
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue every group on one stream (default: one stream per group)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help=f"finish with {COPY_PROBE_REPS} plain device copies of {COPY_PROBE_BYTES >> 20} MiB "
-                         "(the reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--summarize-counters", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write the profile summary of the dominant kernel from three rocprofv3 output "
-                         "directories (--stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE) and exit")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "BENCH_JSON"),
                     help="write the MFMA counter summary (--pmc MfmaUtil MfmaFlopsF16) of every GEMM kernel, "
                          "with the algorithmic FLOPs from the same run's bench.py line, to --out and exit")
-    ap.add_argument("--kernel", default=None, help="kernel name for --summarize-counters")
-    ap.add_argument("--out", default=None, help="output file for --summarize-counters")
-    ap.add_argument("--command", default="", help="the profiled command, recorded by --summarize-counters")
+    ap.add_argument("--traffic-run", metavar="TRACE_JSON",
+                    help="one serial step per group with the library's launch trace on (no timing), the "
+                         "trace's per-launch algorithmic bytes written to TRACE_JSON; run under rocprofv3 --pmc "
+                         "for --summarize-traffic")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("READ_DIR", "WRITE_DIR", "TRACE_JSON"),
+                    help="HBM-side bytes per kernel from two rocprofv3 --pmc passes over --traffic-run (L2-to-"
+                         "memory read requests by size, write requests by size) against the trace's algorithmic "
+                         "bytes; writes --out and exits")
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
+                    help="write the rocprofv3 --kernel-trace --stats table to --out and exit")
+    ap.add_argument("--out", default=None, help="output file of the --summarize-* modes")
+    ap.add_argument("--command", default="", help="the profiled command, recorded by the --summarize-* modes")
     return ap.parse_args()
 
 
-COPY_PROBE_BYTES = 1 << 30
 TRACED_STEPS_MAX = 30  # steps of the serial, per-launch traced pass
-COPY_PROBE_REPS = 3
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_step_amd", "csrc")
 
@@ -115,15 +116,15 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def traffic_file(kernel: str, workload: str) -> str:
-    safe = "".join(c if c.isalnum() else "_" for c in kernel).strip("_")
-    return os.path.join(PROFILES, f"{safe}_{workload}_traffic.txt")
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
 
 
 def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from its committed counter summary, or
-    None when there is none or the sources changed since it was taken."""
-    path = traffic_file(kernel, workload)
+    """Bytes moved between L2 and memory per launch of `kernel` from the
+    committed counter summary, or None when there is none or the sources
+    changed since it was taken."""
+    path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -132,9 +133,10 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != source_digest() or fields.get("kernel") != kernel:
+    key = f"traffic_bytes_per_launch[{kernel}]"
+    if fields.get("source_sha256") != source_digest() or key not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[key])
 
 
 def _csv_rows(d: str, suffix: str):
@@ -148,58 +150,120 @@ def _csv_rows(d: str, suffix: str):
     return rows
 
 
-def summarize_counters(args):
-    """Write the profile summary of args.kernel: its rocprofv3 --stats line,
-    and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same counters
-    read for the plain copies of --copy-probe."""
-    stats = [r for r in _csv_rows(args.summarize_counters[0], "kernel_stats.csv") if args.kernel in r["Name"]]
-    if len(stats) != 1:
-        raise SystemExit(f"expected one kernel_stats line for {args.kernel}, found {len(stats)}")
-    st = stats[0]
+READ_COUNTERS = ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")
 
-    def per_dispatch(d, counter):
-        vals, copies = [], []
-        for r in _csv_rows(d, "counter_collection.csv"):
-            if r["Counter_Name"] != counter:
-                continue
-            v = float(r["Counter_Value"])
-            if args.kernel in r["Kernel_Name"]:
-                vals.append(v)
-            elif "copy" in r["Kernel_Name"].lower() and int(r["Grid_Size"]) > 0:
-                copies.append(v)
-        if not vals or not copies:
-            raise SystemExit(f"{counter}: no dispatches of {args.kernel} or of the copy probe in {d}")
-        copy_kib = sorted(copies)[-COPY_PROBE_REPS:]
-        return sum(vals) / len(vals), sum(copy_kib) / len(copy_kib)
 
-    fetch, copy_fetch = per_dispatch(args.summarize_counters[1], "FETCH_SIZE")
-    write, copy_write = per_dispatch(args.summarize_counters[2], "WRITE_SIZE")
-    f_fetch = COPY_PROBE_BYTES / 1024.0 / copy_fetch
-    f_write = COPY_PROBE_BYTES / 1024.0 / copy_write
-    traffic = (fetch * f_fetch + write * f_write) * 1024.0
-    avg_ns = float(st["AverageNs"])
-    lines = [
-        f"kernel: {args.kernel}",
-        f"workload: {args.workload}",
-        f"command: {args.command}",
-        f"source_sha256: {source_digest()}",
-        f"rocprof_calls: {st['Calls']}",
-        f"rocprof_average_us: {avg_ns / 1e3:.2f}",
-        f"rocprof_min_us: {float(st['MinNs']) / 1e3:.2f}",
-        f"rocprof_max_us: {float(st['MaxNs']) / 1e3:.2f}",
-        f"rocprof_total_pct: {float(st['Percentage']):.2f}",
-        f"fetch_kib_per_launch_raw: {fetch:.1f}",
-        f"write_kib_per_launch_raw: {write:.1f}",
-        f"copy_probe_bytes: {COPY_PROBE_BYTES}",
-        f"copy_probe_fetch_kib_raw: {copy_fetch:.1f}",
-        f"copy_probe_write_kib_raw: {copy_write:.1f}",
-        f"scale_fetch: {f_fetch:.4f}",
-        f"scale_write: {f_write:.4f}",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
-    ]
+def _short_kernel(name: str) -> str:
+    """'void muon::(anonymous namespace)::norm_kernel<1>(muon::NormArgs)' -> 'norm_kernel<1>'."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0].split("::")[-1].strip()
+
+
+def _dispatch_counters(d: str):
+    """Per dispatch of the library's kernels (in dispatch order): (short
+    kernel name, {counter: value summed over instances})."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if "muon::" not in r["Kernel_Name"]:
+            continue
+        key = int(r["Dispatch_Id"])
+        ent = per.setdefault(key, [_short_kernel(r["Kernel_Name"]), {}])
+        ent[1][r["Counter_Name"]] = ent[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def summarize_traffic(args):
+    """Bytes moved between the L2 and memory per kernel, from the raw request
+    counters: reads = 32 n32 + 64 n64 + 128 n128 (requests by size), writes =
+    64 n64 + 32 (n - n64).  The library's launches of --traffic-run are
+    matched one by one, in order, with their dispatches, so every kernel's
+    counter bytes stand beside the algorithmic bytes of the same launches.
+    Writes are attributed to the dispatch during which the write-back L2
+    evicts them, so per kernel they are approximate; their sum is not."""
+    with open(args.summarize_traffic[2]) as f:
+        trace = json.load(f)
+    names = {t["kernel"] for t in trace["launches"]}
+    n = len(trace["launches"])
+
+    def split(d):
+        """The first n dispatches of traced kernels, then every later dispatch
+        of the library (the untraced low-bit step)."""
+        allx = _dispatch_counters(d)
+        matched, i = [], 0
+        while i < len(allx) and len(matched) < n:
+            if allx[i][0] in names:
+                matched.append(allx[i])
+            i += 1
+        return matched, allx[i:]
+
+    rd, rd_rest = split(args.summarize_traffic[0])
+    wr, wr_rest = split(args.summarize_traffic[1])
+    if not (len(rd) == len(wr) == n) or [x[0] for x in rd_rest] != [x[0] for x in wr_rest]:
+        raise SystemExit(f"dispatch counts differ: read pass {len(rd)}, write pass {len(wr)}, trace {n}")
+    tab = {}
+    for (kr, cr), (kw, cw), t in zip(rd, wr, trace["launches"]):
+        if not (kr == kw == t["kernel"]):
+            raise SystemExit(f"dispatch order differs: {kr} / {kw} / {t['kernel']}")
+        e = tab.setdefault(kr, dict(n=0, alg=0.0, rd=0.0, wr=0.0, req=0.0, req_split=0.0))
+        n32, n64, n128 = (cr.get(c, 0.0) for c in READ_COUNTERS[1:])
+        e["n"] += 1
+        e["alg"] += t["bytes"]
+        e["rd"] += 32 * n32 + 64 * n64 + 128 * n128
+        e["req"] += cr.get("TCC_EA0_RDREQ", 0.0)
+        e["req_split"] += n32 + n64 + n128
+        e["wr"] += 64 * cw.get("TCC_EA0_WRREQ_64B", 0.0) + 32 * (cw.get("TCC_EA0_WRREQ", 0.0) -
+                                                                 cw.get("TCC_EA0_WRREQ_64B", 0.0))
+    lines = [f"workload: {trace['workload']}",
+             f"command: {args.command}",
+             f"source_sha256: {source_digest()}",
+             "reads = 32 TCC_EA0_RDREQ_32B + 64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B; "
+             "writes = 64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B)",
+             "per launch, MB (1e6 bytes); algorithmic = the library's count (operands once, outputs once)",
+             f"{'kernel':34s} {'launches':>8s} {'alg_MB':>10s} {'read_MB':>10s} {'write_MB':>10s} "
+             f"{'(r+w)/alg':>9s} {'req_by_size/req':>15s}"]
+    tot = dict(alg=0.0, rd=0.0, wr=0.0)
+    for k in sorted(tab, key=lambda k: -tab[k]["alg"]):
+        e = tab[k]
+        for x in tot:
+            tot[x] += e[x]
+        lines.append(f"{k:34s} {e['n']:8d} {e['alg'] / e['n'] / 1e6:10.1f} {e['rd'] / e['n'] / 1e6:10.1f} "
+                     f"{e['wr'] / e['n'] / 1e6:10.1f} {(e['rd'] + e['wr']) / e['alg']:9.3f} "
+                     f"{e['req_split'] / max(e['req'], 1.0):15.4f}")
+        lines.append(f"traffic_bytes_per_launch[{k}]: {(e['rd'] + e['wr']) / e['n']:.0f}")
+    lines.append(f"all kernels: algorithmic {tot['alg'] / 1e9:.3f} GB, read {tot['rd'] / 1e9:.3f} GB, "
+                 f"write {tot['wr'] / 1e9:.3f} GB")
+    if rd_rest:
+        lines.append("the step with the low-bit momentum state (k = rank / 16), per kernel: dispatches, read MB "
+                     "and write MB per dispatch (no algorithmic count: not traced)")
+        other = {}
+        for (k, cr), (_, cw) in zip(rd_rest, wr_rest):
+            e = other.setdefault(k, [0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += 32 * cr.get("TCC_EA0_RDREQ_32B", 0.0) + 64 * cr.get("TCC_EA0_RDREQ_64B", 0.0) + \
+                128 * cr.get("TCC_EA0_RDREQ_128B", 0.0)
+            e[2] += 64 * cw.get("TCC_EA0_WRREQ_64B", 0.0) + 32 * (cw.get("TCC_EA0_WRREQ", 0.0) -
+                                                                 cw.get("TCC_EA0_WRREQ_64B", 0.0))
+        for k in sorted(other, key=lambda k: -(other[k][1] + other[k][2])):
+            c, r_, w_ = other[k]
+            lines.append(f"  {k:34s} {c:8d} {r_ / c / 1e6:10.1f} {w_ / c / 1e6:10.1f}")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_stats(args):
+    """The rocprofv3 --kernel-trace --stats table, one line per kernel."""
+    rows = _csv_rows(args.summarize_stats, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["Percentage"]))
+    out = [f"command: {args.command}", f"source_sha256: {source_digest()}",
+           f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in rows:
+        out.append(f"{_short_kernel(r['Name']):44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def summarize_mfma(args):
@@ -240,11 +304,14 @@ def summarize_mfma(args):
 
 def main():
     args = parse()
-    if args.summarize_counters:
-        summarize_counters(args)
-        return
     if args.summarize_mfma:
         summarize_mfma(args)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
+    if args.summarize_stats:
+        summarize_stats(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the step shards by "
@@ -366,6 +433,32 @@ def main():
             "algorithmic_flops_per_step": alg,
         }
 
+    if args.traffic_run:  # one serial step, traced, for the counter passes
+        mu.trace_enable(True)
+        step(args.variant, serial=True)
+        torch.cuda.synchronize()
+        recs = mu.trace_collect()
+        mu.trace_enable(False)
+        with open(args.traffic_run, "w") as f:
+            json.dump({"workload": wl.key, "variant": args.variant,
+                       "launches": [{"kernel": r["kernel"], "role": r["role"], "bytes": r["bytes"]} for r in recs]},
+                      f)
+        log(f"[bench] traffic run: {len(recs)} launches traced to {args.traffic_run}")
+        if not args.no_low_bit:  # then the step with the low-bit state (k = rank / 16), untraced
+            for gi, x in enumerate(groups):
+                g = x["g"]
+                k = max(1, min(g.rows, g.cols) // 16)
+                R0 = [syn.random_matrix(100 + gi * 64 + i, g.cols, k).to(dev) for i in range(g.count)]
+                st = mu.GraspState(g.count, g.rows, g.cols, k, dev, R_init=R0)
+                gws = torch.empty(mu.grasp_workspace_size(g.count, g.rows, g.cols, k, args.variant, cfg_for(args.variant)),
+                                  dtype=torch.uint8, device=dev)
+                torch.cuda.synchronize()
+                mu.grasp_step(x["W"], st, x["G"], 0.95, 0.02, 0.0, args.variant, cfg_for(args.variant), workspace=gws)
+                torch.cuda.synchronize()
+                del st, gws
+            log("[bench] traffic run: low-bit state step done")
+        return
+
     results = {}
     variants = [args.variant] + ([] if args.no_other_variant else [v for v in ("gram", "standard") if v != args.variant])
     for x in groups:  # outputs of the orthogonalisation-alone timing
@@ -435,16 +528,6 @@ def main():
                    "gbs": v["bytes"] / (v["ms"] / 1e3) / 1e9} for k, v in kern.items()}
     role_tab = {k: {"ms_per_step": v["ms"], "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None}
                 for k, v in sorted(roles.items(), key=lambda kv: -kv[1]["ms"])}
-
-    if args.copy_probe:  # reference dispatches for the HBM byte counters
-        # uint8 -> int8 keeps every byte but makes torch run its copy kernel
-        # (a same-dtype copy would go to the DMA engine, which has no counters)
-        src = torch.zeros(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty(COPY_PROBE_BYTES, dtype=torch.int8, device=dev)
-        for _ in range(COPY_PROBE_REPS):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     low_bit = None if args.no_low_bit else time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev)
 
