@@ -59,19 +59,24 @@ extern "C" {
 #define MUON_GRASP_MAX_K 1024
 
 /* Element types.  F32 = IEEE binary32, BF16 = bfloat16, F16 = IEEE binary16. */
-typedef enum { MUON_F32 = 0, MUON_BF16 = 1, MUON_F16 = 2 } muon_dtype;
+/* Each enum's last enumerator is no value to pass: it gives the type the range
+ * of a 32-bit int, so the library can check any value a caller passes and
+ * reject the ones it does not know (MUON_ERR_INVALID_ARG, "unknown status"). */
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1, MUON_F16 = 2, MUON_DTYPE_RANGE_ = 0x7fffffff } muon_dtype;
 
 typedef enum {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARG = 1, /* bad shape, count, pointer, or parameter   */
   MUON_ERR_UNSUPPORTED = 2, /* a dtype combination the library lacks     */
   MUON_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required   */
-  MUON_ERR_HIP = 4          /* a HIP runtime call or launch failed       */
+  MUON_ERR_HIP = 4,         /* a HIP runtime call or launch failed       */
+  MUON_STATUS_RANGE_ = 0x7fffffff
 } muon_status;
 
 typedef enum {
   MUON_NS_STANDARD = 0, /* [GNS §1.2 eq.(2)]                              */
-  MUON_NS_GRAM = 1      /* [GNS §2.3 Alg.1] / [GNS §3.4 Alg.2] (restarts) */
+  MUON_NS_GRAM = 1,     /* [GNS §2.3 Alg.1] / [GNS §3.4 Alg.2] (restarts) */
+  MUON_NS_VARIANT_RANGE_ = 0x7fffffff
 } muon_ns_variant;
 
 /*

@@ -50,22 +50,40 @@ def _finish(proc: subprocess.Popen, what: str, verbose: bool) -> None:
         print(msgs, file=sys.stderr)
 
 
-def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB, defines=()) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (the device code is
+# built as usual): for checking the argument checks, workspace planning and
+# schedule derivation on the CPU.  Load the result with the clang sanitizer
+# runtime preloaded (see sanitizer_runtime()).
+SANITIZE_COMPILE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_LINK = ["-fsanitize=address", "-fsanitize=undefined", "-fno-gpu-sanitize", "-shared-libsan"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime that a sanitized build links against."""
+    out = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
+def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB, defines=(), sanitize: bool = False) -> str:
     """Always recompiles (one process per source, in parallel); writes the
     library (default libmuon.so next to this file) atomically and returns its
-    path.  ``csrc``, ``lib`` and ``defines`` (-D flags) build a variant."""
+    path.  ``csrc``, ``lib`` and ``defines`` (-D flags) build a variant;
+    ``sanitize`` instruments the host code (see SANITIZE_COMPILE)."""
     objdir = tempfile.mkdtemp(prefix="muon_build_")
     try:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
-            procs.append((src, _run([hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-c", "-o", obj,
+            san = SANITIZE_COMPILE if sanitize else []
+            procs.append((src, _run([hipcc(), *HIPCC_FLAGS, *san, *[f"-D{d}" for d in defines], "-c", "-o", obj,
                                      os.path.join(csrc, src)], verbose)))
         for src, proc in procs:
             _finish(proc, src, verbose)
         tmp = lib + ".tmp"
-        _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose), "link", verbose)
+        _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SANITIZE_LINK if sanitize else []),
+                      "-o", tmp, *objs], verbose), "link", verbose)
         os.replace(tmp, lib)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
@@ -73,4 +91,8 @@ def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB, defines=()) -
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv[1:]:
+        print(build(verbose=True, lib=os.path.join(HERE, "libmuon_sanitized.so"), sanitize=True))
+        print("runtime to preload:", sanitizer_runtime())
+    else:
+        print(build(verbose=True))

@@ -1214,6 +1214,7 @@ const char* muon_status_string(muon_status status) {
     case MUON_ERR_UNSUPPORTED: return "unsupported dtype combination";
     case MUON_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MUON_ERR_HIP: return "HIP launch failed";
+    default: break;
   }
   return "unknown status";
 }
