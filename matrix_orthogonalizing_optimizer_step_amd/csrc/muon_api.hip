@@ -841,8 +841,9 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.Pout = P;
     MUON_LAUNCH(traced(s, "gram64_kernel+gram_sum", "grasp_gram", rows * kd * kd * batch, rows * kd * 4.0 * batch,
                        [&] { return launch_gram(a, batch, s); }));
-    MUON_LAUNCH(traced(s, "chol_panel_kernel", "grasp_cholesky", kd * kd * kd / 3.0 * batch, kd * kd * 16.0 * batch,
-                       [&] { return launch_chol(a, batch, s); }));
+    const bool reg = k <= kRegRankK;
+    MUON_LAUNCH(traced(s, reg ? "chol_reg_kernel" : "chol_panel_kernel", "grasp_cholesky", kd * kd * kd / 3.0 * batch,
+                       kd * kd * 16.0 * batch, [&] { return launch_chol(a, batch, s); }));
     MUON_LAUNCH(traced(s, "row_solve_kernel", "grasp_row_solve", rows * kd * kd * batch, rows * kd * 8.0 * batch,
                        [&] { return launch_row_solve(a, batch, s); }));
     Group8Args q{};

@@ -86,6 +86,10 @@ struct CholArgs {
   int panel;                                    // Cholesky panel rows (set by the launcher)
 };
 
+// Largest subspace rank of the register-resident Cholesky; larger ranks take
+// the panel kernel.
+constexpr int kRegRankK = 256;
+
 // Largest subspace rank the kernels take.
 constexpr int kMaxRankK = 1024;
 

@@ -488,15 +488,53 @@ __device__ __forceinline__ void store_pair(const PairRegs& r, uint16_t* hi, uint
 }
 
 // acc += A B over k in [kbeg, kend).  BPS: B comes pre-split (a.Bh, a.Bl:
-// planes of bf16 hi / lo, element (col, k) at col * b_row + k).
+// planes of bf16 hi / lo, element (col, k) at col * b_row + k).  With BPS and
+// A not k-contiguous (M_t^T: each load instruction reads 256 contiguous bytes
+// of a row), smem holds two stages (8 planes), the global loads run two
+// stages ahead of the MFMAs (two register sets) and a stage takes one
+// barrier; measured slower for the k-contiguous A of M_t Q, whose loads are
+// 128-byte pieces of 128 rows.  Otherwise one stage (4 planes), loads one
+// stage ahead.
 template <bool AKC, bool BKC, bool BPS = false>
 __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, int col0, int kbeg, int kend,
                                           uint16_t* smem, gq_f32x16 (&acc)[2][2]) {
   const float* A = a.A + static_cast<int64_t>(b) * a.sA;
-  uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
-  TileRegs ra;
-  load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
-  if constexpr (BPS) {
+  if constexpr (BPS && !AKC) {
+    const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
+    const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
+    const int nst = (kend - kbeg + kTK - 1) / kTK;
+    TileRegs ra[2];
+    PairRegs rb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < nst) {
+        load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg + q * kTK, a.M, kend, ra[q]);
+        load_pair(Bhi, Blo, a.b_row, col0, kbeg + q * kTK, a.N, kend, rb[q]);
+      }
+    for (int st = 0; st < nst; st += 2) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (st + q < nst) {
+          uint16_t* base = smem + q * 4 * kStageHalves;
+          uint16_t *Ah = base, *Al = base + kStageHalves, *Bh = base + 2 * kStageHalves, *Bl = base + 3 * kStageHalves;
+          store_split<AKC, true>(ra[q], Ah, Al);
+          store_pair(rb[q], Bh, Bl);
+          // LDS set q was last read two stages ago, before the previous barrier
+          __syncthreads();
+          const int kn = kbeg + (st + q + 2) * kTK;
+          if (kn < kend) {
+            load_f32<AKC>(A, a.a_row, a.a_k, row0, kn, a.M, kend, ra[q]);
+            load_pair(Bhi, Blo, a.b_row, col0, kn, a.N, kend, rb[q]);
+          }
+          mma_stage<true>(Ah, Al, Bh, Bl, acc);
+        }
+      }
+    }
+    __syncthreads();  // the caller may reuse smem
+  } else if constexpr (BPS) {
+    uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
+    TileRegs ra;
+    load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
     const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
     const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
     PairRegs rb;
@@ -513,6 +551,9 @@ __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, in
       __syncthreads();
     }
   } else {
+    uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
+    TileRegs ra;
+    load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
     const float* B = a.B + static_cast<int64_t>(b) * a.sB;
     TileRegs rb;
     load_f32<BKC>(B, a.b_row, a.b_k, col0, kbeg, a.N, kend, rb);
@@ -556,6 +597,27 @@ __global__ __launch_bounds__(kGT) void split_t_kernel(const float* X, int64_t sX
   }
 }
 
+// Tile order of the tiled state kernels (grid: x = tile column, y = tile
+// row, z = matrix or matrix x k piece).  Blocks are dealt to the 8 XCDs in
+// turn, each with its own L2: the linear block id is renumbered so that each
+// XCD takes a contiguous run of tiles, and the run goes through groups of 8
+// tile rows column by column, so the tiles in flight on one XCD share their
+// operand blocks (the row blocks of the group, one column block at a time)
+// through its L2 instead of fetching them again from memory.
+__device__ __forceinline__ void grouped_tile(int& bi, int& bj, int& z) {
+  const int64_t ncols = gridDim.x, nrows = gridDim.y;
+  const int64_t G = ncols * nrows * gridDim.z;
+  const int64_t p = blockIdx.x + ncols * (blockIdx.y + nrows * static_cast<int64_t>(blockIdx.z));
+  const int64_t q = G >> 3, rem = G & 7, xcd = p & 7, slot = p >> 3;
+  const int64_t L = xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+  const int64_t per = ncols * nrows;
+  z = static_cast<int>(L / per);
+  const int64_t t = L - z * per, g = t / (8 * ncols), w = t - g * 8 * ncols;
+  const int64_t rows_in = min(static_cast<int64_t>(8), nrows - 8 * g);
+  bi = static_cast<int>(8 * g + w % rows_in);
+  bj = static_cast<int>(w / rows_in);
+}
+
 // Tile element (row, col) of accumulator register v of block (x, y).
 __device__ __forceinline__ int acc_row(int x, int v) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -568,15 +630,17 @@ __device__ __forceinline__ int acc_col(int y) {
 
 // C (or a k-piece of C) = A B, stored fp32.  grid: (N tiles, M tiles, batch * pieces).
 template <bool AKC, bool BKC, bool BPS>
-__global__ __launch_bounds__(kGT) void tall_gemm_kernel(TallArgs a) {
-  __shared__ __align__(16) uint16_t smem[4 * kStageHalves];
-  const int b = blockIdx.z / a.pieces, piece = blockIdx.z - b * a.pieces;
-  const int row0 = blockIdx.y * kTT, col0 = blockIdx.x * kTT;
+__global__ __launch_bounds__(kGT, 2) void tall_gemm_kernel(TallArgs a) {
+  __shared__ __align__(16) uint16_t smem[(BPS && !AKC ? 8 : 4) * kStageHalves];
+  int bi, bj, z;
+  grouped_tile(bi, bj, z);
+  const int b = z / a.pieces, piece = z - b * a.pieces;
+  const int row0 = bi * kTT, col0 = bj * kTT;
   const int kbeg = piece * a.kchunk, kend = min(a.K, kbeg + a.kchunk);
   gq_f32x16 acc[2][2];
   zero_acc(acc);
   tall_loop<AKC, BKC, BPS>(a, b, row0, col0, kbeg, kend, smem, acc);
-  float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.sC;
+  float* C = a.C + static_cast<int64_t>(z) * a.sC;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -734,40 +798,45 @@ __global__ __launch_bounds__(kGT) void residual_kernel(ResidualArgs a) {
   __shared__ float cpart[4][kGB];
   uint16_t* smem = reinterpret_cast<uint16_t*>(raw);
   float* tile = reinterpret_cast<float*>(raw);
-  const int b = blockIdx.z, bi = blockIdx.y, bj = blockIdx.x;
+  int bi, bj, b;
+  grouped_tile(bi, bj, b);
   const int row0 = bi * kTT, col0 = bj * kTT;
-  gq_f32x16 acc[2][2];
-  zero_acc(acc);
-  tall_loop<true, true>(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
-  // tall_loop ends with a barrier, so the staging area can take the tile
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tile[acc_row(x, v) * kRL + acc_col(y)] = acc[x][y][v];
-  __syncthreads();
   const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
   const int rows = a.rows, cols = a.cols;
   const int j0 = col0 + 8 * cg, n = min(8, cols - j0);
   const float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
   const bool vec = (cols & 7) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.codes[b]) & 3u) | (reinterpret_cast<uintptr_t>(mt) & 15u)) == 0;
+  // this thread's M_t values first: their loads are in flight during the product
   float x[8][8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const int r = rs + 16 * s, i = row0 + r;
+    const int i = row0 + rs + 16 * s;
     float v[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) v[c] = 0.0f;
-    if (i < rows && n > 0) {
-      load8_f32(mt, static_cast<int64_t>(i) * cols + j0, 0, vec, n, v);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (c < n) v[c] -= tile[r * kRL + 8 * cg + c];
-    }
+    if (i < rows && n > 0) load8_f32(mt, static_cast<int64_t>(i) * cols + j0, 0, vec, n, v);
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[s][c] = v[c];
+  }
+  gq_f32x16 acc[2][2];
+  zero_acc(acc);
+  tall_loop<true, true>(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
+  // tall_loop ends with a barrier, so the staging area can take the tile
+#pragma unroll
+  for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tile[acc_row(xx, v) * kRL + acc_col(y)] = acc[xx][y][v];
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = rs + 16 * s, i = row0 + r;
+    if (i < rows)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < n) x[s][c] -= tile[r * kRL + 8 * cg + c];
   }
   encode_block(x, static_cast<uint8_t*>(a.codes[b]), static_cast<float*>(a.sr[b]), static_cast<float*>(a.sc[b]), rows,
                cols, bi, bj, vec, cpart);
@@ -996,10 +1065,11 @@ __global__ __launch_bounds__(kGT) void chol_panel_kernel(CholArgs a) {
 // P = P~ U^{-1} by forward substitution along each row (P U = P~).  A block
 // of 4 waves takes 4 RPW rows; column block jb (64 columns, lane l owning
 // column j = 64 jb + l) first takes the finished columns of earlier blocks
-// (their fp64 values in LDS times rows of U read from L2), then stages U's
-// 64 x 64 diagonal block in LDS and finishes its columns one at a time, each
-// broadcast from the lane that owns it.  Dead columns are zero.  fp64
-// arithmetic, fp32 result.
+// (their fp64 values in LDS times U's rows, staged through LDS 64 x 64 at a
+// time), then stages U's 64 x 64 diagonal block and finishes its columns one
+// at a time: lane q scales its value by its own 1 / U_qq (formed once per
+// block, zero for a dead column, so dead columns are zero) and the result is
+// broadcast by readlane.  fp64 arithmetic, fp32 result.
 template <int RPW>
 __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
   extern __shared__ double lds[];  // U block 64 x 64 | rows: 4 waves x RPW x k
@@ -1015,32 +1085,40 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
   for (int j0 = 0; j0 < k; j0 += 64) {
     const int j = j0 + lane, nb = min(64, k - j0);
     const bool in = j < k;
+    const bool dj = in ? dead[j] != 0 : true;
     double acc[RPW];
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       const int r = r0 + q;
       acc[q] = in && r < a.m ? static_cast<double>(Pt[static_cast<int64_t>(r) * k + j]) : 0.0;
     }
-#pragma unroll 4
-    for (int l = 0; l < j0; ++l) {
-      const double u = in ? U[static_cast<int64_t>(l) * k + j] : 0.0;
+    for (int l0 = 0; l0 < j0; l0 += 64) {
+      __syncthreads();  // the previous U block is no longer read
+      for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
+        const int rr = e >> 6, cc = e & 63;
+        ub[e] = j0 + cc < k ? U[static_cast<int64_t>(l0 + rr) * k + j0 + cc] : 0.0;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int l = 0; l < 64; ++l) {
+        const double u = ub[l * 64 + lane];
 #pragma unroll
-      for (int q = 0; q < RPW; ++q) acc[q] = fma(-prow[q * k + l], u, acc[q]);
+        for (int q = 0; q < RPW; ++q) acc[q] = fma(-prow[q * k + l0 + l], u, acc[q]);
+      }
     }
-    __syncthreads();  // the previous U block is no longer read
+    __syncthreads();
     for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
       const int rr = e >> 6, cc = e & 63;
       ub[rr * 64 + cc] = (rr < nb && cc < nb && cc >= rr) ? U[static_cast<int64_t>(j0 + rr) * k + j0 + cc] : 0.0;
     }
     __syncthreads();
+    const double rdiag = (lane < nb && !dj) ? 1.0 / ub[lane * 64 + lane] : 0.0;
     for (int q = 0; q < nb; ++q) {
       const int l = j0 + q;
-      const bool dl = dead[l] != 0;
-      const double diag = ub[q * 64 + q], u = ub[q * 64 + lane];
+      const double u = ub[q * 64 + lane];
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
-        const double mine = (lane == q && !dl) ? acc[rr] / diag : 0.0;
-        const double pl = __shfl(mine, q);
+        const double pl = readlane_f64(dj ? 0.0 : acc[rr] * rdiag, q);
         if (lane > q) acc[rr] = fma(-pl, u, acc[rr]);
         if (lane == q) prow[rr * k + l] = pl;
       }
@@ -1051,6 +1129,120 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
       if (in && r < a.m) Po[static_cast<int64_t>(r) * k + j] = static_cast<float>(prow[q * k + j]);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3 for k <= kRegRankK (256), every value in fp64, one block of 512
+// threads per matrix, with the k x k matrix in registers: thread (tr,
+// tc) = (t / 32, t % 32) holds the entries (tr + 16 i, tc + 32 j), i < 16,
+// j < 8, of the upper triangle (the slots with j >= i / 2; the rest would lie
+// below the diagonal).  A step publishes one row through LDS (two buffers,
+// so one barrier per step) and updates whole row blocks without branches:
+// rows that must not change get a zero multiplier, and slots outside the
+// matrix or below its diagonal take values that nothing reads.  Global
+// memory is touched outside the step loop only, and the loop holds no
+// division or square root (a dependent fp64 operation costs tens of cycles,
+// and the steps form one chain).
+//
+// Right-looking Cholesky one column at a time, in the form S = L' diag(d)
+// L'^T: step p publishes S[p][.], takes d_p = S[p][p] and 1 / d_p
+// (the hardware reciprocal and two Newton steps) and subtracts S[p][r]
+// S[p][c] / d_p from the entries of the rows r > p.  Row p of the slots
+// keeps S[p][.]; at the end U[p][p] = sqrt(d_p) and U[p][c] = S[p][c] /
+// sqrt(d_p).  The dead-column rule is the panel kernel's: a dead row p is
+// e_p in U and takes nothing from later columns.
+//
+// ---------------------------------------------------------------------------
+constexpr int kRegT = 512;
+constexpr int kRegBR = kRegRankK / 16;  // row blocks of 16
+constexpr int kRegBC = kRegRankK / 32;  // column blocks of 32
+
+// 1 / x for a positive normal x: the hardware estimate and two Newton steps.
+__device__ __forceinline__ double recip_f64(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  double e = fma(-x, y, 1.0);
+  y = fma(y, e, y);
+  e = fma(-x, y, 1.0);
+  return fma(y, e, y);
+}
+
+__global__ __launch_bounds__(kRegT) void chol_reg_kernel(CholArgs a) {
+  __shared__ double rowbuf[2][kRegRankK];
+  __shared__ double diag0[kRegRankK], dval[kRegRankK];
+  __shared__ int deads[kRegRankK];
+  const int b = blockIdx.x, k = a.k;
+  const int tr = threadIdx.x >> 5, tc = threadIdx.x & 31;
+  double* U = a.S + static_cast<int64_t>(b) * k * k;
+  double s[kRegBR][kRegBC];
+#pragma unroll
+  for (int i = 0; i < kRegBR; ++i)
+#pragma unroll
+    for (int j = i >> 1; j < kRegBC; ++j) {
+      const int r = tr + 16 * i, c = tc + 32 * j;
+      s[i][j] = (r < k && c < k && c >= r) ? U[static_cast<int64_t>(r) * k + c] : 0.0;
+    }
+  if (threadIdx.x < kRegRankK) {
+    const int c = threadIdx.x;
+    diag0[c] = c < k ? U[static_cast<int64_t>(c) * k + c] : 0.0;
+    rowbuf[0][c] = 0.0;
+    rowbuf[1][c] = 0.0;
+  }
+  __syncthreads();
+  for (int p = 0; p < k; ++p) {
+    const int pi = p >> 4;
+    const int pr = p & 15;
+    double* rb = rowbuf[p & 1];
+    if (tr == pr) {
+      // entries left of p are published as zero, so every slot stays finite
+#pragma unroll
+      for (int i = 0; i < kRegBR; ++i)
+        if (i == pi) {
+#pragma unroll
+          for (int j = i >> 1; j < kRegBC; ++j) rb[tc + 32 * j] = tc + 32 * j >= p ? s[i][j] : 0.0;
+        }
+    }
+    __syncthreads();
+    double uc[kRegBC], ur[kRegBR];
+#pragma unroll
+    for (int j = 0; j < kRegBC; ++j) uc[j] = rb[tc + 32 * j];
+#pragma unroll
+    for (int i = 0; i < kRegBR; ++i) ur[i] = rb[tr + 16 * i];
+    const double d = rb[p], d0 = diag0[p];
+    const bool is_dead = !(d0 > 0.0) || !(d > 1e-12 * d0);
+    if (threadIdx.x == 0) {
+      dval[p] = d;
+      deads[p] = is_dead ? 1 : 0;
+    }
+    if (!is_dead) {
+      const double rd = recip_f64(d);
+#pragma unroll
+      for (int i = 0; i < kRegBR; ++i) {
+        if (i >= pi) {
+          // rows up to p keep S[r][.] for the end: a zero multiplier
+          const double x = (i > pi || tr > pr) ? ur[i] * rd : 0.0;
+#pragma unroll
+          for (int j = i >> 1; j < kRegBC; ++j) s[i][j] = fma(-x, uc[j], s[i][j]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // U's rows: sqrt(d_r) on the diagonal, S[r][.] / sqrt(d_r) right of it (zero for a dead row)
+#pragma unroll
+  for (int i = 0; i < kRegBR; ++i) {
+    const int r = tr + 16 * i;
+    if (r < k) {
+      const bool dr = deads[r] != 0;
+      const double pv = dr ? 1.0 : sqrt(dval[r]);
+      const double iv = 1.0 / pv;
+#pragma unroll
+      for (int j = i >> 1; j < kRegBC; ++j) {
+        const int c = tc + 32 * j;
+        if (c >= r && c < k) U[static_cast<int64_t>(r) * k + c] = c == r ? pv : (dr ? 0.0 : s[i][j] * iv);
+      }
+    }
+  }
+  if (threadIdx.x < k) a.dead[static_cast<int64_t>(b) * k + threadIdx.x] = deads[threadIdx.x];
 }
 
 __global__ void ptr_table_kernel(float* base, int64_t stride, int batch, float** out) {
@@ -1149,6 +1341,10 @@ hipError_t launch_gram(const CholArgs& a, int batch, hipStream_t s) {
 }
 
 hipError_t launch_chol(const CholArgs& a, int batch, hipStream_t s) {
+  if (a.k <= kRegRankK) {
+    hipLaunchKernelGGL(chol_reg_kernel, dim3(batch), dim3(kRegT), 0, s, a);
+    return hipGetLastError();
+  }
   CholArgs c = a;
   c.panel = 32;
   while (c.panel > 1 && c.panel * a.k > kPanelElems) c.panel >>= 1;
