@@ -918,6 +918,69 @@ __global__ __launch_bounds__(kGT) void gram64_kernel(CholArgs a) {
   }
 }
 
+// Stage 1 for k <= kRegRankK on the fp64 MFMA.  Block (chunk, pass, matrix)
+// adds, over the chunk's rows, p_r p_r^T into the 16 x 16 blocks (I, J),
+// I <= J, of the upper triangle, numbered row by row; the pass takes 32 of
+// them, 8 per wave, each in one accumulator (v_mfma_f64_16x16x4f64, 4 rows
+// per instruction: lane l gives A[l % 16][l / 16] = P~[r + l / 16][16 I +
+// l % 16] and B[l / 16][l % 16] = P~[r + l / 16][16 J + l % 16], and holds
+// D[l / 16 + 4 v][l % 16] in register v).  Rows come through LDS 64 at a
+// time as fp32 (exact in fp64), zero past the chunk and past column k.
+constexpr int kGramMfmaRows = 64;
+constexpr int kGramMfmaLd = kRegRankK + 16;  // row stride: consecutive rows 16 banks apart
+constexpr int kGramPairsPerWave = 8;
+constexpr int kGramPairsPerPass = 4 * kGramPairsPerWave;
+typedef double gq_f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGT) void gram_mfma_kernel(CholArgs a) {
+  __shared__ float rows[kGramMfmaRows * kGramMfmaLd];
+  const int ch = blockIdx.x, pass = blockIdx.y, b = blockIdx.z;
+  const int k = a.k, nbk = (k + 15) / 16, kw = 16 * nbk, npairs = nbk * (nbk + 1) / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float* P = a.P + static_cast<int64_t>(b) * a.sP;
+  const int i0 = ch * a.chunk, i1 = min(a.m, i0 + a.chunk);
+  int pI[kGramPairsPerWave], pJ[kGramPairsPerWave];
+  gq_f64x4 acc[kGramPairsPerWave];
+#pragma unroll
+  for (int q = 0; q < kGramPairsPerWave; ++q) {
+    int p = pass * kGramPairsPerPass + w * kGramPairsPerWave + q, I = 0, len = nbk;
+    while (p >= len && I < nbk) {
+      p -= len;
+      ++I;
+      --len;
+    }
+    pI[q] = I < nbk ? I : -1;
+    pJ[q] = I < nbk ? I + p : -1;
+    acc[q] = gq_f64x4{0.0, 0.0, 0.0, 0.0};
+  }
+  for (int r0 = i0; r0 < i1; r0 += kGramMfmaRows) {
+    const int nr = min(kGramMfmaRows, i1 - r0);
+    __syncthreads();  // the previous rows are no longer read
+    for (int e = threadIdx.x; e < kGramMfmaRows * kw; e += kGT) {
+      const int rr = e / kw, c = e - rr * kw;
+      rows[rr * kGramMfmaLd + c] = (rr < nr && c < k) ? P[static_cast<int64_t>(r0 + rr) * k + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int s0 = 0; s0 < nr; s0 += 4) {
+      const float* row = rows + (s0 + (lane >> 4)) * kGramMfmaLd + (lane & 15);
+#pragma unroll
+      for (int q = 0; q < kGramPairsPerWave; ++q)
+        if (pI[q] >= 0)
+          acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(row[16 * pI[q]]),
+                                                        static_cast<double>(row[16 * pJ[q]]), acc[q], 0, 0, 0);
+    }
+  }
+  double* out = a.spart + (static_cast<int64_t>(b) * a.nchunk + ch) * k * k;
+#pragma unroll
+  for (int q = 0; q < kGramPairsPerWave; ++q)
+    if (pI[q] >= 0)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * pI[q] + (lane >> 4) + 4 * v, j = 16 * pJ[q] + (lane & 15);
+        if (i < k && j < k) out[static_cast<int64_t>(i) * k + j] = acc[q][v];
+      }
+}
+
 __global__ __launch_bounds__(kGT) void gram_sum_kernel(CholArgs a) {
   const int b = blockIdx.y;
   const int64_t kk = static_cast<int64_t>(a.k) * a.k;
@@ -1330,8 +1393,14 @@ hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s) {
 }
 
 hipError_t launch_gram(const CholArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(gram64_kernel, dim3(a.nchunk, batch), dim3(kGT),
-                     static_cast<size_t>(kGramRows) * a.k * sizeof(double), s, a);
+  if (a.k <= kRegRankK) {
+    const int nbk = (a.k + 15) / 16, npairs = nbk * (nbk + 1) / 2;
+    const dim3 grid(a.nchunk, (npairs + kGramPairsPerPass - 1) / kGramPairsPerPass, batch);
+    hipLaunchKernelGGL(gram_mfma_kernel, grid, dim3(kGT), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(gram64_kernel, dim3(a.nchunk, batch), dim3(kGT),
+                       static_cast<size_t>(kGramRows) * a.k * sizeof(double), s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t blocks = (static_cast<int64_t>(a.k) * a.k + kGT - 1) / kGT;
