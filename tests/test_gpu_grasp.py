@@ -217,7 +217,10 @@ def test_grasp_step_without_subspace_bitexact(rows, cols):
     (256, 4096, 16, "gram"),      # M_t Q split along k
     (4096, 256, 16, "standard"),  # M_t^T P split along k
     (200, 150, 1, "standard"),
-    (600, 700, 300, "gram"),      # k > 224: 16-row Cholesky panels, one row per wave in the solve, 3 groups
+    (600, 700, 300, "gram"),      # k > 256: the panel Cholesky (16-row panels), one row per wave in the solve, 3 groups
+    (300, 520, 256, "standard"),  # the largest k of the register-resident Cholesky: every slot block in use
+    (400, 300, 255, "gram"),      # k odd, next to that limit, iterated transposed
+    (270, 300, 257, "standard"),  # the smallest k of the panel Cholesky
     (257, 1, 1, "standard"),      # a column: k = min(rows, cols) = 1
     (1, 300, 1, "gram"),          # a row
 ])
