@@ -844,8 +844,9 @@ __global__ __launch_bounds__(kGT) void residual_kernel(ResidualArgs a) {
 
 // ---------------------------------------------------------------------------
 // CholeskyQR: P = P~ U^{-1} with P~^T P~ = U^T U.  Stage 1: fp64 partial
-// Gram matrices over chunks of 256 rows (upper triangle, 4 x 4 register
-// blocks, 8 rows at a time through LDS).  Stage 2: the partials summed in
+// Gram matrices over row chunks of gram_chunk_rows rows (here for k > 256:
+// upper triangle, 4 x 4 register blocks, 8 rows at a time through LDS; the
+// fp64 MFMA kernel below for smaller k).  Stage 2: the partials summed in
 // chunk order.  Stages 3 and 4 below: the Cholesky factor and the solve.
 // ---------------------------------------------------------------------------
 constexpr int kGramRows = 8;
@@ -994,8 +995,9 @@ __global__ __launch_bounds__(kGT) void gram_sum_kernel(CholArgs a) {
   }
 }
 
-// Stage 3, one block per matrix: blocked right-looking Cholesky S = U^T U
-// on the upper triangle (fp64, in place), panels of W <= 32 rows (W k <= 7168
+// Stage 3 for k > 256 (the register-resident kernel below takes smaller k),
+// one block per matrix: blocked right-looking Cholesky S = U^T U on the
+// upper triangle (fp64, in place), panels of W <= 32 rows (W k <= 7168
 // doubles, 56 KB of LDS).  Per panel: wave 0 factors the W x W diagonal block
 // in registers (lane c holds column c; row j of U is broadcast lane by lane),
 // all waves solve for the rest of the panel rows (U11^T U12 = S12, a column
@@ -1214,7 +1216,6 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
 // keeps S[p][.]; at the end U[p][p] = sqrt(d_p) and U[p][c] = S[p][c] /
 // sqrt(d_p).  The dead-column rule is the panel kernel's: a dead row p is
 // e_p in U and takes nothing from later columns.
-//
 // ---------------------------------------------------------------------------
 constexpr int kRegT = 512;
 constexpr int kRegBR = kRegRankK / 16;  // row blocks of 16
