@@ -294,10 +294,10 @@ size_t muon_grasp_workspace_size(int batch, int rows, int cols, int k, muon_ns_v
  *            on `stream`; the call ends by making `stream` wait for it, so the
  *            whole step is complete when `stream` passes the call.  Other work
  *            on aux_stream must not touch the state or the workspace meanwhile.
- * The products with fp32 operands (M_t Q, M_t^T P, P U^{-1}, P R^T) run on
- * the bf16 MFMA with each operand split into two bf16 parts (about 16
- * significant bits per product); the Gram matrix and its Cholesky factor are
- * fp64.  Errors as for muon_step.
+ * The products with fp32 operands (M_t Q, M_t^T P, P R^T) run on the bf16
+ * MFMA with each operand split into two bf16 parts (about 16 significant bits
+ * per product); the Gram matrix P~^T P~, its Cholesky factor and the solve
+ * P = P~ U^{-1} are fp64.  Errors as for muon_step.
  */
 muon_status muon_grasp_step(int batch, int rows, int cols, int k,
                             void *const *W, muon_dtype w_dtype,
