@@ -934,7 +934,7 @@ constexpr int kGramPairsPerPass = 4 * kGramPairsPerWave;
 typedef double gq_f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kGT) void gram_mfma_kernel(CholArgs a) {
-  __shared__ float rows[kGramMfmaRows * kGramMfmaLd];
+  __shared__ __align__(16) float rows[kGramMfmaRows * kGramMfmaLd];
   const int ch = blockIdx.x, pass = blockIdx.y, b = blockIdx.z;
   const int k = a.k, nbk = (k + 15) / 16, kw = 16 * nbk, npairs = nbk * (nbk + 1) / 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -954,12 +954,33 @@ __global__ __launch_bounds__(kGT) void gram_mfma_kernel(CholArgs a) {
     pJ[q] = I < nbk ? I + p : -1;
     acc[q] = gq_f64x4{0.0, 0.0, 0.0, 0.0};
   }
+  // rows staged 4 floats per thread and load, every load of a chunk in flight at once
+  const int kw4 = kw / 4;
+  const bool vec = (k & 3) == 0 && (reinterpret_cast<uintptr_t>(P) & 15u) == 0;
   for (int r0 = i0; r0 < i1; r0 += kGramMfmaRows) {
     const int nr = min(kGramMfmaRows, i1 - r0);
     __syncthreads();  // the previous rows are no longer read
-    for (int e = threadIdx.x; e < kGramMfmaRows * kw; e += kGT) {
-      const int rr = e / kw, c = e - rr * kw;
-      rows[rr * kGramMfmaLd + c] = (rr < nr && c < k) ? P[static_cast<int64_t>(r0 + rr) * k + c] : 0.0f;
+    float4 v[kGramMfmaRows * (kRegRankK / 4) / kGT];
+#pragma unroll
+    for (int q = 0; q < kGramMfmaRows * (kRegRankK / 4) / kGT; ++q) {
+      const int e = threadIdx.x + q * kGT, rr = e / kw4, c = 4 * (e - rr * kw4);
+      v[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (e < kGramMfmaRows * kw4 && rr < nr) {
+        const float* src = P + static_cast<int64_t>(r0 + rr) * k + c;
+        if (vec) {
+          if (c < k) v[q] = *reinterpret_cast<const float4*>(src);  // k % 4 == 0: whole or outside
+        } else {
+          v[q].x = c < k ? src[0] : 0.0f;
+          v[q].y = c + 1 < k ? src[1] : 0.0f;
+          v[q].z = c + 2 < k ? src[2] : 0.0f;
+          v[q].w = c + 3 < k ? src[3] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGramMfmaRows * (kRegRankK / 4) / kGT; ++q) {
+      const int e = threadIdx.x + q * kGT, rr = e / kw4, c = 4 * (e - rr * kw4);
+      if (e < kGramMfmaRows * kw4) *reinterpret_cast<float4*>(rows + rr * kGramMfmaLd + c) = v[q];
     }
     __syncthreads();
     for (int s0 = 0; s0 < nr; s0 += 4) {
@@ -989,8 +1010,18 @@ __global__ __launch_bounds__(kGT) void gram_sum_kernel(CholArgs a) {
        e += static_cast<int64_t>(gridDim.x) * kGT) {
     const int r = static_cast<int>(e / a.k), c = static_cast<int>(e - static_cast<int64_t>(r) * a.k);
     if (r > c) continue;
+    // in chunk order; eight loads in flight at a time
+    const double* src = a.spart + static_cast<int64_t>(b) * a.nchunk * kk + e;
     double s = 0.0;
-    for (int p = 0; p < a.nchunk; ++p) s += a.spart[(static_cast<int64_t>(b) * a.nchunk + p) * kk + e];
+    int p = 0;
+    for (; p + 8 <= a.nchunk; p += 8) {
+      double x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = src[static_cast<int64_t>(p + q) * kk];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += x[q];
+    }
+    for (; p < a.nchunk; ++p) s += src[static_cast<int64_t>(p) * kk];
     a.S[static_cast<int64_t>(b) * kk + e] = s;
   }
 }
@@ -1158,11 +1189,16 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
       acc[q] = in && r < a.m ? static_cast<double>(Pt[static_cast<int64_t>(r) * k + j]) : 0.0;
     }
     for (int l0 = 0; l0 < j0; l0 += 64) {
-      __syncthreads();  // the previous U block is no longer read
-      for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
-        const int rr = e >> 6, cc = e & 63;
-        ub[e] = j0 + cc < k ? U[static_cast<int64_t>(l0 + rr) * k + j0 + cc] : 0.0;
+      // the block's 16 values per thread loaded together, then stored
+      double v[64 * 64 / kGT];
+#pragma unroll
+      for (int q = 0; q < 64 * 64 / kGT; ++q) {
+        const int e = threadIdx.x + q * kGT, rr = e >> 6, cc = e & 63;
+        v[q] = j0 + cc < k ? U[static_cast<int64_t>(l0 + rr) * k + j0 + cc] : 0.0;
       }
+      __syncthreads();  // the previous U block is no longer read
+#pragma unroll
+      for (int q = 0; q < 64 * 64 / kGT; ++q) ub[threadIdx.x + q * kGT] = v[q];
       __syncthreads();
 #pragma unroll 8
       for (int l = 0; l < 64; ++l) {
@@ -1171,10 +1207,16 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
         for (int q = 0; q < RPW; ++q) acc[q] = fma(-prow[q * k + l0 + l], u, acc[q]);
       }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += kGT) {
-      const int rr = e >> 6, cc = e & 63;
-      ub[rr * 64 + cc] = (rr < nb && cc < nb && cc >= rr) ? U[static_cast<int64_t>(j0 + rr) * k + j0 + cc] : 0.0;
+    {
+      double v[64 * 64 / kGT];
+#pragma unroll
+      for (int q = 0; q < 64 * 64 / kGT; ++q) {
+        const int e = threadIdx.x + q * kGT, rr = e >> 6, cc = e & 63;
+        v[q] = (rr < nb && cc < nb && cc >= rr) ? U[static_cast<int64_t>(j0 + rr) * k + j0 + cc] : 0.0;
+      }
+      __syncthreads();  // the previous U block is no longer read
+#pragma unroll
+      for (int q = 0; q < 64 * 64 / kGT; ++q) ub[threadIdx.x + q * kGT] = v[q];
     }
     __syncthreads();
     const double rdiag = (lane < nb && !dj) ? 1.0 / ub[lane * 64 + lane] : 0.0;
