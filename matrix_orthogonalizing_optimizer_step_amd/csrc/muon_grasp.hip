@@ -281,8 +281,18 @@ __global__ __launch_bounds__(kGT) void colsq_kernel(UnitArgs a) {
 __global__ __launch_bounds__(kGT) void colinv_kernel(UnitArgs a) {
   const int b = blockIdx.x, k = a.k;
   for (int c = threadIdx.x; c < k; c += kGT) {
+    // in chunk order; eight loads in flight at a time
+    const double* src = a.part + static_cast<int64_t>(b) * a.nchunk * k + c;
     double ss = 0.0;
-    for (int p = 0; p < a.nchunk; ++p) ss += a.part[(static_cast<int64_t>(b) * a.nchunk + p) * k + c];
+    int p = 0;
+    for (; p + 8 <= a.nchunk; p += 8) {
+      double x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = src[static_cast<int64_t>(p + q) * k];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ss += x[q];
+    }
+    for (; p < a.nchunk; ++p) ss += src[static_cast<int64_t>(p) * k];
     a.inv[static_cast<int64_t>(b) * k + c] = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
   }
 }
