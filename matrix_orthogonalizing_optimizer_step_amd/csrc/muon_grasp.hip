@@ -182,45 +182,77 @@ __global__ __launch_bounds__(kGT) void grid_kernel(GridArgs a) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) oc[c] = (MODE != 0 && c < n) ? sc[static_cast<int64_t>(bi) * cols + j0 + c] : 0.0f;
   float x[8][8];
+  if constexpr (MODE == 1) {
+    // every load of the thread's 8 rows first, then the arithmetic and the
+    // stores: the stores of M_t could alias G for the compiler, so loads
+    // interleaved with them would take a memory round trip per row
+    float rsc[8];
+    uint32_t word[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int i = bi * kGB + rs + 16 * s;
-    float v[8];
+    for (int s = 0; s < 8; ++s) {
+      const int i = bi * kGB + rs + 16 * s;
+      rsc[s] = 0.0f;
+      word[s] = 0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = 0.0f;
-    if (i < rows && n > 0) {
-      const int64_t e = static_cast<int64_t>(i) * cols + j0;
-      if constexpr (MODE == 0) {
-        load8_f32(a.X[b], e, 0, vec, n, v);
-      } else {
-        const float r = sr[static_cast<int64_t>(i) * nbc + bj];
+      for (int c = 0; c < 8; ++c) x[s][c] = 0.0f;
+      if (i < rows && n > 0) {
+        const int64_t e = static_cast<int64_t>(i) * cols + j0;
+        rsc[s] = sr[static_cast<int64_t>(i) * nbc + bj];
         const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
-        uint32_t word = 0;
         if (vec) {
-          word = *reinterpret_cast<const uint32_t*>(src);
+          word[s] = *reinterpret_cast<const uint32_t*>(src);
         } else {
-          for (int q = 0; 2 * q < n; ++q) word |= static_cast<uint32_t>(src[q]) << (8 * q);
+          for (int q = 0; 2 * q < n; ++q) word[s] |= static_cast<uint32_t>(src[q]) << (8 * q);
         }
-        double d[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) d[c] = c < n ? decode(sext4((word >> (4 * c)) & 15u), nan_min(r, oc[c]), 7.0) : 0.0;
-        if constexpr (MODE == 2) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) v[c] = static_cast<float>(d[c]);
-          store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
-        } else {
-          float g[8];
-          load8_f32(a.G[b], e, a.g_dtype, vec, n, g);
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-            v[c] = c < n ? static_cast<float>(__dadd_rn(__dmul_rn(a.mu, d[c]), static_cast<double>(g[c]))) : 0.0f;
-          store8_f32(a.mt + static_cast<int64_t>(b) * a.s_mt + e, vec, n, v);
-          if (a.Y != nullptr) store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
-        }
+        load8_f32(a.G[b], e, a.g_dtype, vec, n, x[s]);  // G, replaced by M_t below
       }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) x[s][c] = v[c];
+    for (int s = 0; s < 8; ++s) {
+      const int i = bi * kGB + rs + 16 * s;
+      if (i < rows && n > 0) {
+        const int64_t e = static_cast<int64_t>(i) * cols + j0;
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const double d = c < n ? decode(sext4((word[s] >> (4 * c)) & 15u), nan_min(rsc[s], oc[c]), 7.0) : 0.0;
+          v[c] = c < n ? static_cast<float>(__dadd_rn(__dmul_rn(a.mu, d), static_cast<double>(x[s][c]))) : 0.0f;
+        }
+        store8_f32(a.mt + static_cast<int64_t>(b) * a.s_mt + e, vec, n, v);
+        if (a.Y != nullptr) store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[s][c] = v[c];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int i = bi * kGB + rs + 16 * s;
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+      if (i < rows && n > 0) {
+        const int64_t e = static_cast<int64_t>(i) * cols + j0;
+        if constexpr (MODE == 0) {
+          load8_f32(a.X[b], e, 0, vec, n, v);
+        } else {  // MODE 2: decode into Y
+          const float r = sr[static_cast<int64_t>(i) * nbc + bj];
+          const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
+          uint32_t word = 0;
+          if (vec) {
+            word = *reinterpret_cast<const uint32_t*>(src);
+          } else {
+            for (int q = 0; 2 * q < n; ++q) word |= static_cast<uint32_t>(src[q]) << (8 * q);
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            v[c] = c < n ? static_cast<float>(decode(sext4((word >> (4 * c)) & 15u), nan_min(r, oc[c]), 7.0)) : 0.0f;
+          store8_f32(static_cast<float*>(a.Y[b]) + e, vec, n, v);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[s][c] = v[c];
+    }
   }
   if constexpr (MODE != 2) encode_block(x, codes, sr, sc, rows, cols, bi, bj, vec, cpart);
 }
@@ -769,26 +801,38 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
   const bool vec = (a.cols & 7) == 0 && mis == 0;
   float cs[8];
   load8_f32(sc, static_cast<int64_t>(bi) * a.cols + j0, 0, vec, n, cs);
+  // both rows' loads before any store (the stores of M_t could alias G for
+  // the compiler, which would hold the second row's loads behind them)
+  constexpr int kRecPer = kRecRows / 16;
+  float rsc[kRecPer], g[kRecPer][8];
+  uint32_t word[kRecPer];
 #pragma unroll
-  for (int s = 0; s < kRecRows / 16; ++s) {
+  for (int s = 0; s < kRecPer; ++s) {
+    const int i = row0 + rs + 16 * s;
+    rsc[s] = 0.0f;
+    word[s] = 0;
+    if (i < a.rows) {
+      rsc[s] = sr[static_cast<int64_t>(i) * nbc + bj];
+      const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
+      if (vec) {
+        word[s] = *reinterpret_cast<const uint32_t*>(src);
+      } else {
+        for (int q = 0; 2 * q < n; ++q) word[s] |= static_cast<uint32_t>(src[q]) << (8 * q);
+      }
+      load8_f32(a.G[b], static_cast<int64_t>(i) * a.cols + j0, a.g_dtype, vec, n, g[s]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kRecPer; ++s) {
     const int r = rs + 16 * s, i = row0 + r;
     if (i >= a.rows) break;
-    const float rsc = sr[static_cast<int64_t>(i) * nbc + bj];
-    const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
-    uint32_t word = 0;
-    if (vec) {
-      word = *reinterpret_cast<const uint32_t*>(src);
-    } else {
-      for (int q = 0; 2 * q < n; ++q) word |= static_cast<uint32_t>(src[q]) << (8 * q);
-    }
     const int64_t e = static_cast<int64_t>(i) * a.cols + j0;
-    float g[8], m[8];
-    load8_f32(a.G[b], e, a.g_dtype, vec, n, g);
+    float m[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int q = sext4((word >> (4 * c)) & 15u);
-      const double res = static_cast<double>(q) * static_cast<double>(nan_min(rsc, cs[c])) * kInv7;
-      m[c] = static_cast<float>(fma(a.mu, res + tile[r * kTT + 8 * cg + c], static_cast<double>(g[c])));
+      const int q = sext4((word[s] >> (4 * c)) & 15u);
+      const double res = static_cast<double>(q) * static_cast<double>(nan_min(rsc[s], cs[c])) * kInv7;
+      m[c] = static_cast<float>(fma(a.mu, res + tile[r * kTT + 8 * cg + c], static_cast<double>(g[s][c])));
     }
     store8_f32(mt + e, vec, n, m);
     if (Y != nullptr) store8_f32(Y + e, vec, n, m);
