@@ -293,6 +293,26 @@ def test_grasp_zero_column_of_R():
     compare_state(gs, st1, det, rows, cols, k)
 
 
+@pytest.mark.parametrize("rows,cols,k", [(200, 300, 20), (300, 250, 224)], ids=["k20", "k224-transposed"])
+def test_grasp_all_zero_momentum(rows, cols, k):
+    """A zero gradient on the zero state: M_t = 0, so P~ = M_t Q = 0, S = 0
+    and every column of the Cholesky factor is dead (its diagonal entry is not
+    positive), which the solve turns into P = 0; then R = 0, the residual and
+    all codes are zero, O = 0 and W does not move, on both sides."""
+    R_init = seeded(90, cols, k)
+    st = go.new_state(rows, cols, k, R_init=R_init)
+    gs = gpu_state_from(st, rows, cols, k)
+    W = seeded(91, rows, cols)
+    G = np.zeros((rows, cols), np.float32)
+    (Wg, Og, Mg), (W1, st1, O1, M1, det) = run_both(W, st, gs, G, k, "gram")
+    assert not np.any(M1) and not np.any(Mg)
+    assert not np.any(det["P"]) and not np.any(O1) and not np.any(Og)
+    for name in ("P_codes", "P_scales", "R_codes", "R_scales"):
+        assert not np.any(st1[name]) and not np.any(host(getattr(gs, name)[0])), name
+    assert not np.any(host(gs.res_codes[0])) and not np.any(host(gs.res_row_scales[0]))
+    assert np.array_equal(Wg, W) and np.array_equal(W1.astype(np.float32), W)
+
+
 @pytest.mark.parametrize("rows,cols,k", [(3584, 18944, 224), (3584, 512, 32)], ids=["qwen-mlp", "qwen-kv"])
 def test_grasp_state_full_size(rows, cols, k):
     """Full-size matrices of the Qwen2.5-7B layer set at rank / 16, from a
