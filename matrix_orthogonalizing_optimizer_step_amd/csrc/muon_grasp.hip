@@ -1405,6 +1405,129 @@ __global__ __launch_bounds__(kRegT) void chol_reg_kernel(CholArgs a) {
   if (threadIdx.x < k) a.dead[static_cast<int64_t>(b) * k + threadIdx.x] = deads[threadIdx.x];
 }
 
+// k <= 224: the same in pairs of columns, one barrier per pair.  Rows p and
+// q = p + 1 are published together; each thread applies row p's update to
+// its copies of row q's values (t = S[q][.] - S[p][q] / d_p S[p][.], d_q =
+// t[q]) and then both rank-one updates to its slots, so rows below q take
+// both terms, row q takes row p's, and rows up to p none.  The slot layout
+// is the one above restricted to 14 row blocks and 7 column blocks, which
+// leaves registers for both rows' values.
+constexpr int kPairK = 224;
+constexpr int kPairBR = kPairK / 16, kPairBC = kPairK / 32;
+
+__global__ __launch_bounds__(kRegT) void chol_pair_kernel(CholArgs a) {
+  __shared__ double rowbuf[2][2][kPairK];
+  __shared__ double diag0[kPairK], dval[kPairK];
+  __shared__ int deads[kPairK];
+  const int b = blockIdx.x, k = a.k;
+  const int tr = threadIdx.x >> 5, tc = threadIdx.x & 31;
+  double* U = a.S + static_cast<int64_t>(b) * k * k;
+  double s[kPairBR][kPairBC];
+#pragma unroll
+  for (int i = 0; i < kPairBR; ++i)
+#pragma unroll
+    for (int j = i >> 1; j < kPairBC; ++j) {
+      const int r = tr + 16 * i, c = tc + 32 * j;
+      s[i][j] = (r < k && c < k && c >= r) ? U[static_cast<int64_t>(r) * k + c] : 0.0;
+    }
+  if (threadIdx.x < kPairK) {
+    const int c = threadIdx.x;
+    diag0[c] = c < k ? U[static_cast<int64_t>(c) * k + c] : 0.0;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) rowbuf[x][0][c] = rowbuf[x][1][c] = 0.0;
+  }
+  __syncthreads();
+  for (int p = 0; p < k; p += 2) {
+    const int q = p + 1;
+    const bool two = q < k;
+    const int pi = p >> 4, qi = q >> 4;
+    double* rb0 = rowbuf[(p >> 1) & 1][0];
+    double* rb1 = rowbuf[(p >> 1) & 1][1];
+    // entries left of a row's diagonal are published as zero, so every slot stays finite
+    if (tr == (p & 15)) {
+#pragma unroll
+      for (int i = 0; i < kPairBR; ++i)
+        if (i == pi) {
+#pragma unroll
+          for (int j = i >> 1; j < kPairBC; ++j) rb0[tc + 32 * j] = tc + 32 * j >= p ? s[i][j] : 0.0;
+        }
+    }
+    if (two && tr == (q & 15)) {
+#pragma unroll
+      for (int i = 0; i < kPairBR; ++i)
+        if (i == qi) {
+#pragma unroll
+          for (int j = i >> 1; j < kPairBC; ++j) rb1[tc + 32 * j] = tc + 32 * j >= q ? s[i][j] : 0.0;
+        }
+    }
+    __syncthreads();
+    double u0c[kPairBC], u0r[kPairBR], u1c[kPairBC], u1r[kPairBR];
+#pragma unroll
+    for (int j = 0; j < kPairBC; ++j) {
+      u0c[j] = rb0[tc + 32 * j];
+      u1c[j] = rb1[tc + 32 * j];
+    }
+#pragma unroll
+    for (int i = 0; i < kPairBR; ++i) {
+      u0r[i] = rb0[tr + 16 * i];
+      u1r[i] = rb1[tr + 16 * i];
+    }
+    const double d0 = rb0[p], e0 = diag0[p];
+    const bool dead0 = !(e0 > 0.0) || !(d0 > 1e-12 * e0);
+    const double r0 = recip_f64(d0);
+    const double rd0 = dead0 ? 0.0 : r0;
+    double rd1 = 0.0, d1 = 0.0;
+    bool dead1 = true;
+    if (two) {
+      const double f = rb0[q] * rd0;  // S[p][q] / d_p (zero for a dead row p)
+      d1 = fma(-f, rb0[q], rb1[q]);
+      const double e1 = diag0[q];
+      dead1 = !(e1 > 0.0) || !(d1 > 1e-12 * e1);
+      const double r1 = recip_f64(d1);
+      rd1 = dead1 ? 0.0 : r1;
+#pragma unroll
+      for (int j = 0; j < kPairBC; ++j) u1c[j] = fma(-f, u0c[j], u1c[j]);
+#pragma unroll
+      for (int i = 0; i < kPairBR; ++i) u1r[i] = fma(-f, u0r[i], u1r[i]);
+    }
+    if (threadIdx.x == 0) {
+      dval[p] = d0;
+      deads[p] = dead0 ? 1 : 0;
+      if (two) {
+        dval[q] = d1;
+        deads[q] = dead1 ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPairBR; ++i) {
+      if (i >= pi) {
+        const int r = tr + 16 * i;
+        const double x0 = r > p ? u0r[i] * rd0 : 0.0;
+        const double x1 = r > q ? u1r[i] * rd1 : 0.0;
+#pragma unroll
+        for (int j = i >> 1; j < kPairBC; ++j) s[i][j] = fma(-x1, u1c[j], fma(-x0, u0c[j], s[i][j]));
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPairBR; ++i) {
+    const int r = tr + 16 * i;
+    if (r < k) {
+      const bool dr = deads[r] != 0;
+      const double pv = dr ? 1.0 : sqrt(dval[r]);
+      const double iv = 1.0 / pv;
+#pragma unroll
+      for (int j = i >> 1; j < kPairBC; ++j) {
+        const int c = tc + 32 * j;
+        if (c >= r && c < k) U[static_cast<int64_t>(r) * k + c] = c == r ? pv : (dr ? 0.0 : s[i][j] * iv);
+      }
+    }
+  }
+  if (threadIdx.x < k) a.dead[static_cast<int64_t>(b) * k + threadIdx.x] = deads[threadIdx.x];
+}
+
+
 __global__ void ptr_table_kernel(float* base, int64_t stride, int batch, float** out) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < batch) out[b] = base + static_cast<int64_t>(b) * stride;
@@ -1507,6 +1630,10 @@ hipError_t launch_gram(const CholArgs& a, int batch, hipStream_t s) {
 }
 
 hipError_t launch_chol(const CholArgs& a, int batch, hipStream_t s) {
+  if (a.k <= kPairK) {
+    hipLaunchKernelGGL(chol_pair_kernel, dim3(batch), dim3(kRegT), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.k <= kRegRankK) {
     hipLaunchKernelGGL(chol_reg_kernel, dim3(batch), dim3(kRegT), 0, s, a);
     return hipGetLastError();
