@@ -1293,8 +1293,9 @@ __global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Stage 3 for k <= kRegRankK (256), every value in fp64, one block of 512
-// threads per matrix, with the k x k matrix in registers: thread (tr,
+// Stage 3 for 224 < k <= kRegRankK (256) (smaller k take the paired version
+// below), every value in fp64, one block of 512 threads per matrix, with the
+// k x k matrix in registers: thread (tr,
 // tc) = (t / 32, t % 32) holds the entries (tr + 16 i, tc + 32 j), i < 16,
 // j < 8, of the upper triangle (the slots with j >= i / 2; the rest would lie
 // below the diagonal).  A step publishes one row through LDS (two buffers,
