@@ -647,18 +647,31 @@ constexpr int kGraspMaxBatch = 65535 / kGraspMaxPieces;  // the state kernels pu
 
 int nblk(int x, int b) { return (x + b - 1) / b; }
 
-// k pieces for a product with `tiles` output tiles and K of length `K`: enough
-// blocks for about two rounds on the device, each piece at least 256 long.
-// Planned for the 256 compute units of the MI355X so that the workspace size
-// depends on the shapes only.
+// k pieces for a product with `tiles` output tiles and K of length `K`, each
+// piece at least 256 long.  The tall products run two blocks per compute
+// unit, and a block's time is set by its k length (its loads wait on memory
+// latency, not on bandwidth shared with the others), so a launch of B blocks
+// takes about ceil(B / slots) rounds of K / pieces each: with fewer tiles than
+// slots, the count that minimises rounds / pieces is taken (the smallest on a
+// tie, for the fewest partial sums).  Planned for the 256 compute units of the
+// MI355X so that the workspace size depends on the shapes only.
 constexpr int kGraspPlanCUs = 256;
+constexpr int kTallBlocksPerCU = 2;
 
 void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
-  const int cu = kGraspPlanCUs;
-  int pcs = tiles >= 2 * cu ? 1 : static_cast<int>((2 * cu + tiles - 1) / tiles);
-  pcs = pcs < kGraspMaxPieces ? pcs : kGraspMaxPieces;
-  const int maxp = K / 256 > 1 ? K / 256 : 1;
-  pcs = pcs < maxp ? pcs : maxp;
+  const int64_t slots = static_cast<int64_t>(kGraspPlanCUs) * kTallBlocksPerCU;
+  const int maxp = K / 256 > 1 ? (K / 256 < kGraspMaxPieces ? K / 256 : kGraspMaxPieces) : 1;
+  int pcs = 1;
+  if (tiles < slots) {
+    double best = 0.0;
+    for (int q = 1; q <= maxp; ++q) {
+      const double cost = static_cast<double>((tiles * q + slots - 1) / slots) / q;
+      if (q == 1 || cost < best - 1e-12) {
+        best = cost;
+        pcs = q;
+      }
+    }
+  }
   int chunk = static_cast<int>(round_up(static_cast<size_t>((K + pcs - 1) / pcs), 32));
   *kchunk = chunk;
   *pieces = (K + chunk - 1) / chunk;
@@ -687,7 +700,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->gchunk = gram_chunk_rows(rows, batch);
     g->nch_m = nblk(rows, g->gchunk);
     g->q = take(B * c * kk * 4);
-    g->qs = take(B * c * kk * 4);  // Q^T split into bf16 hi and lo planes
+    g->qs = take(B * c * kk * 4);  // Q^T split into bf16 hi and lo planes, later R
     g->colpart = take(B * g->nch_n * kk * 8);
     g->colinv = take(B * kk * 8);
     int pcs = 1, chunk = 0;
@@ -698,7 +711,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->S = take(B * kk * kk * 8);
     g->dead = take(B * kk * 4);
     g->P = take(B * r * kk * 4);
-    g->ps = take(B * r * kk * 4);  // P^T split into bf16 hi and lo planes
+    g->ps = take(B * r * kk * 4);  // P^T split into bf16 hi and lo planes, later P
     grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &pcs, &chunk);
     g->rpart = take(pcs > 1 ? B * pcs * c * kk * 4 : 0);
     g->R = take(B * c * kk * 4);
@@ -820,7 +833,7 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.ppart) : ptil;
     MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 1, 1>", "grasp_MQ", 2.0 * elems * kd,
                        elems * 4.0 + (cols + rows * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, true, true, batch, s); }));
+                       [&] { return launch_tall(a, true, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MQ_sum", 0.0, rows * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, ptil, batch, s); }));
@@ -882,7 +895,7 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.rpart) : R;
     MUON_LAUNCH(traced(s, "tall_gemm_kernel<0, 1, 1>", "grasp_MtP", 2.0 * elems * kd,
                        elems * 4.0 + (rows + cols * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, false, true, batch, s); }));
+                       [&] { return launch_tall(a, false, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MtP_sum", 0.0, cols * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, R, batch, s); }));
@@ -896,22 +909,31 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     MUON_LAUNCH(traced(s, "group8_kernel<0>", "grasp_R_code", 0.0, cols * kd * 5.0 * batch,
                        [&] { return launch_group8(q, false, batch, s); }));
   }
-  // 7. grid code of M_res = M_t - P R^T
+  // 7. grid code of M_res = M_t - P R^T, P and R split once into bf16 planes
+  // (in the buffers of the split Q^T and P^T, which M_t Q and M_t^T P have used)
   {
+    uint16_t* rsp = qs;
+    MUON_LAUNCH(traced(s, "split_kernel", "grasp_PR_split", 0.0, (rows + cols) * kd * batch * 8.0, [&] {
+      hipError_t e = launch_split(P, static_cast<int64_t>(rows) * k, static_cast<int64_t>(rows) * k, ps,
+                                  ps + static_cast<int64_t>(rows) * k, s_ps, batch, s);
+      if (e != hipSuccess) return e;
+      return launch_split(R, static_cast<int64_t>(cols) * k, static_cast<int64_t>(cols) * k, rsp,
+                          rsp + static_cast<int64_t>(cols) * k, s_qs, batch, s);
+    }));
     ResidualArgs a{};
     a.rows = rows;
     a.cols = cols;
     a.prod.M = rows;
     a.prod.N = cols;
     a.prod.K = k;
-    a.prod.A = P;
-    a.prod.sA = static_cast<int64_t>(rows) * k;
+    a.prod.Ah = ps;
+    a.prod.Al = ps + static_cast<int64_t>(rows) * k;
+    a.prod.sA = s_ps;
     a.prod.a_row = k;
-    a.prod.a_k = 1;
-    a.prod.B = R;
-    a.prod.sB = static_cast<int64_t>(cols) * k;
+    a.prod.Bh = rsp;
+    a.prod.Bl = rsp + static_cast<int64_t>(cols) * k;
+    a.prod.sB = s_qs;
     a.prod.b_row = k;
-    a.prod.b_k = 1;
     a.prod.pieces = 1;
     a.prod.kchunk = k;
     a.mt = mt;

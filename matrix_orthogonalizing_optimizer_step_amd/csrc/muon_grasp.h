@@ -45,6 +45,8 @@ struct UnitArgs {
 // and writes C + z sC (partial products, summed by launch_sum_pieces).
 // Bh / Bl non-null: B comes pre-split into bf16 planes (hi, lo), element
 // (col, k) at + b sB + col b_row + k (k contiguous); B and b_k are unused.
+// Ah / Al likewise for A (element (row, k) at + b sA + row a_row + k), taken
+// by the residual kernel only.
 struct TallArgs {
   int M, N, K;
   const float* A; int64_t sA, a_row, a_k;
@@ -53,6 +55,8 @@ struct TallArgs {
   int pieces, kchunk;
   const uint16_t* Bh = nullptr;
   const uint16_t* Bl = nullptr;
+  const uint16_t* Ah = nullptr;
+  const uint16_t* Al = nullptr;
 };
 
 // M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G.
@@ -66,7 +70,8 @@ struct ReconArgs {
   void* const* Y;                               // optional copy of M_t
 };
 
-// New grid code of M_t - P R^T (prod: A = P, B = R, both k-contiguous).
+// New grid code of M_t - P R^T (prod: A = P, B = R, both pre-split into bf16
+// planes, k contiguous).
 struct ResidualArgs {
   int rows, cols;
   TallArgs prod;
@@ -102,9 +107,11 @@ inline int gram_chunk_rows(int m, int batch) {
 hipError_t launch_grid(const GridArgs& a, int mode, int batch, hipStream_t s);
 hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStream_t s);
 hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s);
-hipError_t launch_tall(const TallArgs& a, bool a_kcontig, bool b_kcontig, int batch, hipStream_t s);
+hipError_t launch_tall(const TallArgs& a, bool a_kcontig, int batch, hipStream_t s);  // B pre-split
 hipError_t launch_split_t(const float* X, int64_t sX, int rows, int k, uint16_t* hi, uint16_t* lo, int64_t sT,
                           int batch, hipStream_t s);
+hipError_t launch_split(const float* X, int64_t sX, int64_t count, uint16_t* hi, uint16_t* lo, int64_t sT, int batch,
+                        hipStream_t s);
 hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float* out, int batch, hipStream_t s);
 hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s);
 hipError_t launch_residual(const ResidualArgs& a, int batch, hipStream_t s);

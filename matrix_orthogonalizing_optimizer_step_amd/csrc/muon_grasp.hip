@@ -487,31 +487,35 @@ __device__ __forceinline__ void zero_acc(gq_f32x16 (&acc)[2][2]) {
       for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.0f;
 }
 
-// acc += A[row0.., kbeg..kend) B[kbeg..kend), col0..] for fp32 operands
-// (split).  smem: 4 planes of kStageHalves bf16.
 // An operand already split into bf16 planes (hi, lo), k contiguous: the
 // thread's four runs of 4 consecutive k, 8 bytes per plane each.
 struct PairRegs {
   uint2 h[4], l[4];
 };
 
+// Addresses: the tile's first row as a uniform base, 32-bit offsets from it
+// (128 rows of at most MUON_MAX_DIM entries each), so each load takes one
+// address register.
 __device__ __forceinline__ void load_pair(const uint16_t* hi, const uint16_t* lo, int64_t s_row, int row0, int k0,
                                           int nrows, int K, PairRegs& r) {
+  const uint16_t* hb = hi + static_cast<int64_t>(row0) * s_row;
+  const uint16_t* lb = lo + static_cast<int64_t>(row0) * s_row;
+  const bool al = (((reinterpret_cast<uintptr_t>(hb) | reinterpret_cast<uintptr_t>(lb)) & 7u) | (s_row & 3)) == 0;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = threadIdx.x + kGT * p;
     const int row = row0 + (e >> 3), k = k0 + (e & 7) * 4;
-    const int64_t off = static_cast<int64_t>(row) * s_row + k;
-    if (row < nrows && k + 3 < K && ((reinterpret_cast<uintptr_t>(hi + off) | reinterpret_cast<uintptr_t>(lo + off)) & 7u) == 0) {
-      r.h[p] = *reinterpret_cast<const uint2*>(hi + off);
-      r.l[p] = *reinterpret_cast<const uint2*>(lo + off);
+    const uint32_t off = static_cast<uint32_t>(e >> 3) * static_cast<uint32_t>(s_row) + static_cast<uint32_t>(k);
+    if (al && row < nrows && k + 3 < K) {
+      r.h[p] = *reinterpret_cast<const uint2*>(hb + off);
+      r.l[p] = *reinterpret_cast<const uint2*>(lb + off);
     } else {
       uint32_t h[2] = {0u, 0u}, l[2] = {0u, 0u};
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (row < nrows && k + q < K) {
-          h[q >> 1] |= static_cast<uint32_t>(hi[off + q]) << (16 * (q & 1));
-          l[q >> 1] |= static_cast<uint32_t>(lo[off + q]) << (16 * (q & 1));
+          h[q >> 1] |= static_cast<uint32_t>(hb[off + q]) << (16 * (q & 1));
+          l[q >> 1] |= static_cast<uint32_t>(lb[off + q]) << (16 * (q & 1));
         }
       r.h[p] = make_uint2(h[0], h[1]);
       r.l[p] = make_uint2(l[0], l[1]);
@@ -529,19 +533,20 @@ __device__ __forceinline__ void store_pair(const PairRegs& r, uint16_t* hi, uint
   }
 }
 
-// acc += A B over k in [kbeg, kend).  BPS: B comes pre-split (a.Bh, a.Bl:
-// planes of bf16 hi / lo, element (col, k) at col * b_row + k).  With BPS and
-// A not k-contiguous (M_t^T: each load instruction reads 256 contiguous bytes
-// of a row), smem holds two stages (8 planes), the global loads run two
-// stages ahead of the MFMAs (two register sets) and a stage takes one
-// barrier; measured slower for the k-contiguous A of M_t Q, whose loads are
-// 128-byte pieces of 128 rows.  Otherwise one stage (4 planes), loads one
-// stage ahead.
-template <bool AKC, bool BKC, bool BPS = false>
+// acc += A B over k in [kbeg, kend) for an fp32 A, split as it is staged,
+// and a B that comes pre-split (BPS: a.Bh, a.Bl, planes of bf16 hi / lo,
+// element (col, k) at col * b_row + k, k contiguous).  With A not
+// k-contiguous (M_t^T: each load instruction reads 256 contiguous bytes of a
+// row), smem holds two stages (8 planes), the global loads run two stages
+// ahead of the MFMAs (two register sets) and a stage takes one barrier;
+// measured slower for the k-contiguous A of M_t Q, whose loads are 128-byte
+// pieces of 128 rows: there one stage (4 planes), loads one stage ahead.
+template <bool AKC, bool BKC, bool BPS>
 __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, int col0, int kbeg, int kend,
                                           uint16_t* smem, gq_f32x16 (&acc)[2][2]) {
+  static_assert(BKC && BPS, "B comes pre-split, k contiguous");
   const float* A = a.A + static_cast<int64_t>(b) * a.sA;
-  if constexpr (BPS && !AKC) {
+  if constexpr (!AKC) {
     const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
     const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
     const int nst = (kend - kbeg + kTK - 1) / kTK;
@@ -573,7 +578,7 @@ __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, in
       }
     }
     __syncthreads();  // the caller may reuse smem
-  } else if constexpr (BPS) {
+  } else {
     uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
     TileRegs ra;
     load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
@@ -592,24 +597,50 @@ __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, in
       mma_stage<true>(Ah, Al, Bh, Bl, acc);
       __syncthreads();
     }
-  } else {
-    uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
-    TileRegs ra;
-    load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
-    const float* B = a.B + static_cast<int64_t>(b) * a.sB;
-    TileRegs rb;
-    load_f32<BKC>(B, a.b_row, a.b_k, col0, kbeg, a.N, kend, rb);
-    for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-      store_split<AKC, true>(ra, Ah, Al);
-      store_split<BKC, true>(rb, Bh, Bl);
-      __syncthreads();
-      if (k0 + kTK < kend) {
-        load_f32<AKC>(A, a.a_row, a.a_k, row0, k0 + kTK, a.M, kend, ra);
-        load_f32<BKC>(B, a.b_row, a.b_k, col0, k0 + kTK, a.N, kend, rb);
-      }
-      mma_stage<true>(Ah, Al, Bh, Bl, acc);
-      __syncthreads();
+  }
+}
+
+// acc += A B over k in [kbeg, kend) with both operands pre-split into bf16
+// planes, k contiguous (a.Ah / a.Al and a.Bh / a.Bl): the loads run one
+// stage ahead and go to LDS unconverted.
+__device__ __forceinline__ void presplit_loop(const TallArgs& a, int b, int row0, int col0, int kbeg, int kend,
+                                              uint16_t* smem, gq_f32x16 (&acc)[2][2]) {
+  uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
+  const uint16_t* Ahi = a.Ah + static_cast<int64_t>(b) * a.sA;
+  const uint16_t* Alo = a.Al + static_cast<int64_t>(b) * a.sA;
+  const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
+  const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
+  PairRegs ra, rb;
+  load_pair(Ahi, Alo, a.a_row, row0, kbeg, a.M, kend, ra);
+  load_pair(Bhi, Blo, a.b_row, col0, kbeg, a.N, kend, rb);
+  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+    store_pair(ra, Ah, Al);
+    store_pair(rb, Bh, Bl);
+    __syncthreads();
+    if (k0 + kTK < kend) {
+      load_pair(Ahi, Alo, a.a_row, row0, k0 + kTK, a.M, kend, ra);
+      load_pair(Bhi, Blo, a.b_row, col0, k0 + kTK, a.N, kend, rb);
     }
+    mma_stage<true>(Ah, Al, Bh, Bl, acc);
+    __syncthreads();
+  }
+}
+
+// X (count fp32 per matrix, matrix b at X + b sX) -> bf16 planes hi, lo of
+// the same layout (matrix b at hi + b sT, lo + b sT): the split of an operand
+// done once.
+__global__ __launch_bounds__(kGT) void split_kernel(const float* X, int64_t sX, int64_t count, uint16_t* hi,
+                                                    uint16_t* lo, int64_t sT) {
+  const int b = blockIdx.y;
+  const float* Xm = X + static_cast<int64_t>(b) * sX;
+  uint16_t* H = hi + static_cast<int64_t>(b) * sT;
+  uint16_t* L = lo + static_cast<int64_t>(b) * sT;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kGT + threadIdx.x; e < count;
+       e += static_cast<int64_t>(gridDim.x) * kGT) {
+    const float x = Xm[e];
+    const uint16_t h = f32_to_bf16(x);
+    H[e] = h;
+    L[e] = f32_to_bf16(x - bf16_to_f32(h));
   }
 }
 
@@ -673,7 +704,7 @@ __device__ __forceinline__ int acc_col(int y) {
 // C (or a k-piece of C) = A B, stored fp32.  grid: (N tiles, M tiles, batch * pieces).
 template <bool AKC, bool BKC, bool BPS>
 __global__ __launch_bounds__(kGT, 2) void tall_gemm_kernel(TallArgs a) {
-  __shared__ __align__(16) uint16_t smem[(BPS && !AKC ? 8 : 4) * kStageHalves];
+  __shared__ __align__(16) uint16_t smem[(!AKC ? 8 : 4) * kStageHalves];
   int bi, bj, z;
   grouped_tile(bi, bj, z);
   const int b = z / a.pieces, piece = z - b * a.pieces;
@@ -840,13 +871,13 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The residual M_t - P R^T of one grid block (P R^T on the split MFMA path,
-// k = the subspace rank), staged through LDS into the thread layout of
-// encode_block, then its grid code.
+// The residual M_t - P R^T of one grid block (P R^T on the split MFMA path
+// from pre-split operands, k = the subspace rank), staged through LDS into the
+// thread layout of encode_block, then its grid code.
 // ---------------------------------------------------------------------------
 constexpr int kRL = kTT + 1;  // staged residual row length (floats)
 
-__global__ __launch_bounds__(kGT) void residual_kernel(ResidualArgs a) {
+__global__ __launch_bounds__(kGT, 2) void residual_kernel(ResidualArgs a) {
   __shared__ __align__(16) unsigned char raw[kTT * kRL * 4];
   static_assert(kTT * kRL * 4 >= 4 * kStageHalves * 2, "staging fits under the residual tile");
   __shared__ float cpart[4][kGB];
@@ -875,8 +906,8 @@ __global__ __launch_bounds__(kGT) void residual_kernel(ResidualArgs a) {
   }
   gq_f32x16 acc[2][2];
   zero_acc(acc);
-  tall_loop<true, true>(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
-  // tall_loop ends with a barrier, so the staging area can take the tile
+  presplit_loop(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
+  // the loop ends with a barrier, so the staging area can take the tile
 #pragma unroll
   for (int xx = 0; xx < 2; ++xx)
 #pragma unroll
@@ -990,7 +1021,7 @@ typedef double gq_f64x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kGT) void gram_mfma_kernel(CholArgs a) {
   __shared__ __align__(16) float rows[kGramMfmaRows * kGramMfmaLd];
   const int ch = blockIdx.x, pass = blockIdx.y, b = blockIdx.z;
-  const int k = a.k, nbk = (k + 15) / 16, kw = 16 * nbk, npairs = nbk * (nbk + 1) / 2;
+  const int k = a.k, nbk = (k + 15) / 16, kw = 16 * nbk;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* P = a.P + static_cast<int64_t>(b) * a.sP;
   const int i0 = ch * a.chunk, i1 = min(a.m, i0 + a.chunk);
@@ -1570,20 +1601,11 @@ hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_tall(const TallArgs& a, bool akc, bool bkc, int batch, hipStream_t s) {
+hipError_t launch_tall(const TallArgs& a, bool akc, int batch, hipStream_t s) {
+  if (a.Bh == nullptr || a.Bl == nullptr) return hipErrorInvalidValue;  // B comes pre-split
   const dim3 g((a.N + kTT - 1) / kTT, (a.M + kTT - 1) / kTT, batch * a.pieces);
-  if (a.Bh != nullptr) {  // B pre-split (k contiguous)
-    if (akc) hipLaunchKernelGGL((tall_gemm_kernel<true, true, true>), g, dim3(kGT), 0, s, a);
-    else hipLaunchKernelGGL((tall_gemm_kernel<false, true, true>), g, dim3(kGT), 0, s, a);
-  } else if (akc && bkc) {
-    hipLaunchKernelGGL((tall_gemm_kernel<true, true, false>), g, dim3(kGT), 0, s, a);
-  } else if (akc) {
-    hipLaunchKernelGGL((tall_gemm_kernel<true, false, false>), g, dim3(kGT), 0, s, a);
-  } else if (bkc) {
-    hipLaunchKernelGGL((tall_gemm_kernel<false, true, false>), g, dim3(kGT), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((tall_gemm_kernel<false, false, false>), g, dim3(kGT), 0, s, a);
-  }
+  if (akc) hipLaunchKernelGGL((tall_gemm_kernel<true, true, true>), g, dim3(kGT), 0, s, a);
+  else hipLaunchKernelGGL((tall_gemm_kernel<false, true, true>), g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1591,6 +1613,15 @@ hipError_t launch_split_t(const float* X, int64_t sX, int rows, int k, uint16_t*
                           int batch, hipStream_t s) {
   const dim3 g((k + 63) / 64, (rows + 63) / 64, batch);
   hipLaunchKernelGGL(split_t_kernel, g, dim3(kGT), 0, s, X, sX, rows, k, hi, lo, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const float* X, int64_t sX, int64_t count, uint16_t* hi, uint16_t* lo, int64_t sT, int batch,
+                        hipStream_t s) {
+  int64_t blocks = (count + kGT - 1) / kGT;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(split_kernel, dim3(static_cast<unsigned>(blocks), batch), dim3(kGT), 0, s, X, sX, count, hi, lo,
+                     sT);
   return hipGetLastError();
 }
 
