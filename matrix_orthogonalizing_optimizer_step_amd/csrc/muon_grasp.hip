@@ -405,42 +405,6 @@ __device__ __forceinline__ void store_split(const TileRegs& r, uint16_t* hi, uin
   }
 }
 
-// int8 codes (k contiguous) -> registers (16 bytes per thread, packed) -> LDS
-// as exact bf16.
-struct CodeRegs {
-  uint4 v;
-};
-
-__device__ __forceinline__ void load_i8(const int8_t* base, int64_t s_row, int row0, int k0, int nrows, int K,
-                                        CodeRegs& r) {
-  const int rr = threadIdx.x >> 1, kk = (threadIdx.x & 1) * 16;
-  const int row = row0 + rr, k = k0 + kk;
-  const int8_t* src = base + static_cast<int64_t>(row) * s_row + k;
-  if (row < nrows && k + 15 < K && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-    r.v = *reinterpret_cast<const uint4*>(src);
-  } else {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (row < nrows && k + q < K) w[q >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(src[q])) << (8 * (q & 3));
-    r.v = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-__device__ __forceinline__ void store_i8(const CodeRegs& r, uint16_t* hi) {
-  const int rr = threadIdx.x >> 1, kk = (threadIdx.x & 1) * 16;
-  const uint32_t in[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
-  uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int lo = static_cast<int8_t>((in[q >> 1] >> (16 * (q & 1))) & 0xffu);
-    const int hi8 = static_cast<int8_t>((in[q >> 1] >> (16 * (q & 1) + 8)) & 0xffu);
-    w[q] = f32x2_to_bf16x2(static_cast<float>(lo), static_cast<float>(hi8));
-  }
-  *reinterpret_cast<uint4*>(hi + rr * kTL + kk) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4*>(hi + rr * kTL + kk + 8) = make_uint4(w[4], w[5], w[6], w[7]);
-}
-
 __device__ __forceinline__ gq_f32x16 mfma(const uint4& a, const uint4& b, const gq_f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gq_bf16x8, a), __builtin_bit_cast(gq_bf16x8, b),
                                                  c, 0, 0, 0);
@@ -740,84 +704,164 @@ __global__ __launch_bounds__(kGT) void sum_pieces_kernel(const float* part, int 
 
 // ---------------------------------------------------------------------------
 // M_t = mu (deq(M_res) + deq(P) deq(R)^T) + G for a 32 x 128 tile (a quarter
-// of a grid block: one 32 x 32 MFMA block per wave, so that several waves per
-// SIMD hide the latency of the bandwidth-bound epilogue).  The code product runs group
-// by group (128 k each) as exact integer sums in the fp32 accumulator and is
-// scaled in fp64 by sP sR / 127^2; the 4-bit residual decodes in fp64.  Both
-// scalings multiply by fp64 reciprocals of 7 and 127^2 (within an fp64 ulp of
-// the quotients, far below the fp32 rounding of M_t).
+// of a grid block; wave w computes the 32 x 32 block at columns 32 w ..).
+// The code product runs group by group (128 k each) on the int8 MFMA, exact
+// in its int32 accumulator (a group sums at most 128 products of at most
+// 127^2), and is scaled in fp64 by sP sR / 127^2; the 4-bit residual decodes
+// in fp64.  Both scalings multiply by fp64 reciprocals of 7 and 127^2
+// (within an fp64 ulp of the quotients, far below the fp32 rounding of M_t).
+// Memory latency bounds the kernel, so a block issues the loads of two
+// groups' codes and of its epilogue's operands together before it uses any
+// of them: for k <= 256 one round trip to memory.
 // ---------------------------------------------------------------------------
 constexpr int kRecRows = 32;
+constexpr int kRecLd = kGB + 16;  // LDS row of one group's codes, bytes
+typedef int gq_i32x4 __attribute__((ext_vector_type(4)));
+typedef int gq_i32x16 __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
-  // LDS: the operand staging during the products, then the fp64 product tile
-  __shared__ __align__(16) double tile[kRecRows * kTT];
-  static_assert(sizeof(double) * kRecRows * kTT >= sizeof(uint16_t) * (kRecRows + kTT) * kTL, "staging fits");
+// One group's codes of a tile: 16 bytes of P's rows row0 + t / 8 and four of
+// R's rows col0 + t / 8 + 32 p, at k = 128 g + 16 (t % 8).
+struct RecCodes {
+  uint4 p, r[4];
+};
+
+// 16 code bytes at base + off (base: the tile's first row, a uniform address;
+// off < 2^17): one 16-byte load where the piece is whole and aligned (vec),
+// else byte by byte within the row (rowin) and k < K.
+__device__ __forceinline__ uint4 load_code16(const int8_t* base, uint32_t off, bool vec, bool rowin, int k, int K) {
+  if (vec) return *reinterpret_cast<const uint4*>(base + off);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (rowin && k + q < K) w[q >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(base[off + q])) << (8 * (q & 3));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void load_rec_codes(const int8_t* Pc, const int8_t* Rc, int k, int row0, int col0, int rows,
+                                               int cols, int g, RecCodes& c) {
+  const int t = threadIdx.x, kk = g * kGB + (t & 7) * 16;
+  const int8_t* pb = Pc + static_cast<int64_t>(row0) * k;
+  const int8_t* rb = Rc + static_cast<int64_t>(col0) * k;
+  const bool al = (((reinterpret_cast<uintptr_t>(pb) | reinterpret_cast<uintptr_t>(rb)) & 15u) | (k & 15)) == 0 &&
+                  kk + 15 < k;
+  const uint32_t r8 = static_cast<uint32_t>(t >> 3), uk = static_cast<uint32_t>(k);
+  const bool pin = row0 + (t >> 3) < rows;
+  c.p = load_code16(pb, r8 * uk + kk, al && pin, pin, kk, k);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const bool rin = col0 + (t >> 3) + 32 * p < cols;
+    c.r[p] = load_code16(rb, (r8 + 32 * p) * uk + kk, al && rin, rin, kk, k);
+  }
+}
+
+// 8 consecutive entries of G of dtype GD (0 fp32, 1 bf16, 2 fp16) as raw
+// bits (two 16-byte words for fp32, one for the 16-bit types): loaded early,
+// widened where used.
+template <int GD>
+struct GRaw {
+  uint4 w[GD == 0 ? 2 : 1];
+};
+
+template <int GD>
+__device__ __forceinline__ void load8_raw(const void* p, int64_t e, bool vec, int n, GRaw<GD>& r) {
+  constexpr int kWords = GD == 0 ? 8 : 4;
+  uint32_t w[kWords];
+  if (vec) {
+    if constexpr (GD == 0) {
+      r.w[0] = reinterpret_cast<const uint4*>(static_cast<const float*>(p) + e)[0];
+      r.w[1] = reinterpret_cast<const uint4*>(static_cast<const float*>(p) + e)[1];
+    } else {
+      r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + e);
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < kWords; ++q) w[q] = 0u;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (c < n) {
+      if constexpr (GD == 0) w[c] = static_cast<const uint32_t*>(p)[e + c];
+      else w[c >> 1] |= static_cast<uint32_t>(static_cast<const uint16_t*>(p)[e + c]) << (16 * (c & 1));
+    }
+#pragma unroll
+  for (int q = 0; q < kWords / 4; ++q) r.w[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
+template <int GD>
+__device__ __forceinline__ float raw_at(const GRaw<GD>& r, int c) {
+  const uint4 v = r.w[GD == 0 ? c >> 2 : 0];
+  const int q = GD == 0 ? c & 3 : c >> 1;
+  const uint32_t x = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+  if constexpr (GD == 0) return __uint_as_float(x);
+  const uint16_t h = static_cast<uint16_t>(x >> (16 * (c & 1)));
+  return GD == 1 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+__device__ __forceinline__ void stage_rec_codes(const RecCodes& c, uint8_t* Ab, uint8_t* Bb) {
+  const int t = threadIdx.x, seg = (t & 7) * 16;
+  *reinterpret_cast<uint4*>(Ab + (t >> 3) * kRecLd + seg) = c.p;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) *reinterpret_cast<uint4*>(Bb + ((t >> 3) + 32 * p) * kRecLd + seg) = c.r[p];
+}
+
+// Add group g's code product (staged in Ab, Bb), scaled, to pr.
+__device__ __forceinline__ void recon_group(const uint8_t* Ab, const uint8_t* Bb, int g, int k, int ng, int col,
+                                            int cols, const float* Rs, const float* psc, double (&pr)[16]) {
+  const int lane = threadIdx.x & 63, wc = 32 * (threadIdx.x >> 6);
+  const int steps = (min(kGB, k - g * kGB) + 31) / 32;
+  gq_i32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if (st < steps) {
+      const int kk = 32 * st + 16 * (lane >> 5);
+      const gq_i32x4 av = *reinterpret_cast<const gq_i32x4*>(Ab + (lane & 31) * kRecLd + kk);
+      const gq_i32x4 bv = *reinterpret_cast<const gq_i32x4*>(Bb + (wc + (lane & 31)) * kRecLd + kk);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc, 0, 0, 0);
+    }
+  }
+  constexpr double kInvL8sq = 1.0 / 16129.0;
+  const double sR = col < cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const double sP = psc[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * ng + g];
+    pr[v] = fma(static_cast<double>(acc[v]), sP * sR, pr[v]);
+  }
+}
+
+template <int GD>
+__global__ __launch_bounds__(kGT, GD == 0 ? 2 : 3) void recon_kernel(ReconArgs a) {
+  // LDS: two groups' codes during the product, then the fp64 product tile
+  constexpr int kStage = (kRecRows + kTT) * kRecLd;
+  constexpr int kLds = 2 * kStage > 8 * kRecRows * kTT ? 2 * kStage : 8 * kRecRows * kTT;
+  __shared__ __align__(16) unsigned char lds[kLds];
   __shared__ float psc[kRecRows * (kMaxRankK / kGB)];  // P's group scales for the tile's rows
-  uint16_t* smem = reinterpret_cast<uint16_t*>(tile);
+  static_assert(kRecRows * (kMaxRankK / kGB) <= kGT, "one scale per thread");
+  double* tile = reinterpret_cast<double*>(lds);
+  uint8_t* A0 = lds;
+  uint8_t* B0 = A0 + kRecRows * kRecLd;
+  uint8_t* A1 = lds + kStage;
+  uint8_t* B1 = A1 + kRecRows * kRecLd;
   const int b = blockIdx.z, bj = blockIdx.x;
   const int row0 = blockIdx.y * kRecRows, col0 = bj * kTT, bi = row0 / kGB;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wc = 32 * w;  // wave w: the 32 x 32 block at columns wc..
+  const int t = threadIdx.x, lane = t & 63, wc = 32 * (t >> 6);
   const int k = a.k, ng = (k + kGB - 1) / kGB;
   const int8_t* Pc = static_cast<const int8_t*>(a.P_codes[b]);
   const int8_t* Rc = static_cast<const int8_t*>(a.R_codes[b]);
   const float* Ps = static_cast<const float*>(a.P_scales[b]);
   const float* Rs = static_cast<const float*>(a.R_scales[b]);
-  uint16_t *Ah = smem, *Bh = smem + kRecRows * kTL;
-  const int arows = min(a.rows, row0 + kRecRows);
-  constexpr double kInvL8sq = 1.0 / 16129.0, kInv7 = 1.0 / 7.0;
-  // P's scales for the tile's rows, read from LDS by the fold (the k-loop's
-  // barriers order these stores before the first read)
-  for (int e = threadIdx.x; e < kRecRows * ng; e += kGT) {
-    const int r = e / ng;
-    psc[e] = row0 + r < a.rows ? Ps[static_cast<int64_t>(row0) * ng + e] : 0.0f;
-  }
-  double pr[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) pr[v] = 0.0;
-  for (int g = 0; g < ng; ++g) {
-    const int kbeg = g * kGB, kend = min(k, kbeg + kGB);
-    gq_f32x16 acc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    CodeRegs ra, rb;
-    load_i8(Pc, k, row0, kbeg, arows, kend, ra);
-    load_i8(Rc, k, col0, kbeg, a.cols, kend, rb);
-    for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-      if (threadIdx.x < 2 * kRecRows) store_i8(ra, Ah);
-      store_i8(rb, Bh);
-      __syncthreads();
-      if (k0 + kTK < kend) {
-        load_i8(Pc, k, row0, k0 + kTK, arows, kend, ra);
-        load_i8(Rc, k, col0, k0 + kTK, a.cols, kend, rb);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kk = 16 * s + 8 * (lane >> 5);
-        const uint4 av = *reinterpret_cast<const uint4*>(Ah + (lane & 31) * kTL + kk);
-        const uint4 bv = *reinterpret_cast<const uint4*>(Bh + (wc + (lane & 31)) * kTL + kk);
-        acc = mfma(av, bv, acc);
-      }
-      __syncthreads();
-    }
-    const int col = col0 + wc + (lane & 31);
-    const double sR = col < a.cols ? static_cast<double>(Rs[static_cast<int64_t>(col) * ng + g]) * kInvL8sq : 0.0;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const double sP = psc[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * ng + g];
-      pr[v] = fma(static_cast<double>(acc[v]), sP * sR, pr[v]);
-    }
-  }
-  // the product tile into LDS (the last loop iteration ended with a barrier)
-#pragma unroll
-  for (int v = 0; v < 16; ++v) tile[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kTT + wc + (lane & 31)] = pr[v];
-  __syncthreads();
-  // epilogue in the grid-code layout: thread t holds columns col0 + 8 (t % 16) .. + 7
-  // of rows row0 + t / 16 + 16 s (s < 2), with vector loads and stores where aligned
-  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  // the first two groups' codes
+  RecCodes rc0, rc1;
+  load_rec_codes(Pc, Rc, k, row0, col0, a.rows, a.cols, 0, rc0);
+  if (ng > 1) load_rec_codes(Pc, Rc, k, row0, col0, a.rows, a.cols, 1, rc1);
+  // P's scales for the tile's rows (stored to LDS below, read after a barrier)
+  const float pscale = t < kRecRows * ng && row0 + t / ng < a.rows ? Ps[static_cast<int64_t>(row0) * ng + t] : 0.0f;
+  // the epilogue's operands, in the grid-code layout: thread t holds columns
+  // col0 + 8 (t % 16) .. + 7 of rows row0 + t / 16 + 16 s (s < 2), with
+  // vector loads and stores where aligned
+  const int cg = t & 15, rs = t >> 4;
   const int j0 = col0 + 8 * cg, n = min(8, a.cols - j0);
-  if (n <= 0) return;  // no barrier follows
   const uint8_t* codes = static_cast<const uint8_t*>(a.res_codes[b]);
   const float* sr = static_cast<const float*>(a.res_sr[b]);
   const float* sc = static_cast<const float*>(a.res_sc[b]);
@@ -830,19 +874,19 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
                     reinterpret_cast<uintptr_t>(sc)) & 15u);
   if (Y != nullptr) mis |= reinterpret_cast<uintptr_t>(Y) & 15u;
   const bool vec = (a.cols & 7) == 0 && mis == 0;
-  float cs[8];
-  load8_f32(sc, static_cast<int64_t>(bi) * a.cols + j0, 0, vec, n, cs);
-  // both rows' loads before any store (the stores of M_t could alias G for
-  // the compiler, which would hold the second row's loads behind them)
   constexpr int kRecPer = kRecRows / 16;
-  float rsc[kRecPer], g[kRecPer][8];
+  float cs[8], rsc[kRecPer];
+  GRaw<GD> gv[kRecPer];
   uint32_t word[kRecPer];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cs[c] = 0.0f;
+  if (n > 0) load8_f32(sc, static_cast<int64_t>(bi) * a.cols + j0, 0, vec, n, cs);
 #pragma unroll
   for (int s = 0; s < kRecPer; ++s) {
     const int i = row0 + rs + 16 * s;
     rsc[s] = 0.0f;
     word[s] = 0;
-    if (i < a.rows) {
+    if (i < a.rows && n > 0) {
       rsc[s] = sr[static_cast<int64_t>(i) * nbc + bj];
       const uint8_t* src = codes + static_cast<int64_t>(i) * cb + (j0 >> 1);
       if (vec) {
@@ -850,9 +894,33 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
       } else {
         for (int q = 0; 2 * q < n; ++q) word[s] |= static_cast<uint32_t>(src[q]) << (8 * q);
       }
-      load8_f32(a.G[b], static_cast<int64_t>(i) * a.cols + j0, a.g_dtype, vec, n, g[s]);
+      load8_raw<GD>(a.G[b], static_cast<int64_t>(i) * a.cols + j0, vec, n, gv[s]);
     }
   }
+  psc[t] = pscale;
+  double pr[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) pr[v] = 0.0;
+  const int col = col0 + wc + (lane & 31);
+  // groups in pairs: both staged, one barrier, both products
+  for (int g = 0; g < ng; g += 2) {
+    if (g > 0) {
+      load_rec_codes(Pc, Rc, k, row0, col0, a.rows, a.cols, g, rc0);
+      if (g + 1 < ng) load_rec_codes(Pc, Rc, k, row0, col0, a.rows, a.cols, g + 1, rc1);
+    }
+    stage_rec_codes(rc0, A0, B0);
+    if (g + 1 < ng) stage_rec_codes(rc1, A1, B1);
+    __syncthreads();
+    recon_group(A0, B0, g, k, ng, col, a.cols, Rs, psc, pr);
+    if (g + 1 < ng) recon_group(A1, B1, g + 1, k, ng, col, a.cols, Rs, psc, pr);
+    __syncthreads();
+  }
+  // the product tile into LDS (after the last pair's barrier)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) tile[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * kTT + wc + (lane & 31)] = pr[v];
+  __syncthreads();
+  if (n <= 0) return;  // no barrier follows
+  constexpr double kInv7 = 1.0 / 7.0;
 #pragma unroll
   for (int s = 0; s < kRecPer; ++s) {
     const int r = rs + 16 * s, i = row0 + r;
@@ -863,7 +931,7 @@ __global__ __launch_bounds__(kGT) void recon_kernel(ReconArgs a) {
     for (int c = 0; c < 8; ++c) {
       const int q = sext4((word[s] >> (4 * c)) & 15u);
       const double res = static_cast<double>(q) * static_cast<double>(nan_min(rsc[s], cs[c])) * kInv7;
-      m[c] = static_cast<float>(fma(a.mu, res + tile[r * kTT + 8 * cg + c], static_cast<double>(g[s][c])));
+      m[c] = static_cast<float>(fma(a.mu, res + tile[r * kTT + 8 * cg + c], static_cast<double>(raw_at<GD>(gv[s], c))));
     }
     store8_f32(mt + e, vec, n, m);
     if (Y != nullptr) store8_f32(Y + e, vec, n, m);
@@ -1635,7 +1703,9 @@ hipError_t launch_sum_pieces(const float* part, int pieces, int64_t count, float
 
 hipError_t launch_recon(const ReconArgs& a, int batch, hipStream_t s) {
   const dim3 g((a.cols + kTT - 1) / kTT, (a.rows + kRecRows - 1) / kRecRows, batch);
-  hipLaunchKernelGGL(recon_kernel, g, dim3(kGT), 0, s, a);
+  if (a.g_dtype == 0) hipLaunchKernelGGL(recon_kernel<0>, g, dim3(kGT), 0, s, a);
+  else if (a.g_dtype == 1) hipLaunchKernelGGL(recon_kernel<1>, g, dim3(kGT), 0, s, a);
+  else hipLaunchKernelGGL(recon_kernel<2>, g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
