@@ -680,7 +680,7 @@ void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
 // Workspace after the Newton-Schulz part: M_t and its pointer table, then
 // (k > 0) the power-iteration buffers.
 struct GraspLayout {
-  size_t ptrs, mt, q, qs, colpart, colinv, ppart, ptil, spart, S, dead, P, ps, rpart, R, total;
+  size_t ptrs, mt, q, qs, colpart, colinv, ppart, ptil, spart, S, dead, dinv, P, ps, rpart, R, total;
   int nch_n, nch_m, gchunk;
 };
 
@@ -710,6 +710,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->spart = take(B * g->nch_m * kk * kk * 8);
     g->S = take(B * kk * kk * 8);
     g->dead = take(B * kk * 4);
+    g->dinv = take(B * nblk(k, 64) * 64 * 64 * 8);  // U's 64 x 64 diagonal blocks inverted
     g->P = take(B * r * kk * 4);
     g->ps = take(B * r * kk * 4);  // P^T split into bf16 hi and lo planes, later P
     grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &pcs, &chunk);
@@ -852,12 +853,13 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.S = reinterpret_cast<double*>(ws + lay.S);
     a.dead = reinterpret_cast<int*>(ws + lay.dead);
     a.Pout = P;
+    a.dinv = reinterpret_cast<double*>(ws + lay.dinv);
     MUON_LAUNCH(traced(s, "gram64_kernel+gram_sum", "grasp_gram", rows * kd * kd * batch, rows * kd * 4.0 * batch,
                        [&] { return launch_gram(a, batch, s); }));
     const bool reg = k <= kRegRankK;
     MUON_LAUNCH(traced(s, reg ? "chol_reg_kernel" : "chol_panel_kernel", "grasp_cholesky", kd * kd * kd / 3.0 * batch,
                        kd * kd * 16.0 * batch, [&] { return launch_chol(a, batch, s); }));
-    MUON_LAUNCH(traced(s, "row_solve_kernel", "grasp_row_solve", rows * kd * kd * batch, rows * kd * 8.0 * batch,
+    MUON_LAUNCH(traced(s, "row_solve_mfma_kernel", "grasp_row_solve", rows * kd * kd * batch, rows * kd * 8.0 * batch,
                        [&] { return launch_row_solve(a, batch, s); }));
     Group8Args q{};
     q.rows = rows;

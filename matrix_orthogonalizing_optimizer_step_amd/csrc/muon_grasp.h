@@ -89,6 +89,7 @@ struct CholArgs {
   int* dead;                                    // batch x k: 1 for a dependent or zero column
   float* Pout;                                  // P (m x k, same strides as P~)
   int panel;                                    // Cholesky panel rows (set by the launcher)
+  double* dinv;                                 // batch x ceil(k / 64) x 64 x 64: U's diagonal blocks inverted
 };
 
 // Largest subspace rank of the register-resident Cholesky; larger ranks take

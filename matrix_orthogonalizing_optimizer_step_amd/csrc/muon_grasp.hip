@@ -1311,83 +1311,156 @@ __global__ __launch_bounds__(kGT) void chol_panel_kernel(CholArgs a) {
   }
 }
 
-// P = P~ U^{-1} by forward substitution along each row (P U = P~).  A block
-// of 4 waves takes 4 RPW rows; column block jb (64 columns, lane l owning
-// column j = 64 jb + l) first takes the finished columns of earlier blocks
-// (their fp64 values in LDS times U's rows, staged through LDS 64 x 64 at a
-// time), then stages U's 64 x 64 diagonal block and finishes its columns one
-// at a time: lane q scales its value by its own 1 / U_qq (formed once per
-// block, zero for a dead column, so dead columns are zero) and the result is
-// broadcast by readlane.  fp64 arithmetic, fp32 result.
-template <int RPW>
-__global__ __launch_bounds__(kGT) void row_solve_kernel(CholArgs a) {
-  extern __shared__ double lds[];  // U block 64 x 64 | rows: 4 waves x RPW x k
-  double* ub = lds;
-  const int b = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int k = a.k;
-  double* prow = lds + 64 * 64 + static_cast<int64_t>(w) * RPW * k;
-  const double* U = a.S + static_cast<int64_t>(b) * k * k;
-  const int* dead = a.dead + static_cast<int64_t>(b) * k;
-  const int r0 = (blockIdx.x * 4 + w) * RPW;
+// P = P~ U^{-1} as a blocked solve on the fp64 MFMA (P U = P~, column
+// blocks of 64).  First U's 64 x 64 diagonal blocks are inverted (Dinv, with
+// the columns of dead rows zero, so dead columns of P are zero as in the
+// substitution: a dead row of U is e_p and feeds no later column).  Then a
+// wave takes 16 rows and, block by block, forms A = P~[:, blk] - X[:, :j0]
+// U[:j0, blk] and X[:, blk] = A Dinv_blk; its X rows stay in LDS as the A
+// operand of later blocks.  fp64 arithmetic, fp32 result.
+typedef double gq_f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kSolveBlk = 64;
+
+// Row r (lane r) of Dinv_jb by substitution: x = e_r, then for c = 0..nb-1
+// x_c *= 1 / U_cc (zero for a dead c) and x_c' -= x_c U_cc' for c' > c.  The
+// block is staged in LDS first (a row per load instruction across the lanes)
+// and the reciprocals are formed in parallel, so the chain from one c to the
+// next is a multiply and an FMA.  Rows and columns past the matrix come out
+// zero.
+__global__ __launch_bounds__(kSolveBlk) void diag_inv_kernel(CholArgs a) {
+  __shared__ double ub[kSolveBlk * kSolveBlk];
+  __shared__ double rdg[kSolveBlk];
+  const int jb = blockIdx.x, b = blockIdx.y, r = threadIdx.x;
+  const int k = a.k, j0 = jb * kSolveBlk, nb = min(kSolveBlk, k - j0), nbk = (k + kSolveBlk - 1) / kSolveBlk;
+  const double* U = a.S + static_cast<int64_t>(b) * k * k + static_cast<int64_t>(j0) * k + j0;
+  {
+    double v[kSolveBlk];
+#pragma unroll
+    for (int c = 0; c < kSolveBlk; ++c) {
+      const bool ok = c < nb && r < nb;
+      v[c] = U[ok ? static_cast<int64_t>(c) * k + r : 0];
+      v[c] = ok ? v[c] : 0.0;
+    }
+    const bool live = r < nb && a.dead[static_cast<int64_t>(b) * k + j0 + (r < nb ? r : 0)] == 0;
+    const double d = U[r < nb ? static_cast<int64_t>(r) * k + r : 0];
+#pragma unroll
+    for (int c = 0; c < kSolveBlk; ++c) ub[c * kSolveBlk + r] = v[c];
+    rdg[r] = live ? 1.0 / d : 0.0;
+  }
+  __syncthreads();
+  double x[kSolveBlk];
+#pragma unroll
+  for (int c = 0; c < kSolveBlk; ++c) x[c] = c == r ? 1.0 : 0.0;
+#pragma unroll
+  for (int c = 0; c < kSolveBlk; ++c) {
+    x[c] *= rdg[c];
+#pragma unroll
+    for (int c2 = c + 1; c2 < kSolveBlk; ++c2) x[c2] = fma(-x[c], ub[c * kSolveBlk + c2], x[c2]);
+  }
+  double* out = a.dinv + ((static_cast<int64_t>(b) * nbk + jb) * kSolveBlk + r) * kSolveBlk;
+#pragma unroll
+  for (int c = 0; c < kSolveBlk; ++c) out[c] = x[c];
+}
+
+__global__ __launch_bounds__(64) void row_solve_mfma_kernel(CholArgs a) {
+  extern __shared__ double xs[];  // this wave's 16 rows of X, row length ld
+  const int b = blockIdx.y, lane = threadIdx.x;
+  const int k = a.k, nbk = (k + kSolveBlk - 1) / kSolveBlk, ld = kSolveBlk * nbk + 1;
+  const int r0 = blockIdx.x * 16;
+  const int dr = lane >> 4, dc = lane & 15;  // D and B layouts: row (or k) dr (+ 4 v), column dc
+  const int ar = lane & 15, ak = lane >> 4;  // A layout: row ar, k ak
   const float* Pt = a.P + static_cast<int64_t>(b) * a.sP;
   float* Po = a.Pout + static_cast<int64_t>(b) * a.sP;
-  for (int j0 = 0; j0 < k; j0 += 64) {
-    const int j = j0 + lane, nb = min(64, k - j0);
-    const bool in = j < k;
-    const bool dj = in ? dead[j] != 0 : true;
-    double acc[RPW];
+  const double* U = a.S + static_cast<int64_t>(b) * k * k;
+  const double* Dv = a.dinv + static_cast<int64_t>(b) * nbk * kSolveBlk * kSolveBlk;
+  for (int jb = 0; jb < nbk; ++jb) {
+    const int j0 = jb * kSolveBlk;
+    // P~'s block: every load issued (from a clamped address) before any is used
+    float pv[4][4];
 #pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const int r = r0 + q;
-      acc[q] = in && r < a.m ? static_cast<double>(Pt[static_cast<int64_t>(r) * k + j]) : 0.0;
-    }
-    for (int l0 = 0; l0 < j0; l0 += 64) {
-      // the block's 16 values per thread loaded together, then stored
-      double v[64 * 64 / kGT];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int q = 0; q < 64 * 64 / kGT; ++q) {
-        const int e = threadIdx.x + q * kGT, rr = e >> 6, cc = e & 63;
-        v[q] = j0 + cc < k ? U[static_cast<int64_t>(l0 + rr) * k + j0 + cc] : 0.0;
+      for (int v = 0; v < 4; ++v) {
+        const int row = r0 + dr + 4 * v, col = j0 + 16 * t + dc;
+        const bool ok = row < a.m && col < k;
+        pv[t][v] = Pt[ok ? static_cast<int64_t>(row) * k + col : 0];
+        pv[t][v] = ok ? pv[t][v] : 0.0f;
       }
-      __syncthreads();  // the previous U block is no longer read
+    gq_f64x4 acc[4];
 #pragma unroll
-      for (int q = 0; q < 64 * 64 / kGT; ++q) ub[threadIdx.x + q * kGT] = v[q];
-      __syncthreads();
-#pragma unroll 8
-      for (int l = 0; l < 64; ++l) {
-        const double u = ub[l * 64 + lane];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int q = 0; q < RPW; ++q) acc[q] = fma(-prow[q * k + l0 + l], u, acc[q]);
+      for (int v = 0; v < 4; ++v) acc[t][v] = static_cast<double>(pv[t][v]);
+    // A = P~[:, blk] - X[:, :j0] U[:j0, blk], four k-steps per trip.  U's
+    // entries for the next trip are loaded before this trip's MFMAs; loads
+    // and MFMAs are unconditional (entries outside U[:j0, :k] read as zero
+    // from a clamped address), so nothing branches around them.
+    double bn[4][4];
+    auto load_u = [&](int s0, double (&bv)[4][4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = s0 + 4 * q + dr, col = j0 + 16 * t + dc;
+          const bool ok = row < j0 && col < k;
+          bv[q][t] = U[ok ? static_cast<int64_t>(row) * k + col : 0];
+          bv[q][t] = ok ? bv[q][t] : 0.0;
+        }
+    };
+    auto trip = [&](int s0, const double (&bv)[4][4]) {
+      double av[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[q] = -xs[ar * ld + s0 + 4 * q + ak];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[q], bv[q][t], acc[t], 0, 0, 0);
+    };
+    // two register sets in turn (j0 is a multiple of 64: trips come in fours)
+    double b1[4][4];
+    load_u(0, bn);
+    for (int s0 = 0; s0 < j0; s0 += 32) {
+      load_u(s0 + 16, b1);
+      trip(s0, bn);
+      load_u(s0 + 32, bn);
+      trip(s0 + 16, b1);
+    }
+    // A into LDS (the block's columns of X), then X[:, blk] = A Dinv (upper
+    // triangular: tile t takes k < 16 (t + 1))
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xs[(dr + 4 * v) * ld + j0 + 16 * t + dc] = acc[t][v];
+    gq_f64x4 x[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[t][v] = 0.0;
+    const double* D = Dv + static_cast<int64_t>(jb) * kSolveBlk * kSolveBlk;
+#pragma unroll
+    for (int s0 = 0; s0 < kSolveBlk; s0 += 16) {
+      double av[4], bv[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = xs[ar * ld + j0 + s0 + 4 * q + ak];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bv[q][t] = D[(s0 + 4 * q + dr) * kSolveBlk + 16 * t + dc];
       }
-    }
-    {
-      double v[64 * 64 / kGT];
 #pragma unroll
-      for (int q = 0; q < 64 * 64 / kGT; ++q) {
-        const int e = threadIdx.x + q * kGT, rr = e >> 6, cc = e & 63;
-        v[q] = (rr < nb && cc < nb && cc >= rr) ? U[static_cast<int64_t>(j0 + rr) * k + j0 + cc] : 0.0;
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (s0 < 16 * (t + 1)) x[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[q], bv[q][t], x[t], 0, 0, 0);
+    }
+    // X into LDS (over A: this wave's reads of A above come first) and out
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = r0 + dr + 4 * v, col = j0 + 16 * t + dc;
+        xs[(dr + 4 * v) * ld + j0 + 16 * t + dc] = x[t][v];
+        if (row < a.m && col < k) Po[static_cast<int64_t>(row) * k + col] = static_cast<float>(x[t][v]);
       }
-      __syncthreads();  // the previous U block is no longer read
-#pragma unroll
-      for (int q = 0; q < 64 * 64 / kGT; ++q) ub[threadIdx.x + q * kGT] = v[q];
-    }
-    __syncthreads();
-    const double rdiag = (lane < nb && !dj) ? 1.0 / ub[lane * 64 + lane] : 0.0;
-    for (int q = 0; q < nb; ++q) {
-      const int l = j0 + q;
-      const double u = ub[q * 64 + lane];
-#pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        const double pl = readlane_f64(dj ? 0.0 : acc[rr] * rdiag, q);
-        if (lane > q) acc[rr] = fma(-pl, u, acc[rr]);
-        if (lane == q) prow[rr * k + l] = pl;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const int r = r0 + q;
-      if (in && r < a.m) Po[static_cast<int64_t>(r) * k + j] = static_cast<float>(prow[q * k + j]);
-    }
   }
 }
 
@@ -1749,12 +1822,12 @@ hipError_t launch_chol(const CholArgs& a, int batch, hipStream_t s) {
 }
 
 hipError_t launch_row_solve(const CholArgs& a, int batch, hipStream_t s) {
-  // rows per wave: 4 while the rows' fp64 values fit beside the U block (64 KB)
-  const int rpw = a.k <= 224 ? 4 : 1;
-  const size_t lds = (64 * 64 + static_cast<size_t>(4) * rpw * a.k) * sizeof(double);  // <= 64 KB
-  const dim3 grid((a.m + 4 * rpw - 1) / (4 * rpw), batch);
-  if (rpw == 4) hipLaunchKernelGGL(row_solve_kernel<4>, grid, dim3(kGT), lds, s, a);
-  else hipLaunchKernelGGL(row_solve_kernel<1>, grid, dim3(kGT), lds, s, a);
+  const int nbk = (a.k + kSolveBlk - 1) / kSolveBlk;
+  hipLaunchKernelGGL(diag_inv_kernel, dim3(nbk, batch), dim3(kSolveBlk), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = static_cast<size_t>(16) * (kSolveBlk * nbk + 1) * sizeof(double);  // <= 131 KB (k <= 1024)
+  hipLaunchKernelGGL(row_solve_mfma_kernel, dim3((a.m + 15) / 16, batch), dim3(64), lds, s, a);
   return hipGetLastError();
 }
 

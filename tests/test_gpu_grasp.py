@@ -217,10 +217,12 @@ def test_grasp_step_without_subspace_bitexact(rows, cols):
     (256, 4096, 16, "gram"),      # M_t Q split along k
     (4096, 256, 16, "standard"),  # M_t^T P split along k
     (200, 150, 1, "standard"),
-    (600, 700, 300, "gram"),      # k > 256: the panel Cholesky (16-row panels), one row per wave in the solve, 3 groups
+    (600, 700, 300, "gram"),      # k > 256: the panel Cholesky (16-row panels), 3 groups
     (300, 520, 256, "standard"),  # the largest k of the register-resident Cholesky: every slot block in use
     (400, 300, 255, "gram"),      # k odd, next to that limit, iterated transposed
     (270, 300, 257, "standard"),  # the smallest k of the panel Cholesky
+    (700, 1100, 520, "standard"), # the blocked solve's X rows beyond 64 KB of LDS, 5 groups
+    (1100, 1030, 1024, "gram"),   # the largest k, iterated transposed
     (257, 1, 1, "standard"),      # a column: k = min(rows, cols) = 1
     (1, 300, 1, "gram"),          # a row
 ])
