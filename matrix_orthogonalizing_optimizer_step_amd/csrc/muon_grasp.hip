@@ -940,27 +940,33 @@ __global__ __launch_bounds__(kGT, GD == 0 ? 2 : 3) void recon_kernel(ReconArgs a
 
 // ---------------------------------------------------------------------------
 // The residual M_t - P R^T of one grid block (P R^T on the split MFMA path
-// from pre-split operands, k = the subspace rank), staged through LDS into the
-// thread layout of encode_block, then its grid code.
+// from pre-split operands, k = the subspace rank), then its grid code.  The
+// product tile reaches the thread layout of encode_block through LDS one half
+// (64 rows) at a time, in the space of the operand staging, so a block holds
+// 42 KB of LDS and, at 168 registers, three blocks share a compute unit; M_t
+// is loaded after the product, its latency covered by the other blocks.
 // ---------------------------------------------------------------------------
 constexpr int kRL = kTT + 1;  // staged residual row length (floats)
 
-__global__ __launch_bounds__(kGT, 2) void residual_kernel(ResidualArgs a) {
-  __shared__ __align__(16) unsigned char raw[kTT * kRL * 4];
-  static_assert(kTT * kRL * 4 >= 4 * kStageHalves * 2, "staging fits under the residual tile");
+__global__ __launch_bounds__(kGT, 3) void residual_kernel(ResidualArgs a) {
+  __shared__ __align__(16) unsigned char raw[4 * kStageHalves * 2];
+  static_assert(4 * kStageHalves * 2 >= (kTT / 2) * kRL * 4, "a half tile fits in the staging area");
   __shared__ float cpart[4][kGB];
   uint16_t* smem = reinterpret_cast<uint16_t*>(raw);
   float* tile = reinterpret_cast<float*>(raw);
   int bi, bj, b;
   grouped_tile(bi, bj, b);
   const int row0 = bi * kTT, col0 = bj * kTT;
-  const int t = threadIdx.x, cg = t & 15, rs = t >> 4;
+  const int t = threadIdx.x, w = t >> 6, cg = t & 15, rs = t >> 4;
   const int rows = a.rows, cols = a.cols;
   const int j0 = col0 + 8 * cg, n = min(8, cols - j0);
   const float* mt = a.mt + static_cast<int64_t>(b) * a.s_mt;
   const bool vec = (cols & 7) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.codes[b]) & 3u) | (reinterpret_cast<uintptr_t>(mt) & 15u)) == 0;
-  // this thread's M_t values first: their loads are in flight during the product
+  gq_f32x16 acc[2][2];
+  zero_acc(acc);
+  presplit_loop(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
+  // this thread's M_t values (rows row0 + t / 16 + 16 s)
   float x[8][8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -972,24 +978,27 @@ __global__ __launch_bounds__(kGT, 2) void residual_kernel(ResidualArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[s][c] = v[c];
   }
-  gq_f32x16 acc[2][2];
-  zero_acc(acc);
-  presplit_loop(a.prod, b, row0, col0, 0, a.prod.K, smem, acc);
-  // the loop ends with a barrier, so the staging area can take the tile
+  // the product, half h (rows 64 h ..) from waves 2 h and 2 h + 1; the loop
+  // ended with a barrier, so the staging area can take it
 #pragma unroll
-  for (int xx = 0; xx < 2; ++xx)
+  for (int h = 0; h < 2; ++h) {
+    if ((w >> 1) == h)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+      for (int xx = 0; xx < 2; ++xx)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tile[acc_row(xx, v) * kRL + acc_col(y)] = acc[xx][y][v];
-  __syncthreads();
+        for (int y = 0; y < 2; ++y)
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int r = rs + 16 * s, i = row0 + r;
-    if (i < rows)
+          for (int v = 0; v < 16; ++v) tile[(acc_row(xx, v) - 64 * h) * kRL + acc_col(y)] = acc[xx][y][v];
+    __syncthreads();
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (c < n) x[s][c] -= tile[r * kRL + 8 * cg + c];
+    for (int s = 4 * h; s < 4 * h + 4; ++s) {
+      const int r = rs + 16 * s, i = row0 + r;
+      if (i < rows)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c < n) x[s][c] -= tile[(r - 64 * h) * kRL + 8 * cg + c];
+    }
+    __syncthreads();
   }
   encode_block(x, static_cast<uint8_t*>(a.codes[b]), static_cast<float*>(a.sr[b]), static_cast<float*>(a.sc[b]), rows,
                cols, bi, bj, vec, cpart);
