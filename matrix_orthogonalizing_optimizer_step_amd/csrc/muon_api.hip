@@ -680,7 +680,7 @@ void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
 // Workspace after the Newton-Schulz part: M_t and its pointer table, then
 // (k > 0) the power-iteration buffers.
 struct GraspLayout {
-  size_t ptrs, mt, q, qs, colpart, colinv, ppart, ptil, spart, S, dead, dinv, P, ps, rpart, R, total;
+  size_t ptrs, mt, qs, colpart, colinv, ppart, ptil, spart, S, dead, dinv, P, ps, rpart, R, total;
   int nch_n, nch_m, gchunk;
 };
 
@@ -699,8 +699,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->nch_n = nblk(cols, kUnitRows);
     g->gchunk = gram_chunk_rows(rows, batch);
     g->nch_m = nblk(rows, g->gchunk);
-    g->q = take(B * c * kk * 4);
-    g->qs = take(B * c * kk * 4);  // Q^T split into bf16 hi and lo planes, later R
+    g->qs = take(B * c * kk * 4);  // R's codes transposed (bf16), later R split into bf16 hi and lo planes
     g->colpart = take(B * g->nch_n * kk * 8);
     g->colinv = take(B * kk * 8);
     int pcs = 1, chunk = 0;
@@ -791,8 +790,8 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     if (!ok) return MUON_ERR_HIP;
     s = s2;
   }
-  // 2. Q = unit columns of deq(R_{t-1})
-  float* Q = reinterpret_cast<float*>(ws + lay.q);
+  // 2. Q = unit columns of deq(R_{t-1}), kept as R's codes and scales and the
+  // column norms: the norms, and the codes transposed to bf16 (exact)
   {
     UnitArgs a{};
     a.n = cols;
@@ -802,39 +801,33 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.scales = st->R_scales;
     a.part = reinterpret_cast<double*>(ws + lay.colpart);
     a.inv = reinterpret_cast<double*>(ws + lay.colinv);
-    a.Q = Q;
-    a.sQ = static_cast<int64_t>(cols) * k;
-    MUON_LAUNCH(traced(s, "unit_columns_kernel", "grasp_Q", 0.0, cols * kd * batch * 6.0,
-                       [&] { return launch_unit_columns(a, batch, s); }));
+    MUON_LAUNCH(traced(s, "colsq_kernel+colinv_kernel", "grasp_Q", 0.0, cols * kd * batch * 1.25,
+                       [&] { return launch_col_norms(a, batch, s); }));
   }
-  // Q^T as bf16 hi / lo planes, split once for all row tiles of M_t Q
   uint16_t* qs = reinterpret_cast<uint16_t*>(ws + lay.qs);
   const int64_t s_qs = static_cast<int64_t>(cols) * k * 2;
-  MUON_LAUNCH(traced(s, "split_t_kernel", "grasp_Q_split", 0.0, cols * kd * batch * 8.0, [&] {
-    return launch_split_t(Q, static_cast<int64_t>(cols) * k, cols, k, qs, qs + static_cast<int64_t>(cols) * k, s_qs,
-                          batch, s);
+  MUON_LAUNCH(traced(s, "codes_t_kernel", "grasp_Q_split", 0.0, cols * kd * batch * 3.0, [&] {
+    return launch_codes_t(st->R_codes, cols, k, qs, s_qs, batch, s);
   }));
   // 3. P~ = M_t Q (split along k when the tiles alone do not fill the device)
   float* ptil = reinterpret_cast<float*>(ws + lay.ptil);
   {
-    TallArgs a{};
+    MQArgs a{};
     a.M = rows;
     a.N = k;
     a.K = cols;
     a.A = mt;
     a.sA = s_mt;
-    a.a_row = cols;
-    a.a_k = 1;
-    a.Bh = qs;
-    a.Bl = qs + static_cast<int64_t>(cols) * k;
-    a.sB = s_qs;
-    a.b_row = cols;
+    a.Ct = qs;
+    a.sCt = s_qs;
+    a.rs = st->R_scales;
+    a.inv = reinterpret_cast<double*>(ws + lay.colinv);
     grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(rows) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.ppart) : ptil;
-    MUON_LAUNCH(traced(s, "tall_gemm_kernel<1, 1, 1>", "grasp_MQ", 2.0 * elems * kd,
-                       elems * 4.0 + (cols + rows * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, true, batch, s); }));
+    MUON_LAUNCH(traced(s, "mq_kernel", "grasp_MQ", 2.0 * elems * kd,
+                       elems * 4.0 + (cols * 2.0 + rows * 4.0 * a.pieces) * kd * batch,
+                       [&] { return launch_mq(a, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MQ_sum", 0.0, rows * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, ptil, batch, s); }));
@@ -895,9 +888,9 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(cols) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.rpart) : R;
-    MUON_LAUNCH(traced(s, "tall_gemm_kernel<0, 1, 1>", "grasp_MtP", 2.0 * elems * kd,
+    MUON_LAUNCH(traced(s, "tall_gemm_kernel", "grasp_MtP", 2.0 * elems * kd,
                        elems * 4.0 + (rows + cols * a.pieces) * kd * 4.0 * batch,
-                       [&] { return launch_tall(a, false, batch, s); }));
+                       [&] { return launch_tall(a, batch, s); }));
     if (a.pieces > 1)
       MUON_LAUNCH(traced(s, "sum_pieces_kernel", "grasp_MtP_sum", 0.0, cols * kd * batch * 4.0 * (a.pieces + 1),
                          [&] { return launch_sum_pieces(a.C, a.pieces, a.sC, R, batch, s); }));
@@ -912,7 +905,8 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
                        [&] { return launch_group8(q, false, batch, s); }));
   }
   // 7. grid code of M_res = M_t - P R^T, P and R split once into bf16 planes
-  // (in the buffers of the split Q^T and P^T, which M_t Q and M_t^T P have used)
+  // (in the buffers of R's transposed codes and of the split P^T, which M_t Q
+  // and M_t^T P have used)
   {
     uint16_t* rsp = qs;
     MUON_LAUNCH(traced(s, "split_kernel", "grasp_PR_split", 0.0, (rows + cols) * kd * batch * 8.0, [&] {

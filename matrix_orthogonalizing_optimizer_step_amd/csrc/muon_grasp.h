@@ -29,14 +29,27 @@ struct Group8Args {
   void* const* scales;                          // fp32 rows x ceil(k / 128)
 };
 
-// Q = unit columns of the decoded R_{t-1} (n x k).
+// Column norms of the decoded R_{t-1} (n x k).
 constexpr int kUnitRows = 64;  // rows per chunk of the column sums
 struct UnitArgs {
   int n, k, nchunk;                             // nchunk = ceil(n / kUnitRows)
   const void* const* codes; const void* const* scales;
   double* part;                                 // batch x nchunk x k
   double* inv;                                  // batch x k: 1 / column norm
-  float* Q; int64_t sQ;
+};
+
+// P~ = M_t Q with Q the unit columns of deq(R_{t-1}) (rows x cols times cols x
+// k): Q[j][c] = q_jc s_{j,c/128} inv_c / 127, so the column tile of 128
+// columns c (one 8-bit group g) is (inv_c / 127) sum_j (M_t[i][j] s_{j,g})
+// q_jc, with the codes exact in bf16.  With pieces > 1 as TallArgs.
+struct MQArgs {
+  int M, N, K;                                  // rows, k, cols
+  const float* A; int64_t sA;                   // M_t, matrix b at A + b sA
+  const uint16_t* Ct; int64_t sCt;              // R's codes transposed, bf16 (k x cols), matrix b at + b sCt
+  const void* const* rs;                        // R's group scales (cols x ceil(k / 128)) per matrix
+  const double* inv;                            // batch x k: 1 / column norm of deq(R_{t-1})
+  float* C; int64_t sC;
+  int pieces, kchunk;
 };
 
 // C[b] (M x N, row-major, fp32) = A[b] B[b]; A element (row, k) at
@@ -107,8 +120,11 @@ inline int gram_chunk_rows(int m, int batch) {
 
 hipError_t launch_grid(const GridArgs& a, int mode, int batch, hipStream_t s);
 hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStream_t s);
-hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s);
-hipError_t launch_tall(const TallArgs& a, bool a_kcontig, int batch, hipStream_t s);  // B pre-split
+hipError_t launch_col_norms(const UnitArgs& a, int batch, hipStream_t s);
+hipError_t launch_codes_t(const void* const* codes, int n, int k, uint16_t* ct, int64_t s_ct, int batch,
+                          hipStream_t s);
+hipError_t launch_mq(const MQArgs& a, int batch, hipStream_t s);
+hipError_t launch_tall(const TallArgs& a, int batch, hipStream_t s);  // M_t^T P, B pre-split
 hipError_t launch_split_t(const float* X, int64_t sX, int rows, int k, uint16_t* hi, uint16_t* lo, int64_t sT,
                           int batch, hipStream_t s);
 hipError_t launch_split(const float* X, int64_t sX, int64_t count, uint16_t* hi, uint16_t* lo, int64_t sT, int batch,

@@ -289,10 +289,11 @@ __global__ __launch_bounds__(kGT) void group8_kernel(Group8Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Q = unit columns of the decoded R_{t-1} (n x k, fp32).  Stage 1: per chunk
-// of kUnitRows rows, the fp64 sum of squares of every column.  Stage 2 (one
+// Column norms of the decoded R_{t-1} (n x k).  Stage 1: per chunk of
+// kUnitRows rows, the fp64 sum of squares of every column.  Stage 2 (one
 // block per matrix): 1 / norm per column from the chunk partials summed in
-// chunk order (0 for a zero column).  Stage 3: the scaled rows.
+// chunk order (0 for a zero column).  The unit columns Q themselves are never
+// formed: M_t Q takes the codes and these factors (mq_kernel).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGT) void colsq_kernel(UnitArgs a) {
   const int b = blockIdx.y, ch = blockIdx.x;
@@ -326,20 +327,6 @@ __global__ __launch_bounds__(kGT) void colinv_kernel(UnitArgs a) {
     }
     for (; p < a.nchunk; ++p) ss += src[static_cast<int64_t>(p) * k];
     a.inv[static_cast<int64_t>(b) * k + c] = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
-  }
-}
-
-__global__ __launch_bounds__(kGT) void unit_columns_kernel(UnitArgs a) {
-  const int b = blockIdx.y, ch = blockIdx.x;
-  const int k = a.k, ng = (k + kGB - 1) / kGB;
-  const int8_t* q = static_cast<const int8_t*>(a.codes[b]);
-  const float* sc = static_cast<const float*>(a.scales[b]);
-  const double* inv = a.inv + static_cast<int64_t>(b) * k;
-  float* Q = a.Q + static_cast<int64_t>(b) * a.sQ;
-  const int i0 = ch * kUnitRows, i1 = min(a.n, i0 + kUnitRows);
-  for (int64_t e = static_cast<int64_t>(i0) * k + threadIdx.x; e < static_cast<int64_t>(i1) * k; e += kGT) {
-    const int i = static_cast<int>(e / k), c = static_cast<int>(e - static_cast<int64_t>(i) * k);
-    Q[e] = static_cast<float>(decode(q[e], sc[static_cast<int64_t>(i) * ng + c / kGB], 127.0) * inv[c]);
   }
 }
 
@@ -383,25 +370,22 @@ __device__ __forceinline__ void load_f32(const float* base, int64_t s_row, int64
   }
 }
 
-// Registers -> LDS as bf16 hi (and lo = bf16(x - hi) when SPLIT).
+// Registers -> LDS as bf16 hi (and lo = bf16(x - hi) when SPLIT), two
+// values per conversion instruction.
 template <bool KC, bool SPLIT>
 __device__ __forceinline__ void store_split(const TileRegs& r, uint16_t* hi, uint16_t* lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = threadIdx.x + kGT * p;
     const int rr = KC ? (e >> 3) : (e & 127), kk = KC ? (e & 7) * 4 : (e >> 7) * 4;
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float x = r.v[4 * p + q];
-      h[q] = f32_to_bf16(x);
-      l[q] = SPLIT ? f32_to_bf16(x - bf16_to_f32(h[q])) : 0;
+    const float* x = &r.v[4 * p];
+    const uint32_t h01 = f32x2_to_bf16x2(x[0], x[1]), h23 = f32x2_to_bf16x2(x[2], x[3]);
+    *reinterpret_cast<uint2*>(hi + rr * kTL + kk) = make_uint2(h01, h23);
+    if (SPLIT) {
+      const uint32_t l01 = f32x2_to_bf16x2(x[0] - __uint_as_float(h01 << 16), x[1] - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = f32x2_to_bf16x2(x[2] - __uint_as_float(h23 << 16), x[3] - __uint_as_float(h23 & 0xffff0000u));
+      *reinterpret_cast<uint2*>(lo + rr * kTL + kk) = make_uint2(l01, l23);
     }
-    *reinterpret_cast<uint2*>(hi + rr * kTL + kk) =
-        make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
-    if (SPLIT)
-      *reinterpret_cast<uint2*>(lo + rr * kTL + kk) =
-          make_uint2(l[0] | (static_cast<uint32_t>(l[1]) << 16), l[2] | (static_cast<uint32_t>(l[3]) << 16));
   }
 }
 
@@ -497,71 +481,47 @@ __device__ __forceinline__ void store_pair(const PairRegs& r, uint16_t* hi, uint
   }
 }
 
-// acc += A B over k in [kbeg, kend) for an fp32 A, split as it is staged,
-// and a B that comes pre-split (BPS: a.Bh, a.Bl, planes of bf16 hi / lo,
-// element (col, k) at col * b_row + k, k contiguous).  With A not
-// k-contiguous (M_t^T: each load instruction reads 256 contiguous bytes of a
-// row), smem holds two stages (8 planes), the global loads run two stages
-// ahead of the MFMAs (two register sets) and a stage takes one barrier;
-// measured slower for the k-contiguous A of M_t Q, whose loads are 128-byte
-// pieces of 128 rows: there one stage (4 planes), loads one stage ahead.
-template <bool AKC, bool BKC, bool BPS>
+// acc += A B over k in [kbeg, kend) for an fp32 A that is not k-contiguous
+// (M_t^T: each load instruction reads 256 contiguous bytes of a row), split as
+// it is staged, and a B that comes pre-split (a.Bh, a.Bl: planes of bf16 hi /
+// lo, element (col, k) at col * b_row + k).  smem holds two stages (8 planes),
+// the global loads run two stages ahead of the MFMAs (two register sets) and
+// a stage takes one barrier.  (The k-contiguous M_t of M_t Q, whose loads
+// are 128-byte pieces of 128 rows, measured slower this way.)
 __device__ __forceinline__ void tall_loop(const TallArgs& a, int b, int row0, int col0, int kbeg, int kend,
                                           uint16_t* smem, gq_f32x16 (&acc)[2][2]) {
-  static_assert(BKC && BPS, "B comes pre-split, k contiguous");
   const float* A = a.A + static_cast<int64_t>(b) * a.sA;
-  if constexpr (!AKC) {
-    const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
-    const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
-    const int nst = (kend - kbeg + kTK - 1) / kTK;
-    TileRegs ra[2];
-    PairRegs rb[2];
+  const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
+  const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
+  const int nst = (kend - kbeg + kTK - 1) / kTK;
+  TileRegs ra[2];
+  PairRegs rb[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < nst) {
-        load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg + q * kTK, a.M, kend, ra[q]);
-        load_pair(Bhi, Blo, a.b_row, col0, kbeg + q * kTK, a.N, kend, rb[q]);
-      }
-    for (int st = 0; st < nst; st += 2) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if (st + q < nst) {
-          uint16_t* base = smem + q * 4 * kStageHalves;
-          uint16_t *Ah = base, *Al = base + kStageHalves, *Bh = base + 2 * kStageHalves, *Bl = base + 3 * kStageHalves;
-          store_split<AKC, true>(ra[q], Ah, Al);
-          store_pair(rb[q], Bh, Bl);
-          // LDS set q was last read two stages ago, before the previous barrier
-          __syncthreads();
-          const int kn = kbeg + (st + q + 2) * kTK;
-          if (kn < kend) {
-            load_f32<AKC>(A, a.a_row, a.a_k, row0, kn, a.M, kend, ra[q]);
-            load_pair(Bhi, Blo, a.b_row, col0, kn, a.N, kend, rb[q]);
-          }
-          mma_stage<true>(Ah, Al, Bh, Bl, acc);
-        }
-      }
+  for (int q = 0; q < 2; ++q)
+    if (q < nst) {
+      load_f32<false>(A, a.a_row, a.a_k, row0, kbeg + q * kTK, a.M, kend, ra[q]);
+      load_pair(Bhi, Blo, a.b_row, col0, kbeg + q * kTK, a.N, kend, rb[q]);
     }
-    __syncthreads();  // the caller may reuse smem
-  } else {
-    uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves, *Bl = smem + 3 * kStageHalves;
-    TileRegs ra;
-    load_f32<AKC>(A, a.a_row, a.a_k, row0, kbeg, a.M, kend, ra);
-    const uint16_t* Bhi = a.Bh + static_cast<int64_t>(b) * a.sB;
-    const uint16_t* Blo = a.Bl + static_cast<int64_t>(b) * a.sB;
-    PairRegs rb;
-    load_pair(Bhi, Blo, a.b_row, col0, kbeg, a.N, kend, rb);
-    for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-      store_split<AKC, true>(ra, Ah, Al);
-      store_pair(rb, Bh, Bl);
-      __syncthreads();
-      if (k0 + kTK < kend) {
-        load_f32<AKC>(A, a.a_row, a.a_k, row0, k0 + kTK, a.M, kend, ra);
-        load_pair(Bhi, Blo, a.b_row, col0, k0 + kTK, a.N, kend, rb);
+  for (int st = 0; st < nst; st += 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (st + q < nst) {
+        uint16_t* base = smem + q * 4 * kStageHalves;
+        uint16_t *Ah = base, *Al = base + kStageHalves, *Bh = base + 2 * kStageHalves, *Bl = base + 3 * kStageHalves;
+        store_split<false, true>(ra[q], Ah, Al);
+        store_pair(rb[q], Bh, Bl);
+        // LDS set q was last read two stages ago, before the previous barrier
+        __syncthreads();
+        const int kn = kbeg + (st + q + 2) * kTK;
+        if (kn < kend) {
+          load_f32<false>(A, a.a_row, a.a_k, row0, kn, a.M, kend, ra[q]);
+          load_pair(Bhi, Blo, a.b_row, col0, kn, a.N, kend, rb[q]);
+        }
+        mma_stage<true>(Ah, Al, Bh, Bl, acc);
       }
-      mma_stage<true>(Ah, Al, Bh, Bl, acc);
-      __syncthreads();
     }
   }
+  __syncthreads();  // the caller may reuse smem
 }
 
 // acc += A B over k in [kbeg, kend) with both operands pre-split into bf16
@@ -587,6 +547,98 @@ __device__ __forceinline__ void presplit_loop(const TallArgs& a, int b, int row0
     }
     mma_stage<true>(Ah, Al, Bh, Bl, acc);
     __syncthreads();
+  }
+}
+
+// An operand exact in bf16 (codes), k contiguous: the thread's four runs of 4
+// consecutive k, 8 bytes each (the hi plane of load_pair alone).
+struct HiRegs {
+  uint2 h[4];
+};
+
+__device__ __forceinline__ void load_hi(const uint16_t* hi, int64_t s_row, int row0, int k0, int nrows, int K,
+                                        HiRegs& r) {
+  const uint16_t* hb = hi + static_cast<int64_t>(row0) * s_row;
+  const bool al = ((reinterpret_cast<uintptr_t>(hb) & 7u) | (s_row & 3)) == 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = threadIdx.x + kGT * p;
+    const int row = row0 + (e >> 3), k = k0 + (e & 7) * 4;
+    const uint32_t off = static_cast<uint32_t>(e >> 3) * static_cast<uint32_t>(s_row) + static_cast<uint32_t>(k);
+    if (al && row < nrows && k + 3 < K) {
+      r.h[p] = *reinterpret_cast<const uint2*>(hb + off);
+    } else {
+      uint32_t h[2] = {0u, 0u};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row < nrows && k + q < K) h[q >> 1] |= static_cast<uint32_t>(hb[off + q]) << (16 * (q & 1));
+      r.h[p] = make_uint2(h[0], h[1]);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_hi(const HiRegs& r, uint16_t* hi) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = threadIdx.x + kGT * p;
+    *reinterpret_cast<uint2*>(hi + (e >> 3) * kTL + (e & 7) * 4) = r.h[p];
+  }
+}
+
+// The MFMAs of one LDS stage with A split (hi, lo) and B exact: two per block
+// and k-step.
+__device__ __forceinline__ void mma_stage_exact_b(const uint16_t* Ah, const uint16_t* Al, const uint16_t* Bh,
+                                                  gq_f32x16 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ar = 64 * (w >> 1) + (lane & 31), bc = 64 * (w & 1) + (lane & 31);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = 16 * s + 8 * (lane >> 5);
+    uint4 ah[2], al[2], bh[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      ah[x] = *reinterpret_cast<const uint4*>(Ah + (ar + 32 * x) * kTL + k);
+      al[x] = *reinterpret_cast<const uint4*>(Al + (ar + 32 * x) * kTL + k);
+      bh[x] = *reinterpret_cast<const uint4*>(Bh + (bc + 32 * x) * kTL + k);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        acc[x][y] = mfma(ah[x], bh[y], acc[x][y]);
+        acc[x][y] = mfma(al[x], bh[y], acc[x][y]);
+      }
+  }
+}
+
+// R's codes (n x k int8, per-matrix pointers) -> bf16 (k x n), exact: the B
+// operand of mq_kernel, through a 64 x 64 LDS tile so that both sides are
+// coalesced.
+__global__ __launch_bounds__(kGT) void codes_t_kernel(const void* const* codes, int n, int k, uint16_t* ct,
+                                                      int64_t s_ct) {
+  __shared__ int t[64][65];
+  const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int8_t* q = static_cast<const int8_t*>(codes[b]);
+  int v[64 * 64 / kGT];
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kGT; ++u) {
+    const int e = threadIdx.x + kGT * u, r = e >> 6, c = e & 63;
+    const bool ok = r0 + r < n && c0 + c < k;
+    v[u] = q[ok ? static_cast<int64_t>(r0 + r) * k + c0 + c : 0];
+    v[u] = ok ? v[u] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kGT; ++u) {
+    const int e = threadIdx.x + kGT * u;
+    t[e >> 6][e & 63] = v[u];
+  }
+  __syncthreads();
+  uint16_t* out = ct + static_cast<int64_t>(b) * s_ct;
+#pragma unroll
+  for (int u = 0; u < 64 * 64 / kGT; ++u) {
+    const int e = threadIdx.x + kGT * u, c = e >> 6, r = e & 63;
+    if (c0 + c < k && r0 + r < n)
+      out[static_cast<int64_t>(c0 + c) * n + r0 + r] = f32_to_bf16(static_cast<float>(t[r][c]));
   }
 }
 
@@ -665,10 +717,75 @@ __device__ __forceinline__ int acc_col(int y) {
   return 64 * (w & 1) + 32 * y + (lane & 31);
 }
 
-// C (or a k-piece of C) = A B, stored fp32.  grid: (N tiles, M tiles, batch * pieces).
-template <bool AKC, bool BKC, bool BPS>
+// P~ (or its k pieces) = M_t Q from R's codes: a 128 x 128 tile per block,
+// tile column bj = 8-bit group g.  M_t's entries are scaled by s_{j,g} as they
+// are staged and split; the codes (R^T, bf16) go to LDS as they are; the
+// epilogue scales column c by inv_c / 127 (in fp64).  One stage of 32 k in
+// flight ahead of the MFMAs.
+static_assert(kTT == kGB, "a tile column is one 8-bit group");
+__global__ __launch_bounds__(kGT, 2) void mq_kernel(MQArgs a) {
+  __shared__ __align__(16) uint16_t smem[3 * kStageHalves];
+  uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves;
+  int bi, bj, z;
+  grouped_tile(bi, bj, z);
+  const int b = z / a.pieces, piece = z - b * a.pieces;
+  const int row0 = bi * kTT, col0 = bj * kTT, g = bj;
+  const int kbeg = piece * a.kchunk, kend = min(a.K, kbeg + a.kchunk);
+  const int ng = (a.N + kGB - 1) / kGB;
+  const float* A = a.A + static_cast<int64_t>(b) * a.sA;
+  const uint16_t* Ct = a.Ct + static_cast<int64_t>(b) * a.sCt;
+  const float* rs = static_cast<const float*>(a.rs[b]);
+  gq_f32x16 acc[2][2];
+  zero_acc(acc);
+  TileRegs ra;
+  HiRegs rb;
+  float sv[4];
+  // the thread's four k of a stage: k0 + 4 (t % 8) + q (load_f32's layout)
+  auto load = [&](int k0) {
+    load_f32<true>(A, a.K, 1, row0, k0, a.M, kend, ra);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = k0 + (threadIdx.x & 7) * 4 + q;
+      const bool ok = j < kend;
+      sv[q] = rs[ok ? static_cast<int64_t>(j) * ng + g : 0];
+      sv[q] = ok ? sv[q] : 0.0f;
+    }
+    load_hi(Ct, a.K, col0, k0, a.N, kend, rb);
+  };
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ra.v[4 * p + q] *= sv[q];
+    store_split<true, true>(ra, Ah, Al);
+    store_hi(rb, Bh);
+    __syncthreads();
+    if (k0 + kTK < kend) load(k0 + kTK);
+    mma_stage_exact_b(Ah, Al, Bh, acc);
+    __syncthreads();
+  }
+  const double* inv = a.inv + static_cast<int64_t>(b) * a.N;
+  float* C = a.C + static_cast<int64_t>(z) * a.sC;
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int col = col0 + acc_col(y);
+    const double f = col < a.N ? inv[col] * (1.0 / 127.0) : 0.0;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = row0 + acc_row(x, v);
+        if (row < a.M && col < a.N)
+          C[static_cast<int64_t>(row) * a.N + col] = static_cast<float>(static_cast<double>(acc[x][y][v]) * f);
+      }
+  }
+}
+
+// C (or a k-piece of C) = A B, stored fp32, for M_t^T P (tall_loop).  grid:
+// (N tiles, M tiles, batch * pieces).
 __global__ __launch_bounds__(kGT, 2) void tall_gemm_kernel(TallArgs a) {
-  __shared__ __align__(16) uint16_t smem[(!AKC ? 8 : 4) * kStageHalves];
+  __shared__ __align__(16) uint16_t smem[8 * kStageHalves];
   int bi, bj, z;
   grouped_tile(bi, bj, z);
   const int b = z / a.pieces, piece = z - b * a.pieces;
@@ -676,7 +793,7 @@ __global__ __launch_bounds__(kGT, 2) void tall_gemm_kernel(TallArgs a) {
   const int kbeg = piece * a.kchunk, kend = min(a.K, kbeg + a.kchunk);
   gq_f32x16 acc[2][2];
   zero_acc(acc);
-  tall_loop<AKC, BKC, BPS>(a, b, row0, col0, kbeg, kend, smem, acc);
+  tall_loop(a, b, row0, col0, kbeg, kend, smem, acc);
   float* C = a.C + static_cast<int64_t>(z) * a.sC;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -1739,23 +1856,31 @@ hipError_t launch_group8(const Group8Args& a, bool dequantize, int batch, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_unit_columns(const UnitArgs& a, int batch, hipStream_t s) {
-  const dim3 g(a.nchunk, batch);
-  hipLaunchKernelGGL(colsq_kernel, g, dim3(kGT), 0, s, a);
+hipError_t launch_col_norms(const UnitArgs& a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(colsq_kernel, dim3(a.nchunk, batch), dim3(kGT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(colinv_kernel, dim3(batch), dim3(kGT), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unit_columns_kernel, g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tall(const TallArgs& a, bool akc, int batch, hipStream_t s) {
+hipError_t launch_codes_t(const void* const* codes, int n, int k, uint16_t* ct, int64_t s_ct, int batch,
+                          hipStream_t s) {
+  const dim3 g((k + 63) / 64, (n + 63) / 64, batch);
+  hipLaunchKernelGGL(codes_t_kernel, g, dim3(kGT), 0, s, codes, n, k, ct, s_ct);
+  return hipGetLastError();
+}
+
+hipError_t launch_mq(const MQArgs& a, int batch, hipStream_t s) {
+  const dim3 g((a.N + kTT - 1) / kTT, (a.M + kTT - 1) / kTT, batch * a.pieces);
+  hipLaunchKernelGGL(mq_kernel, g, dim3(kGT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tall(const TallArgs& a, int batch, hipStream_t s) {
   if (a.Bh == nullptr || a.Bl == nullptr) return hipErrorInvalidValue;  // B comes pre-split
   const dim3 g((a.N + kTT - 1) / kTT, (a.M + kTT - 1) / kTT, batch * a.pieces);
-  if (akc) hipLaunchKernelGGL((tall_gemm_kernel<true, true, true>), g, dim3(kGT), 0, s, a);
-  else hipLaunchKernelGGL((tall_gemm_kernel<false, true, true>), g, dim3(kGT), 0, s, a);
+  hipLaunchKernelGGL(tall_gemm_kernel, g, dim3(kGT), 0, s, a);
   return hipGetLastError();
 }
 
