@@ -648,18 +648,19 @@ constexpr int kGraspMaxBatch = 65535 / kGraspMaxPieces;  // the state kernels pu
 int nblk(int x, int b) { return (x + b - 1) / b; }
 
 // k pieces for a product with `tiles` output tiles and K of length `K`, each
-// piece at least 256 long.  The tall products run two blocks per compute
-// unit, and a block's time is set by its k length (its loads wait on memory
-// latency, not on bandwidth shared with the others), so a launch of B blocks
-// takes about ceil(B / slots) rounds of K / pieces each: with fewer tiles than
-// slots, the count that minimises rounds / pieces is taken (the smallest on a
-// tie, for the fewest partial sums).  Planned for the 256 compute units of the
-// MI355X so that the workspace size depends on the shapes only.
+// piece at least 256 long.  The tall products run per_cu blocks per compute
+// unit (M_t Q three, M_t^T P two), and a block's time is set by its k length
+// (its loads wait on memory latency, not on bandwidth shared with the others),
+// so a launch of B blocks takes about ceil(B / slots) rounds of K / pieces
+// each: with fewer tiles than slots, the count that minimises rounds / pieces
+// is taken (the smallest on a tie, for the fewest partial sums).  Planned for
+// the 256 compute units of the MI355X so that the workspace size depends on
+// the shapes only.
 constexpr int kGraspPlanCUs = 256;
-constexpr int kTallBlocksPerCU = 2;
+constexpr int kMQBlocksPerCU = 3, kMtPBlocksPerCU = 2;
 
-void grasp_pieces(int64_t tiles, int K, int* pieces, int* kchunk) {
-  const int64_t slots = static_cast<int64_t>(kGraspPlanCUs) * kTallBlocksPerCU;
+void grasp_pieces(int64_t tiles, int K, int per_cu, int* pieces, int* kchunk) {
+  const int64_t slots = static_cast<int64_t>(kGraspPlanCUs) * per_cu;
   const int maxp = K / 256 > 1 ? (K / 256 < kGraspMaxPieces ? K / 256 : kGraspMaxPieces) : 1;
   int pcs = 1;
   if (tiles < slots) {
@@ -703,7 +704,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->colpart = take(B * g->nch_n * kk * 8);
     g->colinv = take(B * kk * 8);
     int pcs = 1, chunk = 0;
-    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &pcs, &chunk);
+    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, kMQBlocksPerCU, &pcs, &chunk);
     g->ppart = take(pcs > 1 ? B * pcs * r * kk * 4 : 0);
     g->ptil = take(B * r * kk * 4);
     g->spart = take(B * g->nch_m * kk * kk * 8);
@@ -712,7 +713,7 @@ bool grasp_layout(size_t base, int batch, int rows, int cols, int k, GraspLayout
     g->dinv = take(B * nblk(k, 64) * 64 * 64 * 8);  // U's 64 x 64 diagonal blocks inverted
     g->P = take(B * r * kk * 4);
     g->ps = take(B * r * kk * 4);  // P^T split into bf16 hi and lo planes, later P
-    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &pcs, &chunk);
+    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, kMtPBlocksPerCU, &pcs, &chunk);
     g->rpart = take(pcs > 1 ? B * pcs * c * kk * 4 : 0);
     g->R = take(B * c * kk * 4);
   }
@@ -822,7 +823,7 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.sCt = s_qs;
     a.rs = st->R_scales;
     a.inv = reinterpret_cast<double*>(ws + lay.colinv);
-    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, &a.pieces, &a.kchunk);
+    grasp_pieces(static_cast<int64_t>(nblk(rows, 128)) * nblk(k, 128) * batch, cols, kMQBlocksPerCU, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(rows) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.ppart) : ptil;
     MUON_LAUNCH(traced(s, "mq_kernel", "grasp_MQ", 2.0 * elems * kd,
@@ -885,7 +886,7 @@ muon_status run_grasp_state(int batch, int rows, int cols, int k, const muon_gra
     a.Bl = ps + static_cast<int64_t>(rows) * k;
     a.sB = s_ps;
     a.b_row = rows;
-    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, &a.pieces, &a.kchunk);
+    grasp_pieces(static_cast<int64_t>(nblk(cols, 128)) * nblk(k, 128) * batch, rows, kMtPBlocksPerCU, &a.pieces, &a.kchunk);
     a.sC = static_cast<int64_t>(cols) * k;
     a.C = a.pieces > 1 ? reinterpret_cast<float*>(ws + lay.rpart) : R;
     MUON_LAUNCH(traced(s, "tall_gemm_kernel", "grasp_MtP", 2.0 * elems * kd,

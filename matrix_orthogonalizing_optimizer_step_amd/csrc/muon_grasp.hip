@@ -721,9 +721,10 @@ __device__ __forceinline__ int acc_col(int y) {
 // tile column bj = 8-bit group g.  M_t's entries are scaled by s_{j,g} as they
 // are staged and split; the codes (R^T, bf16) go to LDS as they are; the
 // epilogue scales column c by inv_c / 127 (in fp64).  One stage of 32 k in
-// flight ahead of the MFMAs.
+// flight ahead of the MFMAs; three blocks share a compute unit (30 KB of LDS,
+// at most 168 registers).
 static_assert(kTT == kGB, "a tile column is one 8-bit group");
-__global__ __launch_bounds__(kGT, 2) void mq_kernel(MQArgs a) {
+__global__ __launch_bounds__(kGT, 3) void mq_kernel(MQArgs a) {
   __shared__ __align__(16) uint16_t smem[3 * kStageHalves];
   uint16_t *Ah = smem, *Al = smem + kStageHalves, *Bh = smem + 2 * kStageHalves;
   int bi, bj, z;
