@@ -5,6 +5,7 @@ binding (``binding``) and the build script (``_build``)."""
 from .binding import (  # noqa: F401
     BF16, F16, F32, GRAM, STANDARD, GraspState, MuonError, NSConfig, abi_version, grasp_step, grasp_workspace_size,
     gram_ns_orthogonalize, grid_dequantize, grid_quantize, group8_dequantize, group8_quantize, load_library,
-    muon_step, muon_step_fixed_scratch, ns_flops, ns_orthogonalize, pointer_array, quintic_schedule, trace_collect, trace_enable, workspace,
+    mfma_ceiling, muon_step, muon_step_fixed_scratch, ns_flops, ns_orthogonalize, pointer_array, quintic_schedule,
+    trace_collect, trace_enable, workspace,
     workspace_size,
 )

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
 SOURCES = ["muon_gemm_bf16.hip", "muon_gemm_f16.hip", "muon_gemm_f32.hip", "muon_gemm.hip",
-           "muon_elementwise.hip", "muon_grasp.hip", "muon_api.hip", "muon_schedule.cpp"]
+           "muon_elementwise.hip", "muon_grasp.hip", "muon_api.hip", "muon_schedule.cpp", "muon_ceiling.hip"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert {"ns_orthogonalize", "gram_ns_orthogonalize", "muon_step", "muon_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert mu.abi_version() == 5
+    assert mu.abi_version() == 6
 
 
 def test_status_strings():
@@ -281,3 +281,10 @@ def test_implicit_workspace_per_stream_and_pinned_under_capture(monkeypatch):
     assert f is not e and bd._ws_pinned[e.data_ptr()] is e and f.data_ptr() not in bd._ws_pinned
     bd._ws_cache.clear()
     bd._ws_pinned.clear()
+
+
+def test_mfma_ceiling_rejects_bad_arguments():
+    """The ceiling probe checks its arguments before launching anything."""
+    lib = mu.load_library()
+    for blocks, rounds, sink in ((0, 10, 1024), (1 << 21, 10, 1024), (4, 0, 1024), (4, 10, None)):
+        assert lib.muon_mfma_ceiling(blocks, rounds, sink, None) == 1  # MUON_ERR_INVALID_ARG
