@@ -452,6 +452,65 @@ __device__ __forceinline__ void final_block(const GemmArgs& a, const EpiState& s
   final_rows_any<LDE, BW>(a, st, ep, i0, j0, lane);
 }
 
+// The fast update of a staged 32 x 128 block split in two, so that the loads
+// of W can go out before O is staged: final_load_w128 issues the 16
+// four-element loads of W that final_rows_fast<WD, OD, LDE, 128> makes for
+// this lane (rows 2 r + lane / 32, or columns 8 r + lane / 8, r < 16), and
+// final_apply128 then updates and stores them with the staged O (and stores
+// O itself when OD >= 0), element for element as final_rows_fast does.
+template <int WD>
+__device__ __forceinline__ void final_load_w128(const GemmArgs& a, const EpiState& st, int i0, int j0, int lane,
+                                                float4 (&wv)[16]) {
+  constexpr int wsz = WD == kF32 ? 4 : 2;
+  const int64_t ld = a.user_ld;
+  if (!a.transposed) {
+    const int64_t base = static_cast<int64_t>(i0 + (lane >> 5)) * ld + j0 + 4 * (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[r] = ld4<WD>(st.w, (base + 2 * r * ld) * wsz);
+  } else {
+    const int64_t base = static_cast<int64_t>(j0 + (lane >> 3)) * ld + i0 + (lane & 7) * 4;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) wv[t] = ld4<WD>(st.w, (base + 8 * t * ld) * wsz);
+  }
+}
+
+template <int WD, int OD, int LDE>
+__device__ __forceinline__ void final_apply128(const GemmArgs& a, const EpiState& st, const lds_f32* ep, int i0, int j0,
+                                               int lane, float4 (&wv)[16]) {
+  constexpr int wsz = WD == kF32 ? 4 : 2, osz = OD == kF32 ? 4 : 2;
+  const int64_t ld = a.user_ld;
+  const float lr = a.lr, wd = a.wd, os = a.oscale;
+  auto update = [&](float4& nw, const float4& ov) {
+    nw.x -= lr * (os * ov.x + wd * nw.x);
+    nw.y -= lr * (os * ov.y + wd * nw.y);
+    nw.z -= lr * (os * ov.z + wd * nw.z);
+    nw.w -= lr * (os * ov.w + wd * nw.w);
+  };
+  if (!a.transposed) {
+    const int sub = lane >> 5, cl = 4 * (lane & 31);
+    const int64_t base = static_cast<int64_t>(i0 + sub) * ld + j0 + cl;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float4 ov = lds_load4(ep + (2 * r + sub) * LDE + cl);
+      if constexpr (OD >= 0) st4<OD>(st.o, (base + 2 * r * ld) * osz, ov);
+      update(wv[r], ov);
+      st4<WD>(st.w, (base + 2 * r * ld) * wsz, wv[r]);
+    }
+  } else {
+    const int r4 = (lane & 7) * 4;
+    const int64_t base = static_cast<int64_t>(j0 + (lane >> 3)) * ld + i0 + r4;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int c = 8 * t + (lane >> 3);
+      const float4 ov = make_float4(ep[(r4 + 0) * LDE + c], ep[(r4 + 1) * LDE + c], ep[(r4 + 2) * LDE + c],
+                                    ep[(r4 + 3) * LDE + c]);
+      if constexpr (OD >= 0) st4<OD>(st.o, (base + 8 * t * ld) * osz, ov);
+      update(wv[t], ov);
+      st4<WD>(st.w, (base + 8 * t * ld) * wsz, wv[t]);
+    }
+  }
+}
+
 // Final product, general form (ragged edges, unaligned rows): W <- W -
 // lr (O + wd W) and the optional store of O, for rows i0 .. i0 + 31 and
 // columns j0 .. j0 + BW - 1 of O staged in LDS (row-major, LDE floats per
@@ -727,6 +786,28 @@ __device__ __forceinline__ void epi_range(const GemmArgs& a, EpiState& st, const
   epi_run<OP, KIND, MAYDIAG, FN, G, BEGIN, END>(a, st, p, acc, cur, I, dg, wave, lane, id, ep);
 }
 
+// The last product's epilogue for a 256 x 128 tile wholly inside the matrix
+// (every 32 x 128 block passes final_fast_ok): as the general sequence
+// (stage half 0, update it, stage half 1, update it; three block barriers),
+// with each half's W loads issued before that half is staged.
+template <int OP, int KIND, int WD, int OD>
+__device__ __forceinline__ void fin_prefetched(const GemmArgs& a, EpiState& st, const EpiPtrs& p,
+                                               const f32x16_t (&acc)[kFM][TileCfg<kHalfTile>::kFN], int I, int J,
+                                               int wave, int lane, const uint4 (&id)[2], lds_f32* ep) {
+  constexpr int FN = TileCfg<kHalfTile>::kFN, NB = kFM * FN, LDE = kHalfTile + 4;
+  const int i0 = I * kBM + wave * (kBM / kNW), j0 = J * kHalfTile;
+  float4 wv[16];
+  final_load_w128<WD>(a, st, i0, j0, lane, wv);
+  epi_range<OP, KIND, false, FN, 0, FN>(a, st, p, acc, I, 0, wave, lane, id, ep);
+  __syncthreads();
+  final_apply128<WD, OD, LDE>(a, st, ep, i0, j0, lane, wv);
+  final_load_w128<WD>(a, st, i0 + 32, j0, lane, wv);
+  __syncthreads();
+  epi_range<OP, KIND, false, FN, FN, NB>(a, st, p, acc, I, 0, wave, lane, id, ep);
+  __syncthreads();
+  final_apply128<WD, OD, LDE>(a, st, ep, i0 + 32, j0, lane, wv);
+}
+
 // The register epilogue of the wave's 64 x BN sub-tile; the last product
 // stages O through LDS one 32-row block (32 x BN) at a time so
 // that the user's row-major W is read and written along its rows.
@@ -739,6 +820,23 @@ __device__ __forceinline__ void epilogue_mfma(const GemmArgs& a, EpiState& st,
   const EpiPtrs p = epi_ptrs<KIND, BN>(a, b, I, J, wave);
   if constexpr (S.fin) {
     const uint4 id[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};  // no transposes here
+    if constexpr (BN == kHalfTile && KIND == kEpiFin) {
+      // a tile wholly inside the matrix with a W to update: the W loads of
+      // each 32-row half go out before that half of O is staged (not with a
+      // 16-bit epilogue input, whose prefetch leaves no registers for them)
+      if (st.w != nullptr && final_fast_ok<BN>(a, st, I * kBM, J * BN) &&
+          final_fast_ok<BN>(a, st, I * kBM + kBM - 32, J * BN)) {
+        const int odt = st.o != nullptr ? a.o_dtype : -1;
+#define MUON_PREFETCHED(WD, OD)                                                         \
+  if (a.w_dtype == WD && odt == OD) {                                                   \
+    fin_prefetched<OP, KIND, WD, OD>(a, st, p, acc, I, J, wave, lane, id, ep);          \
+    return;                                                                             \
+  }
+        MUON_PREFETCHED(kF32, -1) MUON_PREFETCHED(kBF16, -1) MUON_PREFETCHED(kF32, kF32)
+        MUON_PREFETCHED(kF32, kBF16) MUON_PREFETCHED(kBF16, kF32) MUON_PREFETCHED(kBF16, kBF16)
+#undef MUON_PREFETCHED
+      }
+    }
     epi_range<OP, KIND, false, FN, 0, FN>(a, st, p, acc, I, 0, wave, lane, id, ep);
     __syncthreads();
     final_block<BN + 4, BN>(a, st, ep, I * kBM + wave * (kBM / kNW), J * BN, lane);
