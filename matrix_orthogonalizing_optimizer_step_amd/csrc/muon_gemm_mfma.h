@@ -1032,7 +1032,13 @@ __global__ __launch_bounds__(kNT, BN == kMfmaTile ? 1 : 2) void gemm_nt_mfma(Gem
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* Pm = static_cast<const uint16_t*>(a.P) + static_cast<int64_t>(b) * a.sP;
   const uint16_t* Qm = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(b) * a.sQ;
-  const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pm, static_cast<int64_t>(a.Mdim) * a.ldp * 2);
+  // In a 256 x 128 symmetric tile at J = 2 I + 1 the rows of waves 0 and 1
+  // lie wholly above the diagonal, so none of their values is stored.  Their
+  // P descriptor covers nothing: the loads return zeros without a memory
+  // access, and their MFMAs (the same count, so the block's schedule and
+  // barriers are unchanged) run on zero operands, which draws less power.
+  const bool above_diag = BN == kHalfTile && a.sym != 0 && J == 2 * I + 1 && wave < 2;
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(Pm, above_diag ? 0 : static_cast<int64_t>(a.Mdim) * a.ldp * 2);
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qm, static_cast<int64_t>(a.Ndim) * a.ldq * 2);
   const int voff = lane * 16;
   // byte offset of a row block = (row / 32) * (K / 64) * 4 KB
