@@ -1761,16 +1761,20 @@ __global__ __launch_bounds__(kRegT) void chol_pair_kernel(CholArgs a) {
         }
     }
     __syncthreads();
-    double u0c[kPairBC], u0r[kPairBR], u1c[kPairBC], u1r[kPairBR];
+    // Only row blocks i >= pi are updated, and their slots use column blocks
+    // j >= pi / 2: the published values outside those are not read (the LDS
+    // reads, not the FMAs, dominate a step at these sizes).  pi is uniform, so
+    // the guards are scalar branches.
+    const int pc = pi >> 1;
+    double u0c[kPairBC], u1c[kPairBC];
 #pragma unroll
     for (int j = 0; j < kPairBC; ++j) {
-      u0c[j] = rb0[tc + 32 * j];
-      u1c[j] = rb1[tc + 32 * j];
-    }
-#pragma unroll
-    for (int i = 0; i < kPairBR; ++i) {
-      u0r[i] = rb0[tr + 16 * i];
-      u1r[i] = rb1[tr + 16 * i];
+      u0c[j] = 0.0;
+      u1c[j] = 0.0;
+      if (j >= pc) {
+        u0c[j] = rb0[tc + 32 * j];
+        u1c[j] = rb1[tc + 32 * j];
+      }
     }
     const double d0 = rb0[p], e0 = diag0[p];
     const bool dead0 = !(e0 > 0.0) || !(d0 > 1e-12 * e0);
@@ -1787,9 +1791,8 @@ __global__ __launch_bounds__(kRegT) void chol_pair_kernel(CholArgs a) {
       rd1 = dead1 ? 0.0 : r1;
 #pragma unroll
       for (int j = 0; j < kPairBC; ++j) u1c[j] = fma(-f, u0c[j], u1c[j]);
-#pragma unroll
-      for (int i = 0; i < kPairBR; ++i) u1r[i] = fma(-f, u0r[i], u1r[i]);
     }
+    const double fq = two ? rb0[q] * rd0 : 0.0;  // the same f, for the row values read below
     if (threadIdx.x == 0) {
       dval[p] = d0;
       deads[p] = dead0 ? 1 : 0;
@@ -1802,8 +1805,9 @@ __global__ __launch_bounds__(kRegT) void chol_pair_kernel(CholArgs a) {
     for (int i = 0; i < kPairBR; ++i) {
       if (i >= pi) {
         const int r = tr + 16 * i;
-        const double x0 = r > p ? u0r[i] * rd0 : 0.0;
-        const double x1 = r > q ? u1r[i] * rd1 : 0.0;
+        const double u0r = rb0[r], u1r = fma(-fq, u0r, rb1[r]);
+        const double x0 = r > p ? u0r * rd0 : 0.0;
+        const double x1 = r > q ? u1r * rd1 : 0.0;
 #pragma unroll
         for (int j = i >> 1; j < kPairBC; ++j) s[i][j] = fma(-x1, u1c[j], fma(-x0, u0c[j], s[i][j]));
       }
