@@ -303,32 +303,37 @@ def summarize_mfma(args):
 
 
 def mfma_ceiling(mu, dev, rounds=12500, reps=3):
-    """The 16-bit MFMA rate this device sustains on register operands alone
-    (muon_mfma_ceiling: two blocks per compute unit, every wave issuing MFMAs
-    back to back on hashed data), timed like the step, median of `reps`
-    launches of ~20 ms after one warm-up launch: under a full MFMA load the
-    power limit sets the clock, so this is what any product can approach."""
+    """The 16-bit MFMA rate this device sustains on register operands alone,
+    per operand type (muon_mfma_ceiling: two blocks per compute unit, every
+    wave issuing MFMAs back to back on hashed data), median of `reps`
+    launches of ~15-20 ms after one warm-up launch.  Under a full MFMA load
+    the power the data draw sets the clock, so this is what any product of
+    that operand type can approach."""
     import torch
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks = 2 * cus
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    mu.mfma_ceiling(blocks, rounds, sink)
-    times = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        flops = mu.mfma_ceiling(blocks, rounds, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = sorted(times)[len(times) // 2]
-    tflops = flops / (ms / 1e3) / 1e12
-    log(f"[bench] register-only MFMA ceiling: {tflops:.0f} TFLOP/s ({ms:.2f} ms per launch)")
-    return {"tflops": tflops, "frac_of_dense_peak": tflops / PEAK_16BIT_TFLOPS,
-            "implied_clock_ghz": tflops * 1e3 / (cus * 4096.0), "ms_per_launch": ms, "blocks": blocks,
-            "note": "v_mfma_f32_32x32x16_f16 back to back on register operands with hashed values, no memory "
-                    "traffic; the power limit, not the nominal 2.4 GHz, sets the clock under this load"}
+    out = {}
+    for dt in ("f16", "bf16"):
+        mu.mfma_ceiling(blocks, rounds, sink, dt)
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            flops = mu.mfma_ceiling(blocks, rounds, sink, dt)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        tflops = flops / (ms / 1e3) / 1e12
+        log(f"[bench] register-only MFMA ceiling ({dt}): {tflops:.0f} TFLOP/s ({ms:.2f} ms per launch)")
+        out[dt] = {"tflops": tflops, "frac_of_dense_peak": tflops / PEAK_16BIT_TFLOPS,
+                   "implied_clock_ghz": tflops * 1e3 / (cus * 4096.0), "ms_per_launch": ms}
+    out["blocks"] = blocks
+    out["note"] = ("v_mfma_f32_32x32x16 back to back on register operands with hashed values, no memory traffic; "
+                   "the power the operand data draw, not the nominal 2.4 GHz, sets the clock under this load")
+    return out
 
 
 def main():
@@ -559,11 +564,16 @@ def main():
                 for k, v in sorted(roles.items(), key=lambda kv: -kv[1]["ms"])}
 
     ceiling = mfma_ceiling(mu, dev)
-    if is_mfma:
-        roofline["practical_ceiling_tflops"] = ceiling["tflops"]
-        roofline["frac_of_practical_ceiling"] = achieved / ceiling["tflops"]
-    for v in results.values():
-        v["frac_of_practical_ceiling"] = v["tflops_algorithmic"] / ceiling["tflops"]
+    if is_mfma and not dom_name.endswith("f64acc"):
+        # gemm_nt_mfma<OP, ...>: OP 1 = bf16 operands, 2 = fp16
+        dom_dt = "bf16" if dom_name.startswith("gemm_nt_mfma<1") else "f16"
+        roofline["practical_ceiling_tflops"] = ceiling[dom_dt]["tflops"]
+        roofline["practical_ceiling_dtype"] = dom_dt
+        roofline["frac_of_practical_ceiling"] = achieved / ceiling[dom_dt]["tflops"]
+    for name, v in results.items():
+        dt = args.compute if args.compute in ("f16", "bf16") else ("f16" if name == "gram" else "bf16")
+        if dt in ceiling:
+            v["frac_of_practical_ceiling"] = v["tflops_algorithmic"] / ceiling[dt]["tflops"]
 
     low_bit = None if args.no_low_bit else time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev)
 

@@ -406,18 +406,20 @@ int muon_trace_collect(muon_trace_record *out, int max);
 /*
  * Practical 16-bit MFMA ceiling of the device, for profiling beside the
  * launch trace.  Launches `blocks` blocks of 256 threads on `stream`; every
- * wave issues 32 * rounds v_mfma_f32_32x32x16_f16 (32768 FLOPs each) on
- * register operands only, whose values come from a fixed hash so that they
- * switch like real data, and each thread finally stores one float to
- * sink[block * 256 + thread] (`sink`: device buffer of blocks * 256 floats,
- * owned by the caller; its contents are meaningless).  The caller times the
- * launch with events on the same stream: FLOPs = blocks * 4 * 32 * rounds *
- * 32768.  Under a full MFMA load the clock is set by the power limit, so this
- * rate, not the dense peak at the nominal clock, bounds what any GEMM reaches.
- * Returns MUON_ERR_INVALID_ARG for blocks outside [1, 2^20], rounds < 1 or a
- * NULL sink (nothing launched), MUON_ERR_HIP if the launch fails.
+ * wave issues 32 * rounds v_mfma_f32_32x32x16 instructions of operand type
+ * `dtype` (MUON_F16 or MUON_BF16; 32768 FLOPs each) on register operands
+ * only, whose values come from a fixed hash so that they switch like real
+ * data, and each thread finally stores one float to sink[block * 256 +
+ * thread] (`sink`: device buffer of blocks * 256 floats, owned by the
+ * caller; its contents are meaningless).  The caller times the launch with
+ * events on the same stream: FLOPs = blocks * 4 * 32 * rounds * 32768.
+ * Under a full MFMA load the clock is set by the power the data draw, so
+ * this rate, not the dense peak at the nominal clock, bounds what any GEMM of
+ * that operand type reaches.  Returns MUON_ERR_INVALID_ARG for blocks outside
+ * [1, 2^20], rounds < 1, another dtype or a NULL sink (nothing launched),
+ * MUON_ERR_HIP if the launch fails.
  */
-muon_status muon_mfma_ceiling(int blocks, int rounds, float *sink, void *stream);
+muon_status muon_mfma_ceiling(int blocks, int rounds, muon_dtype dtype, float *sink, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *muon_status_string(muon_status status);

@@ -88,7 +88,7 @@ def load_library():
     lib.muon_trace_enable.restype = i32
     lib.muon_trace_collect.argtypes = [ctypes.POINTER(TraceRecord), i32]
     lib.muon_trace_collect.restype = i32
-    lib.muon_mfma_ceiling.argtypes = [i32, i32, vp, vp]
+    lib.muon_mfma_ceiling.argtypes = [i32, i32, i32, vp, vp]
     lib.muon_mfma_ceiling.restype = i32
     lib.muon_abi_version.argtypes = []
     lib.muon_abi_version.restype = i32
@@ -411,13 +411,17 @@ def trace_enable(on: bool = True) -> bool:
     return bool(load_library().muon_trace_enable(1 if on else 0))
 
 
-def mfma_ceiling(blocks: int, rounds: int, sink: torch.Tensor, stream=None):
-    """Enqueue the register-only MFMA probe (muon_mfma_ceiling) on the stream;
-    ``sink`` is a float32 device tensor of at least blocks * 256 elements.
-    Returns the FLOPs the launch performs (time it with events)."""
+def mfma_ceiling(blocks: int, rounds: int, sink: torch.Tensor, dtype: str = "f16", stream=None):
+    """Enqueue the register-only MFMA probe (muon_mfma_ceiling) of operand
+    type ``dtype`` ("f16" or "bf16") on the stream; ``sink`` is a float32
+    device tensor of at least blocks * 256 elements.  Returns the FLOPs the
+    launch performs (time it with events)."""
     if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks * 256:
         raise ValueError("sink must be a float32 device tensor of at least blocks * 256 elements")
-    _check(load_library().muon_mfma_ceiling(blocks, rounds, ctypes.c_void_p(sink.data_ptr()),
+    codes = {"f16": F16, "bf16": BF16}
+    if dtype not in codes:
+        raise ValueError("dtype must be 'f16' or 'bf16'")
+    _check(load_library().muon_mfma_ceiling(blocks, rounds, codes[dtype], ctypes.c_void_p(sink.data_ptr()),
                                             ctypes.c_void_p(_stream(stream))))
     return float(blocks) * 4 * 32 * rounds * 32768.0
 

@@ -286,5 +286,6 @@ def test_implicit_workspace_per_stream_and_pinned_under_capture(monkeypatch):
 def test_mfma_ceiling_rejects_bad_arguments():
     """The ceiling probe checks its arguments before launching anything."""
     lib = mu.load_library()
-    for blocks, rounds, sink in ((0, 10, 1024), (1 << 21, 10, 1024), (4, 0, 1024), (4, 10, None)):
-        assert lib.muon_mfma_ceiling(blocks, rounds, sink, None) == 1  # MUON_ERR_INVALID_ARG
+    for blocks, rounds, dt, sink in ((0, 10, 2, 1024), (1 << 21, 10, 2, 1024), (4, 0, 1, 1024), (4, 10, 2, None),
+                                     (4, 10, 0, 1024), (4, 10, 7, 1024)):
+        assert lib.muon_mfma_ceiling(blocks, rounds, dt, sink, None) == 1  # MUON_ERR_INVALID_ARG
