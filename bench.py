@@ -54,6 +54,8 @@ def parse():
                          "256x512 comparison with the SVD polar factor")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the register-only MFMA ceiling probe (profiling runs)")
     ap.add_argument("--one-stream", action="store_true",
                     help="issue every group on one stream (default: one stream per group)")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "BENCH_JSON"),
@@ -563,8 +565,8 @@ def main():
     role_tab = {k: {"ms_per_step": v["ms"], "tflops": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["flops"] else None}
                 for k, v in sorted(roles.items(), key=lambda kv: -kv[1]["ms"])}
 
-    ceiling = mfma_ceiling(mu, dev)
-    if is_mfma and not dom_name.endswith("f64acc"):
+    ceiling = None if args.no_ceiling else mfma_ceiling(mu, dev)
+    if ceiling is not None and is_mfma and not dom_name.endswith("f64acc"):
         # gemm_nt_mfma<OP, ...>: OP 1 = bf16 operands, 2 = fp16
         dom_dt = "bf16" if dom_name.startswith("gemm_nt_mfma<1") else "f16"
         roofline["practical_ceiling_tflops"] = ceiling[dom_dt]["tflops"]
@@ -572,7 +574,7 @@ def main():
         roofline["frac_of_practical_ceiling"] = achieved / ceiling[dom_dt]["tflops"]
     for name, v in results.items():
         dt = args.compute if args.compute in ("f16", "bf16") else ("f16" if name == "gram" else "bf16")
-        if dt in ceiling:
+        if ceiling is not None and dt in ceiling:
             v["frac_of_practical_ceiling"] = v["tflops_algorithmic"] / ceiling[dt]["tflops"]
 
     low_bit = None if args.no_low_bit else time_low_bit_state(args, groups, wl, mu, syn, cfg_for, flops_for, dev)

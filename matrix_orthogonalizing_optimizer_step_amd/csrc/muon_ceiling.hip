@@ -36,7 +36,7 @@ __device__ __forceinline__ f32x16_t mfma(const V& a, const V& b, const f32x16_t&
 }
 
 template <typename V, typename E>
-__global__ __launch_bounds__(kCeilThreads) void mfma_ceiling_kernel(float* sink, int rounds) {
+__device__ __forceinline__ void mfma_ceiling_body(float* sink, int rounds) {
   V a[4], b[4];
   unsigned h = threadIdx.x * 2654435761u + blockIdx.x * 40503u + 12345u;
   for (int j = 0; j < 4; ++j)
@@ -59,6 +59,14 @@ __global__ __launch_bounds__(kCeilThreads) void mfma_ceiling_kernel(float* sink,
   sink[static_cast<size_t>(blockIdx.x) * kCeilThreads + threadIdx.x] = s;  // keeps the products live
 }
 
+__global__ __launch_bounds__(kCeilThreads) void mfma_ceiling_f16_kernel(float* sink, int rounds) {
+  mfma_ceiling_body<f16x8_t, _Float16>(sink, rounds);
+}
+
+__global__ __launch_bounds__(kCeilThreads) void mfma_ceiling_bf16_kernel(float* sink, int rounds) {
+  mfma_ceiling_body<bf16x8_t, __bf16>(sink, rounds);
+}
+
 }  // namespace
 
 extern "C" muon_status muon_mfma_ceiling(int blocks, int rounds, muon_dtype dtype, float* sink, void* stream) {
@@ -66,9 +74,9 @@ extern "C" muon_status muon_mfma_ceiling(int blocks, int rounds, muon_dtype dtyp
   if (dtype != MUON_F16 && dtype != MUON_BF16) return MUON_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MUON_F16) {
-    hipLaunchKernelGGL((mfma_ceiling_kernel<f16x8_t, _Float16>), dim3(blocks), dim3(kCeilThreads), 0, s, sink, rounds);
+    hipLaunchKernelGGL(mfma_ceiling_f16_kernel, dim3(blocks), dim3(kCeilThreads), 0, s, sink, rounds);
   } else {
-    hipLaunchKernelGGL((mfma_ceiling_kernel<bf16x8_t, __bf16>), dim3(blocks), dim3(kCeilThreads), 0, s, sink, rounds);
+    hipLaunchKernelGGL(mfma_ceiling_bf16_kernel, dim3(blocks), dim3(kCeilThreads), 0, s, sink, rounds);
   }
   return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
 }
